@@ -1,0 +1,396 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against brute force written independently in pure
+Python (element-wise mask predicates, explicit loops with math.exp), closed
+forms, a library special case (torch's scaled_dot_product_attention in float64)
+or figures printed on the pages (tests/golden/). No GPU is involved.
+"""
+import json
+import math
+import os
+import random
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BLK = 64
+
+
+# ---------------------------------------------------------------------------
+# independent brute force (pure Python)
+# ---------------------------------------------------------------------------
+def bf_attention(q, k, v, scale, allowed):
+    """Row-by-row softmax attention; allowed(i, j) is the full element mask."""
+    n, D = len(q), len(v[0])
+    out = []
+    for i in range(n):
+        js = [j for j in range(n) if allowed(i, j)]
+        if not js:
+            out.append([0.0] * D)
+            continue
+        lg = [scale * sum(q[i][t] * k[j][t] for t in range(len(q[i]))) for j in js]
+        m = max(lg)
+        e = [math.exp(x - m) for x in lg]
+        z = sum(e)
+        out.append([sum(e[u] / z * v[js[u]][t] for u in range(len(js))) for t in range(D)])
+    return np.array(out)
+
+
+def bf_vs_scores(q, k, lq, scale):
+    n = len(q)
+    vs = [0.0] * n
+    ss = [0.0] * n
+    for i in range(n - min(lq, n), n):
+        lg = [scale * sum(a * b for a, b in zip(q[i], k[j])) for j in range(i + 1)]
+        m = max(lg)
+        e = [math.exp(x - m) for x in lg]
+        z = sum(e)
+        for j in range(i + 1):
+            vs[j] += e[j] / z
+            ss[i - j] += e[j] / z
+    return np.array(vs), np.array(ss)
+
+
+def bf_topk(x, k, forced=()):
+    def key(a):
+        y = float(x[a])
+        if math.isnan(y):
+            return -math.inf
+        return 0.0 if y == 0.0 else y
+
+    n = len(x)
+    forced = set(int(f) for f in forced)
+
+    def before(b, a):  # does b rank strictly before a?
+        fb, fa = b in forced, a in forced
+        if fb != fa:
+            return fb
+        if key(b) != key(a):
+            return key(b) > key(a)
+        return b < a
+
+    return [a for a in range(n) if sum(before(b, a) for b in range(n)) < k]
+
+
+def vs_pred(V, S):
+    Vs = set(int(j) for j in V)
+
+    def allowed(i, j):
+        if j > i:
+            return False
+        if j in Vs:
+            return True
+        r0 = (i // BLK) * BLK
+        return any(r0 - d <= j < r0 + BLK - d for d in S)
+    return allowed
+
+
+def rnd(n, D, seed):
+    r = np.random.default_rng(seed)
+    return r.standard_normal((n, D)), r.standard_normal((n, D)), r.standard_normal((n, D))
+
+
+# ---------------------------------------------------------------------------
+# vertical-slash scores
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,lq", [(1, 64), (5, 3), (70, 64), (130, 64), (200, 17)])
+def test_vs_scores_bruteforce(n, lq):
+    q, k, _ = rnd(n, 6, n + lq)
+    q *= 2.0  # peakier softmax: a reversed diagonal would show
+    v, s = O.vs_scores(q, k, lq, 0.4)
+    bv, bs = bf_vs_scores(q.tolist(), k.tolist(), lq, 0.4)
+    np.testing.assert_allclose(v, bv, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(s, bs, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("n,lq", [(1, 64), (64, 64), (300, 64), (1000, 16)])
+def test_vs_scores_identical_keys_closed_form(n, lq):
+    """All keys equal: row i attends uniformly, p = 1/(i+1) on j <= i."""
+    r = np.random.default_rng(0)
+    q = r.standard_normal((n, 8))
+    k = np.tile(r.standard_normal((1, 8)), (n, 1))
+    v, s = O.vs_scores(q, k, lq, 0.3)
+    lqe = min(lq, n)
+    rows = range(n - lqe, n)
+    ev = np.array([sum(1.0 / (i + 1) for i in rows if i >= j) for j in range(n)])
+    es = np.array([sum(1.0 / (i + 1) for i in rows if i >= d) for d in range(n)])
+    np.testing.assert_allclose(v, ev, rtol=1e-12)
+    np.testing.assert_allclose(s, es, rtol=1e-12)
+
+
+def test_vs_scores_mass():
+    """Each window row is a probability distribution: sum v = sum s = lq."""
+    q, k, _ = rnd(3000, 32, 7)
+    v, s = O.vs_scores(q * 3, k, 64, 1 / math.sqrt(32))
+    assert abs(v.sum() - 64) < 1e-9 and abs(s.sum() - 64) < 1e-9
+    assert (v >= 0).all() and (s >= 0).all()
+
+
+def test_window_worked_example():
+    """Novita §2 q start/end restriction: prompt 5000, window 256 -> only
+    5000*256 query-key products, not 5000*5000."""
+    g = json.load(open(os.path.join(GOLDEN, "novita_window_example.json")))
+    n, win = g["prompt_len"], g["window"]
+    assert n * win == g["ops_window"] and n * n == g["ops_full"]
+    q, k, _ = rnd(n, 4, 3)
+    v, s = O.vs_scores(q, k, win, 0.5)
+    q2 = q.copy()
+    q2[: n - win] += 5.0          # rows before the window do not matter
+    v2, s2 = O.vs_scores(q2, k, win, 0.5)
+    assert np.array_equal(v, v2) and np.array_equal(s, s2)
+    q3 = q.copy()
+    q3[n - win] += 5.0            # the first window row does
+    v3, _ = O.vs_scores(q3, k, win, 0.5)
+    assert not np.array_equal(v, v3)
+    k2 = k.copy()
+    k2[0] += 5.0                  # and every key does
+    v4, _ = O.vs_scores(q, k2, win, 0.5)
+    assert not np.array_equal(v, v4)
+
+
+# ---------------------------------------------------------------------------
+# top-k
+# ---------------------------------------------------------------------------
+def test_topk_bruteforce_random():
+    rng = random.Random(5)
+    pool = [0.0, -0.0, 1.0, -1.0, 2.5, float("nan"), float("inf"), -float("inf"), 1e-30]
+    for trial in range(300):
+        n = rng.randint(1, 24)
+        x = np.array([rng.choice(pool) if rng.random() < 0.5 else rng.uniform(-3, 3)
+                      for _ in range(n)], dtype=np.float32)
+        k = rng.randint(0, n + 2)
+        forced = rng.sample(range(n), rng.randint(0, min(2, n)))
+        got = O.topk_indices(x, k, forced).tolist()
+        assert got == bf_topk(x, k, forced), (x, k, forced)
+
+
+def test_topk_ties_lowest_index():
+    assert O.topk_indices(np.zeros(10, np.float32), 4).tolist() == [0, 1, 2, 3]
+    x = np.array([1, 5, 5, 0, 5, 5], np.float32)
+    assert O.topk_indices(x, 3).tolist() == [1, 2, 4]
+    assert O.topk_indices(x, 3, forced=[3]).tolist() == [1, 2, 3]
+    assert O.topk_indices(x, 100).tolist() == list(range(6))
+
+
+# ---------------------------------------------------------------------------
+# vertical-slash sparse format
+# ---------------------------------------------------------------------------
+def test_merge_offsets_cases():
+    assert O.merge_offsets([300, 0, 64, 129]) == [(0, 64), (129, 129), (300, 300)]
+    assert O.merge_offsets([0, 65]) == [(0, 0), (65, 65)]
+    assert O.merge_offsets(list(range(0, 1000, 64))) == [(0, 960)]
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 200, 257, 390])
+def test_vs_mask_bruteforce(n):
+    rng = random.Random(n)
+    for trial in range(6):
+        V = rng.sample(range(n), rng.randint(0, min(n, 12)))
+        S = sorted(set([0] + rng.sample(range(n), rng.randint(0, min(n, 10)))))
+        iv = O.merge_offsets(S)
+        pred = vs_pred(V, S)
+        for a in range(O.num_blocks(n)):
+            keys = set(O.vs_block_keys(iv, V, a, n).tolist())
+            for i in range(a * BLK, min(n, (a + 1) * BLK)):
+                got = {j for j in keys if j <= i}
+                want = {j for j in range(n) if pred(i, j)}
+                assert got == want, (n, a, i, V, S)
+        # canonical form: ranges disjoint and non-adjacent; the column list is
+        # exactly the verticals the block's last row may see that no offset
+        # rectangle covers, ascending
+        for a in range(O.num_blocks(n)):
+            rg = sorted(O.vs_block_ranges(iv, a, n))
+            for (l0, h0), (l1, h1) in zip(rg, rg[1:]):
+                assert h0 < l1
+            cols = O.vs_block_cols(V, rg, a, n)
+            last = min(n, (a + 1) * BLK) - 1
+            r0 = a * BLK
+            want = sorted(j for j in set(V) if j <= last and
+                          not any(r0 - d <= j < r0 + BLK - d for d in S))
+            assert cols.tolist() == want
+
+
+def test_vs_all_offsets_is_one_range():
+    n = 300
+    iv = O.merge_offsets(range(n))
+    assert iv == [(0, n - 1)]
+    for a in range(O.num_blocks(n)):
+        assert O.vs_block_ranges(iv, a, n) == [(0, min(n, a * BLK + BLK))]
+
+
+def test_vs_planted_col_inside_range_removed():
+    n = 512
+    iv = O.merge_offsets([0])
+    # block 3 covers keys [192, 256) through offset 0; verticals 10 and 200
+    rg = O.vs_block_ranges(iv, 3, n)
+    assert rg == [(192, 256)]
+    assert O.vs_block_cols([10, 200, 300], rg, 3, n).tolist() == [10]
+
+
+# ---------------------------------------------------------------------------
+# block-sparse estimate
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [64, 100, 257])
+def test_pool_closed_form(n):
+    x = np.tile(np.arange(n, dtype=np.float64)[:, None], (1, 4))
+    p = O.mean_pool(x)
+    for a in range(O.num_blocks(n)):
+        last = min(n, (a + 1) * BLK) - 1
+        assert np.allclose(p[a], (a * BLK + last) / 2.0)
+
+
+@pytest.mark.parametrize("n,topk", [(64 * 7 + 5, 3), (64 * 5, 1), (64 * 4, 9)])
+def test_block_select_bruteforce(n, topk):
+    q, k, _ = rnd(n, 8, n)
+    L = O.to_f32(O.block_logits(O.mean_pool(q), O.mean_pool(k), 0.7))
+    sel = O.block_select(L, topk)
+    nb = O.num_blocks(n)
+    ql, kl = q.tolist(), k.tolist()
+    for a in range(nb):
+        qa = [sum(ql[i][t] for i in range(a * BLK, min(n, a * BLK + BLK))) /
+              (min(n, a * BLK + BLK) - a * BLK) for t in range(8)]
+        row = []
+        for c in range(a + 1):
+            kc = [sum(kl[i][t] for i in range(c * BLK, min(n, c * BLK + BLK))) /
+                  (min(n, c * BLK + BLK) - c * BLK) for t in range(8)]
+            row.append(np.float32(0.7 * sum(x * y for x, y in zip(qa, kc))))
+        assert abs(float(L[a, a]) - float(row[a])) <= 1e-6 * (1 + abs(float(row[a])))
+        assert sel[a].tolist() == bf_topk(np.array(row, np.float32), topk, [a])
+        assert a in sel[a].tolist()
+
+
+def test_block_select_finds_planted_clusters():
+    w = synthetic.BY_NAME["bs_mha4_32k_bf16"].scaled(seq_len=4096)
+    x = synthetic.make_inputs(w)
+    for h in range(w.q_heads):
+        res = O.bs_head(x.q[0, h], x.k[0, h], x.v[0, h], topk=8, blocks=[])
+        for kb, qbs in x.planted[(0, h)]:
+            for qa in qbs:
+                assert kb in res["sel"][qa].tolist(), (h, kb, qa)
+
+
+# ---------------------------------------------------------------------------
+# streaming mask
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("init,local", [(0, 1), (1, 1), (1, 3), (2, 2), (5, 1)])
+def test_streaming_bruteforce(init, local):
+    n = 64 * 6 + 11
+    for a in range(O.num_blocks(n)):
+        keys = set(O.blocks_to_keys(O.streaming_blocks(a, init, local), n).tolist())
+        for i in range(a * BLK, min(n, a * BLK + BLK)):
+            want = {j for j in range(n)
+                    if j <= i and (j // BLK < init or i // BLK - j // BLK < local)}
+            assert {j for j in keys if j <= i} == want
+
+
+# ---------------------------------------------------------------------------
+# attention under the mask
+# ---------------------------------------------------------------------------
+def test_attention_bruteforce_all_patterns():
+    n, D = 64 * 3 + 9, 4
+    q, k, v = rnd(n, D, 11)
+    q *= 2
+    sc = 0.5
+    ql, kl, vl = q.tolist(), k.tolist(), v.tolist()
+    # vertical-slash with fixed indices
+    V, S = [3, 70, 150], [0, 40, 130]
+    iv = O.merge_offsets(S)
+    out = O._attend_blocks(q, k, v, sc, lambda a: O.vs_block_keys(iv, V, a, n))
+    want = bf_attention(ql, kl, vl, sc, vs_pred(V, S))
+    np.testing.assert_allclose(O.assemble(out, n, D), want, rtol=1e-10, atol=1e-12)
+    # block-sparse with the oracle's own selection
+    res = O.bs_head(q, k, v, topk=2, scale=sc)
+    sel = res["sel"]
+    want = bf_attention(ql, kl, vl, sc,
+                        lambda i, j: j <= i and (j // BLK) in sel[i // BLK].tolist())
+    np.testing.assert_allclose(O.assemble(res["out"], n, D), want, rtol=1e-10, atol=1e-12)
+    # streaming
+    res = O.streaming_head(q, k, v, 1, 2, scale=sc)
+    want = bf_attention(ql, kl, vl, sc,
+                        lambda i, j: j <= i and (j // BLK < 1 or i // BLK - j // BLK < 2))
+    np.testing.assert_allclose(O.assemble(res["out"], n, D), want, rtol=1e-10, atol=1e-12)
+
+
+def _sdpa(q, k, v):
+    Hq, Hkv = q.shape[1], k.shape[1]
+    kk = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=1)
+    vv = torch.from_numpy(v).repeat_interleave(Hq // Hkv, dim=1)
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), kk, vv, is_causal=True).numpy()
+
+
+@pytest.mark.parametrize("n", [100, 64 * 4])
+def test_full_selection_equals_dense_causal(n):
+    """Full selection in any pattern is dense causal attention (library case,
+    with the GQA map of consecutive query heads per kv head)."""
+    r = np.random.default_rng(n)
+    B, Hq, Hkv, D = 2, 4, 2, 16
+    q = r.standard_normal((B, Hq, n, D)) * 2
+    k = r.standard_normal((B, Hkv, n, D))
+    v = r.standard_normal((B, Hkv, n, D))
+    ref = _sdpa(q, k, v)
+    nb = O.num_blocks(n)
+    for o in (O.vertical_slash_sparse_attention(q, k, v, n, 1),
+              O.vertical_slash_sparse_attention(q, k, v, 0, n),
+              O.block_sparse_attention(q, k, v, nb),
+              O.streaming_attention(q, k, v, 1, nb - 1),
+              O.streaming_attention(q, k, v, nb, 1)):
+        np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_large_logits_stay_finite():
+    """Logits in the thousands: the softmax must not overflow; in the limit each
+    row returns the value of its best allowed key."""
+    n, D = 130, 8
+    r = np.random.default_rng(4)
+    q, k, v = r.standard_normal((n, D)) * 300, r.standard_normal((n, D)), r.standard_normal((n, D))
+    res = O.streaming_head(q, k, v, 1, 1, scale=1.0)
+    o = O.assemble(res["out"], n, D)
+    assert np.isfinite(o).all()
+    for i in (5, 70, 129):
+        js = [j for j in range(n) if j <= i and (j // BLK < 1 or i // BLK == j // BLK)]
+        best = max(js, key=lambda j: float(q[i] @ k[j]))
+        assert np.allclose(o[i], v[best], atol=1e-6)
+    vv, ss = O.vs_scores(q, k, 64, 1.0)
+    assert np.isfinite(vv).all() and abs(vv.sum() - 64) < 1e-9
+
+
+def test_attention_closed_forms():
+    n, D = 150, 8
+    r = np.random.default_rng(1)
+    q, k, v = r.standard_normal((n, D)), r.standard_normal((n, D)), r.standard_normal((n, D))
+    V, S = [5, 90], [0, 70]
+    iv = O.merge_offsets(S)
+    keys = lambda a: O.vs_block_keys(iv, V, a, n)  # noqa: E731
+    o = O.assemble(O._attend_blocks(q, k, v, 0.3, keys), n, D)
+    assert np.allclose(o[0], v[0])                       # row 0 sees only key 0
+    o0 = O.assemble(O._attend_blocks(np.zeros_like(q), k, v, 0.3, keys), n, D)
+    pred = vs_pred(V, S)
+    for i in (0, 64, 100, 149):                          # Q = 0: plain mean
+        js = [j for j in range(n) if pred(i, j)]
+        assert np.allclose(o0[i], v[js].mean(axis=0))
+    oc = O.assemble(O._attend_blocks(q, k, np.ones_like(v) * 3.5, 0.3, keys), n, D)
+    assert np.allclose(oc, 3.5)                          # constant V
+    # one-hot V recovers the probabilities: support = mask, rows sum to 1
+    n2 = 96
+    q2, k2 = r.standard_normal((n2, n2)), r.standard_normal((n2, n2))
+    iv2 = O.merge_offsets([0, 80])
+    P = O.assemble(O._attend_blocks(q2, k2, np.eye(n2), 0.1,
+                                    lambda a: O.vs_block_keys(iv2, [7], a, n2)), n2, n2)
+    pred2 = vs_pred([7], [0, 80])
+    for i in range(n2):
+        assert abs(P[i].sum() - 1) < 1e-12
+        assert set(np.nonzero(P[i])[0].tolist()) == {j for j in range(n2) if pred2(i, j)}
+
+
+def test_vs_structure_selects_sink():
+    w = synthetic.BY_NAME["vs_head_4k_f32"].scaled(seq_len=2048)
+    x = synthetic.make_inputs(w)
+    res = O.vs_head(x.q[0, 0], x.k[0, 0], x.v[0, 0], 64, 64, blocks=[])
+    assert 0 in res["V"].tolist() and 0 in res["S"].tolist()
+    assert abs(float(res["v"].astype(np.float64).sum()) - 64) < 1e-3
