@@ -1,0 +1,24 @@
+"""Dynamic sparse attention for the long-context prefill phase on MI355X.
+
+Vertical-slash, block-sparse and streaming (A-shape) heads, each as online
+sparse-index estimation followed by exact block-sparse attention, all in HIP
+kernels for gfx950 behind a C ABI (include/dsa.h). This package is the thin
+Python binding of that library; torch supplies device memory and streams.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    DsaError,
+    block_sparse_attention,
+    block_sparse_workspace_bytes,
+    bs_pool,
+    bs_select,
+    load,
+    sparse_attention_blocks,
+    sparse_attention_vs,
+    streaming_attention,
+    topk,
+    vertical_slash_sparse_attention,
+    vertical_slash_workspace_bytes,
+    vs_build_index,
+    vs_estimate,
+)

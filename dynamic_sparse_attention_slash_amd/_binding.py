@@ -1,0 +1,311 @@
+"""ctypes binding of libdsa.so (include/dsa.h).
+
+Argument marshalling only: tensors are checked for device, dtype and layout,
+turned into raw pointers, and handed to the library together with torch's
+current HIP stream. Every step of the computation runs in the library's
+kernels. When the library is missing, import succeeds but every call raises
+``RuntimeError``: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdsa.so")
+BLOCK = 64
+MAX_HEADS = 256
+
+BF16, F32 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
+
+_lib: Optional[ctypes.CDLL] = None
+_load_error: Optional[str] = None
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {_STATUS.get(code, code)} (status {code})")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_ip = ctypes.POINTER(ctypes.c_int32)
+_SIGS = {
+    "dsa_status_string": ([_i32], ctypes.c_char_p),
+    "dsa_vertical_slash_sparse_attention": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _i32, _i32, _i32, _f32, _ip, _i32, _vp, _sz, _vp], _i32),
+    "dsa_vertical_slash_workspace_bytes": ([ctypes.POINTER(Shape), _i32, _i32, _i32], _sz),
+    "dsa_block_sparse_attention": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _i32, _f32, _ip, _i32, _vp, _sz, _vp], _i32),
+    "dsa_block_sparse_workspace_bytes": ([ctypes.POINTER(Shape), _i32, _i32], _sz),
+    "dsa_streaming_attention": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _i32, _i32, _f32, _ip, _i32, _vp], _i32),
+    "dsa_vs_estimate": ([_vp, _vp, ctypes.POINTER(Shape), _i32, _f32, _ip, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "dsa_vs_estimate_workspace_bytes": ([ctypes.POINTER(Shape), _i32], _sz),
+    "dsa_topk": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
+    "dsa_vs_build_index": ([_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
+    "dsa_bs_pool": ([_vp, _i32, _i32, _i32, _i32, _i32, _ip, _i32, _vp, _vp], _i32),
+    "dsa_bs_select": ([_vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "dsa_bs_select_workspace_bytes": ([_i32, _i32], _sz),
+    "dsa_sparse_attention_vs": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _f32, _ip, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp], _i32),
+    "dsa_sparse_attention_blocks": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _f32, _ip, _i32, _vp, _vp, _i32, _vp], _i32),
+}
+EXPORTED = tuple(_SIGS)
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdsa.so (once) and attach the C signatures."""
+    global _lib, _load_error
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        _load_error = f"{path} is not built (run dynamic_sparse_attention_slash_amd.build)"
+        raise RuntimeError(_load_error)
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _call(name: str, *args) -> None:
+    code = getattr(load(), name)(*args)
+    if code != 0:
+        raise DsaError(name, code)
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _shape_qkv(q, k, v) -> Shape:
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [batch, heads, seq_len, head_dim]")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2:] != k.shape[2:]:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, Hq, n, D = q.shape
+    return Shape(B, Hq, k.shape[1], n, D, _dtype_code(q))
+
+
+def _heads(heads: Optional[Sequence[int]]) -> Tuple[Optional[ctypes.Array], int]:
+    if heads is None:
+        return None, 0
+    arr = (ctypes.c_int32 * max(1, len(heads)))(*[int(h) for h in heads])
+    return arr, len(heads)
+
+
+def _scale(scale: Optional[float]) -> float:
+    return 0.0 if scale is None else float(scale)
+
+
+def _workspace(nbytes: int, device, given: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A caller-supplied uint8 workspace when it is large enough, else a new one."""
+    if given is not None:
+        if given.dtype != torch.uint8 or not given.is_cuda or given.numel() < nbytes:
+            raise ValueError(f"workspace must be a uint8 GPU tensor of >= {nbytes} bytes")
+        return given
+    return torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=device)
+
+
+def vertical_slash_workspace_bytes(q, k, vertical_topk: int, slash_topk: int,
+                                   heads: Optional[Sequence[int]] = None) -> int:
+    sh = Shape(q.shape[0], q.shape[1], k.shape[1], q.shape[2], q.shape[3], _dtype_code(q))
+    nh = sh.q_heads if heads is None else len(heads)
+    return int(load().dsa_vertical_slash_workspace_bytes(ctypes.byref(sh), vertical_topk, slash_topk, nh))
+
+
+def block_sparse_workspace_bytes(q, k, topk: int, heads: Optional[Sequence[int]] = None) -> int:
+    sh = Shape(q.shape[0], q.shape[1], k.shape[1], q.shape[2], q.shape[3], _dtype_code(q))
+    nh = sh.q_heads if heads is None else len(heads)
+    return int(load().dsa_block_sparse_workspace_bytes(ctypes.byref(sh), topk, nh))
+
+
+def _out_like(q: torch.Tensor, out: Optional[torch.Tensor]) -> torch.Tensor:
+    if out is None:
+        return torch.zeros_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must match q")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# the three calls of the kernel-only API
+# ----------------------------------------------------------------------------
+def vertical_slash_sparse_attention(q, k, v, vertical_topk: int, slash_topk: int, *,
+                                    last_q: int = 64, scale: Optional[float] = None,
+                                    heads: Optional[Sequence[int]] = None,
+                                    out: Optional[torch.Tensor] = None,
+                                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    sh = _shape_qkv(q, k, v)
+    o = _out_like(q, out)
+    ha, hn = _heads(heads)
+    nh = sh.q_heads if heads is None else hn
+    ws = _workspace(load().dsa_vertical_slash_workspace_bytes(ctypes.byref(sh), vertical_topk,
+                                                              slash_topk, nh), q.device, workspace)
+    _call("dsa_vertical_slash_sparse_attention", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+          _dev(o, "out"), ctypes.byref(sh), vertical_topk, slash_topk, last_q, _scale(scale),
+          ha, hn, ws.data_ptr(), ws.numel(), _stream(q))
+    return o
+
+
+def block_sparse_attention(q, k, v, topk: int, *, scale: Optional[float] = None,
+                           heads: Optional[Sequence[int]] = None,
+                           out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    sh = _shape_qkv(q, k, v)
+    o = _out_like(q, out)
+    ha, hn = _heads(heads)
+    nh = sh.q_heads if heads is None else hn
+    ws = _workspace(load().dsa_block_sparse_workspace_bytes(ctypes.byref(sh), topk, nh), q.device,
+                    workspace)
+    _call("dsa_block_sparse_attention", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
+          ctypes.byref(sh), topk, _scale(scale), ha, hn, ws.data_ptr(), ws.numel(), _stream(q))
+    return o
+
+
+def streaming_attention(q, k, v, init_blocks: int, local_blocks: int, *,
+                        scale: Optional[float] = None, heads: Optional[Sequence[int]] = None,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    sh = _shape_qkv(q, k, v)
+    o = _out_like(q, out)
+    ha, hn = _heads(heads)
+    _call("dsa_streaming_attention", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
+          ctypes.byref(sh), init_blocks, local_blocks, _scale(scale), ha, hn, _stream(q))
+    return o
+
+
+# ----------------------------------------------------------------------------
+# stage calls
+# ----------------------------------------------------------------------------
+def vs_estimate(q, k, *, last_q: int = 64, scale: Optional[float] = None,
+                heads: Optional[Sequence[int]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Vertical and slash scores, fp32 [batch * n_heads, seq_len] each."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k must be [batch, heads, seq_len, head_dim]")
+    B, Hq, n, D = q.shape
+    sh = Shape(B, Hq, k.shape[1], n, D, _dtype_code(q))
+    ha, hn = _heads(heads)
+    nh = Hq if heads is None else hn
+    rows = B * nh
+    vsc = torch.empty((rows, n), dtype=torch.float32, device=q.device)
+    ssc = torch.empty((rows, n), dtype=torch.float32, device=q.device)
+    ws = _workspace(load().dsa_vs_estimate_workspace_bytes(ctypes.byref(sh), nh), q.device)
+    _call("dsa_vs_estimate", _dev(q, "q"), _dev(k, "k", q.dtype), ctypes.byref(sh), last_q,
+          _scale(scale), ha, hn, vsc.data_ptr(), ssc.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q))
+    return vsc, ssc
+
+
+def topk(scores: torch.Tensor, k: int, forced_index: int = -1) -> torch.Tensor:
+    """Row-wise top-k of fp32 [rows, n] -> int32 [rows, min(k, n)], ascending."""
+    rows, n = scores.shape
+    kk = min(k, n)
+    out = torch.empty((rows, kk), dtype=torch.int32, device=scores.device)
+    _call("dsa_topk", _dev(scores, "scores", torch.float32), rows, n, k, forced_index,
+          out.data_ptr(), _stream(scores))
+    return out
+
+
+def vs_build_index(V: torch.Tensor, S: torch.Tensor, seq_len: int):
+    """(intervals [rows, ns, 2], n_intervals [rows], cols [rows, nb, nv], n_cols [rows, nb])."""
+    rows, nv = V.shape
+    ns = S.shape[1]
+    nb = (seq_len + BLOCK - 1) // BLOCK
+    dev = V.device
+    iv = torch.zeros((rows, ns, 2), dtype=torch.int32, device=dev)
+    n_iv = torch.zeros((rows,), dtype=torch.int32, device=dev)
+    cols = torch.zeros((rows, nb, nv), dtype=torch.int32, device=dev)
+    n_cols = torch.zeros((rows, nb), dtype=torch.int32, device=dev)
+    _call("dsa_vs_build_index", _dev(V, "V", torch.int32), nv, _dev(S, "S", torch.int32), ns, rows,
+          seq_len, iv.data_ptr(), n_iv.data_ptr(), cols.data_ptr(), n_cols.data_ptr(), _stream(V))
+    return iv, n_iv, cols, n_cols
+
+
+def bs_pool(x: torch.Tensor, heads: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """Block means of x [B, H, n, D] -> fp32 [B * n_heads, nb, D]."""
+    B, H, n, D = x.shape
+    ha, hn = _heads(heads)
+    rows = B * (H if heads is None else hn)
+    nb = (n + BLOCK - 1) // BLOCK
+    out = torch.empty((rows, nb, D), dtype=torch.float32, device=x.device)
+    _call("dsa_bs_pool", _dev(x, "x"), _dtype_code(x), B, H, n, D, ha, hn, out.data_ptr(), _stream(x))
+    return out
+
+
+def bs_select(qp: torch.Tensor, kp: torch.Tensor, topk: int, *, scale: Optional[float] = None,
+              return_logits: bool = False):
+    """(sel [rows, nb, min(topk, nb)], n_sel [rows, nb][, logits [rows, nb, nb]])."""
+    rows, nb, D = qp.shape
+    if kp.shape != qp.shape:
+        raise ValueError("qp and kp must have equal shapes")
+    ke = min(topk, nb)
+    sel = torch.zeros((rows, nb, ke), dtype=torch.int32, device=qp.device)
+    n_sel = torch.zeros((rows, nb), dtype=torch.int32, device=qp.device)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if return_logits:
+        lg = torch.full((rows, nb, nb), float("nan"), dtype=torch.float32, device=qp.device)
+        _call("dsa_bs_select", _dev(qp, "qp", torch.float32), _dev(kp, "kp", torch.float32), rows, nb, D,
+              sc, topk, sel.data_ptr(), n_sel.data_ptr(), lg.data_ptr(), None, 0, _stream(qp))
+        return sel, n_sel, lg
+    ws = _workspace(load().dsa_bs_select_workspace_bytes(rows, nb), qp.device)
+    _call("dsa_bs_select", _dev(qp, "qp", torch.float32), _dev(kp, "kp", torch.float32), rows, nb, D,
+          sc, topk, sel.data_ptr(), n_sel.data_ptr(), None, ws.data_ptr(), ws.numel(), _stream(qp))
+    return sel, n_sel
+
+
+def sparse_attention_vs(q, k, v, intervals, n_intervals, cols, n_cols, *,
+                        scale: Optional[float] = None, heads: Optional[Sequence[int]] = None,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    sh = _shape_qkv(q, k, v)
+    o = _out_like(q, out)
+    ha, hn = _heads(heads)
+    _call("dsa_sparse_attention_vs", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
+          ctypes.byref(sh), _scale(scale), ha, hn, _dev(intervals, "intervals", torch.int32),
+          _dev(n_intervals, "n_intervals", torch.int32), intervals.shape[1],
+          _dev(cols, "cols", torch.int32), _dev(n_cols, "n_cols", torch.int32), cols.shape[2],
+          _stream(q))
+    return o
+
+
+def sparse_attention_blocks(q, k, v, sel, n_sel, *, scale: Optional[float] = None,
+                            heads: Optional[Sequence[int]] = None,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    sh = _shape_qkv(q, k, v)
+    o = _out_like(q, out)
+    ha, hn = _heads(heads)
+    _call("dsa_sparse_attention_blocks", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
+          ctypes.byref(sh), _scale(scale), ha, hn, _dev(sel, "sel", torch.int32),
+          _dev(n_sel, "n_sel", torch.int32), sel.shape[2], _stream(q))
+    return o

@@ -1,0 +1,389 @@
+// C ABI of the library (include/dsa.h): host-side argument checks, workspace
+// layout and kernel dispatch. Every argument error is reported before any
+// work is enqueued; nothing here synchronises the stream or allocates.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/dsa.h"
+#include "kernels.hpp"
+
+using namespace dsa;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr size_t LOGITS_BUDGET = (size_t)1 << 30;  // block-logit scratch per launch group
+
+size_t al(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
+
+struct Carver {
+  char* p;
+  size_t used = 0;
+  template <typename T>
+  T* take(size_t count) {
+    T* r = reinterpret_cast<T*>(p + used);
+    used += al(count * sizeof(T));
+    return r;
+  }
+};
+
+dsa_status check_shape(const dsa_shape* s) {
+  if (!s) return DSA_ERR_INVALID_ARG;
+  if (s->batch < 0 || s->q_heads <= 0 || s->kv_heads <= 0 || s->seq_len < 0)
+    return DSA_ERR_INVALID_ARG;
+  if (s->q_heads % s->kv_heads != 0) return DSA_ERR_INVALID_ARG;
+  if (s->head_dim != 64 && s->head_dim != 128) return DSA_ERR_UNSUPPORTED;
+  if (s->dtype != DSA_BF16 && s->dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+// Head list -> HeadMap over a tensor with `heads_total` heads.
+dsa_status make_map(int32_t heads_total, int32_t kv_heads, const int32_t* heads, int32_t n_heads,
+                    HeadMap& hm) {
+  memset(&hm, 0, sizeof(hm));
+  hm.q_heads = heads_total;
+  hm.kv_heads = kv_heads;
+  if (!heads) {
+    if (heads_total > MAX_HEADS) return DSA_ERR_UNSUPPORTED;
+    hm.n = heads_total;
+    for (int32_t i = 0; i < heads_total; ++i) hm.h[i] = i;
+    return DSA_OK;
+  }
+  if (n_heads < 0) return DSA_ERR_INVALID_ARG;
+  if (n_heads > MAX_HEADS) return DSA_ERR_UNSUPPORTED;
+  hm.n = n_heads;
+  for (int32_t i = 0; i < n_heads; ++i) {
+    if (heads[i] < 0 || heads[i] >= heads_total) return DSA_ERR_INVALID_ARG;
+    for (int32_t j = 0; j < i; ++j)
+      if (heads[j] == heads[i]) return DSA_ERR_INVALID_ARG;
+    hm.h[i] = heads[i];
+  }
+  return DSA_OK;
+}
+
+float eff_scale(float scale, int32_t head_dim) {
+  return scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
+}
+
+int32_t nblocks(int32_t n) { return (n + BLOCK - 1) / BLOCK; }
+
+dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, const dsa_shape* s,
+                   float scale, const HeadMap& hm) {
+  AttnArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.seq_len = s->seq_len;
+  a.head_dim = s->head_dim;
+  a.dtype = s->dtype;
+  a.rows = s->batch * hm.n;
+  a.scale_log2 = eff_scale(scale, s->head_dim) * LOG2E;
+  a.hm = hm;
+  return a;
+}
+
+// ---- vertical-slash workspace layout ----
+struct VsWork {
+  void* est; float* v; float* s; int32_t* V; int32_t* S; int32_t* iv; int32_t* n_iv;
+  int32_t* cols; int32_t* n_cols;
+};
+size_t vs_layout(int32_t rows, int32_t n, int32_t vk, int32_t sk, void* base, VsWork* w) {
+  Carver c{static_cast<char*>(base)};
+  const int32_t nb = nblocks(n);
+  void* est = c.take<char>(est_workspace_bytes(rows, n));
+  float* v = c.take<float>((size_t)rows * n);
+  float* s = c.take<float>((size_t)rows * n);
+  int32_t* V = c.take<int32_t>((size_t)rows * vk);
+  int32_t* S = c.take<int32_t>((size_t)rows * sk);
+  int32_t* iv = c.take<int32_t>((size_t)rows * sk * 2);
+  int32_t* n_iv = c.take<int32_t>((size_t)rows);
+  int32_t* cols = c.take<int32_t>((size_t)rows * nb * vk);
+  int32_t* n_cols = c.take<int32_t>((size_t)rows * nb);
+  if (w) *w = VsWork{est, v, s, V, S, iv, n_iv, cols, n_cols};
+  return c.used;
+}
+
+// ---- block-sparse workspace layout ----
+int32_t logit_rows_per_group(int32_t rows, int32_t nb) {
+  const size_t per_row = (size_t)nb * nb * sizeof(float);
+  size_t g = per_row ? LOGITS_BUDGET / per_row : (size_t)rows;
+  if (g < 1) g = 1;
+  if (g > (size_t)rows) g = (size_t)rows;
+  return (int32_t)g;
+}
+struct BsWork { float* qp; float* kp; float* logits; int32_t* sel; int32_t* n_sel; };
+size_t bs_layout(const dsa_shape* s, int32_t rows, int32_t topk, void* base, BsWork* w) {
+  Carver c{static_cast<char*>(base)};
+  const int32_t nb = nblocks(s->seq_len), D = s->head_dim;
+  const int32_t ke = topk < nb ? topk : nb;
+  float* qp = c.take<float>((size_t)rows * nb * D);
+  float* kp = c.take<float>((size_t)s->batch * s->kv_heads * nb * D);
+  float* lg = c.take<float>((size_t)(rows ? logit_rows_per_group(rows, nb) : 0) * nb * nb);
+  int32_t* sel = c.take<int32_t>((size_t)rows * nb * ke);
+  int32_t* n_sel = c.take<int32_t>((size_t)rows * nb);
+  if (w) *w = BsWork{qp, kp, lg, sel, n_sel};
+  return c.used;
+}
+
+// block logits + per-block top-k, in groups of rows bounded by the scratch size
+hipError_t bs_select_rows(const float* qp, const float* kp, int32_t rows, int32_t nb, int32_t D,
+                          float scale, int32_t topk, bool kv_map, const HeadMap& hm,
+                          float* logits, bool logits_full, int32_t* sel, int32_t* n_sel,
+                          hipStream_t st) {
+  const int32_t ke = topk < nb ? topk : nb;
+  const int32_t grp = logits_full ? rows : logit_rows_per_group(rows, nb);
+  for (int32_t r0 = 0; r0 < rows; r0 += grp) {
+    const int32_t nr = rows - r0 < grp ? rows - r0 : grp;
+    float* lg = logits_full ? logits + (size_t)r0 * nb * nb : logits;
+    const float* kpr = kv_map ? kp : kp + (size_t)r0 * nb * D;
+    hipError_t e = launch_block_logits(qp + (size_t)r0 * nb * D, kpr, r0, nr, nb, D, scale,
+                                       kv_map, hm, lg, st);
+    if (e != hipSuccess) return e;
+    e = launch_block_topk(lg, nr, nb, topk, sel + (size_t)r0 * nb * ke, n_sel + (size_t)r0 * nb, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape, dtype or parameter";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+// ------------------------------------------------------------------ VS
+size_t dsa_vs_estimate_workspace_bytes(const dsa_shape* shape, int32_t n_heads) {
+  if (check_shape(shape) != DSA_OK || n_heads < 0) return 0;
+  return est_workspace_bytes(shape->batch * n_heads, shape->seq_len);
+}
+
+dsa_status dsa_vs_estimate(const void* q, const void* k, const dsa_shape* shape, int32_t last_q,
+                           float scale, const int32_t* heads, int32_t n_heads, float* v_scores,
+                           float* s_scores, void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v_scores || !s_scores) return DSA_ERR_INVALID_ARG;
+  if (last_q < 1 || last_q > 64) return DSA_ERR_UNSUPPORTED;
+  HeadMap hm;
+  if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  const int32_t rows = shape->batch * hm.n;
+  const size_t need = est_workspace_bytes(rows, shape->seq_len);
+  if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
+  if (rows == 0 || shape->seq_len == 0) return DSA_OK;
+  EstArgs a;
+  a.q = q; a.k = k;
+  a.seq_len = shape->seq_len; a.head_dim = shape->head_dim; a.dtype = shape->dtype;
+  a.last_q = last_q; a.rows = rows;
+  a.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
+  a.hm = hm;
+  a.v_scores = v_scores; a.s_scores = s_scores;
+  est_carve(a, workspace);
+  return hip_status(launch_vs_estimate(a, static_cast<hipStream_t>(stream)));
+}
+
+dsa_status dsa_topk(const float* scores, int32_t rows, int32_t n, int32_t k, int32_t forced_index,
+                    int32_t* out, void* stream) {
+  if (rows < 0 || n < 0 || k < 0) return DSA_ERR_INVALID_ARG;
+  if (forced_index < -1 || (forced_index >= n && forced_index != -1)) return DSA_ERR_INVALID_ARG;
+  if (rows == 0 || n == 0 || k == 0) return DSA_OK;
+  if (!scores || !out) return DSA_ERR_INVALID_ARG;
+  return hip_status(launch_topk_rows(scores, rows, n, k, forced_index, out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+dsa_status dsa_vs_build_index(const int32_t* V, int32_t nv, const int32_t* S, int32_t ns,
+                              int32_t rows, int32_t seq_len, int32_t* intervals,
+                              int32_t* n_intervals, int32_t* cols, int32_t* n_cols, void* stream) {
+  if (nv < 0 || ns < 0 || rows < 0 || seq_len < 0) return DSA_ERR_INVALID_ARG;
+  if (rows == 0 || seq_len == 0) return DSA_OK;
+  if (!n_intervals || !n_cols || (ns && (!S || !intervals)) || (nv && (!V || !cols)))
+    return DSA_ERR_INVALID_ARG;
+  return hip_status(launch_vs_build_index(V, nv, S, ns, rows, seq_len, intervals, n_intervals, cols,
+                                          n_cols, static_cast<hipStream_t>(stream)));
+}
+
+dsa_status dsa_sparse_attention_vs(const void* q, const void* k, const void* v, void* o,
+                                   const dsa_shape* shape, float scale, const int32_t* heads,
+                                   int32_t n_heads, const int32_t* intervals,
+                                   const int32_t* n_intervals, int32_t max_iv, const int32_t* cols,
+                                   const int32_t* n_cols, int32_t max_cols, void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !o || !n_intervals || !n_cols || max_iv < 0 || max_cols < 0)
+    return DSA_ERR_INVALID_ARG;
+  if ((max_iv && !intervals) || (max_cols && !cols)) return DSA_ERR_INVALID_ARG;
+  HeadMap hm;
+  if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  AttnArgs a = attn_args(q, k, v, o, shape, scale, hm);
+  if (a.rows == 0 || a.seq_len == 0) return DSA_OK;
+  VsIndex ix{intervals, n_intervals, max_iv, cols, n_cols, max_cols};
+  return hip_status(launch_attention_vs(a, ix, static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_vertical_slash_workspace_bytes(const dsa_shape* shape, int32_t vertical_topk,
+                                          int32_t slash_topk, int32_t n_heads) {
+  if (check_shape(shape) != DSA_OK || n_heads < 0 || vertical_topk < 0 || slash_topk < 1) return 0;
+  const int32_t n = shape->seq_len;
+  const int32_t vk = vertical_topk < n ? vertical_topk : n;
+  const int32_t sk = slash_topk < n ? slash_topk : n;
+  return vs_layout(shape->batch * n_heads, n, vk, sk, nullptr, nullptr);
+}
+
+dsa_status dsa_vertical_slash_sparse_attention(const void* q, const void* k, const void* v, void* o,
+                                               const dsa_shape* shape, int32_t vertical_topk,
+                                               int32_t slash_topk, int32_t last_q, float scale,
+                                               const int32_t* heads, int32_t n_heads,
+                                               void* workspace, size_t workspace_bytes,
+                                               void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
+  if (vertical_topk < 0 || slash_topk < 1) return DSA_ERR_INVALID_ARG;
+  if (last_q < 1 || last_q > 64) return DSA_ERR_UNSUPPORTED;
+  HeadMap hm;
+  if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  const int32_t rows = shape->batch * hm.n, n = shape->seq_len;
+  const int32_t vk = vertical_topk < n ? vertical_topk : n;
+  const int32_t sk = slash_topk < n ? slash_topk : n;
+  const size_t need = vs_layout(rows, n, vk, sk, nullptr, nullptr);
+  if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
+  if (rows == 0 || n == 0) return DSA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  VsWork w;
+  vs_layout(rows, n, vk, sk, workspace, &w);
+
+  EstArgs ea;
+  ea.q = q; ea.k = k;
+  ea.seq_len = n; ea.head_dim = shape->head_dim; ea.dtype = shape->dtype;
+  ea.last_q = last_q; ea.rows = rows;
+  ea.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
+  ea.hm = hm;
+  ea.v_scores = w.v; ea.s_scores = w.s;
+  est_carve(ea, w.est);
+  hipError_t e = launch_vs_estimate(ea, s);
+  if (e == hipSuccess) e = launch_topk_rows(w.v, rows, n, vk, -1, w.V, s);
+  if (e == hipSuccess) e = launch_topk_rows(w.s, rows, n, sk, 0, w.S, s);
+  if (e == hipSuccess) e = launch_vs_build_index(w.V, vk, w.S, sk, rows, n, w.iv, w.n_iv, w.cols, w.n_cols, s);
+  if (e == hipSuccess) {
+    AttnArgs a = attn_args(q, k, v, o, shape, scale, hm);
+    e = launch_attention_vs(a, VsIndex{w.iv, w.n_iv, sk, w.cols, w.n_cols, vk}, s);
+  }
+  return hip_status(e);
+}
+
+// ------------------------------------------------------------------ BS
+dsa_status dsa_bs_pool(const void* x, int32_t dtype, int32_t batch, int32_t x_heads, int32_t seq_len,
+                       int32_t head_dim, const int32_t* heads, int32_t n_heads, float* out,
+                       void* stream) {
+  if (batch < 0 || x_heads <= 0 || seq_len < 0) return DSA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return DSA_ERR_UNSUPPORTED;
+  if (dtype != DSA_BF16 && dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
+  if (!x || !out) return DSA_ERR_INVALID_ARG;
+  HeadMap hm;
+  dsa_status st = make_map(x_heads, x_heads, heads, n_heads, hm);
+  if (st != DSA_OK) return st;
+  return hip_status(launch_pool(x, dtype, seq_len, head_dim, batch * hm.n, hm, out,
+                                static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_bs_select_workspace_bytes(int32_t rows, int32_t nb) {
+  if (rows <= 0 || nb <= 0) return 0;
+  return (size_t)logit_rows_per_group(rows, nb) * nb * nb * sizeof(float);
+}
+
+dsa_status dsa_bs_select(const float* qp, const float* kp, int32_t rows, int32_t nb, int32_t head_dim,
+                         float scale, int32_t topk, int32_t* sel, int32_t* n_sel, float* logits,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 0 || nb < 0 || topk < 1) return DSA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return DSA_ERR_UNSUPPORTED;
+  if (rows == 0 || nb == 0) return DSA_OK;
+  if (!qp || !kp || !sel || !n_sel) return DSA_ERR_INVALID_ARG;
+  if (!logits && (workspace_bytes < dsa_bs_select_workspace_bytes(rows, nb) || !workspace))
+    return DSA_ERR_WORKSPACE;
+  HeadMap hm;
+  memset(&hm, 0, sizeof(hm));
+  hipError_t e = bs_select_rows(qp, kp, rows, nb, head_dim, eff_scale(scale, head_dim), topk, false, hm,
+                                logits ? logits : static_cast<float*>(workspace), logits != nullptr,
+                                sel, n_sel, static_cast<hipStream_t>(stream));
+  return hip_status(e);
+}
+
+dsa_status dsa_sparse_attention_blocks(const void* q, const void* k, const void* v, void* o,
+                                       const dsa_shape* shape, float scale, const int32_t* heads,
+                                       int32_t n_heads, const int32_t* sel, const int32_t* n_sel,
+                                       int32_t max_sel, void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !o || !n_sel || max_sel < 0 || (max_sel && !sel)) return DSA_ERR_INVALID_ARG;
+  HeadMap hm;
+  if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  AttnArgs a = attn_args(q, k, v, o, shape, scale, hm);
+  if (a.rows == 0 || a.seq_len == 0) return DSA_OK;
+  return hip_status(launch_attention_blocks(a, BlockIndex{sel, n_sel, max_sel},
+                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_block_sparse_workspace_bytes(const dsa_shape* shape, int32_t topk, int32_t n_heads) {
+  if (check_shape(shape) != DSA_OK || n_heads < 0 || topk < 1) return 0;
+  return bs_layout(shape, shape->batch * n_heads, topk, nullptr, nullptr);
+}
+
+dsa_status dsa_block_sparse_attention(const void* q, const void* k, const void* v, void* o,
+                                      const dsa_shape* shape, int32_t topk, float scale,
+                                      const int32_t* heads, int32_t n_heads, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !o || topk < 1) return DSA_ERR_INVALID_ARG;
+  HeadMap hm;
+  if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  const int32_t rows = shape->batch * hm.n, n = shape->seq_len, nb = nblocks(n), D = shape->head_dim;
+  const size_t need = bs_layout(shape, rows, topk, nullptr, nullptr);
+  if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
+  if (rows == 0 || n == 0) return DSA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  BsWork w;
+  bs_layout(shape, rows, topk, workspace, &w);
+  // pooled K for every kv head the listed heads read
+  HeadMap kvm;
+  memset(&kvm, 0, sizeof(kvm));
+  kvm.q_heads = kvm.kv_heads = shape->kv_heads;
+  kvm.n = shape->kv_heads;
+  for (int32_t i = 0; i < kvm.n; ++i) kvm.h[i] = i;
+  hipError_t e = launch_pool(q, shape->dtype, n, D, rows, hm, w.qp, s);
+  if (e == hipSuccess) e = launch_pool(k, shape->dtype, n, D, shape->batch * kvm.n, kvm, w.kp, s);
+  if (e == hipSuccess)
+    e = bs_select_rows(w.qp, w.kp, rows, nb, D, eff_scale(scale, D), topk, true, hm, w.logits, false,
+                       w.sel, w.n_sel, s);
+  if (e == hipSuccess) {
+    const int32_t ke = topk < nb ? topk : nb;
+    e = launch_attention_blocks(attn_args(q, k, v, o, shape, scale, hm), BlockIndex{w.sel, w.n_sel, ke}, s);
+  }
+  return hip_status(e);
+}
+
+// ------------------------------------------------------------------ streaming
+dsa_status dsa_streaming_attention(const void* q, const void* k, const void* v, void* o,
+                                   const dsa_shape* shape, int32_t init_blocks, int32_t local_blocks,
+                                   float scale, const int32_t* heads, int32_t n_heads, void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !o || init_blocks < 0 || local_blocks < 1) return DSA_ERR_INVALID_ARG;
+  HeadMap hm;
+  if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  AttnArgs a = attn_args(q, k, v, o, shape, scale, hm);
+  if (a.rows == 0 || a.seq_len == 0) return DSA_OK;
+  return hip_status(launch_attention_stream(a, StreamIndex{init_blocks, local_blocks},
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Host-side launchers of the gfx950 kernels (each defined in its own .hip file).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace dsa {
+
+// ---- sparse attention (sparse_attention.hip) ----
+struct VsIndex {       // vertical-slash sparse format
+  const int32_t* iv;   // [rows][max_iv][2] (d_lo, d_hi) ascending
+  const int32_t* n_iv; // [rows]
+  int32_t max_iv;
+  const int32_t* cols;   // [rows][nb][max_cols]
+  const int32_t* n_cols; // [rows][nb]
+  int32_t max_cols;
+};
+struct BlockIndex {    // explicit key-block lists
+  const int32_t* sel;  // [rows][nb][max_sel]
+  const int32_t* n_sel;
+  int32_t max_sel;
+};
+struct StreamIndex {   // closed-form A-shape
+  int32_t init_blocks, local_blocks;
+};
+
+struct AttnArgs {
+  const void* q; const void* k; const void* v; void* o;
+  int32_t seq_len, head_dim, dtype;
+  int32_t rows;        // batch * listed heads
+  float scale_log2;    // softmax scale * log2(e)
+  HeadMap hm;
+};
+
+hipError_t launch_attention_vs(const AttnArgs& a, const VsIndex& ix, hipStream_t s);
+hipError_t launch_attention_blocks(const AttnArgs& a, const BlockIndex& ix, hipStream_t s);
+hipError_t launch_attention_stream(const AttnArgs& a, const StreamIndex& ix, hipStream_t s);
+
+// ---- vertical-slash estimate (vs_estimate.hip) ----
+constexpr int EST_CHUNK = 256;  // keys per estimator work-group
+struct EstArgs {
+  const void* q; const void* k;
+  int32_t seq_len, head_dim, dtype, last_q;
+  int32_t rows;
+  float scale_log2;
+  HeadMap hm;
+  float* v_scores; float* s_scores;       // [rows][seq_len]
+  float* part_stats;  // [rows][nchunks][64][2]
+  float* row_stats;   // [rows][64]
+  float* s_part;      // [rows][nchunks][EST_CHUNK + 63]
+  __host__ __device__ int32_t lq_eff() const { return last_q < seq_len ? last_q : seq_len; }
+};
+size_t est_workspace_bytes(int32_t rows, int32_t seq_len);
+void est_carve(EstArgs& a, void* ws);
+hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s);
+
+// ---- top-k (topk.hip) ----
+hipError_t launch_topk_rows(const float* scores, int32_t rows, int32_t n, int32_t k,
+                            int32_t forced, int32_t* out, hipStream_t s);
+// per (row, query block a): top-min(topk, a+1) of logits[row][a][0..a], a forced
+hipError_t launch_block_topk(const float* logits, int32_t rows, int32_t nb, int32_t topk,
+                             int32_t* sel, int32_t* n_sel, hipStream_t s);
+
+// ---- vertical-slash index builder (vs_index.hip) ----
+hipError_t launch_vs_build_index(const int32_t* V, int32_t nv, const int32_t* S, int32_t ns,
+                                 int32_t rows, int32_t seq_len, int32_t* iv, int32_t* n_iv,
+                                 int32_t* cols, int32_t* n_cols, hipStream_t s);
+
+// ---- block-sparse estimate (bs_estimate.hip) ----
+// rows = (batch, listed head of hm) over a tensor with hm.q_heads heads
+hipError_t launch_pool(const void* x, int32_t dtype, int32_t seq_len, int32_t head_dim,
+                       int32_t rows, const HeadMap& hm, float* out, hipStream_t s);
+// Logits of rows [row0, row0 + rows) of a call: qp and logits point at row0's
+// data. kp: with kv_map false it points at row0's data too (row r scores
+// against kp row r); with kv_map true it is the whole pooled-K array
+// [batch * kv_heads][nb][dim] and row r reads kp row b * kv_heads + kv head.
+hipError_t launch_block_logits(const float* qp, const float* kp, int32_t row0, int32_t rows,
+                               int32_t nb, int32_t head_dim, float scale, bool kv_map,
+                               const HeadMap& hm, float* logits, hipStream_t s);
+
+}  // namespace dsa

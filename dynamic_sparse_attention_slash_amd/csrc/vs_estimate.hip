@@ -1,0 +1,319 @@
+// Vertical-slash score estimate, gfx950.
+//
+// For one query head and its kv head, with the window rows i_r = n - lq + r
+// (r < lq = min(last_q, n)) and p[r][j] the causal softmax of row i_r:
+//   v[j] = sum_r p[r][j]            (vertical / column scores)
+//   s[d] = sum_r p[r][i_r - d]      (slash / diagonal scores)
+// [MInference 1.0 article, §2.2 Vertical-Slash Head: the last queries times
+// all keys give the estimated attention; Novita blog, §2 Modificación de
+// Atención: rowmax and l of a first pass turn a second pass into softmax
+// probabilities, restricted to the window's query rows.]
+//
+// Pass 1 (stats): per (row, chunk of 256 keys) one wave computes
+//   S = Q_window K_chunk^T with MFMA (lane = one key column, 16 query rows) and
+//   keeps a running (max, sum) per query row; partials go to workspace.
+// Combine: per row, max / log-sum over the chunks -> F_r = m_r + log2 Z_r.
+// Pass 2 (scores): recompute S, p = exp2(S*scale*log2e - F_r). Column sums are
+//   register sums plus two cross-lane steps (the loop runs key-major, so a
+//   key's scores stay in one lane column). Diagonal sums stage each 64x64 tile
+//   of p in LDS and add it along diagonals, one thread per diagonal, into a
+//   per-chunk accumulator: no atomics, fixed order, bit-reproducible.
+// S-combine: s[d] adds the (at most two) chunk partials covering offset d in
+//   ascending chunk order.
+#include "kernels.hpp"
+
+namespace dsa {
+namespace {
+
+constexpr int C = EST_CHUNK;       // keys per work-group
+constexpr int SACC = C + 63;       // diagonal offsets one chunk touches
+
+struct Window {
+  int32_t n, lq;
+  __device__ int32_t pos(int32_t r) const { return n - lq + r; }  // sequence row of window row r
+};
+
+// S tile for 16 keys [j0, j0+16): lane holds key column j0 + l16 and window
+// rows 16qb + 4g + i. Returns masked scores * scale_log2 (-inf when masked).
+template <typename T, int D>
+struct Tile;
+
+template <int D>
+struct Tile<uint16_t, D> {
+  static constexpr int DS = D / 32;
+  u32x4 qop[4][DS];
+  __device__ void load_q(const uint16_t* qs, const Window& w) {
+    const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      int32_t r = min(16 * qb + l16, w.lq - 1);
+      const u32x4* src = reinterpret_cast<const u32x4*>(qs + (size_t)w.pos(r) * D + (D / 4) * g);
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qop[qb][s] = src[s];
+    }
+  }
+  __device__ void scores(const uint16_t* ks, int32_t j0, const Window& w, float scale_log2,
+                         f32x4 (&out)[4]) const {
+    const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+    int32_t key = min(j0 + l16, w.n - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(ks + (size_t)key * D + (D / 4) * g);
+    u32x4 kop[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) kop[s] = src[s];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) acc = mfma_bf16(qop[qb][s], kop[s], acc);
+      out[qb] = acc;
+    }
+    mask(out, j0 + l16, w, scale_log2);
+  }
+  __device__ static void mask(f32x4 (&x)[4], int32_t key, const Window& w, float scale_log2) {
+    const int32_t g = threadIdx.x >> 4;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int32_t r = 16 * qb + 4 * g + i;
+        bool ok = r < w.lq && key <= w.pos(r);
+        x[qb][i] = ok ? x[qb][i] * scale_log2 : -INFINITY;
+      }
+  }
+};
+
+template <int D>
+struct Tile<float, D> {
+  static constexpr int DK = D / 4;
+  float qop[4][DK];
+  __device__ void load_q(const float* qs, const Window& w) {
+    const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      int32_t r = min(16 * qb + l16, w.lq - 1);
+      const f32x4* src = reinterpret_cast<const f32x4*>(qs + (size_t)w.pos(r) * D + DK * g);
+#pragma unroll
+      for (int s = 0; s < DK / 4; ++s) {
+        f32x4 x = src[s];
+        qop[qb][4 * s] = x[0]; qop[qb][4 * s + 1] = x[1]; qop[qb][4 * s + 2] = x[2]; qop[qb][4 * s + 3] = x[3];
+      }
+    }
+  }
+  __device__ void scores(const float* ks, int32_t j0, const Window& w, float scale_log2,
+                         f32x4 (&out)[4]) const {
+    const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+    int32_t key = min(j0 + l16, w.n - 1);
+    const f32x4* src = reinterpret_cast<const f32x4*>(ks + (size_t)key * D + DK * g);
+    float kop[DK];
+#pragma unroll
+    for (int s = 0; s < DK / 4; ++s) {
+      f32x4 x = src[s];
+      kop[4 * s] = x[0]; kop[4 * s + 1] = x[1]; kop[4 * s + 2] = x[2]; kop[4 * s + 3] = x[3];
+    }
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DK; ++s) acc = mfma_f32(qop[qb][s], kop[s], acc);
+      out[qb] = acc;
+    }
+    Tile<uint16_t, D>::mask(out, j0 + l16, w, scale_log2);
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void est_stats_kernel(EstArgs a) {
+  const int32_t chunk = blockIdx.x, row = blockIdx.y;
+  const int32_t nchunks = gridDim.x;
+  const Window w{a.seq_len, a.lq_eff()};
+  const T* qs = static_cast<const T*>(a.q) + a.hm.q_slab(row, a.seq_len, D);
+  const T* ks = static_cast<const T*>(a.k) + a.hm.kv_slab(row, a.seq_len, D);
+  Tile<T, D> tile;
+  tile.load_q(qs, w);
+  float m[4][4], z[4][4];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m[qb][i] = NEG_BIG; z[qb][i] = 0.f; }
+
+  const int32_t j_begin = chunk * C, j_end = min(a.seq_len, j_begin + C);
+  for (int32_t j0 = j_begin; j0 < j_end; j0 += 16) {
+    f32x4 x[4];
+    tile.scores(ks, j0, w, a.scale_log2, x);
+    // running (max, sum) with a deferred max: rescale only when a score
+    // exceeds the current max by more than 2^8
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) need |= x[qb][i] > m[qb][i] + 8.f;
+    if (__any(need)) {
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (x[qb][i] > m[qb][i] + 8.f) {
+            z[qb][i] *= fast_exp2(m[qb][i] - x[qb][i]);
+            m[qb][i] = x[qb][i];
+          }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[qb][i] += fast_exp2(x[qb][i] - m[qb][i]);
+  }
+  // merge the 16 key columns of each row (lanes with equal l >> 4)
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mm = m[qb][i], zz = z[qb][i];
+#pragma unroll
+      for (int msk = 1; msk < 16; msk <<= 1) {
+        float mo = __shfl_xor(mm, msk, 64), zo = __shfl_xor(zz, msk, 64);
+        float mn = fmaxf(mm, mo);
+        zz = zz * fast_exp2(mm - mn) + zo * fast_exp2(mo - mn);
+        mm = mn;
+      }
+      m[qb][i] = mm;
+      z[qb][i] = zz;
+    }
+  const int32_t lane = threadIdx.x, g = lane >> 4;
+  if ((lane & 15) == 0) {
+    float* dst = a.part_stats + ((size_t)row * nchunks + chunk) * 64 * 2;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int r = 16 * qb + 4 * g + i;
+        dst[2 * r] = m[qb][i];
+        dst[2 * r + 1] = z[qb][i];
+      }
+  }
+}
+
+// F_r = m_r + log2(Z_r) over all chunks, one thread per window row.
+__global__ __launch_bounds__(64) void est_combine_kernel(EstArgs a, int32_t nchunks) {
+  const int32_t row = blockIdx.x, r = threadIdx.x;
+  const float* src = a.part_stats + (size_t)row * nchunks * 128 + 2 * r;
+  float mm = NEG_BIG;
+  for (int32_t c = 0; c < nchunks; ++c) mm = fmaxf(mm, src[(size_t)c * 128]);
+  float zz = 0.f;
+  for (int32_t c = 0; c < nchunks; ++c)
+    zz += src[(size_t)c * 128 + 1] * fast_exp2(src[(size_t)c * 128] - mm);
+  a.row_stats[(size_t)row * 64 + r] = zz > 0.f ? mm + __log2f(zz) : INFINITY;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void est_scores_kernel(EstArgs a) {
+  constexpr int PS = 65;  // padded LDS row of the 64x64 probability tile
+  __shared__ float ptile[64 * PS];
+  __shared__ float sacc[SACC];
+  const int32_t chunk = blockIdx.x, row = blockIdx.y;
+  const int32_t nchunks = gridDim.x;
+  const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+  const Window w{a.seq_len, a.lq_eff()};
+  const T* qs = static_cast<const T*>(a.q) + a.hm.q_slab(row, a.seq_len, D);
+  const T* ks = static_cast<const T*>(a.k) + a.hm.kv_slab(row, a.seq_len, D);
+  Tile<T, D> tile;
+  tile.load_q(qs, w);
+  float F[4][4];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) F[qb][i] = a.row_stats[(size_t)row * 64 + 16 * qb + 4 * g + i];
+  for (int e = lane; e < SACC; e += 64) sacc[e] = 0.f;
+
+  float* vout = a.v_scores + (size_t)row * a.seq_len;
+  const int32_t j_begin = chunk * C, j_end = min(a.seq_len, j_begin + C);
+  for (int32_t t0 = j_begin; t0 < j_end; t0 += 64) {
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const int32_t j0 = t0 + 16 * sb;
+      f32x4 x[4];
+      tile.scores(ks, j0, w, a.scale_log2, x);
+      float colsum = 0.f;
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = fast_exp2(x[qb][i] - F[qb][i]);
+          colsum += p;
+          ptile[(16 * qb + 4 * g + i) * PS + 16 * sb + l16] = p;
+        }
+      colsum = xor_sum(xor_sum(colsum, 16), 32);
+      if (g == 0 && j0 + l16 < a.seq_len) vout[j0 + l16] = colsum;
+    }
+    __syncthreads();
+    // diagonal e = r - jj of the tile maps to chunk offset index
+    // e + (C - 1) - (t0 - j_begin)
+    const int32_t base = (C - 1) - (t0 - j_begin);
+    for (int32_t t = lane; t < 127; t += 64) {
+      const int32_t e = t - 63;
+      const int32_t r_lo = max(0, e), r_hi = min(63, 63 + e);
+      float sum = 0.f;
+      for (int32_t r = r_lo; r <= r_hi; ++r) sum += ptile[r * PS + (r - e)];
+      sacc[e + base] += sum;
+    }
+    __syncthreads();
+  }
+  float* dst = a.s_part + ((size_t)row * nchunks + chunk) * SACC;
+  for (int e = lane; e < SACC; e += 64) dst[e] = sacc[e];
+}
+
+// s[d] = sum over chunks c covering d (ascending c) of s_part[c][e_c(d)],
+// e_c(d) = d - (n - lq - (c*C + C - 1)).
+__global__ __launch_bounds__(256) void est_scombine_kernel(EstArgs a, int32_t nchunks) {
+  const int32_t row = blockIdx.y;
+  const int32_t d = blockIdx.x * 256 + threadIdx.x;
+  if (d >= a.seq_len) return;
+  const int32_t n = a.seq_len, lq = a.lq_eff();
+  // keys of diagonal d: j in [n - lq - d, n - 1 - d] (clipped at 0)
+  const int32_t j_lo = max(0, n - lq - d), j_hi = n - 1 - d;
+  float sum = 0.f;
+  const float* sp = a.s_part + (size_t)row * nchunks * SACC;
+  for (int32_t c = j_lo / C; c <= j_hi / C; ++c) {
+    const int32_t e = d - (n - lq - (c * C + C - 1));
+    sum += sp[(size_t)c * SACC + e];
+  }
+  a.s_scores[(size_t)row * n + d] = sum;
+}
+
+}  // namespace
+
+size_t est_workspace_bytes(int32_t rows, int32_t seq_len) {
+  const size_t nch = (size_t)(seq_len + C - 1) / C;
+  const size_t part = (size_t)rows * nch * 128 * sizeof(float);
+  const size_t stats = (size_t)rows * 64 * sizeof(float);
+  const size_t spart = (size_t)rows * nch * SACC * sizeof(float);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return al(part) + al(stats) + al(spart);
+}
+
+void est_carve(EstArgs& a, void* ws) {
+  const size_t nch = (size_t)(a.seq_len + C - 1) / C;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char* p = static_cast<char*>(ws);
+  a.part_stats = reinterpret_cast<float*>(p);
+  p += al((size_t)a.rows * nch * 128 * sizeof(float));
+  a.row_stats = reinterpret_cast<float*>(p);
+  p += al((size_t)a.rows * 64 * sizeof(float));
+  a.s_part = reinterpret_cast<float*>(p);
+}
+
+hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s) {
+  if (a.rows == 0 || a.seq_len == 0) return hipSuccess;
+  const int32_t nch = (a.seq_len + C - 1) / C;
+  dim3 grid(nch, a.rows);
+  auto st = a.dtype == BF16 ? (a.head_dim == 64 ? est_stats_kernel<uint16_t, 64> : est_stats_kernel<uint16_t, 128>)
+                            : (a.head_dim == 64 ? est_stats_kernel<float, 64> : est_stats_kernel<float, 128>);
+  auto sc = a.dtype == BF16 ? (a.head_dim == 64 ? est_scores_kernel<uint16_t, 64> : est_scores_kernel<uint16_t, 128>)
+                            : (a.head_dim == 64 ? est_scores_kernel<float, 64> : est_scores_kernel<float, 128>);
+  hipLaunchKernelGGL(st, grid, dim3(64), 0, s, a);
+  hipLaunchKernelGGL(est_combine_kernel, dim3(a.rows), dim3(64), 0, s, a, nch);
+  hipLaunchKernelGGL(sc, grid, dim3(64), 0, s, a);
+  hipLaunchKernelGGL(est_scombine_kernel, dim3((a.seq_len + 255) / 256, a.rows), dim3(256), 0, s, a, nch);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

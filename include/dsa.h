@@ -1,0 +1,204 @@
+/*
+ * dsa.h - dynamic sparse attention for the long-context prefill phase on
+ * gfx950 (MI355X). Plain C ABI: every pointer is a plain host or device
+ * pointer, every size a plain integer, streams are passed as void*
+ * (a hipStream_t; NULL is the default stream).
+ *
+ * Method sources, cited by page title and section:
+ *   [MInf]   "MInference 1.0" summary article (developer.volcengine.com):
+ *            §1 Problem Formulation (attention under a dynamic mask),
+ *            §2.2 Sparsity Indices Approximation and Dynamic Sparse Attention
+ *            Calculation (Vertical-Slash Head, Block-Sparse Head), and the
+ *            kernel-only usage listing (vertical_slash_sparse_attention,
+ *            block_sparse_attention, streaming_forward).
+ *   [Novita] "How KV sparsity achieves 1.5x acceleration for vLLM" (Novita AI
+ *            blog), §2 Modificación de Atención (rowmax / l reuse, key
+ *            scores as sums of softmax probabilities over a window of the last
+ *            queries, q start/end restriction).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Layout. q and o are [batch][q_heads][seq_len][head_dim], k and v are
+ *   [batch][kv_heads][seq_len][head_dim], contiguous row-major, all of the
+ *   element type `dtype` (bf16 or fp32), in device memory. Query head h reads
+ *   kv head h / (q_heads / kv_heads) (grouped-query attention).
+ * Blocks. Query and key blocks are 64 rows: block a covers rows
+ *   [64a, min(64a + 64, seq_len)); nb = ceil(seq_len / 64).
+ * Masks. Attention is causal (key j <= query i) and further restricted by the
+ *   sparse index; masked entries are excluded exactly [MInf §1]. The softmax
+ *   scale is `scale`, or 1/sqrt(head_dim) when scale <= 0. A query row whose
+ *   allowed key set is empty outputs zeros (reachable only through the
+ *   explicit-index calls; the three public calls always keep the diagonal).
+ * Head subsets. `heads` is a HOST array of n_heads distinct query-head ids the
+ *   call processes (at most DSA_MAX_HEADS); NULL means all q_heads in order.
+ *   Outputs of stage calls are "rows" ordered (batch, position in `heads`):
+ *   row = b * n_heads + t. Attention calls write only the listed heads of o.
+ * Top-k order. A top-k keeps the entries ranking first under: forced entries,
+ *   then larger score, then smaller index; -0.0 counts as +0.0 and NaN as
+ *   -inf; k is clamped to the candidate count; indices are returned
+ *   ascending.
+ * Ownership. The caller owns every buffer, including `workspace`; the library
+ *   allocates and frees nothing and keeps no state between calls.
+ * Execution. Calls enqueue work on `stream` and return without synchronising.
+ * Errors. Argument checks happen on the host before anything is enqueued:
+ *   DSA_ERR_INVALID_ARG for a NULL pointer, a negative or inconsistent size,
+ *   q_heads % kv_heads != 0, a duplicated or out-of-range head id or a bad
+ *   top-k/window argument; DSA_ERR_UNSUPPORTED for a head_dim other than 64 or
+ *   128, an unknown dtype, last_q outside [1, 64] or more than DSA_MAX_HEADS
+ *   heads; DSA_ERR_WORKSPACE when workspace_bytes is below what the matching
+ *   *_workspace_bytes call returns; DSA_ERR_HIP when a launch fails.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_BLOCK 64
+#define DSA_MAX_HEADS 256
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,
+  DSA_ERR_UNSUPPORTED = 2,
+  DSA_ERR_WORKSPACE = 3,
+  DSA_ERR_HIP = 4
+} dsa_status;
+
+typedef enum { DSA_BF16 = 0, DSA_F32 = 1 } dsa_dtype;
+
+typedef struct {
+  int32_t batch;
+  int32_t q_heads;
+  int32_t kv_heads;
+  int32_t seq_len;
+  int32_t head_dim; /* 64 or 128 */
+  int32_t dtype;    /* dsa_dtype */
+} dsa_shape;
+
+/* Human-readable name of a status code (static string). */
+const char* dsa_status_string(dsa_status s);
+
+/* ======================================================================
+ * The three calls of the kernel-only API [MInf, usage listing]
+ * ====================================================================== */
+
+/* Vertical-slash heads [MInf §2.2 Vertical-Slash Head; Novita §2].
+ * For each listed head: estimate the vertical and slash scores from the last
+ * last_q query rows (dsa_vs_estimate), keep the top vertical_topk columns and
+ * the top slash_topk diagonal offsets with offset 0 forced (dsa_topk), build
+ * the block sparse format (dsa_vs_build_index) and run exact attention over it
+ * (dsa_sparse_attention_vs). Writes o for the listed heads.
+ * vertical_topk >= 0, slash_topk >= 1, last_q in [1, 64]. workspace: device
+ * memory of at least dsa_vertical_slash_workspace_bytes(...) bytes. */
+dsa_status dsa_vertical_slash_sparse_attention(
+    const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
+    int32_t vertical_topk, int32_t slash_topk, int32_t last_q, float scale,
+    const int32_t* heads, int32_t n_heads, void* workspace, size_t workspace_bytes,
+    void* stream);
+size_t dsa_vertical_slash_workspace_bytes(const dsa_shape* shape, int32_t vertical_topk,
+                                          int32_t slash_topk, int32_t n_heads);
+
+/* Block-sparse heads [MInf §2.2 Block-Sparse Head]. Mean-pool Q and K over
+ * 64-row blocks (dsa_bs_pool), score block pairs scale * Qp[a] . Kp[c] for
+ * c <= a and keep the top `topk` key blocks per query block with the diagonal
+ * block forced (dsa_bs_select), then attend over the kept blocks
+ * (dsa_sparse_attention_blocks). topk >= 1. */
+dsa_status dsa_block_sparse_attention(
+    const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
+    int32_t topk, float scale, const int32_t* heads, int32_t n_heads, void* workspace,
+    size_t workspace_bytes, void* stream);
+size_t dsa_block_sparse_workspace_bytes(const dsa_shape* shape, int32_t topk,
+                                        int32_t n_heads);
+
+/* Streaming (A-shape) heads [MInf usage listing, streaming_forward(init_num,
+ * local_window_num)]: query block a attends to key blocks c <= a with
+ * c < init_blocks or a - c < local_blocks (the window counts the diagonal
+ * block). init_blocks >= 0, local_blocks >= 1. Needs no workspace. */
+dsa_status dsa_streaming_attention(
+    const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
+    int32_t init_blocks, int32_t local_blocks, float scale, const int32_t* heads,
+    int32_t n_heads, void* stream);
+
+/* ======================================================================
+ * Stage calls: the same kernels the calls above run, exposed one by one.
+ * ====================================================================== */
+
+/* Vertical and slash scores [MInf §2.2 VS head; Novita §2]. For each listed
+ * head, with rows i_r = seq_len - lq + r (lq = min(last_q, seq_len)) and
+ * p[r][j] the causal softmax of row i_r over keys j <= i_r:
+ *   v_scores[row][j] = sum_r p[r][j],  s_scores[row][d] = sum_r p[r][i_r - d].
+ * Outputs: fp32 device arrays [batch * n_heads][seq_len]. workspace: at least
+ * dsa_vs_estimate_workspace_bytes(...) bytes. */
+dsa_status dsa_vs_estimate(const void* q, const void* k, const dsa_shape* shape,
+                           int32_t last_q, float scale, const int32_t* heads,
+                           int32_t n_heads, float* v_scores, float* s_scores,
+                           void* workspace, size_t workspace_bytes, void* stream);
+size_t dsa_vs_estimate_workspace_bytes(const dsa_shape* shape, int32_t n_heads);
+
+/* Row-wise top-k of fp32 scores [MInf §2.2: top-k verticals, slashes and
+ * blocks]. scores: device [rows][n]; out: device int32 [rows][min(k, n)],
+ * ascending. forced_index in [-1, n): the entry ranked first in every row
+ * (-1: none). k >= 0. */
+dsa_status dsa_topk(const float* scores, int32_t rows, int32_t n, int32_t k,
+                    int32_t forced_index, int32_t* out, void* stream);
+
+/* Vertical-slash sparse format [MInf §2.2 "convert to sparse format"].
+ * Inputs per row: V [rows][nv] ascending column indices and S [rows][ns]
+ * ascending slash offsets, all in [0, seq_len). Offsets closer than 65 are
+ * merged: intervals [rows][ns][2] receives (d_lo, d_hi) pairs in ascending
+ * order and n_intervals [rows] their count. Query block a then covers the key
+ * ranges [max(0, 64a - d_hi), min(seq_len, 64a + 64 - d_lo)) of every interval
+ * with d_lo < 64a + 64, and the columns cols [rows][nb][nv] (count in
+ * n_cols [rows][nb]): the entries of V below min(seq_len, 64a + 64) that lie
+ * in none of those ranges, ascending. All device int32 arrays. */
+dsa_status dsa_vs_build_index(const int32_t* V, int32_t nv, const int32_t* S, int32_t ns,
+                              int32_t rows, int32_t seq_len, int32_t* intervals,
+                              int32_t* n_intervals, int32_t* cols, int32_t* n_cols,
+                              void* stream);
+
+/* Block mean-pool [MInf §2.2 BS head]: out[row][a][:] = mean of rows
+ * [64a, min(64a+64, seq_len)) of x's head heads[t] (fp32 accumulation).
+ * x: device [batch][x_heads][seq_len][head_dim] of `dtype`; out: device fp32
+ * [batch * n_heads][nb][head_dim]. heads: host ids in [0, x_heads) or NULL. */
+dsa_status dsa_bs_pool(const void* x, int32_t dtype, int32_t batch, int32_t x_heads,
+                       int32_t seq_len, int32_t head_dim, const int32_t* heads,
+                       int32_t n_heads, float* out, void* stream);
+
+/* Block selection [MInf §2.2 BS head]. qp, kp: device fp32 [rows][nb][head_dim]
+ * (row r of qp is scored against row r of kp). L[a][c] = scale * qp[a].kp[c]
+ * for c <= a in fp32; sel [rows][nb][min(topk, nb)] receives the ascending
+ * top-min(topk, a+1) blocks of L[a][0..a] with c = a forced and n_sel
+ * [rows][nb] their count. logits: NULL, or device fp32 [rows][nb][nb] that
+ * receives L (entries c > a are left untouched). workspace: at least
+ * dsa_bs_select_workspace_bytes(...) bytes. */
+dsa_status dsa_bs_select(const float* qp, const float* kp, int32_t rows, int32_t nb,
+                         int32_t head_dim, float scale, int32_t topk, int32_t* sel,
+                         int32_t* n_sel, float* logits, void* workspace,
+                         size_t workspace_bytes, void* stream);
+size_t dsa_bs_select_workspace_bytes(int32_t rows, int32_t nb);
+
+/* Attention over a vertical-slash index (as built by dsa_vs_build_index) for
+ * the listed heads: row = b * n_heads + t indexes intervals [rows][max_iv][2],
+ * n_intervals [rows], cols [rows][nb][max_cols] and n_cols [rows][nb]. */
+dsa_status dsa_sparse_attention_vs(
+    const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
+    float scale, const int32_t* heads, int32_t n_heads, const int32_t* intervals,
+    const int32_t* n_intervals, int32_t max_iv, const int32_t* cols, const int32_t* n_cols,
+    int32_t max_cols, void* stream);
+
+/* Attention over explicit key-block lists: sel [rows][nb][max_sel] holds
+ * n_sel [rows][nb] ascending distinct block ids per query block. */
+dsa_status dsa_sparse_attention_blocks(
+    const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
+    float scale, const int32_t* heads, int32_t n_heads, const int32_t* sel,
+    const int32_t* n_sel, int32_t max_sel, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

@@ -1,0 +1,108 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/dsa.h declares, and rejects bad arguments on the host before any HIP
+call (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_sparse_attention_slash_amd as dsa
+from dynamic_sparse_attention_slash_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dsa.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.dsa_status_string(code)
+
+
+def shape(b=1, hq=4, hkv=2, n=256, d=128, dt=0):
+    return B.Shape(b, hq, hkv, n, d, dt)
+
+
+P = ctypes.c_void_p(16)  # a non-NULL pointer that is never dereferenced
+
+
+def vs_call(lib, sh, vk=8, sk=8, lq=64, heads=None, nh=0, ws=P, wsb=1 << 40, q=P):
+    return lib.dsa_vertical_slash_sparse_attention(q, P, P, P, ctypes.byref(sh), vk, sk, lq, 0.0,
+                                                   heads, nh, ws, wsb, None)
+
+
+def test_vs_argument_errors(lib):
+    assert vs_call(lib, shape(), q=None) == INVALID
+    assert vs_call(lib, shape(hq=3, hkv=2)) == INVALID
+    assert vs_call(lib, shape(d=96)) == UNSUPPORTED
+    assert vs_call(lib, shape(dt=7)) == UNSUPPORTED
+    assert vs_call(lib, shape(n=-1)) == INVALID
+    assert vs_call(lib, shape(), vk=-1) == INVALID
+    assert vs_call(lib, shape(), sk=0) == INVALID
+    assert vs_call(lib, shape(), lq=0) == UNSUPPORTED
+    assert vs_call(lib, shape(), lq=65) == UNSUPPORTED
+    dup = (ctypes.c_int32 * 2)(1, 1)
+    assert vs_call(lib, shape(), heads=dup, nh=2) == INVALID
+    bad = (ctypes.c_int32 * 1)(4)
+    assert vs_call(lib, shape(), heads=bad, nh=1) == INVALID
+    assert vs_call(lib, shape(), wsb=10) == WORKSPACE
+    assert vs_call(lib, shape(), ws=None) == WORKSPACE
+    # nothing to do: zero batch or empty head list succeed without touching memory
+    assert vs_call(lib, shape(b=0), ws=None, wsb=0) == OK
+    assert vs_call(lib, shape(), heads=(ctypes.c_int32 * 1)(0), nh=0, ws=None, wsb=0) == OK
+
+
+def test_workspace_sizes(lib):
+    sh = shape(n=4096)
+    w4 = lib.dsa_vertical_slash_workspace_bytes(ctypes.byref(sh), 256, 256, 4)
+    w2 = lib.dsa_vertical_slash_workspace_bytes(ctypes.byref(sh), 256, 256, 2)
+    assert w4 > w2 > 0
+    # per-block column lists dominate: rows * nb * vk int32
+    assert w4 >= 4 * 64 * 256 * 4
+    assert lib.dsa_vertical_slash_workspace_bytes(ctypes.byref(shape(d=96)), 1, 1, 1) == 0
+    assert lib.dsa_block_sparse_workspace_bytes(ctypes.byref(sh), 8, 4) > 0
+    assert lib.dsa_bs_select_workspace_bytes(3, 512) == 3 * 512 * 512 * 4
+
+
+def test_other_argument_errors(lib):
+    sh = shape()
+    assert lib.dsa_block_sparse_attention(P, P, P, P, ctypes.byref(sh), 0, 0.0, None, 0, P, 1 << 40, None) == INVALID
+    assert lib.dsa_block_sparse_attention(P, P, P, P, ctypes.byref(sh), 4, 0.0, None, 0, P, 8, None) == WORKSPACE
+    assert lib.dsa_streaming_attention(P, P, P, P, ctypes.byref(sh), -1, 1, 0.0, None, 0, None) == INVALID
+    assert lib.dsa_streaming_attention(P, P, P, P, ctypes.byref(sh), 1, 0, 0.0, None, 0, None) == INVALID
+    assert lib.dsa_streaming_attention(P, None, P, P, ctypes.byref(sh), 1, 1, 0.0, None, 0, None) == INVALID
+    assert lib.dsa_topk(P, 1, 10, -1, -1, P, None) == INVALID
+    assert lib.dsa_topk(P, 1, 10, 3, 10, P, None) == INVALID
+    assert lib.dsa_topk(None, 1, 10, 3, -1, P, None) == INVALID
+    assert lib.dsa_topk(None, 0, 10, 3, -1, None, None) == OK
+    assert lib.dsa_vs_build_index(P, -1, P, 1, 1, 10, P, P, P, P, None) == INVALID
+    assert lib.dsa_bs_pool(P, 0, 1, 2, 100, 80, None, 0, P, None) == UNSUPPORTED
+    assert lib.dsa_bs_select(P, P, 1, 4, 128, 0.1, 0, P, P, None, P, 1 << 30, None) == INVALID
+    assert lib.dsa_bs_select(P, P, 1, 4, 128, 0.1, 2, P, P, None, P, 4, None) == WORKSPACE
+    assert lib.dsa_vs_estimate(P, P, ctypes.byref(sh), 64, 0.0, None, 0, P, P, P, 4, None) == WORKSPACE
+    assert lib.dsa_sparse_attention_vs(P, P, P, P, ctypes.byref(sh), 0.0, None, 0, P, None, 1, P, P, 1, None) == INVALID
+    assert lib.dsa_sparse_attention_blocks(P, P, P, P, ctypes.byref(sh), 0.0, None, 0, P, P, -1, None) == INVALID
+    many = (ctypes.c_int32 * 300)(*range(300))
+    big = shape(hq=300, hkv=300)
+    assert lib.dsa_streaming_attention(P, P, P, P, ctypes.byref(big), 1, 1, 0.0, many, 300, None) == UNSUPPORTED
