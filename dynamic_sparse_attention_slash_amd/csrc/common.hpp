@@ -48,8 +48,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return u >> 16;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (low half = lo), round to nearest even; one
+// v_cvt_pk_bf16_f32 on gfx950
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+// sum of the two bf16 values of a packed pair, as floats
+__device__ __forceinline__ float packed_pair_sum(uint32_t u) {
+  return __uint_as_float(u << 16) + __uint_as_float(u & 0xffff0000u);
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {

@@ -157,10 +157,13 @@ __device__ __forceinline__ void mask_tile(f32x4 (&st)[2][4], const SubBlock (&sb
   }
 }
 
-// Online softmax update; returns the rescale factors applied (1 when none).
+// Online softmax update; returns whether any rescale factor differs from 1.
 // The running max is only raised when a new row max exceeds it by more than
 // 2^8, so P stays <= 256 and the O rescale runs rarely; the final O / l is
-// unchanged by the choice of reference max.
+// unchanged by the choice of reference max. SUM: add P to the row sums here
+// (the bf16 kernel instead sums P after rounding it to bf16, so that O / l
+// divides by the sum of exactly the weights the PV product used).
+template <bool SUM>
 __device__ __forceinline__ bool softmax_tile(f32x4 (&st)[2][4], SoftmaxState& ss,
                                              float scale_log2, float (&alpha)[4]) {
   float mt[4];
@@ -194,7 +197,7 @@ __device__ __forceinline__ bool softmax_tile(f32x4 (&st)[2][4], SoftmaxState& ss
       for (int i = 0; i < 4; ++i) {
         float p = fast_exp2(fmaf(st[s2][qb][i], scale_log2, -ss.m[qb]));
         st[s2][qb][i] = p;
-        ss.lsum[qb] += p;
+        if (SUM) ss.lsum[qb] += p;
       }
   return wave_upd;
 }
@@ -300,18 +303,22 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
 
     mask_tile(st, sb, r0, n, lane);
     float alpha[4];
-    if (softmax_tile(st, ss, scale_log2, alpha)) {
+    if (softmax_tile<false>(st, ss, scale_log2, alpha)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) oacc[db][qb] *= alpha[qb];
     }
-    // P^T operands: slots 4g..4g+3 of sub-block 0, then of sub-block 1
+    // P^T operands: slots 4g..4g+3 of sub-block 0, then of sub-block 1; the
+    // row sums add the rounded values
     u32x4 pop[4];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+    for (int qb = 0; qb < 4; ++qb) {
       pop[qb] = u32x4{pack_bf16x2(st[0][qb][0], st[0][qb][1]), pack_bf16x2(st[0][qb][2], st[0][qb][3]),
                       pack_bf16x2(st[1][qb][0], st[1][qb][1]), pack_bf16x2(st[1][qb][2], st[1][qb][3])};
+      ss.lsum[qb] += (packed_pair_sum(pop[qb][0]) + packed_pair_sum(pop[qb][1])) +
+                     (packed_pair_sum(pop[qb][2]) + packed_pair_sum(pop[qb][3]));
+    }
 
     __syncthreads();  // vt written
 #pragma unroll
@@ -401,7 +408,7 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
 
     mask_tile(st, sb, r0, n, lane);
     float alpha[4];
-    if (softmax_tile(st, ss, scale_log2, alpha)) {
+    if (softmax_tile<true>(st, ss, scale_log2, alpha)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -128,8 +128,11 @@ def test_vs_build_index(n, nv, ns, with0):
         S = rng.choice(pool, size=min(ns, len(pool)) - (1 if with0 else 0), replace=False) if len(pool) else np.zeros(0, int)
         if with0:
             S = np.concatenate([[0], S])
-        if r == 1:   # a dense run of nearby offsets
-            S = np.unique(np.concatenate([S[: ns // 2], np.arange(0, min(n, 200), 3)]))[: len(S)]
+        if r == 1 and len(S) > 8:   # a dense run of nearby offsets, same count
+            run = np.arange(0, min(n, 200), 3)
+            rest = np.setdiff1d(np.arange(n), run)
+            extra = rng.choice(rest, size=max(0, len(S) - len(run)), replace=False)
+            S = np.concatenate([run, extra])[: len(S)]
         Ss.append(np.sort(S).astype(np.int32))
         Vs.append(V.astype(np.int32))
     nvv, nss = len(Vs[0]), len(Ss[0])
