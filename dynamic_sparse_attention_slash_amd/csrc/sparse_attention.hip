@@ -7,43 +7,41 @@
 // columns (the vertical-slash sparse format of §2.2), or a list of 64-key blocks
 // (block-sparse heads, §2.2), or the closed-form sink + local window of the
 // streaming pattern (usage listing, streaming_forward). Online softmax with a
-// deferred rescale is used instead of the two-pass form; both give the same
-// result [Novita blog, §2 Modificación de Atención, FlashAttention one-pass
+// deferred rescale replaces the two-pass form; both give the same result
+// [Novita blog, §2 Modificación de Atención, FlashAttention one-pass
 // description].
 //
-// Work decomposition: one wave64 work-group per (row = batch x listed head,
-// query block of 64 rows). The wave keeps the 64 queries in registers and walks
-// the key set in tiles of two 16-key sub-blocks:
-//   S^T (keys x queries) = K_tile * Q^T      MFMA, K rows loaded straight from
+// Work decomposition: one work-group per (row = batch x listed head, query
+// block of 64 rows); the bf16 kernel splits the block's queries over two waves,
+// the fp32 kernel keeps all 64 in one wave. A prologue cuts the block's key set into 16-key sub-blocks and writes their
+// descriptors (first key or list position, count, flags) to LDS, so the hot
+// loop is straight-line code over tiles of two sub-blocks:
+//   S^T (keys x queries) = K_tile * Q^T      MFMA; K rows come straight from
 //                                            global memory (gathers and
 //                                            unaligned ranges cost nothing extra)
-//   P = exp2(S * scale*log2e - m)            fp32, per query column per lane
+//   P = exp2(S * scale*log2e - m)            fp32, one query column per lane
 //   O^T (dims x queries) += V_tile^T * P^T   MFMA; V_tile^T is transposed
 //                                            through LDS (bf16) or read row-wise
 //                                            (fp32, whose MFMA takes one k per
 //                                            lane)
-// In the MFMA output layout a lane holds one query column, so the running max,
-// the sum and the rescale of O^T need no data from other query columns.
+// In the MFMA output layout a lane holds one query column, so the running max
+// and the rescale of O^T need no data from other query columns. In the bf16
+// kernel the softmax denominator is one more MFMA block whose A operand is all
+// ones: it sums exactly the bf16-rounded P the PV product used.
 #include "kernels.hpp"
 
 namespace dsa {
 namespace {
 
-struct SubBlock {
-  int32_t start;        // first key (ranges)
-  int32_t count;        // keys in this sub-block, 0..16
-  const int32_t* list;  // gathered keys, or nullptr for a range
+// ---- 16-key sub-block descriptors ----
+constexpr int32_t SB_CAP = 1024;        // descriptors per refill (8 KiB of LDS)
+constexpr int32_t F_LIST = 1 << 8;      // keys come from the column list
+constexpr int32_t F_MASK = 1 << 9;      // partial, or reaches the diagonal: mask
+struct Desc {
+  int32_t a;  // first key (range) or position in the column list
+  int32_t b;  // count (0..16) | flags
+  __device__ int32_t count() const { return b & 0xff; }
 };
-
-// Key of a slot; gathered entries are clamped into [0, n) so that a bad index
-// can never address memory outside k or v.
-__device__ __forceinline__ int32_t sb_key(const SubBlock& s, int32_t slot, int32_t n) {
-  int32_t sl = slot < s.count ? slot : 0;
-  return s.list ? min(max(s.list[sl], 0), n - 1) : s.start + sl;
-}
-__device__ __forceinline__ int32_t sb_last_key(const SubBlock& s) {
-  return s.count == 0 ? -1 : (s.list ? s.list[s.count - 1] : s.start + s.count - 1);
-}
 
 // ---- key-range sources (all state is wave-uniform) ----
 struct VsRanges {
@@ -90,33 +88,59 @@ struct StreamRanges {
   }
 };
 
+// Fills up to SB_CAP descriptors per call, resuming where the last call
+// stopped: first the ranges, then the column list.
 template <class R>
-struct KeyGen {
+struct DescGen {
   R ranges;
   const int32_t* cols; int32_t n_cols;
-  int32_t p, hi, cp;
-  __device__ SubBlock next() {
-    while (true) {
-      if (p < hi) {
-        int32_t c = min(16, hi - p);
-        SubBlock s{p, c, nullptr};
-        p += c;
-        return s;
+  int32_t p, hi, cp, r0, n;
+  __device__ int32_t fill(Desc* d, int32_t tid, int32_t nthreads) {
+    int32_t cnt = 0;
+    while (cnt < SB_CAP) {
+      if (p >= hi) {
+        int32_t lo2, hi2;
+        if (!ranges.next(lo2, hi2)) break;
+        p = lo2;
+        hi = hi2;
+        continue;
       }
-      int32_t lo2, hi2;
-      if (!ranges.next(lo2, hi2)) break;
-      p = lo2;
-      hi = hi2;
+      const int32_t take = min((hi - p + 15) >> 4, SB_CAP - cnt);
+      for (int32_t t = tid; t < take; t += nthreads) {
+        int32_t s = p + 16 * t, c = min(16, hi - s);
+        d[cnt + t] = Desc{s, c | ((c < 16 || s + c - 1 > r0) ? F_MASK : 0)};
+      }
+      cnt += take;
+      p = min(hi, p + 16 * take);
     }
-    if (cp < n_cols) {
-      int32_t c = min(16, n_cols - cp);
-      SubBlock s{0, c, cols + cp};
-      cp += c;
-      return s;
+    if (cnt < SB_CAP && cp < n_cols) {
+      const int32_t take = min((n_cols - cp + 15) >> 4, SB_CAP - cnt);
+      for (int32_t t = tid; t < take; t += nthreads) {
+        int32_t s = cp + 16 * t, c = min(16, n_cols - s);
+        bool m = c < 16 || cols[s + c - 1] > r0;
+        d[cnt + t] = Desc{s, c | F_LIST | (m ? F_MASK : 0)};
+      }
+      cnt += take;
+      cp = min(n_cols, cp + 16 * take);
     }
-    return SubBlock{0, 0, nullptr};
+    return cnt;
   }
 };
+
+// Descriptor t as wave-uniform values; past the end an empty sub-block, which
+// must carry the mask flag so that its slots are masked out.
+__device__ __forceinline__ Desc uniform_desc(const Desc* d, int32_t t, int32_t cnt) {
+  Desc x = t < cnt ? d[t] : Desc{0, F_MASK};
+  return Desc{__builtin_amdgcn_readfirstlane(x.a), __builtin_amdgcn_readfirstlane(x.b)};
+}
+
+// Key of a slot; gathered entries are clamped into [0, n) so that a bad index
+// can never address memory outside k or v. Empty slots read the first key.
+__device__ __forceinline__ int32_t desc_key(const Desc& d, const int32_t* cols, int32_t slot,
+                                            int32_t n) {
+  int32_t sl = slot < d.count() ? slot : 0;
+  return (d.b & F_LIST) ? min(max(cols[d.a + sl], 0), n - 1) : d.a + sl;
+}
 
 // Work-group -> (row, query block). Blocks of one row go to consecutive
 // work-groups, latest (largest key set) first.
@@ -127,29 +151,24 @@ __device__ __forceinline__ void work_item(int32_t nb, int32_t& row, int32_t& a) 
 }
 
 // ---------------------------------------------------------------------------
-// shared softmax step on a tile of S^T values st[sub-block][query block][i]
-// lane holds query column (l & 15) + 16*qb, key slots 4*(l >> 4) + i
+// softmax pieces on a tile of S^T values st[sub-block][query block][i]:
+// lane holds query column (l & 15) + 16*qb and key slots 4*(l >> 4) + i
 // ---------------------------------------------------------------------------
-struct SoftmaxState {
-  float m[4];     // running max in log2 units (scale*log2e folded in)
-  float lsum[4];  // this lane's part of the row sums
-};
-
-__device__ __forceinline__ void mask_tile(f32x4 (&st)[2][4], const SubBlock (&sb)[2], int32_t r0,
-                                          int32_t n, int32_t lane) {
+template <int QB>
+__device__ __forceinline__ void mask_tile(f32x4 (&st)[2][QB], const Desc (&d)[2], const int32_t* cols,
+                                          int32_t q0, int32_t n, int32_t lane) {
   const int32_t g = lane >> 4, l16 = lane & 15;
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
-    // only partial sub-blocks and those reaching the diagonal need a mask
-    if (sb[s2].count < 16 || sb_last_key(sb[s2]) > r0) {
+    if (d[s2].b & F_MASK) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int32_t slot = 4 * g + i;
-        bool valid = slot < sb[s2].count;
-        int32_t key = sb_key(sb[s2], slot, n);
+        bool valid = slot < d[s2].count();
+        int32_t key = desc_key(d[s2], cols, slot, n);
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          int32_t row = r0 + 16 * qb + l16;
+        for (int qb = 0; qb < QB; ++qb) {
+          int32_t row = q0 + 16 * qb + l16;
           if (!valid || key > row) st[s2][qb][i] = -INFINITY;
         }
       }
@@ -157,187 +176,287 @@ __device__ __forceinline__ void mask_tile(f32x4 (&st)[2][4], const SubBlock (&sb
   }
 }
 
-// Online softmax update; returns whether any rescale factor differs from 1.
-// The running max is only raised when a new row max exceeds it by more than
-// 2^8, so P stays <= 256 and the O rescale runs rarely; the final O / l is
-// unchanged by the choice of reference max. SUM: add P to the row sums here
-// (the bf16 kernel instead sums P after rounding it to bf16, so that O / l
-// divides by the sum of exactly the weights the PV product used).
-template <bool SUM>
-__device__ __forceinline__ bool softmax_tile(f32x4 (&st)[2][4], SoftmaxState& ss,
-                                             float scale_log2, float (&alpha)[4]) {
-  float mt[4];
-  bool upd[4];
+template <int QB>
+__device__ __forceinline__ void mask_tile_lds(f32x4 (&st)[2][QB], const Desc (&d)[2], const int32_t* lcols,
+                                              int32_t q0, int32_t lane);
+
+// New reference maxima: raised only when a row max exceeds the current one by
+// more than 2^8 (P then stays <= 256 and the O rescale runs rarely; O / l does
+// not depend on the reference). Returns whether any lane raised one; alpha
+// holds the factors to apply to O and l.
+template <int QB>
+__device__ __forceinline__ bool update_max(const f32x4 (&st)[2][QB], float (&m)[QB], float scale_log2,
+                                           float (&alpha)[QB]) {
+  float mt[QB];
   bool any_upd = false;
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     float mx = fmaxf(fmaxf(fmaxf(st[0][qb][0], st[0][qb][1]), fmaxf(st[0][qb][2], st[0][qb][3])),
                      fmaxf(fmaxf(st[1][qb][0], st[1][qb][1]), fmaxf(st[1][qb][2], st[1][qb][3])));
     mx = xor_max(mx, 16);
     mx = xor_max(mx, 32);
     mt[qb] = mx * scale_log2;
-    upd[qb] = mt[qb] > ss.m[qb] + 8.0f;
-    any_upd |= upd[qb];
+    any_upd |= mt[qb] > m[qb] + 8.0f;
   }
-  bool wave_upd = __any(any_upd);
+  if (!__any(any_upd)) return false;
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    alpha[qb] = 1.0f;
-    if (wave_upd && upd[qb]) {
-      alpha[qb] = fast_exp2(ss.m[qb] - mt[qb]);
-      ss.m[qb] = mt[qb];
-      ss.lsum[qb] *= alpha[qb];
-    }
+  for (int qb = 0; qb < QB; ++qb) {
+    const bool up = mt[qb] > m[qb] + 8.0f;
+    alpha[qb] = up ? fast_exp2(m[qb] - mt[qb]) : 1.0f;
+    m[qb] = up ? mt[qb] : m[qb];
   }
+  return true;
+}
+
+template <int QB>
+__device__ __forceinline__ void exp_tile(f32x4 (&st)[2][QB], const float (&m)[QB], float scale_log2) {
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float p = fast_exp2(fmaf(st[s2][qb][i], scale_log2, -ss.m[qb]));
-        st[s2][qb][i] = p;
-        if (SUM) ss.lsum[qb] += p;
-      }
-  return wave_upd;
+      for (int i = 0; i < 4; ++i) st[s2][qb][i] = fast_exp2(fmaf(st[s2][qb][i], scale_log2, -m[qb]));
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel
+// bf16 kernel: two waves per query block, wave w owns queries r0 + 32w .. +31.
+//
+// K and V tiles (32 keys) travel global -> LDS with global_load_lds_dwordx4
+// (no registers involved), into a two-stage ring: the loads of tile t+1 are
+// in flight while tile t is computed, and one barrier per tile separates them.
+// Each wave loads one of the two 16-key sub-blocks of a tile. Both matrices
+// are row-major in LDS with the 16-byte chunks of row r XOR-swizzled by r, so
+// that the operand reads below are free of bank conflicts:
+//   K operand (MFMA A, 8 dims of one key per lane): ds_read_b128
+//   V^T operand (MFMA A, 8 keys of one dim per lane): two ds_read_b64_tr_b16,
+//     the gfx950 transposing LDS read (each 16-lane group reads a 16 x 4 block
+//     of b16 and lane i receives element (4j + i/4, i%4) for j = 0..3).
+// The block's column-list entries are staged in LDS together with the
+// sub-block descriptors, so gathered keys cost no global round trip.
 // ---------------------------------------------------------------------------
+constexpr int BF16_WAVES = 2;
+constexpr int32_t BF16_SB_CAP = 512;   // descriptors per refill
+constexpr int32_t COLS_CAP = 1024;     // column-list entries staged per refill
+
+template <int D>
+struct TileLds {
+  static constexpr int ROW = D * 2;           // bytes per key row
+  static constexpr int UNITS = ROW / 16;      // 16-byte chunks per row
+  static constexpr int MAT = 32 * ROW;        // one 32-key matrix
+  static constexpr int STAGE = 2 * MAT;       // K then V
+  static constexpr int RPI = 64 / UNITS;      // rows per global_load_lds_dwordx4
+  static constexpr int INSTR = 16 / RPI;      // instructions per 16-row sub-block
+  // byte offset of logical chunk c of row r
+  __device__ static int off(int r, int c) { return r * ROW + 16 * (c ^ (r & (UNITS - 1))); }
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Key of a slot for the bf16 kernel: gathered entries come from the staged
+// copy of the column list in LDS.
+__device__ __forceinline__ int32_t desc_key_lds(const Desc& d, const int32_t* lcols, int32_t slot) {
+  int32_t sl = slot < d.count() ? slot : 0;
+  return (d.b & F_LIST) ? lcols[d.a + sl] : d.a + sl;
+}
+
+// Fills descriptors like DescGen::fill, but list sub-blocks refer to a copy of
+// the column list staged in LDS (positions relative to that copy), and at most
+// COLS_CAP entries are staged per call. Entries are clamped into [0, n).
+template <class R>
+__device__ int32_t fill_bf16(DescGen<R>& gen, Desc* d, int32_t* lcols, int32_t tid, int32_t nthreads) {
+  int32_t cnt = 0;
+  while (cnt < BF16_SB_CAP) {
+    if (gen.p >= gen.hi) {
+      int32_t lo2, hi2;
+      if (!gen.ranges.next(lo2, hi2)) break;
+      gen.p = lo2;
+      gen.hi = hi2;
+      continue;
+    }
+    const int32_t take = min((gen.hi - gen.p + 15) >> 4, BF16_SB_CAP - cnt);
+    for (int32_t t = tid; t < take; t += nthreads) {
+      int32_t s = gen.p + 16 * t, c = min(16, gen.hi - s);
+      d[cnt + t] = Desc{s, c | ((c < 16 || s + c - 1 > gen.r0) ? F_MASK : 0)};
+    }
+    cnt += take;
+    gen.p = min(gen.hi, gen.p + 16 * take);
+  }
+  if (cnt < BF16_SB_CAP && gen.cp < gen.n_cols) {
+    const int32_t ncol = min(gen.n_cols - gen.cp, min(COLS_CAP, 16 * (BF16_SB_CAP - cnt)));
+    for (int32_t t = tid; t < ncol; t += nthreads) lcols[t] = min(max(gen.cols[gen.cp + t], 0), gen.n - 1);
+    const int32_t take = (ncol + 15) >> 4;
+    for (int32_t t = tid; t < take; t += nthreads) {
+      int32_t s = 16 * t, c = min(16, ncol - s);
+      bool m = c < 16 || gen.cols[gen.cp + s + c - 1] > gen.r0;
+      d[cnt + t] = Desc{s, c | F_LIST | (m ? F_MASK : 0)};
+    }
+    cnt += take;
+    gen.cp += ncol;
+  }
+  return cnt;
+}
+
+template <int QB>
+__device__ __forceinline__ void mask_tile_lds(f32x4 (&st)[2][QB], const Desc (&d)[2], const int32_t* lcols,
+                                              int32_t q0, int32_t lane) {
+  const int32_t g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    if (d[s2].b & F_MASK) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t slot = 4 * g + i;
+        const bool valid = slot < d[s2].count();
+        const int32_t key = desc_key_lds(d[s2], lcols, slot);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int32_t row = q0 + 16 * qb + l16;
+          if (!valid || key > row) st[s2][qb][i] = -INFINITY;
+        }
+      }
+    }
+  }
+}
+
 template <int D, class R>
 __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __restrict__ ks,
                             const uint16_t* __restrict__ vs, uint16_t* __restrict__ os,
-                            int32_t n, int32_t r0, float scale_log2, KeyGen<R> gen) {
+                            int32_t n, int32_t r0, float scale_log2, DescGen<R> gen) {
+  using L = TileLds<D>;
   constexpr int DS = D / 32;      // MFMA k-steps of Q.K
   constexpr int DB = D / 16;      // 16-dim output blocks
-  constexpr int VTS = 32 + 4;     // bf16 per transposed-V row (72 B, 8-B aligned)
-  constexpr int NCH = D / 64;     // 8-dim chunks of V per lane per tile
-  __shared__ __align__(16) uint16_t vt[D * VTS];
+  __shared__ __align__(16) char ring[2 * L::STAGE];
+  __shared__ Desc desc[BF16_SB_CAP];
+  __shared__ int32_t lcols[COLS_CAP];
 
-  const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+  const int32_t tid = threadIdx.x, lane = tid & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int32_t g = lane >> 4, l16 = lane & 15;
+  const int32_t q0 = r0 + 32 * wave;
 
-  // Q^T operands: query row r0 + 16qb + l16, dims (D/4)g + 8s .. + 7
-  u32x4 qop[4][DS];
+  // Q^T operands: query row q0 + 16qb + l16, dims (D/4)g + 8s .. + 7
+  u32x4 qop[2][DS];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    int32_t row = min(r0 + 16 * qb + l16, n - 1);
+  for (int qb = 0; qb < 2; ++qb) {
+    int32_t row = min(q0 + 16 * qb + l16, n - 1);
     const u32x4* src = reinterpret_cast<const u32x4*>(qs + (size_t)row * D + (D / 4) * g);
 #pragma unroll
     for (int s = 0; s < DS; ++s) qop[qb][s] = src[s];
   }
 
-  f32x4 oacc[DB][4];
+  // per-lane LDS offsets, stage-relative
+  // K operand of step s: row l16 (+16 per sub-block), chunk (D/32)g + s
+  int32_t koff[DS];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int s = 0; s < DS; ++s) koff[s] = L::off(l16, (D / 32) * g + s);
+  // V^T operand of dim block db: row 4g + (l16 >> 2) (+16 for the second
+  // sub-block), dims 16db + 4(l16 & 3) .. +3
+  int32_t voff[DB];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  SoftmaxState ss;
-#pragma unroll
-  for (int qb = 0; qb < 4; ++qb) { ss.m[qb] = NEG_BIG; ss.lsum[qb] = 0.f; }
+  for (int db = 0; db < DB; ++db) {
+    const int32_t r = 4 * g + (l16 >> 2), dim = 16 * db + 4 * (l16 & 3);
+    voff[db] = L::MAT + L::off(r, dim >> 3) + 2 * (dim & 7);
+  }
 
-  const int32_t quad = lane & 7;         // V slots 4quad .. 4quad+3 of the tile
+  // O^T blocks 0..DB-1, and block DB = row sums of P (A operand all ones)
+  f32x4 oacc[DB + 1][2];
+#pragma unroll
+  for (int db = 0; db <= DB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {NEG_BIG, NEG_BIG};
+  const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+
+  // global -> LDS loads of this wave's sub-block of a tile into a ring stage
+  auto issue_loads = [&](const Desc& dw, int stage) {
+    char* kdst = ring + stage * L::STAGE + 16 * wave * L::ROW;
+#pragma unroll
+    for (int k = 0; k < L::INSTR; ++k) {
+      const int32_t rr = k * L::RPI + lane / L::UNITS;            // row within the sub-block
+      const int32_t c = (lane % L::UNITS) ^ ((16 * wave + rr) & (L::UNITS - 1));
+      const int32_t key = desc_key_lds(dw, lcols, rr);
+      const size_t goff = (size_t)key * D + 8 * c;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(ks + goff),
+                                       (__attribute__((address_space(3))) void*)(kdst + k * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(vs + goff),
+                                       (__attribute__((address_space(3))) void*)(kdst + L::MAT + k * 1024), 16, 0, 0);
+    }
+  };
+
   while (true) {
-    SubBlock sb[2];
-    sb[0] = gen.next();
-    if (sb[0].count == 0) break;
-    sb[1] = gen.next();
+    __syncthreads();               // previous refill fully consumed
+    const int32_t cnt = fill_bf16(gen, desc, lcols, tid, BF16_WAVES * 64);
+    if (cnt == 0) break;
+    __syncthreads();
+    const int32_t ntiles = (cnt + 1) >> 1;
+    issue_loads(uniform_desc(desc, wave, cnt), 0);
+    for (int32_t tt = 0; tt < ntiles; ++tt) {
+      const int stage = tt & 1;
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile tt have landed
+      __syncthreads();                 // ... and the other wave's; tile tt-1 is consumed
+      if (tt + 1 < ntiles) issue_loads(uniform_desc(desc, 2 * (tt + 1) + wave, cnt), stage ^ 1);
+      const Desc d[2] = {uniform_desc(desc, 2 * tt, cnt), uniform_desc(desc, 2 * tt + 1, cnt)};
+      const char* sk = ring + stage * L::STAGE;
 
-    // K operands: key slot l16 of each sub-block
-    u32x4 kop[2][DS];
+      // S^T = K Q^T
+      f32x4 st[2][2];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      int32_t key = sb_key(sb[s2], l16, n);
-      const u32x4* src = reinterpret_cast<const u32x4*>(ks + (size_t)key * D + (D / 4) * g);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4 kop[DS];
 #pragma unroll
-      for (int s = 0; s < DS; ++s) kop[s2][s] = src[s];
-    }
-    // V rows for the transpose: 4 slots x 8 dims per chunk
-    u32x4 vraw[NCH][4];
-    {
-      const SubBlock& vsb = sb[quad >> 2];
+        for (int s = 0; s < DS; ++s)
+          kop[s] = *reinterpret_cast<const u32x4*>(sk + koff[s] + s2 * 16 * L::ROW);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        int32_t slot = 4 * (quad & 3) + t;
-        bool valid = slot < vsb.count;
-        int32_t key = sb_key(vsb, slot, n);
+        for (int qb = 0; qb < 2; ++qb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          int32_t chunk = (lane >> 3) + 8 * c;
-          u32x4 x = *reinterpret_cast<const u32x4*>(vs + (size_t)key * D + 8 * chunk);
-          vraw[c][t] = valid ? x : u32x4{0u, 0u, 0u, 0u};
+          for (int s = 0; s < DS; ++s) acc = mfma_bf16(kop[s], qop[qb][s], acc);
+          st[s2][qb] = acc;
         }
       }
-    }
 
-    f32x4 st[2][4];
+      if ((d[0].b | d[1].b) & F_MASK) mask_tile_lds<2>(st, d, lcols, q0, lane);
+      float alpha[2];
+      if (update_max<2>(st, m, scale_log2, alpha)) {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+        for (int db = 0; db <= DB; ++db)
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < DS; ++s) acc = mfma_bf16(kop[s2][s], qop[qb][s], acc);
-        st[s2][qb] = acc;
+          for (int qb = 0; qb < 2; ++qb) oacc[db][qb] *= alpha[qb];
       }
+      exp_tile<2>(st, m, scale_log2);
+      // P^T operands: slots 4g..4g+3 of sub-block 0, then of sub-block 1
+      u32x4 pop[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        pop[qb] = u32x4{pack_bf16x2(st[0][qb][0], st[0][qb][1]), pack_bf16x2(st[0][qb][2], st[0][qb][3]),
+                        pack_bf16x2(st[1][qb][0], st[1][qb][1]), pack_bf16x2(st[1][qb][2], st[1][qb][3])};
 
-    __syncthreads();  // previous tile's reads of vt are done
+      // O^T += V^T P^T
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      int32_t chunk = (lane >> 3) + 8 * c;
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 x0 = lds_read_tr16(sk + voff[db]);
+        const u32x2 x1 = lds_read_tr16(sk + voff[db] + 16 * L::ROW);
+        const u32x4 aop = {x0[0], x0[1], x1[0], x1[1]};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int w = e >> 1;
-        uint32_t a0 = vraw[c][0][w], a1 = vraw[c][1][w], a2 = vraw[c][2][w], a3 = vraw[c][3][w];
-        uint32_t lo, hi;
-        if (e & 1) {
-          lo = (a0 >> 16) | (a1 & 0xffff0000u);
-          hi = (a2 >> 16) | (a3 & 0xffff0000u);
-        } else {
-          lo = (a0 & 0xffffu) | (a1 << 16);
-          hi = (a2 & 0xffffu) | (a3 << 16);
-        }
-        *reinterpret_cast<u32x2*>(&vt[(8 * chunk + e) * VTS + 4 * quad]) = u32x2{lo, hi};
+        for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma_bf16(aop, pop[qb], oacc[db][qb]);
       }
-    }
-
-    mask_tile(st, sb, r0, n, lane);
-    float alpha[4];
-    if (softmax_tile<false>(st, ss, scale_log2, alpha)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) oacc[db][qb] *= alpha[qb];
-    }
-    // P^T operands: slots 4g..4g+3 of sub-block 0, then of sub-block 1; the
-    // row sums add the rounded values
-    u32x4 pop[4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      pop[qb] = u32x4{pack_bf16x2(st[0][qb][0], st[0][qb][1]), pack_bf16x2(st[0][qb][2], st[0][qb][3]),
-                      pack_bf16x2(st[1][qb][0], st[1][qb][1]), pack_bf16x2(st[1][qb][2], st[1][qb][3])};
-      ss.lsum[qb] += (packed_pair_sum(pop[qb][0]) + packed_pair_sum(pop[qb][1])) +
-                     (packed_pair_sum(pop[qb][2]) + packed_pair_sum(pop[qb][3]));
-    }
-
-    __syncthreads();  // vt written
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint16_t* rowp = &vt[(16 * db + l16) * VTS];
-      u32x2 x0 = *reinterpret_cast<const u32x2*>(rowp + 4 * g);
-      u32x2 x1 = *reinterpret_cast<const u32x2*>(rowp + 16 + 4 * g);
-      u32x4 aop = {x0[0], x0[1], x1[0], x1[1]};
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) oacc[db][qb] = mfma_bf16(aop, pop[qb], oacc[db][qb]);
+      for (int qb = 0; qb < 2; ++qb) oacc[DB][qb] = mfma_bf16(ones, pop[qb], oacc[DB][qb]);
     }
   }
 
-  // O = O^T / l: lane writes dims 16db + 4g .. +3 of query r0 + 16qb + l16
+  // O = O^T / l: lane writes dims 16db + 4g .. +3 of query q0 + 16qb + l16
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    float lt = xor_sum(xor_sum(ss.lsum[qb], 16), 32);
-    float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    int32_t row = r0 + 16 * qb + l16;
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = oacc[DB][qb][0];
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int32_t row = q0 + 16 * qb + l16;
     if (row < n) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -355,10 +474,12 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
 template <int D, class R>
 __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict__ ks,
                            const float* __restrict__ vs, float* __restrict__ os, int32_t n,
-                           int32_t r0, float scale_log2, KeyGen<R> gen) {
+                           int32_t r0, float scale_log2, DescGen<R> gen) {
   constexpr int DK = D / 4;   // k-steps of Q.K; lane group g holds dims DK*g .. DK*g + DK-1
   constexpr int DB = D / 16;
+  __shared__ Desc desc[SB_CAP];
   const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+  const int32_t* cols = gen.cols;
 
   float qop[4][DK];
 #pragma unroll
@@ -376,66 +497,73 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  SoftmaxState ss;
-#pragma unroll
-  for (int qb = 0; qb < 4; ++qb) { ss.m[qb] = NEG_BIG; ss.lsum[qb] = 0.f; }
+  float m[4] = {NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 
   while (true) {
-    SubBlock sb[2];
-    sb[0] = gen.next();
-    if (sb[0].count == 0) break;
-    sb[1] = gen.next();
-
-    f32x4 st[2][4];
+    __syncthreads();
+    const int32_t cnt = gen.fill(desc, lane, 64);
+    if (cnt == 0) break;
+    __syncthreads();
+    for (int32_t t = 0; t < cnt; t += 2) {
+      const Desc d[2] = {uniform_desc(desc, t, cnt), uniform_desc(desc, t + 1, cnt)};
+      f32x4 st[2][4];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      int32_t key = sb_key(sb[s2], l16, n);
-      const f32x4* src = reinterpret_cast<const f32x4*>(ks + (size_t)key * D + DK * g);
-      float kop[DK];
+      for (int s2 = 0; s2 < 2; ++s2) {
+        int32_t key = desc_key(d[s2], cols, l16, n);
+        const f32x4* src = reinterpret_cast<const f32x4*>(ks + (size_t)key * D + DK * g);
+        float kop[DK];
 #pragma unroll
-      for (int s = 0; s < DK / 4; ++s) {
-        f32x4 x = src[s];
-        kop[4 * s] = x[0]; kop[4 * s + 1] = x[1]; kop[4 * s + 2] = x[2]; kop[4 * s + 3] = x[3];
-      }
+        for (int s = 0; s < DK / 4; ++s) {
+          f32x4 x = src[s];
+          kop[4 * s] = x[0]; kop[4 * s + 1] = x[1]; kop[4 * s + 2] = x[2]; kop[4 * s + 3] = x[3];
+        }
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < 4; ++qb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < DK; ++s) acc = mfma_f32(kop[s], qop[qb][s], acc);
-        st[s2][qb] = acc;
-      }
-    }
-
-    mask_tile(st, sb, r0, n, lane);
-    float alpha[4];
-    if (softmax_tile<true>(st, ss, scale_log2, alpha)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) oacc[db][qb] *= alpha[qb];
-    }
-    // O^T += V^T P^T, one MFMA per (sub-block, i): lane group g carries key
-    // slot 4g + i, whose V row the lane reads at dim 16db + l16.
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int32_t slot = 4 * g + i;
-        bool valid = slot < sb[s2].count;
-        int32_t key = sb_key(sb[s2], slot, n);
-        const float* vrow = vs + (size_t)key * D + l16;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          float a = valid ? vrow[16 * db] : 0.f;
-#pragma unroll
-          for (int qb = 0; qb < 4; ++qb) oacc[db][qb] = mfma_f32(a, st[s2][qb][i], oacc[db][qb]);
+          for (int s = 0; s < DK; ++s) acc = mfma_f32(kop[s], qop[qb][s], acc);
+          st[s2][qb] = acc;
         }
       }
+      if ((d[0].b | d[1].b) & F_MASK) mask_tile<4>(st, d, cols, r0, n, lane);
+      float alpha[4];
+      if (update_max<4>(st, m, scale_log2, alpha)) {
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          lsum[qb] *= alpha[qb];
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha[qb];
+        }
+      }
+      exp_tile<4>(st, m, scale_log2);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) lsum[qb] += (st[s2][qb][0] + st[s2][qb][1]) + (st[s2][qb][2] + st[s2][qb][3]);
+      // O^T += V^T P^T, one MFMA per (sub-block, i): lane group g carries key
+      // slot 4g + i, whose V row the lane reads at dim 16db + l16.
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int32_t slot = 4 * g + i;
+          bool valid = slot < d[s2].count();
+          int32_t key = desc_key(d[s2], cols, slot, n);
+          const float* vrow = vs + (size_t)key * D + l16;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            float a = valid ? vrow[16 * db] : 0.f;
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) oacc[db][qb] = mfma_f32(a, st[s2][qb][i], oacc[db][qb]);
+          }
+        }
+    }
   }
 
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
-    float lt = xor_sum(xor_sum(ss.lsum[qb], 16), 32);
+    float lt = xor_sum(xor_sum(lsum[qb], 16), 32);
     float inv = lt > 0.f ? 1.0f / lt : 0.f;
     int32_t row = r0 + 16 * qb + l16;
     if (row < n) {
@@ -450,7 +578,7 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
 // kernels per index mode
 // ---------------------------------------------------------------------------
 template <typename T, int D, class R>
-__device__ __forceinline__ void attend(const AttnArgs& a, int32_t row, int32_t r0, KeyGen<R> gen) {
+__device__ __forceinline__ void attend(const AttnArgs& a, int32_t row, int32_t r0, DescGen<R> gen) {
   const size_t qoff = a.hm.q_slab(row, a.seq_len, D);
   const size_t kvoff = a.hm.kv_slab(row, a.seq_len, D);
   if constexpr (sizeof(T) == 2) {
@@ -465,47 +593,51 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int32_t row, int32_t r
   }
 }
 
+template <class R>
+__device__ __forceinline__ DescGen<R> make_gen(R r, const int32_t* cols, int32_t n_cols, int32_t r0,
+                                               int32_t n) {
+  DescGen<R> g;
+  g.ranges = r;
+  g.cols = cols;
+  g.n_cols = n_cols;
+  g.p = g.hi = g.cp = 0;
+  g.r0 = r0;
+  g.n = n;
+  return g;
+}
+
+template <typename T> constexpr int threads_of() { return sizeof(T) == 2 ? 64 * BF16_WAVES : 64; }
+template <typename T> constexpr int waves_per_eu() { return sizeof(T) == 2 ? 2 : 1; }
+
 template <typename T, int D>
-__global__ __launch_bounds__(64) void attn_vs_kernel(AttnArgs a, VsIndex ix) {
+__global__ __launch_bounds__(threads_of<T>()) __attribute__((amdgpu_waves_per_eu(waves_per_eu<T>(), waves_per_eu<T>()))) void attn_vs_kernel(AttnArgs a, VsIndex ix) {
   const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
   int32_t row, blk;
   work_item(nb, row, blk);
   const int32_t r0 = blk * BLOCK;
-  KeyGen<VsRanges> gen;
-  gen.ranges = VsRanges{ix.iv + (size_t)row * ix.max_iv * 2, min(ix.n_iv[row], ix.max_iv), 0, r0,
-                        a.seq_len};
   const size_t cb = (size_t)row * nb + blk;
-  gen.cols = ix.cols + cb * ix.max_cols;
-  gen.n_cols = min(ix.n_cols[cb], ix.max_cols);
-  gen.p = gen.hi = gen.cp = 0;
-  attend<T, D>(a, row, r0, gen);
+  VsRanges rg{ix.iv + (size_t)row * ix.max_iv * 2, min(ix.n_iv[row], ix.max_iv), 0, r0, a.seq_len};
+  attend<T, D>(a, row, r0,
+               make_gen(rg, ix.cols + cb * ix.max_cols, min(ix.n_cols[cb], ix.max_cols), r0, a.seq_len));
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(64) void attn_blocks_kernel(AttnArgs a, BlockIndex ix) {
+__global__ __launch_bounds__(threads_of<T>()) __attribute__((amdgpu_waves_per_eu(waves_per_eu<T>(), waves_per_eu<T>()))) void attn_blocks_kernel(AttnArgs a, BlockIndex ix) {
   const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
   int32_t row, blk;
   work_item(nb, row, blk);
   const size_t cb = (size_t)row * nb + blk;
-  KeyGen<BlockRanges> gen;
-  gen.ranges = BlockRanges{ix.sel + cb * ix.max_sel, min(ix.n_sel[cb], ix.max_sel), 0, a.seq_len};
-  gen.cols = nullptr;
-  gen.n_cols = 0;
-  gen.p = gen.hi = gen.cp = 0;
-  attend<T, D>(a, row, blk * BLOCK, gen);
+  BlockRanges rg{ix.sel + cb * ix.max_sel, min(ix.n_sel[cb], ix.max_sel), 0, a.seq_len};
+  attend<T, D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a, StreamIndex ix) {
+__global__ __launch_bounds__(threads_of<T>()) __attribute__((amdgpu_waves_per_eu(waves_per_eu<T>(), waves_per_eu<T>()))) void attn_stream_kernel(AttnArgs a, StreamIndex ix) {
   const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
   int32_t row, blk;
   work_item(nb, row, blk);
-  KeyGen<StreamRanges> gen;
-  gen.ranges = StreamRanges{blk, ix.init_blocks, ix.local_blocks, 0, a.seq_len};
-  gen.cols = nullptr;
-  gen.n_cols = 0;
-  gen.p = gen.hi = gen.cp = 0;
-  attend<T, D>(a, row, blk * BLOCK, gen);
+  StreamRanges rg{blk, ix.init_blocks, ix.local_blocks, 0, a.seq_len};
+  attend<T, D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
 }
 
 }  // namespace
@@ -516,7 +648,7 @@ hipError_t launch_attention_vs(const AttnArgs& a, const VsIndex& ix, hipStream_t
   if (grid == 0) return hipSuccess;
   auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_vs_kernel<uint16_t, 64> : attn_vs_kernel<uint16_t, 128>)
                             : (a.head_dim == 64 ? attn_vs_kernel<float, 64> : attn_vs_kernel<float, 128>);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64), 0, s, a, ix);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(a.dtype == BF16 ? 64 * BF16_WAVES : 64), 0, s, a, ix);
   return hipGetLastError();
 }
 
@@ -526,7 +658,7 @@ hipError_t launch_attention_blocks(const AttnArgs& a, const BlockIndex& ix, hipS
   if (grid == 0) return hipSuccess;
   auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_blocks_kernel<uint16_t, 64> : attn_blocks_kernel<uint16_t, 128>)
                             : (a.head_dim == 64 ? attn_blocks_kernel<float, 64> : attn_blocks_kernel<float, 128>);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64), 0, s, a, ix);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(a.dtype == BF16 ? 64 * BF16_WAVES : 64), 0, s, a, ix);
   return hipGetLastError();
 }
 
@@ -536,7 +668,7 @@ hipError_t launch_attention_stream(const AttnArgs& a, const StreamIndex& ix, hip
   if (grid == 0) return hipSuccess;
   auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_stream_kernel<uint16_t, 64> : attn_stream_kernel<uint16_t, 128>)
                             : (a.head_dim == 64 ? attn_stream_kernel<float, 64> : attn_stream_kernel<float, 128>);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64), 0, s, a, ix);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(a.dtype == BF16 ? 64 * BF16_WAVES : 64), 0, s, a, ix);
   return hipGetLastError();
 }
 
