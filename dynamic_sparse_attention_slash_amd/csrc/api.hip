@@ -79,6 +79,7 @@ AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, const d
   a.rows = s->batch * hm.n;
   a.scale_log2 = eff_scale(scale, s->head_dim) * LOG2E;
   a.hm = hm;
+  a.wo = make_work_order(hm);
   return a;
 }
 
@@ -146,6 +147,23 @@ hipError_t bs_select_rows(const float* qp, const float* kp, int32_t rows, int32_
 }
 
 }  // namespace
+
+namespace dsa {
+WorkOrder make_work_order(const HeadMap& hm) {
+  WorkOrder wo;
+  memset(&wo, 0, sizeof(wo));
+  const int32_t G = hm.q_heads / hm.kv_heads;
+  int32_t pos = 0;
+  for (int32_t kv = 0; kv < hm.kv_heads; ++kv) {
+    const int32_t start = pos;
+    for (int32_t t = 0; t < hm.n; ++t)
+      if (hm.h[t] / G == kv) wo.order[pos++] = (int16_t)t;
+    if (pos > start) wo.gstart[wo.n_groups++] = (int16_t)start;
+  }
+  wo.gstart[wo.n_groups] = (int16_t)pos;
+  return wo;
+}
+}  // namespace dsa
 
 extern "C" {
 

@@ -25,12 +25,25 @@ struct StreamIndex {   // closed-form A-shape
   int32_t init_blocks, local_blocks;
 };
 
+// Order of the attention work items (row, query block): batch, then the
+// groups of listed heads that share a kv head (kv-head order), then query
+// blocks (latest first), then the heads of the group. The heads of a group
+// read the same K/V rows, and neighbouring query blocks of a head read largely
+// the same key ranges, so items close in this order share data.
+struct WorkOrder {
+  int16_t order[MAX_HEADS];       // listed-head positions sorted by kv head
+  int16_t gstart[MAX_HEADS + 1];  // group g is order[gstart[g] .. gstart[g+1])
+  int32_t n_groups;
+};
+WorkOrder make_work_order(const HeadMap& hm);
+
 struct AttnArgs {
   const void* q; const void* k; const void* v; void* o;
   int32_t seq_len, head_dim, dtype;
   int32_t rows;        // batch * listed heads
   float scale_log2;    // softmax scale * log2(e)
   HeadMap hm;
+  WorkOrder wo;
 };
 
 hipError_t launch_attention_vs(const AttnArgs& a, const VsIndex& ix, hipStream_t s);

@@ -142,12 +142,32 @@ __device__ __forceinline__ int32_t desc_key(const Desc& d, const int32_t* cols, 
   return (d.b & F_LIST) ? min(max(cols[d.a + sl], 0), n - 1) : d.a + sl;
 }
 
-// Work-group -> (row, query block). Blocks of one row go to consecutive
-// work-groups, latest (largest key set) first.
-__device__ __forceinline__ void work_item(int32_t nb, int32_t& row, int32_t& a) {
-  int32_t w = blockIdx.x;
-  row = w / nb;
-  a = nb - 1 - (w - row * nb);
+// Work-group -> (row, query block). The hardware deals consecutive work-group
+// ids round-robin over the 8 XCDs, each with its own L2. Work items, ordered
+// by WorkOrder, are cut into chunks of XCD_CHUNK and the chunks are dealt
+// round-robin to the XCDs: the work-groups an XCD runs at one time then share
+// K/V rows in its L2, and every XCD still gets a mix of all kv groups and block
+// positions (whose costs differ). A tail shorter than NUM_XCD chunks keeps the
+// identity mapping.
+constexpr int32_t NUM_XCD = 8;
+constexpr int32_t XCD_CHUNK = 32;
+__device__ __forceinline__ void work_item(const AttnArgs& ar, int32_t nb, int32_t& row, int32_t& a) {
+  const int32_t N = gridDim.x, i = blockIdx.x;
+  const int32_t T = (N / (NUM_XCD * XCD_CHUNK)) * (NUM_XCD * XCD_CHUNK);
+  int32_t w = i;
+  if (i < T) {
+    const int32_t xcd = i % NUM_XCD, k = i / NUM_XCD;
+    w = ((k / XCD_CHUNK) * NUM_XCD + xcd) * XCD_CHUNK + k % XCD_CHUNK;
+  }
+  const int32_t n = ar.hm.n, per_b = nb * n;
+  const int32_t b = w / per_b, w2 = w - b * per_b;
+  int32_t gi = 0;
+  while (gi + 1 < ar.wo.n_groups && ar.wo.gstart[gi + 1] * nb <= w2) ++gi;
+  const int32_t g0 = ar.wo.gstart[gi], size = ar.wo.gstart[gi + 1] - g0;
+  const int32_t off = w2 - g0 * nb;
+  const int32_t a_idx = off / size, j = off - a_idx * size;
+  row = b * n + ar.wo.order[g0 + j];
+  a = nb - 1 - a_idx;
 }
 
 // ---------------------------------------------------------------------------
@@ -324,6 +344,19 @@ __device__ __forceinline__ void mask_tile_lds(f32x4 (&st)[2][QB], const Desc (&d
   }
 }
 
+// Row max over the four lane groups (lanes l, l^16, l^32, l^48 hold the same
+// query column): gfx950 permlane swaps exchange 16-lane rows without LDS.
+__device__ __forceinline__ float group_max4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const uint32_t v = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int D, class R>
 __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __restrict__ ks,
                             const uint16_t* __restrict__ vs, uint16_t* __restrict__ os,
@@ -331,7 +364,10 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
   using L = TileLds<D>;
   constexpr int DS = D / 32;      // MFMA k-steps of Q.K
   constexpr int DB = D / 16;      // 16-dim output blocks
-  __shared__ __align__(16) char ring[2 * L::STAGE];
+  // two ring stages in distinct arrays: the compiler can then prove that the
+  // loads in flight into one stage do not alias the reads of the other
+  __shared__ __align__(16) char ring0[L::STAGE];
+  __shared__ __align__(16) char ring1[L::STAGE];
   __shared__ Desc desc[BF16_SB_CAP];
   __shared__ int32_t lcols[COLS_CAP];
 
@@ -350,7 +386,7 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
     for (int s = 0; s < DS; ++s) qop[qb][s] = src[s];
   }
 
-  // per-lane LDS offsets, stage-relative
+  // per-lane LDS offsets within a stage
   // K operand of step s: row l16 (+16 per sub-block), chunk (D/32)g + s
   int32_t koff[DS];
 #pragma unroll
@@ -363,6 +399,18 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
     const int32_t r = 4 * g + (l16 >> 2), dim = 16 * db + 4 * (l16 & 3);
     voff[db] = L::MAT + L::off(r, dim >> 3) + 2 * (dim & 7);
   }
+  // global -> LDS load k of this wave's sub-block: lane takes row rr(k) of the
+  // sub-block at logical chunk c(k), landing at LDS byte 16*lane of the load
+  int32_t ld_row[L::INSTR], ld_off[L::INSTR];
+#pragma unroll
+  for (int k = 0; k < L::INSTR; ++k) {
+    ld_row[k] = k * L::RPI + lane / L::UNITS;
+    const int32_t c = (lane % L::UNITS) ^ ((16 * wave + ld_row[k]) & (L::UNITS - 1));
+    ld_off[k] = ld_row[k] * L::ROW + 16 * c;    // + first key * ROW for a range
+  }
+  const uint32_t slab_bytes = (uint32_t)n * L::ROW;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)ks, (short)0, slab_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vs, (short)0, slab_bytes, 0x00020000);
 
   // O^T blocks 0..DB-1, and block DB = row sums of P (A operand all ones)
   f32x4 oacc[DB + 1][2];
@@ -373,20 +421,93 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
   float m[2] = {NEG_BIG, NEG_BIG};
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 
-  // global -> LDS loads of this wave's sub-block of a tile into a ring stage
-  auto issue_loads = [&](const Desc& dw, int stage) {
-    char* kdst = ring + stage * L::STAGE + 16 * wave * L::ROW;
+  // loads of this wave's sub-block dw into a stage. Range sub-blocks use the
+  // first key as the scalar offset; slots past the count read the rows that
+  // follow (or zeros past the end of the slab) and are masked out later.
+  auto issue_loads = [&](const Desc& dw, char* stage) {
+    char* dst = stage + 16 * wave * L::ROW;
+    if (dw.b & F_LIST) {
 #pragma unroll
-    for (int k = 0; k < L::INSTR; ++k) {
-      const int32_t rr = k * L::RPI + lane / L::UNITS;            // row within the sub-block
-      const int32_t c = (lane % L::UNITS) ^ ((16 * wave + rr) & (L::UNITS - 1));
-      const int32_t key = desc_key_lds(dw, lcols, rr);
-      const size_t goff = (size_t)key * D + 8 * c;
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(ks + goff),
-                                       (__attribute__((address_space(3))) void*)(kdst + k * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(vs + goff),
-                                       (__attribute__((address_space(3))) void*)(kdst + L::MAT + k * 1024), 16, 0, 0);
+      for (int k = 0; k < L::INSTR; ++k) {
+        const int32_t key = lcols[dw.a + min(ld_row[k], max(dw.count() - 1, 0))];
+        const int32_t vo = ld_off[k] + (key - ld_row[k]) * L::ROW;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + k * 1024), 16, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + L::MAT + k * 1024), 16, vo, 0, 0, 0);
+      }
+    } else {
+      const int32_t so = dw.a * L::ROW;
+#pragma unroll
+      for (int k = 0; k < L::INSTR; ++k) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + k * 1024), 16, ld_off[k], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + L::MAT + k * 1024), 16, ld_off[k], so, 0, 0);
+      }
     }
+  };
+
+  // one tile: wait for its loads, start the next tile's, compute
+  auto tile = [&](int32_t tt, int32_t ntiles, int32_t cnt, const char* cur, char* nxt) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile tt have landed
+    __syncthreads();                 // ... and the other wave's; tile tt-1 is consumed
+    if (tt + 1 < ntiles) issue_loads(uniform_desc(desc, 2 * (tt + 1) + wave, cnt), nxt);
+    const Desc d[2] = {uniform_desc(desc, 2 * tt, cnt), uniform_desc(desc, 2 * tt + 1, cnt)};
+
+    // S^T = K Q^T
+    f32x4 st[2][2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 kop[DS];
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+        kop[s] = *reinterpret_cast<const u32x4*>(cur + koff[s] + s2 * 16 * L::ROW);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) acc = mfma_bf16(kop[s], qop[qb][s], acc);
+        st[s2][qb] = acc;
+      }
+    }
+
+    if ((d[0].b | d[1].b) & F_MASK) mask_tile_lds<2>(st, d, lcols, q0, lane);
+    // running max (raised only past a 2^8 margin), rescale when raised
+    float mt[2];
+    bool up_any = false;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = fmaxf(__builtin_fmaxf(fmaxf(st[0][qb][0], st[0][qb][1]), fmaxf(st[0][qb][2], st[0][qb][3])),
+                       fmaxf(fmaxf(st[1][qb][0], st[1][qb][1]), fmaxf(st[1][qb][2], st[1][qb][3])));
+      mt[qb] = group_max4(mx) * scale_log2;
+      up_any |= mt[qb] > m[qb] + 8.0f;
+    }
+    if (__any(up_any)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const bool up = mt[qb] > m[qb] + 8.0f;
+        const float alpha = up ? fast_exp2(m[qb] - mt[qb]) : 1.0f;
+        m[qb] = up ? mt[qb] : m[qb];
+#pragma unroll
+        for (int db = 0; db <= DB; ++db) oacc[db][qb] *= alpha;
+      }
+    }
+    exp_tile<2>(st, m, scale_log2);
+    // P^T operands: slots 4g..4g+3 of sub-block 0, then of sub-block 1
+    u32x4 pop[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      pop[qb] = u32x4{pack_bf16x2(st[0][qb][0], st[0][qb][1]), pack_bf16x2(st[0][qb][2], st[0][qb][3]),
+                      pack_bf16x2(st[1][qb][0], st[1][qb][1]), pack_bf16x2(st[1][qb][2], st[1][qb][3])};
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const u32x2 x0 = lds_read_tr16(cur + voff[db]);
+      const u32x2 x1 = lds_read_tr16(cur + voff[db] + 16 * L::ROW);
+      const u32x4 aop = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma_bf16(aop, pop[qb], oacc[db][qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) oacc[DB][qb] = mfma_bf16(ones, pop[qb], oacc[DB][qb]);
   };
 
   while (true) {
@@ -395,59 +516,10 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
     if (cnt == 0) break;
     __syncthreads();
     const int32_t ntiles = (cnt + 1) >> 1;
-    issue_loads(uniform_desc(desc, wave, cnt), 0);
-    for (int32_t tt = 0; tt < ntiles; ++tt) {
-      const int stage = tt & 1;
-      __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile tt have landed
-      __syncthreads();                 // ... and the other wave's; tile tt-1 is consumed
-      if (tt + 1 < ntiles) issue_loads(uniform_desc(desc, 2 * (tt + 1) + wave, cnt), stage ^ 1);
-      const Desc d[2] = {uniform_desc(desc, 2 * tt, cnt), uniform_desc(desc, 2 * tt + 1, cnt)};
-      const char* sk = ring + stage * L::STAGE;
-
-      // S^T = K Q^T
-      f32x4 st[2][2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 kop[DS];
-#pragma unroll
-        for (int s = 0; s < DS; ++s)
-          kop[s] = *reinterpret_cast<const u32x4*>(sk + koff[s] + s2 * 16 * L::ROW);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < DS; ++s) acc = mfma_bf16(kop[s], qop[qb][s], acc);
-          st[s2][qb] = acc;
-        }
-      }
-
-      if ((d[0].b | d[1].b) & F_MASK) mask_tile_lds<2>(st, d, lcols, q0, lane);
-      float alpha[2];
-      if (update_max<2>(st, m, scale_log2, alpha)) {
-#pragma unroll
-        for (int db = 0; db <= DB; ++db)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) oacc[db][qb] *= alpha[qb];
-      }
-      exp_tile<2>(st, m, scale_log2);
-      // P^T operands: slots 4g..4g+3 of sub-block 0, then of sub-block 1
-      u32x4 pop[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        pop[qb] = u32x4{pack_bf16x2(st[0][qb][0], st[0][qb][1]), pack_bf16x2(st[0][qb][2], st[0][qb][3]),
-                        pack_bf16x2(st[1][qb][0], st[1][qb][1]), pack_bf16x2(st[1][qb][2], st[1][qb][3])};
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x2 x0 = lds_read_tr16(sk + voff[db]);
-        const u32x2 x1 = lds_read_tr16(sk + voff[db] + 16 * L::ROW);
-        const u32x4 aop = {x0[0], x0[1], x1[0], x1[1]};
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma_bf16(aop, pop[qb], oacc[db][qb]);
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) oacc[DB][qb] = mfma_bf16(ones, pop[qb], oacc[DB][qb]);
+    issue_loads(uniform_desc(desc, wave, cnt), ring0);
+    for (int32_t tt = 0; tt < ntiles; tt += 2) {
+      tile(tt, ntiles, cnt, ring0, ring1);
+      if (tt + 1 < ntiles) tile(tt + 1, ntiles, cnt, ring1, ring0);
     }
   }
 
@@ -613,7 +685,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(threads_of<T>()) __attribute__((amdgpu_waves_per_eu(waves_per_eu<T>(), waves_per_eu<T>()))) void attn_vs_kernel(AttnArgs a, VsIndex ix) {
   const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
   int32_t row, blk;
-  work_item(nb, row, blk);
+  work_item(a, nb, row, blk);
   const int32_t r0 = blk * BLOCK;
   const size_t cb = (size_t)row * nb + blk;
   VsRanges rg{ix.iv + (size_t)row * ix.max_iv * 2, min(ix.n_iv[row], ix.max_iv), 0, r0, a.seq_len};
@@ -625,7 +697,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(threads_of<T>()) __attribute__((amdgpu_waves_per_eu(waves_per_eu<T>(), waves_per_eu<T>()))) void attn_blocks_kernel(AttnArgs a, BlockIndex ix) {
   const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
   int32_t row, blk;
-  work_item(nb, row, blk);
+  work_item(a, nb, row, blk);
   const size_t cb = (size_t)row * nb + blk;
   BlockRanges rg{ix.sel + cb * ix.max_sel, min(ix.n_sel[cb], ix.max_sel), 0, a.seq_len};
   attend<T, D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
@@ -635,7 +707,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(threads_of<T>()) __attribute__((amdgpu_waves_per_eu(waves_per_eu<T>(), waves_per_eu<T>()))) void attn_stream_kernel(AttnArgs a, StreamIndex ix) {
   const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
   int32_t row, blk;
-  work_item(nb, row, blk);
+  work_item(a, nb, row, blk);
   StreamRanges rg{blk, ix.init_blocks, ix.local_blocks, 0, a.seq_len};
   attend<T, D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
 }
