@@ -7,17 +7,33 @@ block selection, attention) and streaming heads (attention), each call over
 its head subset, all writing one output tensor, on one stream. Inputs are
 seeded synthetic tensors resident in HBM before timing starts.
 
+Default workload: the 1M-token Llama-3-8B-shaped mixed layer (the named
+workload that runs every step of the path); the 128K layer is timed beside it.
+
 Prints one JSON line. `value` is the effective TFLOP/s of the layer: the
 attention FLOPs of the computed key blocks (4 * head_dim * sum over query
 blocks of rows x keys, before the causal trim of the diagonal tile) divided by
 the measured layer time. `roofline` reports the dominant kernel (the
 vertical-slash attention launch) against the bf16 MFMA peak, timed alone with
-HIP events on the stream it runs on. `cpu_baseline` times the CPU oracle on a
-bounded sample of the same layer and scales it to the whole layer.
+HIP events on the stream it runs on; its `traffic` comes from the committed
+rocprofv3 counter summary when that summary was taken on the current kernel
+source. `cpu_baseline` times the CPU oracle on a bounded sample of the same
+layer and scales it to the whole layer.
+
+Other modes:
+  --copy-probe MIB      also run one plain device copy of MIB MiB (a counter
+                        calibration point for rocprofv3 --pmc runs)
+  --summarize-pmc DIR   read rocprofv3 --pmc CSVs under DIR (FETCH_SIZE and
+                        WRITE_SIZE passes of a run with --copy-probe) and print
+                        the per-launch traffic summary as JSON (--record also
+                        stores it for --workload in profiles/traffic.json)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -37,10 +53,17 @@ BLK = 64
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "dynamic_sparse_attention_slash_amd", "csrc", "sparse_attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+DOMINANT = "attn_vs_kernel"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path=ATTN_SRC):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
 # ----------------------------------------------------------------------------
@@ -69,25 +92,23 @@ def vs_keys_per_block(iv, n_iv, n_cols, n):
 
 
 def bs_keys_per_block(sel, n_sel, n):
-    sel, n_sel = sel.cpu().numpy(), n_sel.cpu().numpy()
-    rows, nb, _ = sel.shape
+    sel, n_sel = sel.cpu().numpy(), n_sel.cpu().numpy().astype(np.int64)
+    rows, nb, kmax = sel.shape
     last = n - BLK * (nb - 1)
-    keys = np.zeros((rows, nb), np.int64)
-    for r in range(rows):
-        for a in range(nb):
-            cs = sel[r, a, : n_sel[r, a]]
-            keys[r, a] = BLK * len(cs) - (BLK - last) * int((cs == nb - 1).sum())
-    return keys
+    valid = np.arange(kmax)[None, None, :] < n_sel[:, :, None]
+    has_last = ((sel == nb - 1) & valid).sum(axis=2)
+    return BLK * n_sel - (BLK - last) * has_last
 
 
 def st_keys_per_block(n, init_blocks, local_blocks):
     nb = (n + BLK - 1) // BLK
     last = n - BLK * (nb - 1)
-    keys = np.zeros(nb, np.int64)
-    for a in range(nb):
-        cs = [c for c in range(a + 1) if c < init_blocks or a - c < local_blocks]
-        keys[a] = BLK * len(cs) - (BLK - last) * (nb - 1 in cs)
-    return keys
+    a = np.arange(nb)
+    sink = np.minimum(init_blocks, a + 1)
+    local_start = np.maximum(a - local_blocks + 1, sink)
+    nblk = sink + np.maximum(0, a - local_start + 1)
+    has_last = (nb - 1 < sink) | ((nb - 1 >= local_start) & (nb - 1 <= a))
+    return BLK * nblk - (BLK - last) * has_last
 
 
 def attn_flops(keys_rows_blocks, n, D):
@@ -103,7 +124,6 @@ class Layer:
         self.w, self.x = w, x
         self.q, self.k, self.v = x.q, x.k, x.v
         self.o = torch.zeros_like(self.q)
-        self.hp = {p: (hs if hs else None) for p, hs in x.heads.items()}
         all_vs = len(x.heads["vs"]) == w.q_heads
         self.vs_heads = None if all_vs else x.heads["vs"]
         self.ws_vs = self.ws_bs = None
@@ -128,25 +148,6 @@ class Layer:
             dsa.streaming_attention(self.q, self.k, self.v, w.init_blocks, w.local_blocks,
                                     heads=x.heads["st"], out=self.o)
 
-    # indices of the vertical-slash and block-sparse heads through the stage calls
-    def indices(self):
-        w, x = self.w, self.x
-        out = {}
-        if x.heads["vs"]:
-            vg, sg = dsa.vs_estimate(self.q, self.k, last_q=w.last_q, heads=x.heads["vs"])
-            V = dsa.topk(vg, w.vertical_topk)
-            S = dsa.topk(sg, w.slash_topk, 0)
-            out["vs"] = dsa.vs_build_index(V, S, w.seq_len)
-            del vg, sg
-        if x.heads["bs"]:
-            qp = dsa.bs_pool(self.q, x.heads["bs"])
-            kp_all = dsa.bs_pool(self.k)
-            G = w.q_heads // w.kv_heads
-            idx = torch.tensor([b * w.kv_heads + h // G for b in range(w.batch) for h in x.heads["bs"]],
-                               device=self.q.device)
-            out["bs"] = dsa.bs_select(qp, kp_all[idx].contiguous(), w.topk)
-        return out
-
 
 def time_events(fn, reps):
     """Average ms per call of fn, HIP events on torch's current stream (the
@@ -162,10 +163,76 @@ def time_events(fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def stages(layer, reps):
+    """Each stage of the layer through the stage calls, timed alone; also
+    returns the indices (for the FLOP accounting)."""
+    w, x = layer.w, layer.x
+    q, k, v, o = layer.q, layer.k, layer.v, layer.o
+    t, idx = {}, {}
+    if x.heads["vs"]:
+        hs = x.heads["vs"]
+        vg, sg = dsa.vs_estimate(q, k, last_q=w.last_q, heads=hs)
+        t["vs_estimate_ms"] = time_events(lambda: dsa.vs_estimate(q, k, last_q=w.last_q, heads=hs), reps)
+        V = dsa.topk(vg, w.vertical_topk)
+        S = dsa.topk(sg, w.slash_topk, 0)
+        t["vs_topk_ms"] = time_events(lambda: (dsa.topk(vg, w.vertical_topk), dsa.topk(sg, w.slash_topk, 0)), reps)
+        ix = dsa.vs_build_index(V, S, w.seq_len)
+        t["vs_index_ms"] = time_events(lambda: dsa.vs_build_index(V, S, w.seq_len), reps)
+        t["vs_attention_ms"] = time_events(lambda: dsa.sparse_attention_vs(q, k, v, *ix, heads=hs, out=o), reps)
+        idx["vs"] = ix
+        del vg, sg
+    if x.heads["bs"]:
+        hs = x.heads["bs"]
+        G = w.q_heads // w.kv_heads
+        sel_rows = torch.tensor([b * w.kv_heads + h // G for b in range(w.batch) for h in hs], device=q.device)
+        qp = dsa.bs_pool(q, hs)
+        kp_all = dsa.bs_pool(k)
+        t["bs_pool_ms"] = time_events(lambda: (dsa.bs_pool(q, hs), dsa.bs_pool(k)), reps)
+        kp = kp_all[sel_rows].contiguous()
+        sel, n_sel = dsa.bs_select(qp, kp, w.topk)
+        t["bs_select_ms"] = time_events(lambda: dsa.bs_select(qp, kp, w.topk), reps)
+        t["bs_attention_ms"] = time_events(lambda: dsa.sparse_attention_blocks(q, k, v, sel, n_sel, heads=hs, out=o), reps)
+        idx["bs"] = (sel, n_sel)
+        del qp, kp, kp_all
+    if x.heads["st"]:
+        hs = x.heads["st"]
+        t["st_attention_ms"] = time_events(lambda: dsa.streaming_attention(q, k, v, w.init_blocks, w.local_blocks, heads=hs, out=o), reps)
+    return t, idx
+
+
+def layer_flops(w, x, idx):
+    n, D = w.seq_len, w.head_dim
+    fl = {}
+    if "vs" in idx:
+        iv, n_iv, cols, n_cols = idx["vs"]
+        fl["vs"] = attn_flops(vs_keys_per_block(iv, n_iv, n_cols, n), n, D)
+    if "bs" in idx:
+        fl["bs"] = attn_flops(bs_keys_per_block(*idx["bs"], n), n, D)
+    if x.heads["st"]:
+        fl["st"] = attn_flops(st_keys_per_block(n, w.init_blocks, w.local_blocks), n, D) \
+            * w.batch * len(x.heads["st"])
+    return fl
+
+
 # ----------------------------------------------------------------------------
 # CPU oracle on a bounded sample
 # ----------------------------------------------------------------------------
-def cpu_baseline(layer, idx, flops_total, budget_blocks=6):
+def _sampled_blocks(nb, rng, seconds, max_blocks, fn):
+    """Run fn(a) on random query blocks until `seconds` of CPU time are spent
+    (at least two blocks, at most max_blocks); returns (seconds, rows x keys,
+    blocks)."""
+    t_sum, rk_sum, done = 0.0, 0, 0
+    for a in rng.permutation(nb)[:max_blocks]:
+        t0 = time.perf_counter()
+        rk_sum += fn(int(a))
+        t_sum += time.perf_counter() - t0
+        done += 1
+        if done >= 2 and t_sum >= seconds:
+            break
+    return t_sum, rk_sum, done
+
+
+def cpu_baseline(layer, idx, flops_total, seconds=(12.0, 5.0, 1.0)):
     from oracle import dsa_oracle as O
     w, x = layer.w, layer.x
     n, D = w.seq_len, w.head_dim
@@ -184,173 +251,220 @@ def cpu_baseline(layer, idx, flops_total, budget_blocks=6):
         V, S = O.vs_select(O.to_f32(v64), O.to_f32(s64), w.vertical_topk, w.slash_topk)
         iv = O.merge_offsets(S)
         t_est = time.perf_counter() - t0
-        blocks = rng.choice(nb, budget_blocks, replace=False)
-        t0 = time.perf_counter()
-        keys_s = 0
-        for a in blocks:
-            keys = O.vs_block_keys(iv, V, int(a), n)
+
+        def vs_block(a):
+            keys = O.vs_block_keys(iv, V, a, n)
             rows = np.arange(a * BLK, min(n, a * BLK + BLK))
             O.masked_attention(qh[rows], rows, keys, kh, vh, sc)
-            keys_s += len(keys) * len(rows)
-        t_att = time.perf_counter() - t0
-        # scale: estimate per head, attention per (row x key) of all VS heads
+            return len(keys) * len(rows)
+        t_att, keys_s, nblk = _sampled_blocks(nb, rng, seconds[0], 64, vs_block)
         iv_g, n_iv_g, cols_g, n_cols_g = idx["vs"]
-        keys_all = vs_keys_per_block(iv_g, n_iv_g, n_cols_g, n)
-        rk_all = float((keys_all * rows_per_block(n)).sum())
-        rows_vs = w.batch * len(x.heads["vs"])
-        t_total += t_est * rows_vs + t_att * rk_all / keys_s
-        parts.append(f"vs head {h}: full estimate+top-k+intervals, attention of {budget_blocks} blocks")
+        rk_all = float((vs_keys_per_block(iv_g, n_iv_g, n_cols_g, n) * rows_per_block(n)).sum())
+        t_total += t_est * w.batch * len(x.heads["vs"]) + t_att * rk_all / keys_s
+        parts.append(f"one vertical-slash head: full estimate, top-k and intervals; "
+                     f"attention of {nblk} sampled query blocks")
     if x.heads["bs"]:
         h = x.heads["bs"][0]
         qh, kh, vh = f(layer.q[0, h]), f(layer.k[0, h // G]), f(layer.v[0, h // G])
         t0 = time.perf_counter()
         qp, kp = O.mean_pool(qh), O.mean_pool(kh)
         t_pool = time.perf_counter() - t0
-        blocks = rng.choice(nb, budget_blocks, replace=False)
-        t0 = time.perf_counter()
-        keys_s = 0
-        sel_rows = 0
-        for a in blocks:
+
+        def bs_block(a):
             L = O.to_f32(O.block_logits(qp[a:a + 1], kp[: a + 1], sc))[0]
-            sel = O.topk_indices(L, w.topk, forced=(int(a),))
-            keys = O.blocks_to_keys(sel, n)
+            keys = O.blocks_to_keys(O.topk_indices(L, w.topk, forced=(a,)), n)
             rows = np.arange(a * BLK, min(n, a * BLK + BLK))
             O.masked_attention(qh[rows], rows, keys, kh, vh, sc)
-            keys_s += len(keys) * len(rows)
-            sel_rows += 1
-        t_blk = time.perf_counter() - t0
-        sel_g, n_sel_g = idx["bs"]
-        keys_all = bs_keys_per_block(sel_g, n_sel_g, n)
-        rk_all = float((keys_all * rows_per_block(n)).sum())
-        rows_bs = w.batch * len(x.heads["bs"])
-        t_total += t_pool * rows_bs + t_blk * rk_all / keys_s
-        parts.append(f"bs head {h}: pooling, select+attention of {budget_blocks} blocks")
+            return len(keys) * len(rows)
+        t_blk, keys_s, nblk = _sampled_blocks(nb, rng, seconds[1], 64, bs_block)
+        rk_all = float((bs_keys_per_block(*idx["bs"], n) * rows_per_block(n)).sum())
+        t_total += t_pool * w.batch * len(x.heads["bs"]) + t_blk * rk_all / keys_s
+        parts.append(f"one block-sparse head: pooling; block scores, selection and attention of "
+                     f"{nblk} sampled query blocks")
     if x.heads["st"]:
         h = x.heads["st"][0]
         qh, kh, vh = f(layer.q[0, h]), f(layer.k[0, h // G]), f(layer.v[0, h // G])
-        blocks = rng.choice(nb, budget_blocks, replace=False)
-        t0 = time.perf_counter()
-        keys_s = 0
-        for a in blocks:
-            keys = O.blocks_to_keys(O.streaming_blocks(int(a), w.init_blocks, w.local_blocks), n)
+
+        def st_block(a):
+            keys = O.blocks_to_keys(O.streaming_blocks(a, w.init_blocks, w.local_blocks), n)
             rows = np.arange(a * BLK, min(n, a * BLK + BLK))
             O.masked_attention(qh[rows], rows, keys, kh, vh, sc)
-            keys_s += len(keys) * len(rows)
-        t_att = time.perf_counter() - t0
+            return len(keys) * len(rows)
+        t_att, keys_s, nblk = _sampled_blocks(nb, rng, seconds[2], 64, st_block)
         rk = float((st_keys_per_block(n, w.init_blocks, w.local_blocks) * rows_per_block(n)).sum())
         t_total += t_att * rk / keys_s * w.batch * len(x.heads["st"])
-        parts.append(f"st head {h}: attention of {budget_blocks} blocks")
+        parts.append(f"one streaming head: attention of {nblk} sampled query blocks")
     cores = len(os.sched_getaffinity(0))
     return {"value": flops_total / t_total / 1e12, "unit": "TFLOP/s (effective, computed blocks)",
             "cores": cores, "kind": "oracle",
-            "sample": "; ".join(parts) + "; scaled to the whole layer by head count and row x key count",
+            "sample": "; ".join(parts) + "; times scaled to the whole layer by head count and by "
+                      "row x key count (float64 numpy oracle, not a tuned CPU implementation)",
             "extrapolated_ms_per_layer": t_total * 1e3}
 
 
 # ----------------------------------------------------------------------------
+# counter traffic
+# ----------------------------------------------------------------------------
+def summarize_pmc(directory, copy_mib):
+    """Per-launch HBM bytes of the dominant kernel from FETCH_SIZE / WRITE_SIZE
+    passes, each scaled by what the counter reads for the plain copy probe."""
+    def per_kernel(counter):
+        vals = {}
+        for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                key = ("dominant" if DOMINANT in name else
+                       "copy" if "copyBuffer" in name else "neg" if "neg_kernel" in name else None)
+                if key:
+                    vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        return vals
+    nbytes = copy_mib * 2 ** 20
+    out = {"kernel": DOMINANT, "source_sha256_16": source_hash(), "copy_probe_bytes": nbytes}
+    for counter, role in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
+        v = per_kernel(counter)
+        probe = "copy" if "copy" in v else "neg"
+        if "dominant" not in v or probe not in v:
+            raise SystemExit(f"{counter}: dominant or probe kernel missing in {directory}")
+        copy_kib = max(v[probe])                  # the probe is the largest copy
+        out["probe_kernel"] = probe
+        factor = nbytes / (copy_kib * 1024.0)
+        dom_kib = float(np.median(v["dominant"]))
+        out[f"{counter}_kib_per_launch"] = dom_kib
+        out[f"{counter}_copy_kib"] = copy_kib
+        out[f"{role}_scale"] = factor
+        out[f"{role}_bytes_per_launch"] = dom_kib * 1024.0 * factor
+    out["traffic_bytes_per_launch"] = out["read_bytes_per_launch"] + out["write_bytes_per_launch"]
+    return out
+
+
+def committed_traffic(workload):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    t = json.load(open(TRAFFIC_FILE)).get(workload)
+    if not t or t.get("source_sha256_16") != source_hash():
+        return None                               # kernel changed since the counters
+    return t["traffic_bytes_per_launch"]
+
+
+# ----------------------------------------------------------------------------
+def run_layer(w, steps, warmup, with_cpu):
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: generating inputs on {dev}")
+    x = synthetic.make_inputs(w, device=dev)
+    torch.cuda.synchronize()
+    layer = Layer(w, x)
+    log(f"[bench] {w.name}: stages and indices")
+    st, idx = stages(layer, reps=max(2, min(5, steps)))
+    flops = layer_flops(w, x, idx)
+    f_total = sum(flops.values())
+    n, D = w.seq_len, w.head_dim
+    dense = 4.0 * D * (n * (n + 1) / 2) * w.batch * w.q_heads
+    log(f"[bench] {w.name}: warmup {warmup}, timing {steps} steps")
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        layer.step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    log(f"[bench] {w.name}: {ms:.3f} ms/layer; stages {st}")
+    res = {
+        "ms_per_layer": ms, "tflops": f_total / (ms * 1e-3) / 1e12,
+        "flops_computed_blocks": f_total, "flops_per_pattern": flops,
+        "flops_dense_causal": dense, "density_vs_dense": f_total / dense,
+        "stages_ms": st,
+    }
+    if "vs" in flops and w.dtype == "bf16":
+        ach = flops["vs"] / (st["vs_attention_ms"] * 1e-3) / 1e12
+        res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / PEAK_BF16_TFLOPS, "traffic": committed_traffic(w.name),
+                           "kernel": DOMINANT, "flops_per_launch": flops["vs"],
+                           "launch_ms": st["vs_attention_ms"]}
+    if with_cpu:
+        log(f"[bench] {w.name}: cpu baseline (oracle, bounded sample)")
+        res["cpu_baseline"] = cpu_baseline(layer, idx, f_total)
+    del layer, x, idx
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama3_8b_128k_vs_bf16",
+    ap.add_argument("--workload", default="llama3_8b_1m_mixed_bf16",
                     choices=[w.name for w in synthetic.WORKLOADS])
+    ap.add_argument("--secondary", default="llama3_8b_128k_vs_bf16",
+                    help="a second workload timed beside the first ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--record", action="store_true",
+                    help="with --summarize-pmc: store the summary for --workload in the traffic file")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summ = summarize_pmc(args.summarize_pmc, args.copy_probe or 1024)
+        summ["workload"] = args.workload
+        print(json.dumps(summ, indent=1))
+        if args.record:
+            allt = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+            allt[args.workload] = summ
+            json.dump(allt, open(TRAFFIC_FILE, "w"), indent=1)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer shards by "
               "(batch, kv-head group) with no exchange, which this benchmark does not launch.",
               file=sys.stderr)
         sys.exit(2)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    torch.cuda.set_device(0)
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe * 2 ** 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)                            # device-to-device copy (blit kernel)
+        torch.neg(src, out=dst)                   # the same bytes through an elementwise kernel
+        torch.cuda.synchronize()
+        del src, dst
     w = synthetic.BY_NAME[args.workload]
-    log(f"[bench] workload {w.name}: generating inputs on {dev}")
-    x = synthetic.make_inputs(w, device=dev)
-    torch.cuda.synchronize()
-    layer = Layer(w, x)
-    n, D = w.seq_len, w.head_dim
-
-    log("[bench] indices for FLOP accounting")
-    idx = layer.indices()
-    flops = {}
-    if "vs" in idx:
-        iv, n_iv, cols, n_cols = idx["vs"]
-        flops["vs"] = attn_flops(vs_keys_per_block(iv, n_iv, n_cols, n), n, D)
-    if "bs" in idx:
-        flops["bs"] = attn_flops(bs_keys_per_block(*idx["bs"], n), n, D)
-    if x.heads["st"]:
-        flops["st"] = attn_flops(st_keys_per_block(n, w.init_blocks, w.local_blocks), n, D) \
-            * w.batch * len(x.heads["st"])
-    f_total = sum(flops.values())
-    dense = 4.0 * D * (n * (n + 1) / 2) * w.batch * w.q_heads
-
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        layer.step()
-    torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps")
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    e0.record(s)
-    for _ in range(args.steps):
-        layer.step()
-    e1.record(s)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] {ms:.3f} ms/layer (wall {t_wall / args.steps * 1e3:.3f})")
-
-    # per-stage times and the dominant kernel, each timed alone
-    stages = {}
-    reps = max(2, min(10, args.steps))
-    roof = None
-    if "vs" in idx:
-        iv, n_iv, cols, n_cols = idx["vs"]
-        t_attn = time_events(lambda: dsa.sparse_attention_vs(
-            layer.q, layer.k, layer.v, iv, n_iv, cols, n_cols, heads=x.heads["vs"], out=layer.o), reps)
-        stages["vs_attention_ms"] = t_attn
-        stages["vs_estimate_ms"] = time_events(lambda: dsa.vs_estimate(layer.q, layer.k, heads=x.heads["vs"]), reps)
-        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-        ach = flops["vs"] / (t_attn * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
-                "traffic": None, "kernel": "attn_vs_kernel",
-                "flops_per_launch": flops["vs"]}
-    if "bs" in idx:
-        sel, n_sel = idx["bs"]
-        stages["bs_attention_ms"] = time_events(lambda: dsa.sparse_attention_blocks(
-            layer.q, layer.k, layer.v, sel, n_sel, heads=x.heads["bs"], out=layer.o), reps)
-    if x.heads["st"]:
-        stages["st_attention_ms"] = time_events(lambda: dsa.streaming_attention(
-            layer.q, layer.k, layer.v, w.init_blocks, w.local_blocks, heads=x.heads["st"], out=layer.o), reps)
-    log(f"[bench] stages {stages}")
-
-    value = f_total / (ms * 1e-3) / 1e12
+    prim = run_layer(w, args.steps, args.warmup, not args.no_cpu_baseline)
     res = {
         "metric": "sparse prefill attention ms/layer + effective TFLOP/s (% bf16 peak) at 128K/1M",
-        "value": round(value, 3),
+        "value": round(prim["tflops"], 3),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(prim["ms_per_layer"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic",
+        "dtype": w.dtype, "data": "synthetic (seeded; planted sink/slash structure)",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
-                   "seq_len": n, "head_dim": D,
-                   "heads_per_pattern": {p: len(hs) for p, hs in x.heads.items()},
+                   "seq_len": w.seq_len, "head_dim": w.head_dim,
+                   "heads_per_pattern": {p: len(hs) for p, hs in synthetic.head_patterns(w).items()},
                    "vertical_topk": w.vertical_topk, "slash_topk": w.slash_topk, "topk": w.topk,
                    "init_blocks": w.init_blocks, "local_blocks": w.local_blocks},
-        "ms_per_layer": round(ms, 4),
-        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "flops_computed_blocks": f_total, "flops_dense_causal": dense,
-        "density_vs_dense": f_total / dense,
-        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
-        "roofline": roof,
+        "ms_per_layer": round(prim["ms_per_layer"], 4),
+        "pct_bf16_peak": round(100 * prim["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "flops_computed_blocks": prim["flops_computed_blocks"],
+        "flops_per_pattern": prim["flops_per_pattern"],
+        "density_vs_dense": prim["density_vs_dense"],
+        "stages_ms": {k: round(v, 4) for k, v in prim["stages_ms"].items()},
+        "roofline": prim.get("roofline"),
     }
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle, bounded sample)")
-        res["cpu_baseline"] = cpu_baseline(layer, idx, f_total)
+    if "cpu_baseline" in prim:
+        res["cpu_baseline"] = prim["cpu_baseline"]
+    if args.secondary != "none" and args.secondary != w.name:
+        w2 = synthetic.BY_NAME[args.secondary]
+        sec = run_layer(w2, args.steps, args.warmup, False)
+        res["secondary"] = {"workload": w2.name, "ms_per_layer": round(sec["ms_per_layer"], 4),
+                            "tflops": round(sec["tflops"], 3),
+                            "pct_bf16_peak": round(100 * sec["tflops"] / PEAK_BF16_TFLOPS, 2),
+                            "density_vs_dense": sec["density_vs_dense"],
+                            "stages_ms": {k: round(v, 4) for k, v in sec["stages_ms"].items()},
+                            "roofline": sec.get("roofline")}
     print(json.dumps(res), flush=True)
 
 
