@@ -34,6 +34,9 @@ dsa_status check_shape(const dsa_shape* s) {
   if (s->q_heads % s->kv_heads != 0) return DSA_ERR_INVALID_ARG;
   if (s->head_dim != 64 && s->head_dim != 128) return DSA_ERR_UNSUPPORTED;
   if (s->dtype != DSA_BF16 && s->dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
+  // one head's slab is addressed with 32-bit byte offsets
+  const int64_t slab = (int64_t)s->seq_len * s->head_dim * (s->dtype == DSA_BF16 ? 2 : 4);
+  if (slab >= ((int64_t)1 << 31)) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 

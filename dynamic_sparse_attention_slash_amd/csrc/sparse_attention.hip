@@ -196,10 +196,6 @@ __device__ __forceinline__ void mask_tile(f32x4 (&st)[2][QB], const Desc (&d)[2]
   }
 }
 
-template <int QB>
-__device__ __forceinline__ void mask_tile_lds(f32x4 (&st)[2][QB], const Desc (&d)[2], const int32_t* lcols,
-                                              int32_t q0, int32_t lane);
-
 // New reference maxima: raised only when a row max exceeds the current one by
 // more than 2^8 (P then stays <= 256 and the O rescale runs rarely; O / l does
 // not depend on the reference). Returns whether any lane raised one; alpha
@@ -239,35 +235,342 @@ __device__ __forceinline__ void exp_tile(f32x4 (&st)[2][QB], const float (&m)[QB
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel: two waves per query block, wave w owns queries r0 + 32w .. +31.
+// bf16 kernel: a work-group takes a panel of PANEL = 2 consecutive query
+// blocks (rows r0 .. r0 + 127) with four waves; wave w owns the 32 queries
+// starting at r0 + 64 (w >> 1) + 32 (w & 1).
 //
-// K and V tiles (32 keys) travel global -> LDS with global_load_lds_dwordx4
-// (no registers involved), into a two-stage ring: the loads of tile t+1 are
-// in flight while tile t is computed, and one barrier per tile separates them.
-// Each wave loads one of the two 16-key sub-blocks of a tile. Both matrices
-// are row-major in LDS with the 16-byte chunks of row r XOR-swizzled by r, so
-// that the operand reads below are free of bank conflicts:
+// The key sets of the two blocks are walked together as one stream of 16-key
+// sub-blocks, each carrying, per block, a mask of the slots that belong to that
+// block's key set:
+//  * ranges (vertical-slash intervals, the streaming sink and window): per
+//    interval, the union of the two blocks' windows. For a slash interval the
+//    window of block a+1 is the window of block a moved by 64 keys, so the keys
+//    of a wide interval are loaded once for both blocks.
+//  * key-block lists (block-sparse heads): the two ascending lists merged, so
+//    a key block selected by both query blocks is loaded once.
+//  * gathered columns (vertical-slash): in split tiles, keys 0-31 of a tile
+//    from block a's list and keys 32-63 from block a+1's.
+// A tile is 64 keys (4 sub-blocks). K and V tiles travel global -> LDS with
+// buffer_load_dwordx4 ... lds (no registers involved) into a two-stage ring:
+// the loads of tile t+1 are in flight while tile t is computed, and one
+// barrier per tile separates them. Wave w loads sub-block w of a tile; each
+// wave then computes on the tile's two 32-key halves, skipping a half that
+// holds no key of its block. Both matrices are row-major in LDS with the
+// 16-byte chunks of row r XOR-swizzled by r, so that the operand reads are free
+// of bank conflicts:
 //   K operand (MFMA A, 8 dims of one key per lane): ds_read_b128
 //   V^T operand (MFMA A, 8 keys of one dim per lane): two ds_read_b64_tr_b16,
 //     the gfx950 transposing LDS read (each 16-lane group reads a 16 x 4 block
 //     of b16 and lane i receives element (4j + i/4, i%4) for j = 0..3).
-// The block's column-list entries are staged in LDS together with the
-// sub-block descriptors, so gathered keys cost no global round trip.
 // ---------------------------------------------------------------------------
-constexpr int BF16_WAVES = 2;
-constexpr int32_t BF16_SB_CAP = 512;   // descriptors per refill
-constexpr int32_t COLS_CAP = 1024;     // column-list entries staged per refill
+constexpr int PANEL = 2;                // query blocks per work-group
+constexpr int PANEL_WAVES = 2 * PANEL;  // 32 queries per wave
+constexpr int32_t P_SB_CAP = 512;       // sub-block descriptors per refill (128 tiles)
+constexpr int32_t P_COLS_CAP = 512;     // column entries per block staged per refill
+constexpr int32_t P_MERGE = 64;         // list entries per block merged per refill
+constexpr int32_t P_LIST = 1;           // keys come from the staged column list
+constexpr int32_t P_DIAG = 2;           // << j: may hold a key above block j's first row
+
+struct PDesc {
+  int32_t a;    // first key (range) or position in the staged column list
+  uint32_t vm;  // valid slots: bits 0-15 for block 0 of the panel, 16-31 for block 1
+  int32_t f;    // P_LIST | P_DIAG << j | (entries to load, for a list) << 8
+};
+
+__device__ __forceinline__ PDesc uniform_pdesc(const PDesc* d, int32_t t) {
+  const PDesc x = d[t];
+  return PDesc{__builtin_amdgcn_readfirstlane(x.a), (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)x.vm),
+               __builtin_amdgcn_readfirstlane(x.f)};
+}
+
+// Slots s + i (i < 16) that lie in [lo, hi).
+__device__ __forceinline__ uint32_t slot_mask(int32_t s, int32_t lo, int32_t hi) {
+  const int32_t b0 = min(max(lo - s, 0), 16), b1 = min(max(hi - s, 0), 16);
+  return b1 > b0 ? ((1u << b1) - 1u) & ~((1u << b0) - 1u) : 0u;
+}
+
+// ---- window sources: next() gives one interval's key window per block of
+// the panel ([lo, hi) within [0, n), empty when lo >= hi); state is uniform ----
+struct VsPanelRanges {
+  const int32_t* iv; int32_t n_iv, t, r0, n;
+  __device__ bool next(int32_t (&lo)[PANEL], int32_t (&hi)[PANEL]) {
+    while (t < n_iv) {
+      const int32_t d_lo = iv[2 * t], d_hi = iv[2 * t + 1];
+      ++t;
+      if (d_lo >= r0 + PANEL * BLOCK) { t = n_iv; return false; }  // intervals ascend
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < PANEL; ++j) {
+        const int32_t rj = r0 + BLOCK * j;
+        const bool on = rj < n && d_lo < rj + BLOCK;
+        lo[j] = on ? max(0, rj - d_hi) : 0;
+        hi[j] = on ? min(n, rj + BLOCK - d_lo) : 0;
+        any |= lo[j] < hi[j];
+      }
+      if (any) return true;
+    }
+    return false;
+  }
+};
+
+struct StreamPanelRanges {
+  int32_t a0, nb, init_blocks, local_blocks, t, n;
+  __device__ bool next(int32_t (&lo)[PANEL], int32_t (&hi)[PANEL]) {
+    while (t < 2) {
+      const int32_t which = t++;
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < PANEL; ++j) {
+        const int32_t aj = a0 + j;
+        lo[j] = hi[j] = 0;
+        if (aj < nb) {
+          const int32_t sink_end = min(init_blocks, aj + 1);
+          if (which == 0) {
+            hi[j] = min(n, sink_end * BLOCK);
+          } else {
+            const int32_t c0 = max(aj - local_blocks + 1, sink_end);
+            if (c0 <= aj) { lo[j] = c0 * BLOCK; hi[j] = min(n, (aj + 1) * BLOCK); }
+          }
+        }
+        any |= lo[j] < hi[j];
+      }
+      if (any) return true;
+    }
+    return false;
+  }
+};
+
+// Merged key-block list of the panel in LDS: block ids mk[] with membership
+// bits mm[] (bit j: selected by block j).
+struct MergedBlocks {
+  const int32_t* mk; const int32_t* mm; int32_t k, nm, nb, n;
+  __device__ bool next(int32_t (&lo)[PANEL], int32_t (&hi)[PANEL]) {
+    while (k < nm) {
+      const int32_t c = mk[k], bits = mm[k];
+      ++k;
+      const bool ok = c >= 0 && c < nb;
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < PANEL; ++j) {
+        const bool on = ok && ((bits >> j) & 1);
+        lo[j] = on ? c * BLOCK : 0;
+        hi[j] = on ? min(n, c * BLOCK + BLOCK) : 0;
+        any |= lo[j] < hi[j];
+      }
+      if (any) return true;
+    }
+    return false;
+  }
+};
+
+// Cuts the union of each interval's windows into sub-blocks, resuming where
+// the last call stopped. Each interval starts on an even sub-block, so that a
+// half tile never mixes the tail of one interval with the head of the next.
+struct PanelCut {
+  int32_t p, hi, lo_j[PANEL], hi_j[PANEL];
+  bool exhausted;
+};
+
+__device__ __forceinline__ void empty_desc(PDesc* d, int32_t t, int32_t tid) {
+  if (tid == 0) d[t] = PDesc{0, 0u, 0};
+}
+
+template <class R>
+__device__ int32_t cut_ranges(R& src, PanelCut& c, PDesc* d, int32_t cnt, int32_t r0, int32_t tid,
+                              int32_t nth) {
+  while (cnt < P_SB_CAP) {
+    if (c.p >= c.hi) {
+      int32_t lo[PANEL], hi[PANEL];
+      if (!src.next(lo, hi)) { c.exhausted = true; break; }
+      int32_t ulo = 0x7fffffff, uhi = 0;
+#pragma unroll
+      for (int j = 0; j < PANEL; ++j) {
+        if (lo[j] < hi[j]) { ulo = min(ulo, lo[j]); uhi = max(uhi, hi[j]); }
+        c.lo_j[j] = lo[j];
+        c.hi_j[j] = hi[j];
+      }
+      c.p = ulo;
+      c.hi = uhi;
+      if (cnt & 1) empty_desc(d, cnt++, tid);
+      continue;
+    }
+    const int32_t take = min((c.hi - c.p + 15) >> 4, P_SB_CAP - cnt);
+    for (int32_t t = tid; t < take; t += nth) {
+      const int32_t s = c.p + 16 * t;
+      uint32_t vm = 0;
+      int32_t f = 0;
+#pragma unroll
+      for (int j = 0; j < PANEL; ++j) {
+        const uint32_t m = slot_mask(s, c.lo_j[j], c.hi_j[j]);
+        vm |= m << (16 * j);
+        if (m && s + 15 > r0 + BLOCK * j) f |= P_DIAG << j;
+      }
+      d[cnt + t] = PDesc{s, vm, f};
+    }
+    cnt += take;
+    c.p = min(c.hi, c.p + 16 * take);
+  }
+  return cnt;
+}
+
+__device__ __forceinline__ int32_t pad_tiles(PDesc* d, int32_t cnt, int32_t tid) {
+  while (cnt & 3) empty_desc(d, cnt++, tid);
+  return cnt;
+}
+
+// Vertical-slash panel: the intervals, then the two blocks' column lists.
+struct VsPanelSrc {
+  static constexpr int32_t COLS = PANEL * P_COLS_CAP;
+  VsPanelRanges rg;
+  PanelCut cut;
+  const int32_t* cols[PANEL];
+  int32_t ncol[PANEL], cp[PANEL];
+  int32_t r0, n;
+
+  __device__ int32_t fill(PDesc* d, int32_t* lcols, int32_t tid, int32_t nth) {
+    int32_t cnt = cut.exhausted ? 0 : cut_ranges(rg, cut, d, 0, r0, tid, nth);
+    if (cut.exhausted && cnt < P_SB_CAP) {
+      cnt = pad_tiles(d, cnt, tid);  // split tiles start on a tile boundary
+      const int32_t tiles = (P_SB_CAP - cnt) >> 2;
+      int32_t take[PANEL], T = 0;
+#pragma unroll
+      for (int j = 0; j < PANEL; ++j) {
+        take[j] = min(ncol[j] - cp[j], min(P_COLS_CAP, 32 * tiles));
+        T = max(T, (take[j] + 31) >> 5);
+      }
+#pragma unroll
+      for (int j = 0; j < PANEL; ++j)
+        for (int32_t i = tid; i < take[j]; i += nth)
+          lcols[j * P_COLS_CAP + i] = min(max(cols[j][cp[j] + i], 0), n - 1);
+      for (int32_t u = tid; u < 4 * T; u += nth) {
+        // per-lane block index: select, never index the per-block arrays
+        const int32_t j = (u >> 1) & 1, base = 32 * (u >> 2) + 16 * (u & 1);
+        const int32_t tk = j ? take[1] : take[0];
+        const int32_t* src = j ? cols[1] + cp[1] : cols[0] + cp[0];
+        const int32_t c = min(max(tk - base, 0), 16);
+        if (c == 0) {
+          d[cnt + u] = PDesc{0, 0u, 0};
+        } else {
+          const int32_t last = min(max(src[base + c - 1], 0), n - 1);
+          d[cnt + u] = PDesc{j * P_COLS_CAP + base, ((1u << c) - 1u) << (16 * j),
+                             P_LIST | (c << 8) | (last > r0 + BLOCK * j ? P_DIAG << j : 0)};
+        }
+      }
+      cnt += 4 * T;
+#pragma unroll
+      for (int j = 0; j < PANEL; ++j) cp[j] += take[j];
+    }
+    return pad_tiles(d, cnt, tid);
+  }
+};
+
+struct StreamPanelSrc {
+  static constexpr int32_t COLS = 1;
+  StreamPanelRanges rg;
+  PanelCut cut;
+  int32_t r0;
+  __device__ int32_t fill(PDesc* d, int32_t*, int32_t tid, int32_t nth) {
+    const int32_t cnt = cut.exhausted ? 0 : cut_ranges(rg, cut, d, 0, r0, tid, nth);
+    return pad_tiles(d, cnt, tid);
+  }
+};
+
+__device__ __forceinline__ int32_t lower_bound64(const int32_t* a, int32_t len, int32_t x) {
+  int32_t lo = 0, hi = len;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ uint64_t low_bits(int32_t r) { return r >= 64 ? ~0ull : (1ull << r) - 1ull; }
+
+// Block-sparse panel: the two selected-block lists (ascending, distinct) are
+// merged P_MERGE entries at a time: a chunk takes the entries of both lists up
+// to the smaller of their P_MERGE-th remaining entries, and each entry's place
+// in the merged, duplicate-free chunk is its rank in its own list plus its
+// rank in the other list minus the duplicates below it. A list that breaks the
+// order gives wrong sets but never an access outside the chunk arrays.
+struct BsPanelSrc {
+  static constexpr int32_t COLS = 1;
+  const int32_t* sel[PANEL];
+  int32_t nsel[PANEL], cp[PANEL];
+  MergedBlocks mb;
+  PanelCut cut;
+  int32_t r0;
+
+  __device__ void merge(int32_t* mA, int32_t* mB, int32_t* mk, int32_t* mm, int32_t tid) {
+    const int32_t rA = nsel[0] - cp[0], rB = nsel[1] - cp[1];
+    if (tid < P_MERGE) {
+      mA[tid] = tid < rA ? sel[0][cp[0] + tid] : 0x7fffffff;
+      mB[tid] = tid < rB ? sel[1][cp[1] + tid] : 0x7fffffff;
+    }
+    if (tid < 2 * P_MERGE) { mk[tid] = -1; mm[tid] = 0; }
+    __syncthreads();
+    int32_t thr = 0x7fffffff;
+    if (rA > P_MERGE) thr = min(thr, mA[P_MERGE - 1]);
+    if (rB > P_MERGE) thr = min(thr, mB[P_MERGE - 1]);
+    const int32_t l = tid & 63;
+    const int32_t x = mA[l], y = mB[l];
+    const int32_t tA = __popcll(__ballot(l < rA && x <= thr));
+    const int32_t tB = __popcll(__ballot(l < rB && y <= thr));
+    const int32_t ra = lower_bound64(mA, tA, y), rb = lower_bound64(mB, tB, x);
+    const bool dupB = l < tB && ra < tA && mA[ra] == y;
+    const uint64_t dmask = __ballot(dupB);
+    if (tid < 64) {
+      if (l < tA) {
+        const int32_t pos = l + rb - __popcll(dmask & low_bits(rb));
+        mk[pos] = x;
+        mm[pos] = 1 | (rb < tB && mB[rb] == x ? 2 : 0);
+      }
+      if (l < tB && !dupB) {
+        const int32_t pos = l + ra - __popcll(dmask & low_bits(l));
+        mk[pos] = y;
+        mm[pos] = 2;
+      }
+    }
+    cp[0] += tA;
+    cp[1] += tB;
+    mb.k = 0;
+    mb.nm = tA + tB - __popcll(dmask);
+    __syncthreads();
+  }
+
+  __device__ int32_t fill(PDesc* d, int32_t*, int32_t tid, int32_t nth) {
+    __shared__ int32_t mA[P_MERGE], mB[P_MERGE], mk[2 * P_MERGE], mm[2 * P_MERGE];
+    mb.mk = mk;
+    mb.mm = mm;
+    int32_t cnt = 0;
+    while (true) {
+      cnt = cut_ranges(mb, cut, d, cnt, r0, tid, nth);
+      if (!cut.exhausted || cnt > 0 || (cp[0] >= nsel[0] && cp[1] >= nsel[1])) break;
+      merge(mA, mB, mk, mm, tid);
+      cut.exhausted = false;
+    }
+    return pad_tiles(d, cnt, tid);
+  }
+};
 
 template <int D>
 struct TileLds {
   static constexpr int ROW = D * 2;           // bytes per key row
   static constexpr int UNITS = ROW / 16;      // 16-byte chunks per row
   static constexpr int MAT = 32 * ROW;        // one 32-key matrix
-  static constexpr int STAGE = 2 * MAT;       // K then V
-  static constexpr int RPI = 64 / UNITS;      // rows per global_load_lds_dwordx4
+  static constexpr int HALF = 2 * MAT;        // K then V of a 32-key half tile
+  static constexpr int STAGE = 2 * HALF;      // a 64-key tile
+  static constexpr int RPI = 64 / UNITS;      // rows per buffer_load_dwordx4 ... lds
   static constexpr int INSTR = 16 / RPI;      // instructions per 16-row sub-block
+  // Chunk swizzle of row r: an XOR-linear map of r's low four bits (table
+  // below, one nibble per r) under which the K reads (ds_read_b128, 16 rows
+  // at one logical chunk) and the V^T reads (ds_read_b64_tr_b16, 4 rows x 2
+  // chunks per 16 lanes) each touch distinct banks, with 32 or 64 banks and
+  // D = 64 or 128. The plain XOR by r conflicts 2-way on the V^T reads.
+  __device__ static int swz(int r) {
+    return (int)((0xdb8e71249fca3560ull >> (4 * (r & 15))) & 15) & (UNITS - 1);
+  }
   // byte offset of logical chunk c of row r
-  __device__ static int off(int r, int c) { return r * ROW + 16 * (c ^ (r & (UNITS - 1))); }
+  __device__ static int off(int r, int c) { return r * ROW + 16 * (c ^ swz(r)); }
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -278,70 +581,12 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-// Key of a slot for the bf16 kernel: gathered entries come from the staged
-// copy of the column list in LDS.
-__device__ __forceinline__ int32_t desc_key_lds(const Desc& d, const int32_t* lcols, int32_t slot) {
-  int32_t sl = slot < d.count() ? slot : 0;
-  return (d.b & F_LIST) ? lcols[d.a + sl] : d.a + sl;
-}
-
-// Fills descriptors like DescGen::fill, but list sub-blocks refer to a copy of
-// the column list staged in LDS (positions relative to that copy), and at most
-// COLS_CAP entries are staged per call. Entries are clamped into [0, n).
-template <class R>
-__device__ int32_t fill_bf16(DescGen<R>& gen, Desc* d, int32_t* lcols, int32_t tid, int32_t nthreads) {
-  int32_t cnt = 0;
-  while (cnt < BF16_SB_CAP) {
-    if (gen.p >= gen.hi) {
-      int32_t lo2, hi2;
-      if (!gen.ranges.next(lo2, hi2)) break;
-      gen.p = lo2;
-      gen.hi = hi2;
-      continue;
-    }
-    const int32_t take = min((gen.hi - gen.p + 15) >> 4, BF16_SB_CAP - cnt);
-    for (int32_t t = tid; t < take; t += nthreads) {
-      int32_t s = gen.p + 16 * t, c = min(16, gen.hi - s);
-      d[cnt + t] = Desc{s, c | ((c < 16 || s + c - 1 > gen.r0) ? F_MASK : 0)};
-    }
-    cnt += take;
-    gen.p = min(gen.hi, gen.p + 16 * take);
-  }
-  if (cnt < BF16_SB_CAP && gen.cp < gen.n_cols) {
-    const int32_t ncol = min(gen.n_cols - gen.cp, min(COLS_CAP, 16 * (BF16_SB_CAP - cnt)));
-    for (int32_t t = tid; t < ncol; t += nthreads) lcols[t] = min(max(gen.cols[gen.cp + t], 0), gen.n - 1);
-    const int32_t take = (ncol + 15) >> 4;
-    for (int32_t t = tid; t < take; t += nthreads) {
-      int32_t s = 16 * t, c = min(16, ncol - s);
-      bool m = c < 16 || gen.cols[gen.cp + s + c - 1] > gen.r0;
-      d[cnt + t] = Desc{s, c | F_LIST | (m ? F_MASK : 0)};
-    }
-    cnt += take;
-    gen.cp += ncol;
-  }
-  return cnt;
-}
-
-template <int QB>
-__device__ __forceinline__ void mask_tile_lds(f32x4 (&st)[2][QB], const Desc (&d)[2], const int32_t* lcols,
-                                              int32_t q0, int32_t lane) {
-  const int32_t g = lane >> 4, l16 = lane & 15;
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
-    if (d[s2].b & F_MASK) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t slot = 4 * g + i;
-        const bool valid = slot < d[s2].count();
-        const int32_t key = desc_key_lds(d[s2], lcols, slot);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int32_t row = q0 + 16 * qb + l16;
-          if (!valid || key > row) st[s2][qb][i] = -INFINITY;
-        }
-      }
-    }
-  }
+// max of three floats in one instruction: fmaxf would first quiet each
+// operand (v_max_f32 x, x, x) under the IEEE mode the kernels run in
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // Row max over the four lane groups (lanes l, l^16, l^32, l^48 hold the same
@@ -357,36 +602,38 @@ __device__ __forceinline__ float group_max4(float x) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, class R>
-__device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __restrict__ ks,
-                            const uint16_t* __restrict__ vs, uint16_t* __restrict__ os,
-                            int32_t n, int32_t r0, float scale_log2, DescGen<R> gen) {
+template <int D, class Src>
+__device__ void attend_panel(const uint16_t* __restrict__ qs, const uint16_t* __restrict__ ks,
+                             const uint16_t* __restrict__ vs, uint16_t* __restrict__ os,
+                             int32_t n, int32_t r0, float scale_log2, Src src) {
   using L = TileLds<D>;
   constexpr int DS = D / 32;      // MFMA k-steps of Q.K
   constexpr int DB = D / 16;      // 16-dim output blocks
+  constexpr int NTH = 64 * PANEL_WAVES;
   // two ring stages in distinct arrays: the compiler can then prove that the
   // loads in flight into one stage do not alias the reads of the other
   __shared__ __align__(16) char ring0[L::STAGE];
   __shared__ __align__(16) char ring1[L::STAGE];
-  __shared__ Desc desc[BF16_SB_CAP];
-  __shared__ int32_t lcols[COLS_CAP];
+  __shared__ PDesc desc[P_SB_CAP];
+  __shared__ int32_t lcols[Src::COLS];
 
   const int32_t tid = threadIdx.x, lane = tid & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int32_t blk = wave >> 1;                                  // block of the panel
   const int32_t g = lane >> 4, l16 = lane & 15;
-  const int32_t q0 = r0 + 32 * wave;
+  const int32_t q0 = r0 + BLOCK * blk + 32 * (wave & 1);
 
   // Q^T operands: query row q0 + 16qb + l16, dims (D/4)g + 8s .. + 7
   u32x4 qop[2][DS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    int32_t row = min(q0 + 16 * qb + l16, n - 1);
-    const u32x4* src = reinterpret_cast<const u32x4*>(qs + (size_t)row * D + (D / 4) * g);
+    const int32_t row = min(q0 + 16 * qb + l16, n - 1);
+    const u32x4* qsrc = reinterpret_cast<const u32x4*>(qs + (size_t)row * D + (D / 4) * g);
 #pragma unroll
-    for (int s = 0; s < DS; ++s) qop[qb][s] = src[s];
+    for (int s = 0; s < DS; ++s) qop[qb][s] = qsrc[s];
   }
 
-  // per-lane LDS offsets within a stage
+  // per-lane LDS offsets within a half tile
   // K operand of step s: row l16 (+16 per sub-block), chunk (D/32)g + s
   int32_t koff[DS];
 #pragma unroll
@@ -399,15 +646,17 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
     const int32_t r = 4 * g + (l16 >> 2), dim = 16 * db + 4 * (l16 & 3);
     voff[db] = L::MAT + L::off(r, dim >> 3) + 2 * (dim & 7);
   }
-  // global -> LDS load k of this wave's sub-block: lane takes row rr(k) of the
-  // sub-block at logical chunk c(k), landing at LDS byte 16*lane of the load
+  // global -> LDS load k of this wave's sub-block: lane takes row ld_row[k] of
+  // the sub-block at logical chunk c(k), landing at LDS byte 16*lane of the load
   int32_t ld_row[L::INSTR], ld_off[L::INSTR];
 #pragma unroll
   for (int k = 0; k < L::INSTR; ++k) {
     ld_row[k] = k * L::RPI + lane / L::UNITS;
-    const int32_t c = (lane % L::UNITS) ^ ((16 * wave + ld_row[k]) & (L::UNITS - 1));
-    ld_off[k] = ld_row[k] * L::ROW + 16 * c;    // + first key * ROW for a range
+    const int32_t c = (lane % L::UNITS) ^ L::swz(16 * (wave & 1) + ld_row[k]);
+    ld_off[k] = ld_row[k] * L::ROW + 16 * c;
   }
+  // The whole key offset goes into the per-lane offset, which the buffer
+  // range check covers: rows past the end of the head's slab read as zeros.
   const uint32_t slab_bytes = (uint32_t)n * L::ROW;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)ks, (short)0, slab_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vs, (short)0, slab_bytes, 0x00020000);
@@ -419,38 +668,44 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {NEG_BIG, NEG_BIG};
+  // a raw logit above raise[qb] lifts the row's reference past the margin
+  const float inv_scale_log2 = 1.0f / scale_log2;
+  float raise[2] = {(NEG_BIG + 8.0f) * inv_scale_log2, (NEG_BIG + 8.0f) * inv_scale_log2};
+  // row + 1 - 4g for query qb of this lane: keys up to the row, counted from
+  // the lane's first slot
+  int32_t rp1[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) rp1[qb] = q0 + 16 * qb + l16 + 1 - 4 * g;
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 
-  // loads of this wave's sub-block dw into a stage. Range sub-blocks use the
-  // first key as the scalar offset; slots past the count read the rows that
-  // follow (or zeros past the end of the slab) and are masked out later.
-  auto issue_loads = [&](const Desc& dw, char* stage) {
-    char* dst = stage + 16 * wave * L::ROW;
-    if (dw.b & F_LIST) {
+  // loads of sub-block dw into this wave's quarter of a stage. Slots past a
+  // range's end read the rows that follow (zeros past the slab) and slots past
+  // a list's count repeat its last entry; the masks drop them.
+  auto issue_loads = [&](const PDesc& dw, char* stage) {
+    char* dst = stage + blk * L::HALF + 16 * (wave & 1) * L::ROW;
+    if (dw.f & P_LIST) {
+      const int32_t last = max(((dw.f >> 8) & 31) - 1, 0);
 #pragma unroll
       for (int k = 0; k < L::INSTR; ++k) {
-        const int32_t key = lcols[dw.a + min(ld_row[k], max(dw.count() - 1, 0))];
+        const int32_t key = lcols[dw.a + min(ld_row[k], last)];
         const int32_t vo = ld_off[k] + (key - ld_row[k]) * L::ROW;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + k * 1024), 16, vo, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + L::MAT + k * 1024), 16, vo, 0, 0, 0);
       }
     } else {
-      const int32_t so = dw.a * L::ROW;
+      const int32_t base = dw.a * L::ROW;
 #pragma unroll
       for (int k = 0; k < L::INSTR; ++k) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + k * 1024), 16, ld_off[k], so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + L::MAT + k * 1024), 16, ld_off[k], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + k * 1024), 16, base + ld_off[k], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + L::MAT + k * 1024), 16, base + ld_off[k], 0, 0, 0);
       }
     }
   };
 
-  // one tile: wait for its loads, start the next tile's, compute
-  auto tile = [&](int32_t tt, int32_t ntiles, int32_t cnt, const char* cur, char* nxt) {
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile tt have landed
-    __syncthreads();                 // ... and the other wave's; tile tt-1 is consumed
-    if (tt + 1 < ntiles) issue_loads(uniform_desc(desc, 2 * (tt + 1) + wave, cnt), nxt);
-    const Desc d[2] = {uniform_desc(desc, 2 * tt, cnt), uniform_desc(desc, 2 * tt + 1, cnt)};
-
+  // one 32-key half tile (sub-blocks d0, d1) for this wave's queries
+  auto half = [&](const char* cur, const PDesc& d0, const PDesc& d1) {
+    const uint32_t m0 = (d0.vm >> (16 * blk)) & 0xffffu, m1 = (d1.vm >> (16 * blk)) & 0xffffu;
+    if ((m0 | m1) == 0u) return;
     // S^T = K Q^T
     f32x4 st[2][2];
 #pragma unroll
@@ -467,24 +722,78 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
         st[s2][qb] = acc;
       }
     }
-
-    if ((d[0].b | d[1].b) & F_MASK) mask_tile_lds<2>(st, d, lcols, q0, lane);
-    // running max (raised only past a 2^8 margin), rescale when raised
-    float mt[2];
+    if ((m0 & m1) != 0xffffu || ((d0.f | d1.f) & (P_DIAG << blk))) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const PDesc& dd = s2 ? d1 : d0;
+        const uint32_t ms = s2 ? m1 : m0;
+        if (dd.f & P_LIST) {
+          // gathered keys: slot validity and key <= row, element by element
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int32_t slot = 4 * g + i;
+            const bool valid = (ms >> slot) & 1u;
+            const int32_t key = lcols[dd.a + slot];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              if (!valid || key > q0 + 16 * qb + l16) st[s2][qb][i] = -INFINITY;
+          }
+        } else {
+          // a range: the valid slots are one run [lo, hi), and key <= row
+          // keeps slots below row + 1 - a; lane slot 4g + i is kept when
+          // i < min(hi, row + 1 - a) - 4g (and i >= lo - 4g)
+          const int32_t lo = ms ? __builtin_ctz(ms) : 16;
+          const int32_t hi = ms ? 32 - __builtin_clz(ms) : 0;
+          if (dd.f & (P_DIAG << blk)) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              const int32_t ub = min(hi - 4 * g, rp1[qb] - dd.a);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (i >= ub) st[s2][qb][i] = -INFINITY;
+            }
+          } else if (hi < 16) {
+            // below the diagonal only the run's end bounds the slots
+            const int32_t ub = hi - 4 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool drop = i >= ub;
+#pragma unroll
+              for (int qb = 0; qb < 2; ++qb)
+                if (drop) st[s2][qb][i] = -INFINITY;
+            }
+          }
+          if (lo > 0) {
+            const int32_t lb = lo - 4 * g;
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (i < lb) st[s2][qb][i] = -INFINITY;
+          }
+        }
+      }
+    }
+    // running max, raised only past a 2^8 margin: a lane compares its own
+    // part of the row with the raise threshold; only when some row crosses it
+    // are the row maxima gathered and O rescaled
+    float mx[2];
     bool up_any = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float mx = fmaxf(__builtin_fmaxf(fmaxf(st[0][qb][0], st[0][qb][1]), fmaxf(st[0][qb][2], st[0][qb][3])),
-                       fmaxf(fmaxf(st[1][qb][0], st[1][qb][1]), fmaxf(st[1][qb][2], st[1][qb][3])));
-      mt[qb] = group_max4(mx) * scale_log2;
-      up_any |= mt[qb] > m[qb] + 8.0f;
+      mx[qb] = max3f(max3f(st[0][qb][0], st[0][qb][1], st[0][qb][2]),
+                     max3f(st[0][qb][3], st[1][qb][0], st[1][qb][1]),
+                     max3f(st[1][qb][2], st[1][qb][3], st[1][qb][3]));
+      up_any |= mx[qb] > raise[qb];
     }
     if (__any(up_any)) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const bool up = mt[qb] > m[qb] + 8.0f;
-        const float alpha = up ? fast_exp2(m[qb] - mt[qb]) : 1.0f;
-        m[qb] = up ? mt[qb] : m[qb];
+        const float mt = group_max4(mx[qb]) * scale_log2;
+        const bool up = mt > m[qb] + 8.0f;
+        const float alpha = up ? fast_exp2(m[qb] - mt) : 1.0f;
+        m[qb] = up ? mt : m[qb];
+        raise[qb] = (m[qb] + 8.0f) * inv_scale_log2;
 #pragma unroll
         for (int db = 0; db <= DB; ++db) oacc[db][qb] *= alpha;
       }
@@ -496,7 +805,6 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
     for (int qb = 0; qb < 2; ++qb)
       pop[qb] = u32x4{pack_bf16x2(st[0][qb][0], st[0][qb][1]), pack_bf16x2(st[0][qb][2], st[0][qb][3]),
                       pack_bf16x2(st[1][qb][0], st[1][qb][1]), pack_bf16x2(st[1][qb][2], st[1][qb][3])};
-
     // O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -510,16 +818,25 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
     for (int qb = 0; qb < 2; ++qb) oacc[DB][qb] = mfma_bf16(ones, pop[qb], oacc[DB][qb]);
   };
 
+  // one tile: wait for its loads, start the next tile's, compute both halves
+  auto tile = [&](int32_t tt, int32_t ntiles, const char* cur, char* nxt) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile tt have landed
+    __syncthreads();                 // ... and the other waves'; tile tt-1 is consumed
+    if (tt + 1 < ntiles) issue_loads(uniform_pdesc(desc, 4 * (tt + 1) + wave), nxt);
+    half(cur, uniform_pdesc(desc, 4 * tt), uniform_pdesc(desc, 4 * tt + 1));
+    half(cur + L::HALF, uniform_pdesc(desc, 4 * tt + 2), uniform_pdesc(desc, 4 * tt + 3));
+  };
+
   while (true) {
     __syncthreads();               // previous refill fully consumed
-    const int32_t cnt = fill_bf16(gen, desc, lcols, tid, BF16_WAVES * 64);
+    const int32_t cnt = src.fill(desc, lcols, tid, NTH);   // a multiple of 4
     if (cnt == 0) break;
     __syncthreads();
-    const int32_t ntiles = (cnt + 1) >> 1;
-    issue_loads(uniform_desc(desc, wave, cnt), ring0);
+    const int32_t ntiles = cnt >> 2;
+    issue_loads(uniform_pdesc(desc, wave), ring0);
     for (int32_t tt = 0; tt < ntiles; tt += 2) {
-      tile(tt, ntiles, cnt, ring0, ring1);
-      if (tt + 1 < ntiles) tile(tt + 1, ntiles, cnt, ring1, ring0);
+      tile(tt, ntiles, ring0, ring1);
+      if (tt + 1 < ntiles) tile(tt + 1, ntiles, ring1, ring0);
     }
   }
 
@@ -532,7 +849,7 @@ __device__ void attend_bf16(const uint16_t* __restrict__ qs, const uint16_t* __r
     if (row < n) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        f32x4 x = oacc[db][qb] * inv;
+        const f32x4 x = oacc[db][qb] * inv;
         *reinterpret_cast<u32x2*>(os + (size_t)row * D + 16 * db + 4 * g) =
             u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
       }
@@ -648,23 +965,9 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
 
 // ---------------------------------------------------------------------------
 // kernels per index mode
+// fp32: one work-group (one wave) per (row, query block)
+// bf16: one work-group (four waves) per (row, panel of two query blocks)
 // ---------------------------------------------------------------------------
-template <typename T, int D, class R>
-__device__ __forceinline__ void attend(const AttnArgs& a, int32_t row, int32_t r0, DescGen<R> gen) {
-  const size_t qoff = a.hm.q_slab(row, a.seq_len, D);
-  const size_t kvoff = a.hm.kv_slab(row, a.seq_len, D);
-  if constexpr (sizeof(T) == 2) {
-    attend_bf16<D, R>(static_cast<const uint16_t*>(a.q) + qoff,
-                      static_cast<const uint16_t*>(a.k) + kvoff,
-                      static_cast<const uint16_t*>(a.v) + kvoff,
-                      static_cast<uint16_t*>(a.o) + qoff, a.seq_len, r0, a.scale_log2, gen);
-  } else {
-    attend_f32<D, R>(static_cast<const float*>(a.q) + qoff, static_cast<const float*>(a.k) + kvoff,
-                     static_cast<const float*>(a.v) + kvoff, static_cast<float*>(a.o) + qoff,
-                     a.seq_len, r0, a.scale_log2, gen);
-  }
-}
-
 template <class R>
 __device__ __forceinline__ DescGen<R> make_gen(R r, const int32_t* cols, int32_t n_cols, int32_t r0,
                                                int32_t n) {
@@ -678,69 +981,150 @@ __device__ __forceinline__ DescGen<R> make_gen(R r, const int32_t* cols, int32_t
   return g;
 }
 
-template <typename T> constexpr int threads_of() { return sizeof(T) == 2 ? 64 * BF16_WAVES : 64; }
-template <typename T> constexpr int waves_per_eu() { return sizeof(T) == 2 ? 2 : 1; }
+template <int D, class R>
+__device__ __forceinline__ void attend_block_f32(const AttnArgs& a, int32_t row, int32_t r0, DescGen<R> gen) {
+  const size_t qoff = a.hm.q_slab(row, a.seq_len, D);
+  const size_t kvoff = a.hm.kv_slab(row, a.seq_len, D);
+  attend_f32<D, R>(static_cast<const float*>(a.q) + qoff, static_cast<const float*>(a.k) + kvoff,
+                   static_cast<const float*>(a.v) + kvoff, static_cast<float*>(a.o) + qoff,
+                   a.seq_len, r0, a.scale_log2, gen);
+}
 
-template <typename T, int D>
-__global__ __launch_bounds__(threads_of<T>()) __attribute__((amdgpu_waves_per_eu(waves_per_eu<T>(), waves_per_eu<T>()))) void attn_vs_kernel(AttnArgs a, VsIndex ix) {
-  const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
+template <int D, class Src>
+__device__ __forceinline__ void attend_panel_bf16(const AttnArgs& a, int32_t row, int32_t r0, const Src& src) {
+  const size_t qoff = a.hm.q_slab(row, a.seq_len, D);
+  const size_t kvoff = a.hm.kv_slab(row, a.seq_len, D);
+  attend_panel<D, Src>(static_cast<const uint16_t*>(a.q) + qoff, static_cast<const uint16_t*>(a.k) + kvoff,
+                       static_cast<const uint16_t*>(a.v) + kvoff, static_cast<uint16_t*>(a.o) + qoff,
+                       a.seq_len, r0, a.scale_log2, src);
+}
+
+__device__ __forceinline__ int32_t num_blocks(int32_t n) { return (n + BLOCK - 1) / BLOCK; }
+__device__ __forceinline__ int32_t num_panels(int32_t n) { return (num_blocks(n) + PANEL - 1) / PANEL; }
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_vs_f32_kernel(AttnArgs a, VsIndex ix) {
+  const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
   work_item(a, nb, row, blk);
   const int32_t r0 = blk * BLOCK;
   const size_t cb = (size_t)row * nb + blk;
   VsRanges rg{ix.iv + (size_t)row * ix.max_iv * 2, min(ix.n_iv[row], ix.max_iv), 0, r0, a.seq_len};
-  attend<T, D>(a, row, r0,
-               make_gen(rg, ix.cols + cb * ix.max_cols, min(ix.n_cols[cb], ix.max_cols), r0, a.seq_len));
+  attend_block_f32<D>(a, row, r0,
+                      make_gen(rg, ix.cols + cb * ix.max_cols, min(ix.n_cols[cb], ix.max_cols), r0, a.seq_len));
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(threads_of<T>()) __attribute__((amdgpu_waves_per_eu(waves_per_eu<T>(), waves_per_eu<T>()))) void attn_blocks_kernel(AttnArgs a, BlockIndex ix) {
-  const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
+template <int D>
+__global__ __launch_bounds__(64) void attn_blocks_f32_kernel(AttnArgs a, BlockIndex ix) {
+  const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
   work_item(a, nb, row, blk);
   const size_t cb = (size_t)row * nb + blk;
   BlockRanges rg{ix.sel + cb * ix.max_sel, min(ix.n_sel[cb], ix.max_sel), 0, a.seq_len};
-  attend<T, D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
+  attend_block_f32<D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(threads_of<T>()) __attribute__((amdgpu_waves_per_eu(waves_per_eu<T>(), waves_per_eu<T>()))) void attn_stream_kernel(AttnArgs a, StreamIndex ix) {
-  const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
+template <int D>
+__global__ __launch_bounds__(64) void attn_stream_f32_kernel(AttnArgs a, StreamIndex ix) {
+  const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
   work_item(a, nb, row, blk);
   StreamRanges rg{blk, ix.init_blocks, ix.local_blocks, 0, a.seq_len};
-  attend<T, D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
+  attend_block_f32<D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
 }
+
+#define PANEL_KERNEL __global__ __launch_bounds__(64 * PANEL_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+
+template <int D>
+PANEL_KERNEL void attn_vs_bf16_kernel(AttnArgs a, VsIndex ix) {
+  const int32_t nb = num_blocks(a.seq_len);
+  int32_t row, p;
+  work_item(a, num_panels(a.seq_len), row, p);
+  const int32_t a0 = PANEL * p, r0 = a0 * BLOCK;
+  VsPanelSrc src;
+  src.rg = VsPanelRanges{ix.iv + (size_t)row * ix.max_iv * 2, min(ix.n_iv[row], ix.max_iv), 0, r0, a.seq_len};
+  src.cut = PanelCut{};
+#pragma unroll
+  for (int j = 0; j < PANEL; ++j) {
+    const size_t cb = (size_t)row * nb + a0 + j;
+    const bool on = a0 + j < nb;
+    src.cols[j] = on ? ix.cols + cb * ix.max_cols : ix.cols;
+    src.ncol[j] = on ? max(0, min(ix.n_cols[cb], ix.max_cols)) : 0;
+    src.cp[j] = 0;
+  }
+  src.r0 = r0;
+  src.n = a.seq_len;
+  attend_panel_bf16<D>(a, row, r0, src);
+}
+
+template <int D>
+PANEL_KERNEL void attn_blocks_bf16_kernel(AttnArgs a, BlockIndex ix) {
+  const int32_t nb = num_blocks(a.seq_len);
+  int32_t row, p;
+  work_item(a, num_panels(a.seq_len), row, p);
+  const int32_t a0 = PANEL * p, r0 = a0 * BLOCK;
+  BsPanelSrc src;
+#pragma unroll
+  for (int j = 0; j < PANEL; ++j) {
+    const size_t cb = (size_t)row * nb + a0 + j;
+    const bool on = a0 + j < nb;
+    src.sel[j] = on ? ix.sel + cb * ix.max_sel : ix.sel;
+    src.nsel[j] = on ? max(0, min(ix.n_sel[cb], ix.max_sel)) : 0;
+    src.cp[j] = 0;
+  }
+  src.mb = MergedBlocks{nullptr, nullptr, 0, 0, nb, a.seq_len};
+  src.cut = PanelCut{};
+  src.r0 = r0;
+  attend_panel_bf16<D>(a, row, r0, src);
+}
+
+template <int D>
+PANEL_KERNEL void attn_stream_bf16_kernel(AttnArgs a, StreamIndex ix) {
+  const int32_t nb = num_blocks(a.seq_len);
+  int32_t row, p;
+  work_item(a, num_panels(a.seq_len), row, p);
+  const int32_t a0 = PANEL * p;
+  StreamPanelSrc src;
+  src.rg = StreamPanelRanges{a0, nb, ix.init_blocks, ix.local_blocks, 0, a.seq_len};
+  src.cut = PanelCut{};
+  src.r0 = a0 * BLOCK;
+  attend_panel_bf16<D>(a, row, a0 * BLOCK, src);
+}
+
+// grid: rows x (panels for bf16, blocks for fp32)
+dim3 attn_grid(const AttnArgs& a) {
+  const long long nb = (a.seq_len + BLOCK - 1) / BLOCK;
+  const long long units = a.dtype == BF16 ? (nb + PANEL - 1) / PANEL : nb;
+  return dim3((unsigned)((long long)a.rows * units));
+}
+dim3 attn_block(const AttnArgs& a) { return dim3(a.dtype == BF16 ? 64 * PANEL_WAVES : 64); }
 
 }  // namespace
 
 hipError_t launch_attention_vs(const AttnArgs& a, const VsIndex& ix, hipStream_t s) {
-  const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
-  const long long grid = (long long)a.rows * nb;
-  if (grid == 0) return hipSuccess;
-  auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_vs_kernel<uint16_t, 64> : attn_vs_kernel<uint16_t, 128>)
-                            : (a.head_dim == 64 ? attn_vs_kernel<float, 64> : attn_vs_kernel<float, 128>);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(a.dtype == BF16 ? 64 * BF16_WAVES : 64), 0, s, a, ix);
+  const dim3 grid = attn_grid(a);
+  if (grid.x == 0) return hipSuccess;
+  auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_vs_bf16_kernel<64> : attn_vs_bf16_kernel<128>)
+                            : (a.head_dim == 64 ? attn_vs_f32_kernel<64> : attn_vs_f32_kernel<128>);
+  hipLaunchKernelGGL(fn, grid, attn_block(a), 0, s, a, ix);
   return hipGetLastError();
 }
 
 hipError_t launch_attention_blocks(const AttnArgs& a, const BlockIndex& ix, hipStream_t s) {
-  const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
-  const long long grid = (long long)a.rows * nb;
-  if (grid == 0) return hipSuccess;
-  auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_blocks_kernel<uint16_t, 64> : attn_blocks_kernel<uint16_t, 128>)
-                            : (a.head_dim == 64 ? attn_blocks_kernel<float, 64> : attn_blocks_kernel<float, 128>);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(a.dtype == BF16 ? 64 * BF16_WAVES : 64), 0, s, a, ix);
+  const dim3 grid = attn_grid(a);
+  if (grid.x == 0) return hipSuccess;
+  auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_blocks_bf16_kernel<64> : attn_blocks_bf16_kernel<128>)
+                            : (a.head_dim == 64 ? attn_blocks_f32_kernel<64> : attn_blocks_f32_kernel<128>);
+  hipLaunchKernelGGL(fn, grid, attn_block(a), 0, s, a, ix);
   return hipGetLastError();
 }
 
 hipError_t launch_attention_stream(const AttnArgs& a, const StreamIndex& ix, hipStream_t s) {
-  const int32_t nb = (a.seq_len + BLOCK - 1) / BLOCK;
-  const long long grid = (long long)a.rows * nb;
-  if (grid == 0) return hipSuccess;
-  auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_stream_kernel<uint16_t, 64> : attn_stream_kernel<uint16_t, 128>)
-                            : (a.head_dim == 64 ? attn_stream_kernel<float, 64> : attn_stream_kernel<float, 128>);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(a.dtype == BF16 ? 64 * BF16_WAVES : 64), 0, s, a, ix);
+  const dim3 grid = attn_grid(a);
+  if (grid.x == 0) return hipSuccess;
+  auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_stream_bf16_kernel<64> : attn_stream_bf16_kernel<128>)
+                            : (a.head_dim == 64 ? attn_stream_f32_kernel<64> : attn_stream_f32_kernel<128>);
+  hipLaunchKernelGGL(fn, grid, attn_block(a), 0, s, a, ix);
   return hipGetLastError();
 }
 

@@ -44,8 +44,8 @@
  *   DSA_ERR_INVALID_ARG for a NULL pointer, a negative or inconsistent size,
  *   q_heads % kv_heads != 0, a duplicated or out-of-range head id or a bad
  *   top-k/window argument; DSA_ERR_UNSUPPORTED for a head_dim other than 64 or
- *   128, an unknown dtype, last_q outside [1, 64] or more than DSA_MAX_HEADS
- *   heads; DSA_ERR_WORKSPACE when workspace_bytes is below what the matching
+ *   128, an unknown dtype, last_q outside [1, 64], more than DSA_MAX_HEADS
+ *   heads or a head slab (seq_len * head_dim * element size) of 2 GiB or more; DSA_ERR_WORKSPACE when workspace_bytes is below what the matching
  *   *_workspace_bytes call returns; DSA_ERR_HIP when a launch fails.
  */
 #ifndef DSA_H
