@@ -206,6 +206,7 @@ dsa_status dsa_vs_estimate(const void* q, const void* k, const dsa_shape* shape,
   a.last_q = last_q; a.rows = rows;
   a.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
   a.hm = hm;
+  a.wo = make_work_order(hm);
   a.v_scores = v_scores; a.s_scores = s_scores;
   est_carve(a, workspace);
   return hip_status(launch_vs_estimate(a, static_cast<hipStream_t>(stream)));
@@ -288,6 +289,7 @@ dsa_status dsa_vertical_slash_sparse_attention(const void* q, const void* k, con
   ea.last_q = last_q; ea.rows = rows;
   ea.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
   ea.hm = hm;
+  ea.wo = make_work_order(hm);
   ea.v_scores = w.v; ea.s_scores = w.s;
   est_carve(ea, w.est);
   hipError_t e = launch_vs_estimate(ea, s);

@@ -7,8 +7,10 @@
 //   the partial sums meet in LDS in a fixed order, and the mean is written in
 //   fp32. HBM-bound: every input byte is read once.
 // logits_kernel: L[a][c] = scale * Qp[a] . Kp[c] for the causal triangle
-//   c <= a, in 64x64 tiles with fp32 MFMA (16x16x4): fp32 products keep the
-//   logits within rounding of the exact dot, which the block ranking needs.
+//   c <= a, in 64x64 tiles. The fp32 dot products run on the bf16 MFMA as
+//   three products of hi/lo bf16 splits with fp32 accumulation, which keeps
+//   them within about 2^-16 relative of the exact dot at five times the rate
+//   of the fp32 MFMA.
 #include "kernels.hpp"
 
 namespace dsa {
@@ -51,11 +53,29 @@ __global__ __launch_bounds__(POOL_THREADS) void pool_kernel(const T* __restrict_
   }
 }
 
+// Eight fp32 values as bf16 pairs: hi = bf16(x) (nearest even) and
+// lo = bf16(x - hi), so x - hi - lo is below 2^-17 |x|.
+__device__ __forceinline__ void split8(const float* p, u32x4& hi, u32x4& lo) {
+  const f32x4 x0 = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
+  const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    hi[e] = h;
+    lo[e] = pack_bf16x2(x[2 * e] - __uint_as_float(h << 16), x[2 * e + 1] - __uint_as_float(h & 0xffff0000u));
+  }
+}
+
+// One wave per 64x64 tile of the causal triangle. Each fp32 product
+// qp . kp is taken as hi.hi + hi.lo + lo.hi of the bf16 splits on the bf16
+// MFMA (16x16x32), accumulated in fp32: the dropped lo.lo term and the split
+// residuals stay below about 2^-16 of |qp| |kp| per product.
 template <int D>
 __global__ __launch_bounds__(64) void logits_kernel(const float* __restrict__ qp, const float* __restrict__ kp,
                                                     int32_t row0, int32_t nb, float scale, int32_t kv_map,
                                                     HeadMap hm, float* __restrict__ logits) {
-  constexpr int DK = D / 4;  // lane group g holds dims DK*g .. DK*g + DK - 1
+  constexpr int KS = D / 32;  // k-steps; lane group g holds dims 32s + 8g .. + 7
   const int32_t t = blockIdx.x, lrow = blockIdx.y;
   // triangle tile index t -> (at, ct), ct <= at
   int32_t at = (int32_t)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
@@ -76,22 +96,25 @@ __global__ __launch_bounds__(64) void logits_kernel(const float* __restrict__ qp
   const float* kc[4];
 #pragma unroll
   for (int b4 = 0; b4 < 4; ++b4) {
-    qa[b4] = q + (size_t)min(at * 64 + 16 * b4 + l16, nb - 1) * D + DK * g;
-    kc[b4] = k + (size_t)min(ct * 64 + 16 * b4 + l16, nb - 1) * D + DK * g;
+    qa[b4] = q + (size_t)min(at * 64 + 16 * b4 + l16, nb - 1) * D + 8 * g;
+    kc[b4] = k + (size_t)min(ct * 64 + 16 * b4 + l16, nb - 1) * D + 8 * g;
   }
-  for (int s4 = 0; s4 < DK; s4 += 4) {
-    f32x4 av[4], bv[4];
+#pragma unroll 1
+  for (int s = 0; s < KS; ++s) {
+    u32x4 ah[4], al[4];
 #pragma unroll
-    for (int b4 = 0; b4 < 4; ++b4) {
-      av[b4] = *reinterpret_cast<const f32x4*>(qa[b4] + s4);
-      bv[b4] = *reinterpret_cast<const f32x4*>(kc[b4] + s4);
+    for (int ib = 0; ib < 4; ++ib) split8(qa[ib] + 32 * s, ah[ib], al[ib]);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      u32x4 bh, bl;
+      split8(kc[jb] + 32 * s, bh, bl);
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        acc[ib][jb] = mfma_bf16(ah[ib], bh, acc[ib][jb]);
+        acc[ib][jb] = mfma_bf16(ah[ib], bl, acc[ib][jb]);
+        acc[ib][jb] = mfma_bf16(al[ib], bh, acc[ib][jb]);
+      }
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) acc[ib][jb] = mfma_f32(av[ib][e], bv[jb][e], acc[ib][jb]);
   }
   float* L = logits + (size_t)lrow * nb * nb;
 #pragma unroll

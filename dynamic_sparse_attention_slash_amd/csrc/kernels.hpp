@@ -37,6 +37,36 @@ struct WorkOrder {
 };
 WorkOrder make_work_order(const HeadMap& hm);
 
+// Work-group -> (row, unit) for a grid of rows x units items, units visited
+// latest first. The hardware deals consecutive work-group ids round-robin over
+// the 8 XCDs, each with its own L2. Work items, ordered by WorkOrder (batch,
+// kv group, unit, head of the group), are cut into chunks of XCD_CHUNK and the
+// chunks are dealt round-robin to the XCDs: the work-groups an XCD runs at one
+// time then share K/V rows in its L2, and every XCD still gets a mix of all kv
+// groups and unit positions (whose costs differ). A tail shorter than NUM_XCD
+// chunks keeps the identity mapping.
+constexpr int32_t NUM_XCD = 8;
+constexpr int32_t XCD_CHUNK = 32;
+__device__ __forceinline__ void work_item(const HeadMap& hm, const WorkOrder& wo, int32_t units,
+                                          int32_t& row, int32_t& unit) {
+  const int32_t N = gridDim.x, i = blockIdx.x;
+  const int32_t T = (N / (NUM_XCD * XCD_CHUNK)) * (NUM_XCD * XCD_CHUNK);
+  int32_t w = i;
+  if (i < T) {
+    const int32_t xcd = i % NUM_XCD, k = i / NUM_XCD;
+    w = ((k / XCD_CHUNK) * NUM_XCD + xcd) * XCD_CHUNK + k % XCD_CHUNK;
+  }
+  const int32_t n = hm.n, per_b = units * n;
+  const int32_t b = w / per_b, w2 = w - b * per_b;
+  int32_t gi = 0;
+  while (gi + 1 < wo.n_groups && wo.gstart[gi + 1] * units <= w2) ++gi;
+  const int32_t g0 = wo.gstart[gi], size = wo.gstart[gi + 1] - g0;
+  const int32_t off = w2 - g0 * units;
+  const int32_t u_idx = off / size, j = off - u_idx * size;
+  row = b * n + wo.order[g0 + j];
+  unit = units - 1 - u_idx;
+}
+
 struct AttnArgs {
   const void* q; const void* k; const void* v; void* o;
   int32_t seq_len, head_dim, dtype;
@@ -58,6 +88,7 @@ struct EstArgs {
   int32_t rows;
   float scale_log2;
   HeadMap hm;
+  WorkOrder wo;
   float* v_scores; float* s_scores;       // [rows][seq_len]
   float* part_stats;  // [rows][nchunks][64][2]
   float* row_stats;   // [rows][64]

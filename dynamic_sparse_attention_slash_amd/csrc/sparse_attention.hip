@@ -142,34 +142,6 @@ __device__ __forceinline__ int32_t desc_key(const Desc& d, const int32_t* cols, 
   return (d.b & F_LIST) ? min(max(cols[d.a + sl], 0), n - 1) : d.a + sl;
 }
 
-// Work-group -> (row, query block). The hardware deals consecutive work-group
-// ids round-robin over the 8 XCDs, each with its own L2. Work items, ordered
-// by WorkOrder, are cut into chunks of XCD_CHUNK and the chunks are dealt
-// round-robin to the XCDs: the work-groups an XCD runs at one time then share
-// K/V rows in its L2, and every XCD still gets a mix of all kv groups and block
-// positions (whose costs differ). A tail shorter than NUM_XCD chunks keeps the
-// identity mapping.
-constexpr int32_t NUM_XCD = 8;
-constexpr int32_t XCD_CHUNK = 32;
-__device__ __forceinline__ void work_item(const AttnArgs& ar, int32_t nb, int32_t& row, int32_t& a) {
-  const int32_t N = gridDim.x, i = blockIdx.x;
-  const int32_t T = (N / (NUM_XCD * XCD_CHUNK)) * (NUM_XCD * XCD_CHUNK);
-  int32_t w = i;
-  if (i < T) {
-    const int32_t xcd = i % NUM_XCD, k = i / NUM_XCD;
-    w = ((k / XCD_CHUNK) * NUM_XCD + xcd) * XCD_CHUNK + k % XCD_CHUNK;
-  }
-  const int32_t n = ar.hm.n, per_b = nb * n;
-  const int32_t b = w / per_b, w2 = w - b * per_b;
-  int32_t gi = 0;
-  while (gi + 1 < ar.wo.n_groups && ar.wo.gstart[gi + 1] * nb <= w2) ++gi;
-  const int32_t g0 = ar.wo.gstart[gi], size = ar.wo.gstart[gi + 1] - g0;
-  const int32_t off = w2 - g0 * nb;
-  const int32_t a_idx = off / size, j = off - a_idx * size;
-  row = b * n + ar.wo.order[g0 + j];
-  a = nb - 1 - a_idx;
-}
-
 // ---------------------------------------------------------------------------
 // softmax pieces on a tile of S^T values st[sub-block][query block][i]:
 // lane holds query column (l & 15) + 16*qb and key slots 4*(l >> 4) + i
@@ -1006,7 +978,7 @@ template <int D>
 __global__ __launch_bounds__(64) void attn_vs_f32_kernel(AttnArgs a, VsIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
-  work_item(a, nb, row, blk);
+  work_item(a.hm, a.wo, nb, row, blk);
   const int32_t r0 = blk * BLOCK;
   const size_t cb = (size_t)row * nb + blk;
   VsRanges rg{ix.iv + (size_t)row * ix.max_iv * 2, min(ix.n_iv[row], ix.max_iv), 0, r0, a.seq_len};
@@ -1018,7 +990,7 @@ template <int D>
 __global__ __launch_bounds__(64) void attn_blocks_f32_kernel(AttnArgs a, BlockIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
-  work_item(a, nb, row, blk);
+  work_item(a.hm, a.wo, nb, row, blk);
   const size_t cb = (size_t)row * nb + blk;
   BlockRanges rg{ix.sel + cb * ix.max_sel, min(ix.n_sel[cb], ix.max_sel), 0, a.seq_len};
   attend_block_f32<D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
@@ -1028,7 +1000,7 @@ template <int D>
 __global__ __launch_bounds__(64) void attn_stream_f32_kernel(AttnArgs a, StreamIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
-  work_item(a, nb, row, blk);
+  work_item(a.hm, a.wo, nb, row, blk);
   StreamRanges rg{blk, ix.init_blocks, ix.local_blocks, 0, a.seq_len};
   attend_block_f32<D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
 }
@@ -1039,7 +1011,7 @@ template <int D>
 PANEL_KERNEL void attn_vs_bf16_kernel(AttnArgs a, VsIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, p;
-  work_item(a, num_panels(a.seq_len), row, p);
+  work_item(a.hm, a.wo, num_panels(a.seq_len), row, p);
   const int32_t a0 = PANEL * p, r0 = a0 * BLOCK;
   VsPanelSrc src;
   src.rg = VsPanelRanges{ix.iv + (size_t)row * ix.max_iv * 2, min(ix.n_iv[row], ix.max_iv), 0, r0, a.seq_len};
@@ -1061,7 +1033,7 @@ template <int D>
 PANEL_KERNEL void attn_blocks_bf16_kernel(AttnArgs a, BlockIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, p;
-  work_item(a, num_panels(a.seq_len), row, p);
+  work_item(a.hm, a.wo, num_panels(a.seq_len), row, p);
   const int32_t a0 = PANEL * p, r0 = a0 * BLOCK;
   BsPanelSrc src;
 #pragma unroll
@@ -1082,7 +1054,7 @@ template <int D>
 PANEL_KERNEL void attn_stream_bf16_kernel(AttnArgs a, StreamIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, p;
-  work_item(a, num_panels(a.seq_len), row, p);
+  work_item(a.hm, a.wo, num_panels(a.seq_len), row, p);
   const int32_t a0 = PANEL * p;
   StreamPanelSrc src;
   src.rg = StreamPanelRanges{a0, nb, ix.init_blocks, ix.local_blocks, 0, a.seq_len};

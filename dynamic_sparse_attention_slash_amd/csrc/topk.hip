@@ -8,12 +8,15 @@
 //
 // Method: scores map to order-preserving 32-bit keys (the forced entry gets
 // the maximum key, which no canonical float reaches). A 4-pass MSB-first radix
-// select (8 bits per pass, per-wave LDS histograms) finds the k-th largest key
-// T and how many entries equal to T must be kept (need_eq). A compaction pass
-// then walks the entries in index order, each wave owning one contiguous
-// segment: an entry is kept when key > T, or key == T and fewer than need_eq
-// equal keys precede it. Ballot prefix counts give each kept entry its output
-// slot, so the result comes out ascending with no sort.
+// select (8 bits per pass) finds the k-th largest key T and how many entries
+// equal to T must be kept (need_eq). Each pass counts digits into LDS
+// histograms, one copy per wave and lane group so that the few bins a float
+// exponent range fills are not hit by a whole wave at once; the bin holding
+// the k-th largest key comes from a parallel suffix scan over the 256 bins.
+// A compaction pass then walks the entries in index order, each wave owning
+// one contiguous segment (which it also visits in the counting passes): an entry is kept when key > T, or key == T and fewer
+// than need_eq equal keys precede it. Ballot prefix counts give each kept
+// entry its output slot, so the result comes out ascending with no sort.
 #include "kernels.hpp"
 
 namespace dsa {
@@ -27,64 +30,97 @@ __device__ __forceinline__ uint32_t score_key(float x) {
 }
 constexpr uint32_t FORCED_KEY = 0xffffffffu;
 
-template <int NW>
+template <int NW, int NC>
 struct SelectShared {
-  uint32_t hist[NW][256];
-  uint32_t tot[256];
+  uint32_t hist[NW * NC][256];  // per wave and lane group
+  uint32_t scan[256];           // wave-local suffix sums of the bin totals
+  uint32_t wsum[4];             // bin totals per 64-bin wave slice
   uint32_t wcnt[NW][2];
   uint32_t digit, rem;
 };
 
-// Top kk (1 <= kk < m) of the m keys get(i), written ascending to out[0..kk).
-template <int NW, class Get>
-__device__ void select_topk(const Get& get, int32_t m, int32_t kk, int32_t* __restrict__ out,
-                            SelectShared<NW>& sh) {
+// The keys of one wave's segment [s0, s1) of the candidates, visited in
+// ascending position order 64 at a time: visit(f) calls f(j, key, valid) for
+// position s0 + 64 j + lane, j < trips (trips is uniform over the wave).
+struct GlobalSeg {
+  const float* x; int32_t forced, s0, s1, trips, lane;
+  template <class F>
+  __device__ __forceinline__ void visit(F&& f) const {
+    for (int32_t j = 0; j < trips; ++j) {
+      const int32_t i = s0 + 64 * j + lane;
+      const bool valid = i < s1;
+      f(j, valid ? (i == forced ? FORCED_KEY : score_key(x[i])) : 0u, valid);
+    }
+  }
+};
+// Wave w's segment of m candidates: [w * seg, (w + 1) * seg) clipped to m.
+template <int NW>
+__device__ __forceinline__ void wave_segment(int32_t m, int32_t& s0, int32_t& s1, int32_t& trips) {
+  const int32_t wave = threadIdx.x >> 6;
+  const int32_t seg = ((m + NW * 64 - 1) / (NW * 64)) * 64;
+  s0 = min(m, wave * seg);
+  s1 = min(m, s0 + seg);
+  trips = (s1 - s0 + 63) >> 6;
+}
+
+// Top kk (1 <= kk < m) of the m candidates, each wave visiting its segment
+// through `seg`, written ascending to out[0..kk). NC histogram copies per wave
+// (lane groups of 64 / NC lanes).
+template <int NW, int NC, class Seg>
+__device__ __forceinline__ void select_topk(const Seg& seg, int32_t kk, int32_t* __restrict__ out,
+                            SelectShared<NW, NC>& sh) {
+  static_assert(NW >= 4, "the digit scan uses the first four waves");
   const int32_t tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int NT = NW * 64;
+  uint32_t* hist = &sh.hist[wave * NC + lane / (64 / NC)][0];
   uint32_t prefix = 0, pmask = 0;
-  if (tid == 0) sh.rem = (uint32_t)kk;
+  uint32_t rem = (uint32_t)kk;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < NW * 256; i += NT) (&sh.hist[0][0])[i] = 0;
+    for (int i = tid; i < NW * NC * 256; i += NT) (&sh.hist[0][0])[i] = 0;
     __syncthreads();
-    for (int32_t i = tid; i < m; i += NT) {
-      uint32_t key = get(i);
-      if ((key & pmask) == prefix) atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
-    }
+    seg.visit([&](int32_t, uint32_t key, bool valid) {
+      if (valid && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    });
     __syncthreads();
-    for (int b = tid; b < 256; b += NT) {
-      uint32_t t = 0;
+    // the digit: the largest bin b whose suffix count S(b) (entries with a
+    // digit >= b) reaches rem; thread b of the first four waves owns bin b
+    uint32_t t = 0, s = 0;
+    if (tid < 256) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) t += sh.hist[w][b];
-      sh.tot[b] = t;
+      for (int c = 0; c < NW * NC; ++c) t += sh.hist[c][tid];
+      s = t;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_down(s, d);
+        if (lane + d < 64) s += o;
+      }
+      sh.scan[tid] = s;
+      if (lane == 0) sh.wsum[wave] = s;
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t cum = 0, rem = sh.rem;
-      int b = 255;
-      for (; b > 0; --b) {
-        if (cum + sh.tot[b] >= rem) break;
-        cum += sh.tot[b];
+    if (tid < 256) {
+      uint32_t above = 0;
+      for (int w = wave + 1; w < 4; ++w) above += sh.wsum[w];
+      const uint32_t S = s + above, S1 = S - t;  // S(b), S(b + 1)
+      if (S >= rem && S1 < rem) {
+        sh.digit = (uint32_t)tid;
+        sh.rem = rem - S1;
       }
-      sh.digit = (uint32_t)b;
-      sh.rem = rem - cum;
     }
     __syncthreads();
     prefix |= sh.digit << shift;
     pmask |= 255u << shift;
+    rem = sh.rem;
   }
   const uint32_t T = prefix;
-  const uint32_t need_eq = sh.rem;
+  const uint32_t need_eq = rem;
 
-  // compaction in index order, wave w owns [w*seg, (w+1)*seg)
-  const int32_t seg = ((m + NW * 64 - 1) / (NW * 64)) * 64;
-  const int32_t s0 = min(m, wave * seg), s1 = min(m, s0 + seg);
+  // compaction in index order over the waves' segments
   uint32_t n_gt = 0, n_eq = 0;
-  for (int32_t i0 = s0; i0 < s1; i0 += 64) {
-    int32_t i = i0 + lane;
-    uint32_t key = i < s1 ? get(i) : 0u;
-    n_gt += __popcll(__ballot(i < s1 && key > T));
-    n_eq += __popcll(__ballot(i < s1 && key == T));
-  }
+  seg.visit([&](int32_t, uint32_t key, bool valid) {
+    n_gt += __popcll(__ballot(valid && key > T));
+    n_eq += __popcll(__ballot(valid && key == T));
+  });
   if (lane == 0) { sh.wcnt[wave][0] = n_gt; sh.wcnt[wave][1] = n_eq; }
   __syncthreads();
   uint32_t gt_before = 0, eq_before = 0;
@@ -92,54 +128,45 @@ __device__ void select_topk(const Get& get, int32_t m, int32_t kk, int32_t* __re
   uint32_t eq_seen = eq_before;
   uint32_t pos = gt_before + min(eq_before, need_eq);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int32_t i0 = s0; i0 < s1; i0 += 64) {
-    int32_t i = i0 + lane;
-    uint32_t key = i < s1 ? get(i) : 0u;
-    bool eq = i < s1 && key == T;
-    uint64_t eq_mask = __ballot(eq);
-    uint32_t eq_rank = eq_seen + __popcll(eq_mask & lt_mask);
-    bool keep = i < s1 && (key > T || (eq && eq_rank < need_eq));
-    uint64_t keep_mask = __ballot(keep);
+  seg.visit([&](int32_t j, uint32_t key, bool valid) {
+    const bool eq = valid && key == T;
+    const uint64_t eq_mask = __ballot(eq);
+    const uint32_t eq_rank = eq_seen + __popcll(eq_mask & lt_mask);
+    const bool keep = valid && (key > T || (eq && eq_rank < need_eq));
+    const uint64_t keep_mask = __ballot(keep);
     const uint32_t slot = pos + __popcll(keep_mask & lt_mask);
-    if (keep && slot < (uint32_t)kk) out[slot] = i;
+    if (keep && slot < (uint32_t)kk) out[slot] = seg.s0 + 64 * j + lane;
     pos += __popcll(keep_mask);
     eq_seen += __popcll(eq_mask);
-  }
+  });
 }
-
-struct GlobalKeys {
-  const float* x; int32_t forced;
-  __device__ uint32_t operator()(int32_t i) const { return i == forced ? FORCED_KEY : score_key(x[i]); }
-};
-struct LdsKeys {
-  const uint32_t* k;
-  __device__ uint32_t operator()(int32_t i) const { return k[i]; }
-};
 
 constexpr int ROW_WAVES = 16;
 __global__ __launch_bounds__(ROW_WAVES * 64) void topk_rows_kernel(const float* __restrict__ scores,
                                                                    int32_t n, int32_t kk, int32_t forced,
                                                                    int32_t* __restrict__ out) {
-  __shared__ SelectShared<ROW_WAVES> sh;
+  __shared__ SelectShared<ROW_WAVES, 2> sh;
   const int32_t row = blockIdx.x;
   int32_t* o = out + (size_t)row * kk;
   if (kk >= n) {
     for (int32_t i = threadIdx.x; i < n; i += ROW_WAVES * 64) o[i] = i;
     return;
   }
-  select_topk<ROW_WAVES>(GlobalKeys{scores + (size_t)row * n, forced}, n, kk, o, sh);
+  GlobalSeg seg{scores + (size_t)row * n, forced, 0, 0, 0, (int32_t)(threadIdx.x & 63)};
+  wave_segment<ROW_WAVES>(n, seg.s0, seg.s1, seg.trips);
+  select_topk<ROW_WAVES, 2>(seg, kk, o, sh);
 }
 
 // One work-group per (row, query block a): top min(topk, a+1) of
-// logits[row][a][0..a] with entry a forced.
+// logits[row][a][0..a] with entry a forced. The candidates are read from
+// memory in every pass (the row stays in cache); LDS holds only the
+// histograms, which keeps eight work-groups resident per CU.
 constexpr int BLK_WAVES = 4;
-constexpr int LDS_KEYS = 16384;
 __global__ __launch_bounds__(BLK_WAVES * 64) void block_topk_kernel(const float* __restrict__ logits,
                                                                     int32_t nb, int32_t topk,
                                                                     int32_t* __restrict__ sel,
                                                                     int32_t* __restrict__ n_sel) {
-  __shared__ SelectShared<BLK_WAVES> sh;
-  __shared__ uint32_t keys[LDS_KEYS];
+  __shared__ SelectShared<BLK_WAVES, 2> sh;
   const int32_t a = blockIdx.x, row = blockIdx.y;
   const int32_t m = a + 1;
   const int32_t kk = min(topk, m);
@@ -151,14 +178,9 @@ __global__ __launch_bounds__(BLK_WAVES * 64) void block_topk_kernel(const float*
     for (int32_t i = threadIdx.x; i < m; i += BLK_WAVES * 64) o[i] = i;
     return;
   }
-  const float* x = logits + cb * nb;
-  if (m <= LDS_KEYS) {
-    for (int32_t i = threadIdx.x; i < m; i += BLK_WAVES * 64) keys[i] = i == a ? FORCED_KEY : score_key(x[i]);
-    __syncthreads();
-    select_topk<BLK_WAVES>(LdsKeys{keys}, m, kk, o, sh);
-  } else {
-    select_topk<BLK_WAVES>(GlobalKeys{x, a}, m, kk, o, sh);
-  }
+  GlobalSeg seg{logits + cb * nb, a, 0, 0, 0, (int32_t)(threadIdx.x & 63)};
+  wave_segment<BLK_WAVES>(m, seg.s0, seg.s1, seg.trips);
+  select_topk<BLK_WAVES, 2>(seg, kk, o, sh);
 }
 
 }  // namespace

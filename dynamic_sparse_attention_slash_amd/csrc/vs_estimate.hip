@@ -13,6 +13,9 @@
 //   S = Q_window K_chunk^T with MFMA (lane = one key column, 16 query rows) and
 //   keeps a running (max, sum) per query row; partials go to workspace.
 // Combine: per row, max / log-sum over the chunks -> F_r = m_r + log2 Z_r.
+// Work-groups of both passes are mapped like the attention's: the heads of a
+// kv group take the same key chunk on the same XCD at about the same time, so
+// a chunk of K is fetched from memory once per group.
 // Pass 2 (scores): recompute S, p = exp2(S*scale*log2e - F_r). Column sums are
 //   register sums plus two cross-lane steps (the loop runs key-major, so a
 //   key's scores stay in one lane column). Diagonal sums stage each 64x64 tile
@@ -123,8 +126,9 @@ struct Tile<float, D> {
 
 template <typename T, int D>
 __global__ __launch_bounds__(64) void est_stats_kernel(EstArgs a) {
-  const int32_t chunk = blockIdx.x, row = blockIdx.y;
-  const int32_t nchunks = gridDim.x;
+  const int32_t nchunks = (a.seq_len + C - 1) / C;
+  int32_t row, chunk;
+  work_item(a.hm, a.wo, nchunks, row, chunk);
   const Window w{a.seq_len, a.lq_eff()};
   const T* qs = static_cast<const T*>(a.q) + a.hm.q_slab(row, a.seq_len, D);
   const T* ks = static_cast<const T*>(a.k) + a.hm.kv_slab(row, a.seq_len, D);
@@ -192,16 +196,34 @@ __global__ __launch_bounds__(64) void est_stats_kernel(EstArgs a) {
   }
 }
 
-// F_r = m_r + log2(Z_r) over all chunks, one thread per window row.
-__global__ __launch_bounds__(64) void est_combine_kernel(EstArgs a, int32_t nchunks) {
-  const int32_t row = blockIdx.x, r = threadIdx.x;
+// F_r = m_r + log2(Z_r) over all chunks. One work-group per row: thread t
+// merges window row t % 64 over the chunks c = t / 64 (mod COMB_SPLIT) with a
+// running (max, sum), then the COMB_SPLIT partials of each window row meet in
+// LDS in a fixed order.
+constexpr int COMB_SPLIT = 16;
+__global__ __launch_bounds__(64 * COMB_SPLIT) void est_combine_kernel(EstArgs a, int32_t nchunks) {
+  __shared__ float pm[COMB_SPLIT][64], pz[COMB_SPLIT][64];
+  const int32_t row = blockIdx.x, r = threadIdx.x & 63, part = threadIdx.x >> 6;
   const float* src = a.part_stats + (size_t)row * nchunks * 128 + 2 * r;
-  float mm = NEG_BIG;
-  for (int32_t c = 0; c < nchunks; ++c) mm = fmaxf(mm, src[(size_t)c * 128]);
-  float zz = 0.f;
-  for (int32_t c = 0; c < nchunks; ++c)
-    zz += src[(size_t)c * 128 + 1] * fast_exp2(src[(size_t)c * 128] - mm);
-  a.row_stats[(size_t)row * 64 + r] = zz > 0.f ? mm + __log2f(zz) : INFINITY;
+  float mm = NEG_BIG, zz = 0.f;
+  for (int32_t c = part; c < nchunks; c += COMB_SPLIT) {
+    const float mc = src[(size_t)c * 128], zc = src[(size_t)c * 128 + 1];
+    const float mn = fmaxf(mm, mc);
+    zz = zz * fast_exp2(mm - mn) + zc * fast_exp2(mc - mn);
+    mm = mn;
+  }
+  pm[part][r] = mm;
+  pz[part][r] = zz;
+  __syncthreads();
+  if (part == 0) {
+    float m2 = NEG_BIG;
+#pragma unroll
+    for (int t = 0; t < COMB_SPLIT; ++t) m2 = fmaxf(m2, pm[t][r]);
+    float z2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < COMB_SPLIT; ++t) z2 += pz[t][r] * fast_exp2(pm[t][r] - m2);
+    a.row_stats[(size_t)row * 64 + r] = z2 > 0.f ? m2 + __log2f(z2) : INFINITY;
+  }
 }
 
 template <typename T, int D>
@@ -209,8 +231,9 @@ __global__ __launch_bounds__(64) void est_scores_kernel(EstArgs a) {
   constexpr int PS = 65;  // padded LDS row of the 64x64 probability tile
   __shared__ float ptile[64 * PS];
   __shared__ float sacc[SACC];
-  const int32_t chunk = blockIdx.x, row = blockIdx.y;
-  const int32_t nchunks = gridDim.x;
+  const int32_t nchunks = (a.seq_len + C - 1) / C;
+  int32_t row, chunk;
+  work_item(a.hm, a.wo, nchunks, row, chunk);
   const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
   const Window w{a.seq_len, a.lq_eff()};
   const T* qs = static_cast<const T*>(a.q) + a.hm.q_slab(row, a.seq_len, D);
@@ -304,13 +327,13 @@ void est_carve(EstArgs& a, void* ws) {
 hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s) {
   if (a.rows == 0 || a.seq_len == 0) return hipSuccess;
   const int32_t nch = (a.seq_len + C - 1) / C;
-  dim3 grid(nch, a.rows);
+  const dim3 grid((unsigned)((long long)nch * a.rows));
   auto st = a.dtype == BF16 ? (a.head_dim == 64 ? est_stats_kernel<uint16_t, 64> : est_stats_kernel<uint16_t, 128>)
                             : (a.head_dim == 64 ? est_stats_kernel<float, 64> : est_stats_kernel<float, 128>);
   auto sc = a.dtype == BF16 ? (a.head_dim == 64 ? est_scores_kernel<uint16_t, 64> : est_scores_kernel<uint16_t, 128>)
                             : (a.head_dim == 64 ? est_scores_kernel<float, 64> : est_scores_kernel<float, 128>);
   hipLaunchKernelGGL(st, grid, dim3(64), 0, s, a);
-  hipLaunchKernelGGL(est_combine_kernel, dim3(a.rows), dim3(64), 0, s, a, nch);
+  hipLaunchKernelGGL(est_combine_kernel, dim3(a.rows), dim3(64 * COMB_SPLIT), 0, s, a, nch);
   hipLaunchKernelGGL(sc, grid, dim3(64), 0, s, a);
   hipLaunchKernelGGL(est_scombine_kernel, dim3((a.seq_len + 255) / 256, a.rows), dim3(256), 0, s, a, nch);
   return hipGetLastError();
