@@ -171,7 +171,9 @@ dsa_status dsa_bs_pool(const void* x, int32_t dtype, int32_t batch, int32_t x_he
 
 /* Block selection [MInf §2.2 BS head]. qp, kp: device fp32 [rows][nb][head_dim]
  * (row r of qp is scored against row r of kp). L[a][c] = scale * qp[a].kp[c]
- * for c <= a in fp32; sel [rows][nb][min(topk, nb)] receives the ascending
+ * for c <= a in fp32 (each product as hi.hi + hi.lo + lo.hi of bf16 splits,
+ * within about 2^-16 relative of the exact dot); sel [rows][nb][min(topk, nb)]
+ * receives the ascending
  * top-min(topk, a+1) blocks of L[a][0..a] with c = a forced and n_sel
  * [rows][nb] their count. logits: NULL, or device fp32 [rows][nb][nb] that
  * receives L (entries c > a are left untouched). workspace: at least
