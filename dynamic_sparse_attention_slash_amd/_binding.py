@@ -50,7 +50,8 @@ _SIGS = {
     "dsa_streaming_attention": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _i32, _i32, _f32, _ip, _i32, _vp], _i32),
     "dsa_vs_estimate": ([_vp, _vp, ctypes.POINTER(Shape), _i32, _f32, _ip, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "dsa_vs_estimate_workspace_bytes": ([ctypes.POINTER(Shape), _i32], _sz),
-    "dsa_topk": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
+    "dsa_topk": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp], _i32),
+    "dsa_topk_workspace_bytes": ([_i32, _i32, _i32], _sz),
     "dsa_vs_build_index": ([_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
     "dsa_bs_pool": ([_vp, _i32, _i32, _i32, _i32, _i32, _ip, _i32, _vp, _vp], _i32),
     "dsa_bs_select": ([_vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -233,8 +234,9 @@ def topk(scores: torch.Tensor, k: int, forced_index: int = -1) -> torch.Tensor:
     rows, n = scores.shape
     kk = min(k, n)
     out = torch.empty((rows, kk), dtype=torch.int32, device=scores.device)
+    ws = _workspace(load().dsa_topk_workspace_bytes(rows, n, k), scores.device)
     _call("dsa_topk", _dev(scores, "scores", torch.float32), rows, n, k, forced_index,
-          out.data_ptr(), _stream(scores))
+          out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(scores))
     return out
 
 

@@ -3,6 +3,7 @@
 // work is enqueued; nothing here synchronises the stream or allocates.
 #include <math.h>
 #include <string.h>
+#include <algorithm>
 
 #include "../../include/dsa.h"
 #include "kernels.hpp"
@@ -89,7 +90,7 @@ AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, const d
 // ---- vertical-slash workspace layout ----
 struct VsWork {
   void* est; float* v; float* s; int32_t* V; int32_t* S; int32_t* iv; int32_t* n_iv;
-  int32_t* cols; int32_t* n_cols;
+  int32_t* cols; int32_t* n_cols; void* tk;
 };
 size_t vs_layout(int32_t rows, int32_t n, int32_t vk, int32_t sk, void* base, VsWork* w) {
   Carver c{static_cast<char*>(base)};
@@ -103,7 +104,10 @@ size_t vs_layout(int32_t rows, int32_t n, int32_t vk, int32_t sk, void* base, Vs
   int32_t* n_iv = c.take<int32_t>((size_t)rows);
   int32_t* cols = c.take<int32_t>((size_t)rows * nb * vk);
   int32_t* n_cols = c.take<int32_t>((size_t)rows * nb);
-  if (w) *w = VsWork{est, v, s, V, S, iv, n_iv, cols, n_cols};
+  // one top-k scratch serves both selections (they run in turn on one stream)
+  const size_t tkb = std::max(topk_workspace_bytes(rows, n, vk), topk_workspace_bytes(rows, n, sk));
+  void* tk = c.take<char>(tkb);
+  if (w) *w = VsWork{est, v, s, V, S, iv, n_iv, cols, n_cols, tk};
   return c.used;
 }
 
@@ -212,13 +216,20 @@ dsa_status dsa_vs_estimate(const void* q, const void* k, const dsa_shape* shape,
   return hip_status(launch_vs_estimate(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t dsa_topk_workspace_bytes(int32_t rows, int32_t n, int32_t k) {
+  if (rows < 0 || n < 0 || k < 0) return 0;
+  return topk_workspace_bytes(rows, n, k);
+}
+
 dsa_status dsa_topk(const float* scores, int32_t rows, int32_t n, int32_t k, int32_t forced_index,
-                    int32_t* out, void* stream) {
+                    int32_t* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 0 || n < 0 || k < 0) return DSA_ERR_INVALID_ARG;
   if (forced_index < -1 || (forced_index >= n && forced_index != -1)) return DSA_ERR_INVALID_ARG;
   if (rows == 0 || n == 0 || k == 0) return DSA_OK;
   if (!scores || !out) return DSA_ERR_INVALID_ARG;
-  return hip_status(launch_topk_rows(scores, rows, n, k, forced_index, out,
+  const size_t need = topk_workspace_bytes(rows, n, k);
+  if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
+  return hip_status(launch_topk_rows(scores, rows, n, k, forced_index, out, workspace,
                                      static_cast<hipStream_t>(stream)));
 }
 
@@ -293,8 +304,8 @@ dsa_status dsa_vertical_slash_sparse_attention(const void* q, const void* k, con
   ea.v_scores = w.v; ea.s_scores = w.s;
   est_carve(ea, w.est);
   hipError_t e = launch_vs_estimate(ea, s);
-  if (e == hipSuccess) e = launch_topk_rows(w.v, rows, n, vk, -1, w.V, s);
-  if (e == hipSuccess) e = launch_topk_rows(w.s, rows, n, sk, 0, w.S, s);
+  if (e == hipSuccess) e = launch_topk_rows(w.v, rows, n, vk, -1, w.V, w.tk, s);
+  if (e == hipSuccess) e = launch_topk_rows(w.s, rows, n, sk, 0, w.S, w.tk, s);
   if (e == hipSuccess) e = launch_vs_build_index(w.V, vk, w.S, sk, rows, n, w.iv, w.n_iv, w.cols, w.n_cols, s);
   if (e == hipSuccess) {
     AttnArgs a = attn_args(q, k, v, o, shape, scale, hm);

@@ -100,8 +100,10 @@ void est_carve(EstArgs& a, void* ws);
 hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s);
 
 // ---- top-k (topk.hip) ----
+// scratch of launch_topk_rows (0 when the rows are short enough for one pass)
+size_t topk_workspace_bytes(int32_t rows, int32_t n, int32_t k);
 hipError_t launch_topk_rows(const float* scores, int32_t rows, int32_t n, int32_t k,
-                            int32_t forced, int32_t* out, hipStream_t s);
+                            int32_t forced, int32_t* out, void* ws, hipStream_t s);
 // per (row, query block a): top-min(topk, a+1) of logits[row][a][0..a], a forced
 hipError_t launch_block_topk(const float* logits, int32_t rows, int32_t nb, int32_t topk,
                              int32_t* sel, int32_t* n_sel, hipStream_t s);

@@ -44,6 +44,7 @@ struct SelectShared {
 // position s0 + 64 j + lane, j < trips (trips is uniform over the wave).
 struct GlobalSeg {
   const float* x; int32_t forced, s0, s1, trips, lane;
+  int32_t base;  // index of x[0] in the output
   template <class F>
   __device__ __forceinline__ void visit(F&& f) const {
     for (int32_t j = 0; j < trips; ++j) {
@@ -52,6 +53,20 @@ struct GlobalSeg {
       f(j, valid ? (i == forced ? FORCED_KEY : score_key(x[i])) : 0u, valid);
     }
   }
+  __device__ __forceinline__ int32_t index(int32_t j) const { return base + s0 + 64 * j + lane; }
+};
+// Candidates given as (key, index) lists, keys already mapped.
+struct KeySeg {
+  const uint32_t* keys; const int32_t* idx; int32_t s0, s1, trips, lane;
+  template <class F>
+  __device__ __forceinline__ void visit(F&& f) const {
+    for (int32_t j = 0; j < trips; ++j) {
+      const int32_t i = s0 + 64 * j + lane;
+      const bool valid = i < s1;
+      f(j, valid ? keys[i] : 0u, valid);
+    }
+  }
+  __device__ __forceinline__ int32_t index(int32_t j) const { return idx[s0 + 64 * j + lane]; }
 };
 // Wave w's segment of m candidates: [w * seg, (w + 1) * seg) clipped to m.
 template <int NW>
@@ -64,11 +79,12 @@ __device__ __forceinline__ void wave_segment(int32_t m, int32_t& s0, int32_t& s1
 }
 
 // Top kk (1 <= kk < m) of the m candidates, each wave visiting its segment
-// through `seg`, written ascending to out[0..kk). NC histogram copies per wave
+// through `seg`, written ascending to out[0..kk) (and their keys to
+// out_key[0..kk) when out_key is not null). NC histogram copies per wave
 // (lane groups of 64 / NC lanes).
 template <int NW, int NC, class Seg>
 __device__ __forceinline__ void select_topk(const Seg& seg, int32_t kk, int32_t* __restrict__ out,
-                            SelectShared<NW, NC>& sh) {
+                                            uint32_t* __restrict__ out_key, SelectShared<NW, NC>& sh) {
   static_assert(NW >= 4, "the digit scan uses the first four waves");
   const int32_t tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int NT = NW * 64;
@@ -135,7 +151,10 @@ __device__ __forceinline__ void select_topk(const Seg& seg, int32_t kk, int32_t*
     const bool keep = valid && (key > T || (eq && eq_rank < need_eq));
     const uint64_t keep_mask = __ballot(keep);
     const uint32_t slot = pos + __popcll(keep_mask & lt_mask);
-    if (keep && slot < (uint32_t)kk) out[slot] = seg.s0 + 64 * j + lane;
+    if (keep && slot < (uint32_t)kk) {
+      out[slot] = seg.index(j);
+      if (out_key) out_key[slot] = key;
+    }
     pos += __popcll(keep_mask);
     eq_seen += __popcll(eq_mask);
   });
@@ -152,9 +171,63 @@ __global__ __launch_bounds__(ROW_WAVES * 64) void topk_rows_kernel(const float* 
     for (int32_t i = threadIdx.x; i < n; i += ROW_WAVES * 64) o[i] = i;
     return;
   }
-  GlobalSeg seg{scores + (size_t)row * n, forced, 0, 0, 0, (int32_t)(threadIdx.x & 63)};
+  GlobalSeg seg{scores + (size_t)row * n, forced, 0, 0, 0, (int32_t)(threadIdx.x & 63), 0};
   wave_segment<ROW_WAVES>(n, seg.s0, seg.s1, seg.trips);
-  select_topk<ROW_WAVES, 2>(seg, kk, o, sh);
+  select_topk<ROW_WAVES, 2>(seg, kk, o, nullptr, sh);
+}
+
+// Long rows in two passes. Pass 1: every TOPK_CHUNK-long chunk of a row keeps
+// its own top kk (indices and keys, ascending) in the workspace; the row's
+// top kk are among them, since an entry's rank inside its chunk is at most its
+// rank in the row. Pass 2: one work-group per row selects the top kk of the
+// candidates, which lie in index order, so ties and the output order are those
+// of the single pass.
+constexpr int32_t TOPK_CHUNK = 65536;
+__global__ __launch_bounds__(ROW_WAVES * 64) void topk_chunks_kernel(const float* __restrict__ scores,
+                                                                     int32_t n, int32_t kk, int32_t forced,
+                                                                     int32_t* __restrict__ cand_idx,
+                                                                     uint32_t* __restrict__ cand_key) {
+  __shared__ SelectShared<ROW_WAVES, 2> sh;
+  const int32_t c = blockIdx.x, row = blockIdx.y, nch = gridDim.x;
+  const int32_t c0 = c * TOPK_CHUNK, m = min(TOPK_CHUNK, n - c0);
+  const size_t off = ((size_t)row * nch + c) * kk;
+  int32_t* oi = cand_idx + off;
+  uint32_t* ok = cand_key + off;
+  const float* x = scores + (size_t)row * n + c0;
+  const int32_t f = (forced >= c0 && forced < c0 + m) ? forced - c0 : -1;
+  if (kk >= m) {
+    for (int32_t i = threadIdx.x; i < m; i += ROW_WAVES * 64) {
+      oi[i] = c0 + i;
+      ok[i] = i == f ? FORCED_KEY : score_key(x[i]);
+    }
+    return;
+  }
+  GlobalSeg seg{x, f, 0, 0, 0, (int32_t)(threadIdx.x & 63), c0};
+  wave_segment<ROW_WAVES>(m, seg.s0, seg.s1, seg.trips);
+  select_topk<ROW_WAVES, 2>(seg, kk, oi, ok, sh);
+}
+
+__global__ __launch_bounds__(ROW_WAVES * 64) void topk_merge_kernel(const int32_t* __restrict__ cand_idx,
+                                                                    const uint32_t* __restrict__ cand_key,
+                                                                    int32_t n, int32_t nch, int32_t kk,
+                                                                    int32_t* __restrict__ out) {
+  __shared__ SelectShared<ROW_WAVES, 2> sh;
+  const int32_t row = blockIdx.x;
+  const int32_t m_last = n - (nch - 1) * TOPK_CHUNK;
+  const int32_t m = (nch - 1) * kk + min(kk, m_last);  // candidates, contiguous
+  const size_t off = (size_t)row * nch * kk;
+  int32_t* o = out + (size_t)row * kk;
+  if (kk >= m) {
+    for (int32_t i = threadIdx.x; i < m; i += ROW_WAVES * 64) o[i] = cand_idx[off + i];
+    return;
+  }
+  KeySeg seg{cand_key + off, cand_idx + off, 0, 0, 0, (int32_t)(threadIdx.x & 63)};
+  wave_segment<ROW_WAVES>(m, seg.s0, seg.s1, seg.trips);
+  select_topk<ROW_WAVES, 2>(seg, kk, o, nullptr, sh);
+}
+
+__host__ __device__ constexpr bool two_pass(int32_t n, int32_t kk) {
+  return n > 2 * TOPK_CHUNK && kk <= TOPK_CHUNK / 4;
 }
 
 // One work-group per (row, query block a): top min(topk, a+1) of
@@ -178,19 +251,36 @@ __global__ __launch_bounds__(BLK_WAVES * 64) void block_topk_kernel(const float*
     for (int32_t i = threadIdx.x; i < m; i += BLK_WAVES * 64) o[i] = i;
     return;
   }
-  GlobalSeg seg{logits + cb * nb, a, 0, 0, 0, (int32_t)(threadIdx.x & 63)};
+  GlobalSeg seg{logits + cb * nb, a, 0, 0, 0, (int32_t)(threadIdx.x & 63), 0};
   wave_segment<BLK_WAVES>(m, seg.s0, seg.s1, seg.trips);
-  select_topk<BLK_WAVES, 2>(seg, kk, o, sh);
+  select_topk<BLK_WAVES, 2>(seg, kk, o, nullptr, sh);
 }
 
 }  // namespace
 
+size_t topk_workspace_bytes(int32_t rows, int32_t n, int32_t k) {
+  const int32_t kk = k < n ? k : n;
+  if (rows <= 0 || !two_pass(n, kk)) return 0;
+  const size_t nch = (size_t)(n + TOPK_CHUNK - 1) / TOPK_CHUNK;
+  return (size_t)rows * nch * kk * (sizeof(int32_t) + sizeof(uint32_t));
+}
+
 hipError_t launch_topk_rows(const float* scores, int32_t rows, int32_t n, int32_t k,
-                            int32_t forced, int32_t* out, hipStream_t s) {
+                            int32_t forced, int32_t* out, void* ws, hipStream_t s) {
   const int32_t kk = k < n ? k : n;
   if (rows == 0 || kk == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(ROW_WAVES * 64), 0, s, scores, n, kk,
-                     forced, out);
+  if (!two_pass(n, kk)) {
+    hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(ROW_WAVES * 64), 0, s, scores, n, kk,
+                       forced, out);
+    return hipGetLastError();
+  }
+  const int32_t nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
+  int32_t* cand_idx = static_cast<int32_t*>(ws);
+  uint32_t* cand_key = reinterpret_cast<uint32_t*>(cand_idx + (size_t)rows * nch * kk);
+  hipLaunchKernelGGL(topk_chunks_kernel, dim3(nch, rows), dim3(ROW_WAVES * 64), 0, s, scores, n, kk,
+                     forced, cand_idx, cand_key);
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(ROW_WAVES * 64), 0, s, cand_idx, cand_key,
+                     n, nch, kk, out);
   return hipGetLastError();
 }
 

@@ -143,9 +143,13 @@ size_t dsa_vs_estimate_workspace_bytes(const dsa_shape* shape, int32_t n_heads);
 /* Row-wise top-k of fp32 scores [MInf §2.2: top-k verticals, slashes and
  * blocks]. scores: device [rows][n]; out: device int32 [rows][min(k, n)],
  * ascending. forced_index in [-1, n): the entry ranked first in every row
- * (-1: none). k >= 0. */
+ * (-1: none). k >= 0. workspace: device memory of at least
+ * dsa_topk_workspace_bytes(rows, n, k) bytes (0 for rows short enough to be
+ * selected in one pass; NULL is then accepted). */
 dsa_status dsa_topk(const float* scores, int32_t rows, int32_t n, int32_t k,
-                    int32_t forced_index, int32_t* out, void* stream);
+                    int32_t forced_index, int32_t* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+size_t dsa_topk_workspace_bytes(int32_t rows, int32_t n, int32_t k);
 
 /* Vertical-slash sparse format [MInf §2.2 "convert to sparse format"].
  * Inputs per row: V [rows][nv] ascending column indices and S [rows][ns]

@@ -83,6 +83,10 @@ def test_workspace_sizes(lib):
     assert lib.dsa_vertical_slash_workspace_bytes(ctypes.byref(shape(d=96)), 1, 1, 1) == 0
     assert lib.dsa_block_sparse_workspace_bytes(ctypes.byref(sh), 8, 4) > 0
     assert lib.dsa_bs_select_workspace_bytes(3, 512) == 3 * 512 * 512 * 4
+    # top-k: one pass (no scratch) for short rows, candidates of 64K chunks for long ones
+    assert lib.dsa_topk_workspace_bytes(4, 131072, 1000) == 0
+    assert lib.dsa_topk_workspace_bytes(2, 1 << 20, 1000) == 2 * 16 * 1000 * 8
+    assert lib.dsa_topk_workspace_bytes(2, 1 << 20, 20000) == 0
 
 
 def test_other_argument_errors(lib):
@@ -92,10 +96,11 @@ def test_other_argument_errors(lib):
     assert lib.dsa_streaming_attention(P, P, P, P, ctypes.byref(sh), -1, 1, 0.0, None, 0, None) == INVALID
     assert lib.dsa_streaming_attention(P, P, P, P, ctypes.byref(sh), 1, 0, 0.0, None, 0, None) == INVALID
     assert lib.dsa_streaming_attention(P, None, P, P, ctypes.byref(sh), 1, 1, 0.0, None, 0, None) == INVALID
-    assert lib.dsa_topk(P, 1, 10, -1, -1, P, None) == INVALID
-    assert lib.dsa_topk(P, 1, 10, 3, 10, P, None) == INVALID
-    assert lib.dsa_topk(None, 1, 10, 3, -1, P, None) == INVALID
-    assert lib.dsa_topk(None, 0, 10, 3, -1, None, None) == OK
+    assert lib.dsa_topk(P, 1, 10, -1, -1, P, None, 0, None) == INVALID
+    assert lib.dsa_topk(P, 1, 10, 3, 10, P, None, 0, None) == INVALID
+    assert lib.dsa_topk(None, 1, 10, 3, -1, P, None, 0, None) == INVALID
+    assert lib.dsa_topk(None, 0, 10, 3, -1, None, None, 0, None) == OK
+    assert lib.dsa_topk(P, 2, 1 << 20, 1000, -1, P, P, 8, None) == WORKSPACE
     assert lib.dsa_vs_build_index(P, -1, P, 1, 1, 10, P, P, P, P, None) == INVALID
     assert lib.dsa_bs_pool(P, 0, 1, 2, 100, 80, None, 0, P, None) == UNSUPPORTED
     assert lib.dsa_bs_select(P, P, 1, 4, 128, 0.1, 0, P, P, None, P, 1 << 30, None) == INVALID

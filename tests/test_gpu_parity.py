@@ -95,7 +95,10 @@ def _special_scores(rows, n, seed):
 
 @pytest.mark.parametrize("n,k,forced", [(100, 7, -1), (100, 7, 0), (100, 100, -1), (100, 150, 0),
                                         (1, 1, 0), (5000, 256, 0), (5000, 1, -1), (131072, 6096, 0),
-                                        (131072, 1000, -1), (4097, 4096, 4096)])
+                                        (131072, 1000, -1), (4097, 4096, 4096),
+                                        # rows longer than two 64K chunks take the two-pass path
+                                        (200001, 1000, 200000), (300000, 6096, 0),
+                                        (1 << 20, 6096, 123457), (1 << 20, 1000, -1)])
 def test_topk(n, k, forced):
     say(f"topk n={n} k={k} forced={forced}")
     x = _special_scores(3, n, n + k)
@@ -105,10 +108,14 @@ def test_topk(n, k, forced):
         assert np.array_equal(out[r], want), (r, out[r][:10], want[:10])
 
 
-def test_topk_all_ties():
-    x = torch.zeros(2, 70000, device="cuda")
+@pytest.mark.parametrize("n", [70000, 300000])
+def test_topk_all_ties(n):
+    x = torch.zeros(2, n, device="cuda")
     out = dsa.topk(x, 300, 0).cpu().numpy()
     assert (out[0] == np.arange(300)).all() and (out[1] == np.arange(300)).all()
+    out = dsa.topk(x, 300, n - 1).cpu().numpy()
+    want = np.concatenate([np.arange(299), [n - 1]])
+    assert (out[0] == want).all() and (out[1] == want).all()
 
 
 # ---------------------------------------------------------------------------
