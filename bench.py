@@ -55,7 +55,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 ATTN_SRC = os.path.join(ROOT, "dynamic_sparse_attention_slash_amd", "csrc", "sparse_attention.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-DOMINANT = "attn_vs_bf16_kernel"
+DOMINANT = "attn_vs_single_kernel"
 
 
 def log(*a):

@@ -12,18 +12,20 @@
 // description].
 //
 // Work decomposition: one work-group per (row = batch x listed head, query
-// block of 64 rows); the bf16 kernel splits the block's queries over two waves,
-// the fp32 kernel keeps all 64 in one wave. A prologue cuts the block's key set into 16-key sub-blocks and writes their
-// descriptors (first key or list position, count, flags) to LDS, so the hot
-// loop is straight-line code over tiles of two sub-blocks:
-//   S^T (keys x queries) = K_tile * Q^T      MFMA; K rows come straight from
-//                                            global memory (gathers and
-//                                            unaligned ranges cost nothing extra)
+// block of 64 rows) for the vertical-slash and block-sparse patterns (bf16:
+// two waves of 32 queries; fp32: one wave of 64), and one per panel of two
+// query blocks for the streaming pattern (bf16: four waves). A prologue cuts
+// the key set into 16-key sub-blocks and writes their descriptors to LDS, so
+// the hot loop is straight-line code over tiles of sub-blocks:
+//   S^T (keys x queries) = K_tile * Q^T      MFMA; bf16 K/V tiles go global
+//                                            -> LDS by DMA (gathered rows and
+//                                            unaligned ranges alike); fp32 K
+//                                            rows are read straight to registers
 //   P = exp2(S * scale*log2e - m)            fp32, one query column per lane
-//   O^T (dims x queries) += V_tile^T * P^T   MFMA; V_tile^T is transposed
-//                                            through LDS (bf16) or read row-wise
-//                                            (fp32, whose MFMA takes one k per
-//                                            lane)
+//   O^T (dims x queries) += V_tile^T * P^T   MFMA; V_tile^T comes from a
+//                                            transposing LDS read (bf16) or is
+//                                            read row-wise (fp32, whose MFMA
+//                                            takes one k per lane)
 // In the MFMA output layout a lane holds one query column, so the running max
 // and the rescale of O^T need no data from other query columns. In the bf16
 // kernel the softmax denominator is one more MFMA block whose A operand is all
@@ -207,22 +209,15 @@ __device__ __forceinline__ void exp_tile(f32x4 (&st)[2][QB], const float (&m)[QB
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel: a work-group takes a panel of PANEL = 2 consecutive query
-// blocks (rows r0 .. r0 + 127) with four waves; wave w owns the 32 queries
-// starting at r0 + 64 (w >> 1) + 32 (w & 1).
+// bf16 panel kernel (streaming heads): a work-group takes a panel of PANEL = 2
+// consecutive query blocks (rows r0 .. r0 + 127) with four waves; wave w owns
+// the 32 queries starting at r0 + 64 (w >> 1) + 32 (w & 1).
 //
 // The key sets of the two blocks are walked together as one stream of 16-key
 // sub-blocks, each carrying, per block, a mask of the slots that belong to that
-// block's key set:
-//  * ranges (vertical-slash intervals, the streaming sink and window): per
-//    interval, the union of the two blocks' windows. For a slash interval the
-//    window of block a+1 is the window of block a moved by 64 keys, so the keys
-//    of a wide interval are loaded once for both blocks.
-//  * key-block lists (block-sparse heads): the two ascending lists merged, so
-//    a key block selected by both query blocks is loaded once.
-//  * gathered columns (vertical-slash): in split tiles, keys 0-31 of a tile
-//    from block a's list and keys 32-63 from block a+1's.
-// A tile is 64 keys (4 sub-blocks). K and V tiles travel global -> LDS with
+// block's key set. Each window (the sink, the local window) is cut as the union
+// of the two blocks' windows, which overlap in all but one key block, so the
+// keys are loaded once for both blocks. A tile is 64 keys (4 sub-blocks). K and V tiles travel global -> LDS with
 // buffer_load_dwordx4 ... lds (no registers involved) into a two-stage ring:
 // the loads of tile t+1 are in flight while tile t is computed, and one
 // barrier per tile separates them. Wave w loads sub-block w of a tile; each
@@ -238,8 +233,6 @@ __device__ __forceinline__ void exp_tile(f32x4 (&st)[2][QB], const float (&m)[QB
 constexpr int PANEL = 2;                // query blocks per work-group
 constexpr int PANEL_WAVES = 2 * PANEL;  // 32 queries per wave
 constexpr int32_t P_SB_CAP = 512;       // sub-block descriptors per refill (128 tiles)
-constexpr int32_t P_COLS_CAP = 512;     // column entries per block staged per refill
-constexpr int32_t P_MERGE = 64;         // list entries per block merged per refill
 constexpr int32_t P_LIST = 1;           // keys come from the staged column list
 constexpr int32_t P_DIAG = 2;           // << j: may hold a key above block j's first row
 
@@ -263,28 +256,6 @@ __device__ __forceinline__ uint32_t slot_mask(int32_t s, int32_t lo, int32_t hi)
 
 // ---- window sources: next() gives one interval's key window per block of
 // the panel ([lo, hi) within [0, n), empty when lo >= hi); state is uniform ----
-struct VsPanelRanges {
-  const int32_t* iv; int32_t n_iv, t, r0, n;
-  __device__ bool next(int32_t (&lo)[PANEL], int32_t (&hi)[PANEL]) {
-    while (t < n_iv) {
-      const int32_t d_lo = iv[2 * t], d_hi = iv[2 * t + 1];
-      ++t;
-      if (d_lo >= r0 + PANEL * BLOCK) { t = n_iv; return false; }  // intervals ascend
-      bool any = false;
-#pragma unroll
-      for (int j = 0; j < PANEL; ++j) {
-        const int32_t rj = r0 + BLOCK * j;
-        const bool on = rj < n && d_lo < rj + BLOCK;
-        lo[j] = on ? max(0, rj - d_hi) : 0;
-        hi[j] = on ? min(n, rj + BLOCK - d_lo) : 0;
-        any |= lo[j] < hi[j];
-      }
-      if (any) return true;
-    }
-    return false;
-  }
-};
-
 struct StreamPanelRanges {
   int32_t a0, nb, init_blocks, local_blocks, t, n;
   __device__ bool next(int32_t (&lo)[PANEL], int32_t (&hi)[PANEL]) {
@@ -304,29 +275,6 @@ struct StreamPanelRanges {
             if (c0 <= aj) { lo[j] = c0 * BLOCK; hi[j] = min(n, (aj + 1) * BLOCK); }
           }
         }
-        any |= lo[j] < hi[j];
-      }
-      if (any) return true;
-    }
-    return false;
-  }
-};
-
-// Merged key-block list of the panel in LDS: block ids mk[] with membership
-// bits mm[] (bit j: selected by block j).
-struct MergedBlocks {
-  const int32_t* mk; const int32_t* mm; int32_t k, nm, nb, n;
-  __device__ bool next(int32_t (&lo)[PANEL], int32_t (&hi)[PANEL]) {
-    while (k < nm) {
-      const int32_t c = mk[k], bits = mm[k];
-      ++k;
-      const bool ok = c >= 0 && c < nb;
-      bool any = false;
-#pragma unroll
-      for (int j = 0; j < PANEL; ++j) {
-        const bool on = ok && ((bits >> j) & 1);
-        lo[j] = on ? c * BLOCK : 0;
-        hi[j] = on ? min(n, c * BLOCK + BLOCK) : 0;
         any |= lo[j] < hi[j];
       }
       if (any) return true;
@@ -390,52 +338,6 @@ __device__ __forceinline__ int32_t pad_tiles(PDesc* d, int32_t cnt, int32_t tid)
   return cnt;
 }
 
-// Vertical-slash panel: the intervals, then the two blocks' column lists.
-struct VsPanelSrc {
-  static constexpr int32_t COLS = PANEL * P_COLS_CAP;
-  VsPanelRanges rg;
-  PanelCut cut;
-  const int32_t* cols[PANEL];
-  int32_t ncol[PANEL], cp[PANEL];
-  int32_t r0, n;
-
-  __device__ int32_t fill(PDesc* d, int32_t* lcols, int32_t tid, int32_t nth) {
-    int32_t cnt = cut.exhausted ? 0 : cut_ranges(rg, cut, d, 0, r0, tid, nth);
-    if (cut.exhausted && cnt < P_SB_CAP) {
-      cnt = pad_tiles(d, cnt, tid);  // split tiles start on a tile boundary
-      const int32_t tiles = (P_SB_CAP - cnt) >> 2;
-      int32_t take[PANEL], T = 0;
-#pragma unroll
-      for (int j = 0; j < PANEL; ++j) {
-        take[j] = min(ncol[j] - cp[j], min(P_COLS_CAP, 32 * tiles));
-        T = max(T, (take[j] + 31) >> 5);
-      }
-#pragma unroll
-      for (int j = 0; j < PANEL; ++j)
-        for (int32_t i = tid; i < take[j]; i += nth)
-          lcols[j * P_COLS_CAP + i] = min(max(cols[j][cp[j] + i], 0), n - 1);
-      for (int32_t u = tid; u < 4 * T; u += nth) {
-        // per-lane block index: select, never index the per-block arrays
-        const int32_t j = (u >> 1) & 1, base = 32 * (u >> 2) + 16 * (u & 1);
-        const int32_t tk = j ? take[1] : take[0];
-        const int32_t* src = j ? cols[1] + cp[1] : cols[0] + cp[0];
-        const int32_t c = min(max(tk - base, 0), 16);
-        if (c == 0) {
-          d[cnt + u] = PDesc{0, 0u, 0};
-        } else {
-          const int32_t last = min(max(src[base + c - 1], 0), n - 1);
-          d[cnt + u] = PDesc{j * P_COLS_CAP + base, ((1u << c) - 1u) << (16 * j),
-                             P_LIST | (c << 8) | (last > r0 + BLOCK * j ? P_DIAG << j : 0)};
-        }
-      }
-      cnt += 4 * T;
-#pragma unroll
-      for (int j = 0; j < PANEL; ++j) cp[j] += take[j];
-    }
-    return pad_tiles(d, cnt, tid);
-  }
-};
-
 struct StreamPanelSrc {
   static constexpr int32_t COLS = 1;
   StreamPanelRanges rg;
@@ -443,83 +345,6 @@ struct StreamPanelSrc {
   int32_t r0;
   __device__ int32_t fill(PDesc* d, int32_t*, int32_t tid, int32_t nth) {
     const int32_t cnt = cut.exhausted ? 0 : cut_ranges(rg, cut, d, 0, r0, tid, nth);
-    return pad_tiles(d, cnt, tid);
-  }
-};
-
-__device__ __forceinline__ int32_t lower_bound64(const int32_t* a, int32_t len, int32_t x) {
-  int32_t lo = 0, hi = len;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi) >> 1;
-    if (a[mid] < x) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
-__device__ __forceinline__ uint64_t low_bits(int32_t r) { return r >= 64 ? ~0ull : (1ull << r) - 1ull; }
-
-// Block-sparse panel: the two selected-block lists (ascending, distinct) are
-// merged P_MERGE entries at a time: a chunk takes the entries of both lists up
-// to the smaller of their P_MERGE-th remaining entries, and each entry's place
-// in the merged, duplicate-free chunk is its rank in its own list plus its
-// rank in the other list minus the duplicates below it. A list that breaks the
-// order gives wrong sets but never an access outside the chunk arrays.
-struct BsPanelSrc {
-  static constexpr int32_t COLS = 1;
-  const int32_t* sel[PANEL];
-  int32_t nsel[PANEL], cp[PANEL];
-  MergedBlocks mb;
-  PanelCut cut;
-  int32_t r0;
-
-  __device__ void merge(int32_t* mA, int32_t* mB, int32_t* mk, int32_t* mm, int32_t tid) {
-    const int32_t rA = nsel[0] - cp[0], rB = nsel[1] - cp[1];
-    if (tid < P_MERGE) {
-      mA[tid] = tid < rA ? sel[0][cp[0] + tid] : 0x7fffffff;
-      mB[tid] = tid < rB ? sel[1][cp[1] + tid] : 0x7fffffff;
-    }
-    if (tid < 2 * P_MERGE) { mk[tid] = -1; mm[tid] = 0; }
-    __syncthreads();
-    int32_t thr = 0x7fffffff;
-    if (rA > P_MERGE) thr = min(thr, mA[P_MERGE - 1]);
-    if (rB > P_MERGE) thr = min(thr, mB[P_MERGE - 1]);
-    const int32_t l = tid & 63;
-    const int32_t x = mA[l], y = mB[l];
-    const int32_t tA = __popcll(__ballot(l < rA && x <= thr));
-    const int32_t tB = __popcll(__ballot(l < rB && y <= thr));
-    const int32_t ra = lower_bound64(mA, tA, y), rb = lower_bound64(mB, tB, x);
-    const bool dupB = l < tB && ra < tA && mA[ra] == y;
-    const uint64_t dmask = __ballot(dupB);
-    if (tid < 64) {
-      if (l < tA) {
-        const int32_t pos = l + rb - __popcll(dmask & low_bits(rb));
-        mk[pos] = x;
-        mm[pos] = 1 | (rb < tB && mB[rb] == x ? 2 : 0);
-      }
-      if (l < tB && !dupB) {
-        const int32_t pos = l + ra - __popcll(dmask & low_bits(l));
-        mk[pos] = y;
-        mm[pos] = 2;
-      }
-    }
-    cp[0] += tA;
-    cp[1] += tB;
-    mb.k = 0;
-    mb.nm = tA + tB - __popcll(dmask);
-    __syncthreads();
-  }
-
-  __device__ int32_t fill(PDesc* d, int32_t*, int32_t tid, int32_t nth) {
-    __shared__ int32_t mA[P_MERGE], mB[P_MERGE], mk[2 * P_MERGE], mm[2 * P_MERGE];
-    mb.mk = mk;
-    mb.mm = mm;
-    int32_t cnt = 0;
-    while (true) {
-      cnt = cut_ranges(mb, cut, d, cnt, r0, tid, nth);
-      if (!cut.exhausted || cnt > 0 || (cp[0] >= nsel[0] && cp[1] >= nsel[1])) break;
-      merge(mA, mB, mk, mm, tid);
-      cut.exhausted = false;
-    }
     return pad_tiles(d, cnt, tid);
   }
 };
@@ -830,6 +655,252 @@ __device__ void attend_panel(const uint16_t* __restrict__ qs, const uint16_t* __
 }
 
 // ---------------------------------------------------------------------------
+// bf16 single-block kernel: one work-group per (row, query block), two waves
+// of 32 queries, over the block's own key set cut into 16-key sub-blocks
+// (first key or list position, count, flags) by DescGen. 32-key tiles go
+// global -> LDS through a two-stage ring as in the panel kernel (same
+// swizzle, masks and softmax); a work-group needs 40 KB of LDS, so four are
+// resident per CU.
+// ---------------------------------------------------------------------------
+constexpr int SB_WAVES = 2;
+constexpr int32_t SB1_CAP = 512;       // descriptors per refill
+constexpr int32_t SB1_COLS = 1024;     // column-list entries staged per refill
+
+// Fills descriptors like DescGen::fill, but list sub-blocks refer to a copy of
+// the column list staged in LDS (positions relative to that copy), at most
+// SB1_COLS entries per call, clamped into [0, n).
+template <class R>
+__device__ int32_t fill_single(DescGen<R>& gen, Desc* d, int32_t* lcols, int32_t tid, int32_t nthreads) {
+  int32_t cnt = 0;
+  while (cnt < SB1_CAP) {
+    if (gen.p >= gen.hi) {
+      int32_t lo2, hi2;
+      if (!gen.ranges.next(lo2, hi2)) break;
+      gen.p = lo2;
+      gen.hi = hi2;
+      continue;
+    }
+    const int32_t take = min((gen.hi - gen.p + 15) >> 4, SB1_CAP - cnt);
+    for (int32_t t = tid; t < take; t += nthreads) {
+      const int32_t s = gen.p + 16 * t, c = min(16, gen.hi - s);
+      d[cnt + t] = Desc{s, c | ((c < 16 || s + c - 1 > gen.r0) ? F_MASK : 0)};
+    }
+    cnt += take;
+    gen.p = min(gen.hi, gen.p + 16 * take);
+  }
+  if (cnt < SB1_CAP && gen.cp < gen.n_cols) {
+    const int32_t ncol = min(gen.n_cols - gen.cp, min(SB1_COLS, 16 * (SB1_CAP - cnt)));
+    for (int32_t t = tid; t < ncol; t += nthreads) lcols[t] = min(max(gen.cols[gen.cp + t], 0), gen.n - 1);
+    const int32_t take = (ncol + 15) >> 4;
+    for (int32_t t = tid; t < take; t += nthreads) {
+      const int32_t s = 16 * t, c = min(16, ncol - s);
+      const bool m = c < 16 || min(max(gen.cols[gen.cp + s + c - 1], 0), gen.n - 1) > gen.r0;
+      d[cnt + t] = Desc{s, c | F_LIST | (m ? F_MASK : 0)};
+    }
+    cnt += take;
+    gen.cp += ncol;
+  }
+  return cnt;
+}
+
+template <int D, class R>
+__device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* __restrict__ ks,
+                              const uint16_t* __restrict__ vs, uint16_t* __restrict__ os,
+                              int32_t n, int32_t r0, float scale_log2, DescGen<R> gen) {
+  using L = TileLds<D>;
+  constexpr int DS = D / 32;
+  constexpr int DB = D / 16;
+  constexpr int NTH = 64 * SB_WAVES;
+  __shared__ __align__(16) char ring0[L::HALF];
+  __shared__ __align__(16) char ring1[L::HALF];
+  __shared__ Desc desc[SB1_CAP];
+  __shared__ int32_t lcols[SB1_COLS];
+
+  const int32_t tid = threadIdx.x, lane = tid & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t g = lane >> 4, l16 = lane & 15;
+  const int32_t q0 = r0 + 32 * wave;
+
+  u32x4 qop[2][DS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int32_t row = min(q0 + 16 * qb + l16, n - 1);
+    const u32x4* qsrc = reinterpret_cast<const u32x4*>(qs + (size_t)row * D + (D / 4) * g);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qop[qb][s] = qsrc[s];
+  }
+  int32_t koff[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) koff[s] = L::off(l16, (D / 32) * g + s);
+  int32_t voff[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int32_t r = 4 * g + (l16 >> 2), dim = 16 * db + 4 * (l16 & 3);
+    voff[db] = L::MAT + L::off(r, dim >> 3) + 2 * (dim & 7);
+  }
+  // wave w loads sub-block w of a tile
+  int32_t ld_row[L::INSTR], ld_off[L::INSTR];
+#pragma unroll
+  for (int k = 0; k < L::INSTR; ++k) {
+    ld_row[k] = k * L::RPI + lane / L::UNITS;
+    const int32_t c = (lane % L::UNITS) ^ L::swz(16 * wave + ld_row[k]);
+    ld_off[k] = ld_row[k] * L::ROW + 16 * c;
+  }
+  const uint32_t slab_bytes = (uint32_t)n * L::ROW;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)ks, (short)0, slab_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vs, (short)0, slab_bytes, 0x00020000);
+
+  f32x4 oacc[DB + 1][2];
+#pragma unroll
+  for (int db = 0; db <= DB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {NEG_BIG, NEG_BIG};
+  const float inv_scale_log2 = 1.0f / scale_log2;
+  float raise[2] = {(NEG_BIG + 8.0f) * inv_scale_log2, (NEG_BIG + 8.0f) * inv_scale_log2};
+  int32_t rp1[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) rp1[qb] = q0 + 16 * qb + l16 + 1 - 4 * g;
+  const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+
+  auto issue_loads = [&](const Desc& dw, char* stage) {
+    char* dst = stage + 16 * wave * L::ROW;
+    if (dw.b & F_LIST) {
+      const int32_t last = max(dw.count() - 1, 0);
+#pragma unroll
+      for (int k = 0; k < L::INSTR; ++k) {
+        const int32_t key = lcols[dw.a + min(ld_row[k], last)];
+        const int32_t vo = ld_off[k] + (key - ld_row[k]) * L::ROW;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + k * 1024), 16, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + L::MAT + k * 1024), 16, vo, 0, 0, 0);
+      }
+    } else {
+      const int32_t base = dw.a * L::ROW;
+#pragma unroll
+      for (int k = 0; k < L::INSTR; ++k) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + k * 1024), 16, base + ld_off[k], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + L::MAT + k * 1024), 16, base + ld_off[k], 0, 0, 0);
+      }
+    }
+  };
+
+  auto tile = [&](int32_t tt, int32_t ntiles, int32_t cnt, const char* cur, char* nxt) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tt + 1 < ntiles) issue_loads(uniform_desc(desc, 2 * (tt + 1) + wave, cnt), nxt);
+    const Desc d[2] = {uniform_desc(desc, 2 * tt, cnt), uniform_desc(desc, 2 * tt + 1, cnt)};
+    f32x4 st[2][2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 kop[DS];
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+        kop[s] = *reinterpret_cast<const u32x4*>(cur + koff[s] + s2 * 16 * L::ROW);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) acc = mfma_bf16(kop[s], qop[qb][s], acc);
+        st[s2][qb] = acc;
+      }
+    }
+    if ((d[0].b | d[1].b) & F_MASK) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const Desc& dd = d[s2];
+        if (!(dd.b & F_MASK)) continue;
+        const int32_t c = dd.count();
+        if (dd.b & F_LIST) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int32_t sl = 4 * g + i;
+            const bool valid = sl < c;
+            const int32_t key = lcols[dd.a + min(sl, max(c - 1, 0))];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              if (!valid || key > q0 + 16 * qb + l16) st[s2][qb][i] = -INFINITY;
+          }
+        } else {
+          // a range: slots [0, c) valid and key = a + slot <= row
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const int32_t ub = min(c - 4 * g, rp1[qb] - dd.a);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (i >= ub) st[s2][qb][i] = -INFINITY;
+          }
+        }
+      }
+    }
+    float mx[2];
+    bool up_any = false;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      mx[qb] = max3f(max3f(st[0][qb][0], st[0][qb][1], st[0][qb][2]),
+                     max3f(st[0][qb][3], st[1][qb][0], st[1][qb][1]),
+                     max3f(st[1][qb][2], st[1][qb][3], st[1][qb][3]));
+      up_any |= mx[qb] > raise[qb];
+    }
+    if (__any(up_any)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mt = group_max4(mx[qb]) * scale_log2;
+        const bool up = mt > m[qb] + 8.0f;
+        const float alpha = up ? fast_exp2(m[qb] - mt) : 1.0f;
+        m[qb] = up ? mt : m[qb];
+        raise[qb] = (m[qb] + 8.0f) * inv_scale_log2;
+#pragma unroll
+        for (int db = 0; db <= DB; ++db) oacc[db][qb] *= alpha;
+      }
+    }
+    exp_tile<2>(st, m, scale_log2);
+    u32x4 pop[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      pop[qb] = u32x4{pack_bf16x2(st[0][qb][0], st[0][qb][1]), pack_bf16x2(st[0][qb][2], st[0][qb][3]),
+                      pack_bf16x2(st[1][qb][0], st[1][qb][1]), pack_bf16x2(st[1][qb][2], st[1][qb][3])};
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const u32x2 x0 = lds_read_tr16(cur + voff[db]);
+      const u32x2 x1 = lds_read_tr16(cur + voff[db] + 16 * L::ROW);
+      const u32x4 aop = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma_bf16(aop, pop[qb], oacc[db][qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) oacc[DB][qb] = mfma_bf16(ones, pop[qb], oacc[DB][qb]);
+  };
+
+  while (true) {
+    __syncthreads();
+    const int32_t cnt = fill_single(gen, desc, lcols, tid, NTH);
+    if (cnt == 0) break;
+    __syncthreads();
+    const int32_t ntiles = (cnt + 1) >> 1;
+    issue_loads(uniform_desc(desc, wave, cnt), ring0);
+    for (int32_t tt = 0; tt < ntiles; tt += 2) {
+      tile(tt, ntiles, cnt, ring0, ring1);
+      if (tt + 1 < ntiles) tile(tt + 1, ntiles, cnt, ring1, ring0);
+    }
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = oacc[DB][qb][0];
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int32_t row = q0 + 16 * qb + l16;
+    if (row < n) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f32x4 x = oacc[db][qb] * inv;
+        *reinterpret_cast<u32x2*>(os + (size_t)row * D + 16 * db + 4 * g) =
+            u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel (MFMA 16x16x4 f32: one k value per lane, so V needs no transpose)
 // ---------------------------------------------------------------------------
 template <int D, class R>
@@ -1008,49 +1079,6 @@ __global__ __launch_bounds__(64) void attn_stream_f32_kernel(AttnArgs a, StreamI
 #define PANEL_KERNEL __global__ __launch_bounds__(64 * PANEL_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 template <int D>
-PANEL_KERNEL void attn_vs_bf16_kernel(AttnArgs a, VsIndex ix) {
-  const int32_t nb = num_blocks(a.seq_len);
-  int32_t row, p;
-  work_item(a.hm, a.wo, num_panels(a.seq_len), row, p);
-  const int32_t a0 = PANEL * p, r0 = a0 * BLOCK;
-  VsPanelSrc src;
-  src.rg = VsPanelRanges{ix.iv + (size_t)row * ix.max_iv * 2, min(ix.n_iv[row], ix.max_iv), 0, r0, a.seq_len};
-  src.cut = PanelCut{};
-#pragma unroll
-  for (int j = 0; j < PANEL; ++j) {
-    const size_t cb = (size_t)row * nb + a0 + j;
-    const bool on = a0 + j < nb;
-    src.cols[j] = on ? ix.cols + cb * ix.max_cols : ix.cols;
-    src.ncol[j] = on ? max(0, min(ix.n_cols[cb], ix.max_cols)) : 0;
-    src.cp[j] = 0;
-  }
-  src.r0 = r0;
-  src.n = a.seq_len;
-  attend_panel_bf16<D>(a, row, r0, src);
-}
-
-template <int D>
-PANEL_KERNEL void attn_blocks_bf16_kernel(AttnArgs a, BlockIndex ix) {
-  const int32_t nb = num_blocks(a.seq_len);
-  int32_t row, p;
-  work_item(a.hm, a.wo, num_panels(a.seq_len), row, p);
-  const int32_t a0 = PANEL * p, r0 = a0 * BLOCK;
-  BsPanelSrc src;
-#pragma unroll
-  for (int j = 0; j < PANEL; ++j) {
-    const size_t cb = (size_t)row * nb + a0 + j;
-    const bool on = a0 + j < nb;
-    src.sel[j] = on ? ix.sel + cb * ix.max_sel : ix.sel;
-    src.nsel[j] = on ? max(0, min(ix.n_sel[cb], ix.max_sel)) : 0;
-    src.cp[j] = 0;
-  }
-  src.mb = MergedBlocks{nullptr, nullptr, 0, 0, nb, a.seq_len};
-  src.cut = PanelCut{};
-  src.r0 = r0;
-  attend_panel_bf16<D>(a, row, r0, src);
-}
-
-template <int D>
 PANEL_KERNEL void attn_stream_bf16_kernel(AttnArgs a, StreamIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, p;
@@ -1063,40 +1091,88 @@ PANEL_KERNEL void attn_stream_bf16_kernel(AttnArgs a, StreamIndex ix) {
   attend_panel_bf16<D>(a, row, a0 * BLOCK, src);
 }
 
-// grid: rows x (panels for bf16, blocks for fp32)
-dim3 attn_grid(const AttnArgs& a) {
+
+#define SINGLE_KERNEL __global__ __launch_bounds__(64 * SB_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+
+template <int D, class R>
+__device__ __forceinline__ void attend_single_bf16(const AttnArgs& a, int32_t row, int32_t r0, DescGen<R> gen) {
+  const size_t qoff = a.hm.q_slab(row, a.seq_len, D);
+  const size_t kvoff = a.hm.kv_slab(row, a.seq_len, D);
+  attend_single<D, R>(static_cast<const uint16_t*>(a.q) + qoff, static_cast<const uint16_t*>(a.k) + kvoff,
+                      static_cast<const uint16_t*>(a.v) + kvoff, static_cast<uint16_t*>(a.o) + qoff,
+                      a.seq_len, r0, a.scale_log2, gen);
+}
+
+template <int D>
+SINGLE_KERNEL void attn_vs_single_kernel(AttnArgs a, VsIndex ix) {
+  const int32_t nb = num_blocks(a.seq_len);
+  int32_t row, blk;
+  work_item(a.hm, a.wo, nb, row, blk);
+  const int32_t r0 = blk * BLOCK;
+  const size_t cb = (size_t)row * nb + blk;
+  VsRanges rg{ix.iv + (size_t)row * ix.max_iv * 2, min(ix.n_iv[row], ix.max_iv), 0, r0, a.seq_len};
+  attend_single_bf16<D>(a, row, r0,
+                        make_gen(rg, ix.cols + cb * ix.max_cols, max(0, min(ix.n_cols[cb], ix.max_cols)), r0, a.seq_len));
+}
+
+template <int D>
+SINGLE_KERNEL void attn_blocks_single_kernel(AttnArgs a, BlockIndex ix) {
+  const int32_t nb = num_blocks(a.seq_len);
+  int32_t row, blk;
+  work_item(a.hm, a.wo, nb, row, blk);
+  const size_t cb = (size_t)row * nb + blk;
+  BlockRanges rg{ix.sel + cb * ix.max_sel, min(ix.n_sel[cb], ix.max_sel), 0, a.seq_len};
+  attend_single_bf16<D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
+}
+
+// grid: rows x query blocks (or x panels of two blocks for the panel kernel)
+dim3 attn_grid(const AttnArgs& a, bool panels) {
   const long long nb = (a.seq_len + BLOCK - 1) / BLOCK;
-  const long long units = a.dtype == BF16 ? (nb + PANEL - 1) / PANEL : nb;
+  const long long units = panels ? (nb + PANEL - 1) / PANEL : nb;
   return dim3((unsigned)((long long)a.rows * units));
 }
-dim3 attn_block(const AttnArgs& a) { return dim3(a.dtype == BF16 ? 64 * PANEL_WAVES : 64); }
 
 }  // namespace
 
+// Vertical-slash and block-sparse heads run the single-block bf16 kernel:
+// their key sets differ between neighbouring query blocks in many narrow
+// pieces, and four independent work-groups per CU beat the panel's sharing
+// there (measured on MI355X: 6% at 128K, 3-14% on the mixed layers).
+// Streaming heads, whose windows two blocks share almost whole, run the panel.
 hipError_t launch_attention_vs(const AttnArgs& a, const VsIndex& ix, hipStream_t s) {
-  const dim3 grid = attn_grid(a);
+  const dim3 grid = attn_grid(a, false);
   if (grid.x == 0) return hipSuccess;
-  auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_vs_bf16_kernel<64> : attn_vs_bf16_kernel<128>)
-                            : (a.head_dim == 64 ? attn_vs_f32_kernel<64> : attn_vs_f32_kernel<128>);
-  hipLaunchKernelGGL(fn, grid, attn_block(a), 0, s, a, ix);
+  if (a.dtype == BF16)
+    hipLaunchKernelGGL(a.head_dim == 64 ? attn_vs_single_kernel<64> : attn_vs_single_kernel<128>, grid,
+                       dim3(64 * SB_WAVES), 0, s, a, ix);
+  else
+    hipLaunchKernelGGL(a.head_dim == 64 ? attn_vs_f32_kernel<64> : attn_vs_f32_kernel<128>, grid, dim3(64), 0,
+                       s, a, ix);
   return hipGetLastError();
 }
 
 hipError_t launch_attention_blocks(const AttnArgs& a, const BlockIndex& ix, hipStream_t s) {
-  const dim3 grid = attn_grid(a);
+  const dim3 grid = attn_grid(a, false);
   if (grid.x == 0) return hipSuccess;
-  auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_blocks_bf16_kernel<64> : attn_blocks_bf16_kernel<128>)
-                            : (a.head_dim == 64 ? attn_blocks_f32_kernel<64> : attn_blocks_f32_kernel<128>);
-  hipLaunchKernelGGL(fn, grid, attn_block(a), 0, s, a, ix);
+  if (a.dtype == BF16)
+    hipLaunchKernelGGL(a.head_dim == 64 ? attn_blocks_single_kernel<64> : attn_blocks_single_kernel<128>, grid,
+                       dim3(64 * SB_WAVES), 0, s, a, ix);
+  else
+    hipLaunchKernelGGL(a.head_dim == 64 ? attn_blocks_f32_kernel<64> : attn_blocks_f32_kernel<128>, grid,
+                       dim3(64), 0, s, a, ix);
   return hipGetLastError();
 }
 
 hipError_t launch_attention_stream(const AttnArgs& a, const StreamIndex& ix, hipStream_t s) {
-  const dim3 grid = attn_grid(a);
+  const bool bf16 = a.dtype == BF16;
+  const dim3 grid = attn_grid(a, bf16);
   if (grid.x == 0) return hipSuccess;
-  auto fn = a.dtype == BF16 ? (a.head_dim == 64 ? attn_stream_bf16_kernel<64> : attn_stream_bf16_kernel<128>)
-                            : (a.head_dim == 64 ? attn_stream_f32_kernel<64> : attn_stream_f32_kernel<128>);
-  hipLaunchKernelGGL(fn, grid, attn_block(a), 0, s, a, ix);
+  if (bf16)
+    hipLaunchKernelGGL(a.head_dim == 64 ? attn_stream_bf16_kernel<64> : attn_stream_bf16_kernel<128>, grid,
+                       dim3(64 * PANEL_WAVES), 0, s, a, ix);
+  else
+    hipLaunchKernelGGL(a.head_dim == 64 ? attn_stream_f32_kernel<64> : attn_stream_f32_kernel<128>, grid,
+                       dim3(64), 0, s, a, ix);
   return hipGetLastError();
 }
 
