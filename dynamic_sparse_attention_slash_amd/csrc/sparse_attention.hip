@@ -662,6 +662,58 @@ __device__ void attend_panel(const uint16_t* __restrict__ qs, const uint16_t* __
 // swizzle, masks and softmax); a work-group needs 40 KB of LDS, so four are
 // resident per CU.
 // ---------------------------------------------------------------------------
+// A global int32 list read through an LDS window: get(i) is called with the
+// same i by every thread of the work-group; when i leaves the window, the
+// threads load the next `cap` entries together (one round trip instead of one
+// per entry).
+struct StagedList {
+  const int32_t* src; int32_t n;
+  int32_t* buf; int32_t cap;
+  int32_t base, cnt;
+  int32_t tid, nth;
+  __device__ int32_t get(int32_t i) {
+    if (i >= base + cnt) {
+      __syncthreads();   // the window's last entries are consumed
+      base = i;
+      cnt = min(cap, n - i);
+      for (int32_t j = tid; j < cnt; j += nth) buf[j] = src[i + j];
+      __syncthreads();
+    }
+    return buf[i - base];
+  }
+};
+
+// VsRanges and BlockRanges over staged lists (the interval pairs, the block ids)
+struct VsRangesStaged {
+  StagedList iv; int32_t n_iv, t, r0, n;
+  __device__ void stage_into(int32_t* buf) { iv.buf = buf; }
+  __device__ bool next(int32_t& lo, int32_t& hi) {
+    while (t < n_iv) {
+      const int32_t d_lo = iv.get(2 * t), d_hi = iv.get(2 * t + 1);
+      ++t;
+      if (d_lo >= r0 + BLOCK) { t = n_iv; return false; }  // intervals ascend
+      lo = max(0, r0 - d_hi);
+      hi = min(n, r0 + BLOCK - d_lo);
+      if (lo < hi) return true;
+    }
+    return false;
+  }
+};
+struct BlockRangesStaged {
+  StagedList sel; int32_t n_sel, t, n;
+  __device__ void stage_into(int32_t* buf) { sel.buf = buf; }
+  __device__ bool next(int32_t& lo, int32_t& hi) {
+    while (t < n_sel) {
+      const int32_t c = sel.get(t++);
+      if (c < 0) continue;
+      lo = c * BLOCK;
+      hi = min(n, lo + BLOCK);
+      if (lo < hi) return true;
+    }
+    return false;
+  }
+};
+
 constexpr int SB_WAVES = 2;
 constexpr int32_t SB1_CAP = 512;       // descriptors per refill
 constexpr int32_t SB1_COLS = 1024;     // column-list entries staged per refill
@@ -690,11 +742,28 @@ __device__ int32_t fill_single(DescGen<R>& gen, Desc* d, int32_t* lcols, int32_t
   }
   if (cnt < SB1_CAP && gen.cp < gen.n_cols) {
     const int32_t ncol = min(gen.n_cols - gen.cp, min(SB1_COLS, 16 * (SB1_CAP - cnt)));
-    for (int32_t t = tid; t < ncol; t += nthreads) lcols[t] = min(max(gen.cols[gen.cp + t], 0), gen.n - 1);
+    // the column buffer also holds the staged range lists: every thread is
+    // done with them here (the ranges are exhausted)
+    __syncthreads();
+    constexpr int BATCH = 4;  // loads in flight per thread
+    for (int32_t t0 = 0; t0 < ncol; t0 += BATCH * nthreads) {
+      int32_t v[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int32_t t = t0 + u * nthreads + tid;
+        v[u] = t < ncol ? gen.cols[gen.cp + t] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int32_t t = t0 + u * nthreads + tid;
+        if (t < ncol) lcols[t] = min(max(v[u], 0), gen.n - 1);
+      }
+    }
+    __syncthreads();
     const int32_t take = (ncol + 15) >> 4;
     for (int32_t t = tid; t < take; t += nthreads) {
       const int32_t s = 16 * t, c = min(16, ncol - s);
-      const bool m = c < 16 || min(max(gen.cols[gen.cp + s + c - 1], 0), gen.n - 1) > gen.r0;
+      const bool m = c < 16 || lcols[s + c - 1] > gen.r0;
       d[cnt + t] = Desc{s, c | F_LIST | (m ? F_MASK : 0)};
     }
     cnt += take;
@@ -720,6 +789,7 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
   const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t g = lane >> 4, l16 = lane & 15;
   const int32_t q0 = r0 + 32 * wave;
+  gen.ranges.stage_into(lcols);
 
   u32x4 qop[2][DS];
 #pragma unroll
@@ -1110,7 +1180,10 @@ SINGLE_KERNEL void attn_vs_single_kernel(AttnArgs a, VsIndex ix) {
   work_item(a.hm, a.wo, nb, row, blk);
   const int32_t r0 = blk * BLOCK;
   const size_t cb = (size_t)row * nb + blk;
-  VsRanges rg{ix.iv + (size_t)row * ix.max_iv * 2, min(ix.n_iv[row], ix.max_iv), 0, r0, a.seq_len};
+  const int32_t niv = max(0, min(ix.n_iv[row], ix.max_iv));
+  VsRangesStaged rg{StagedList{ix.iv + (size_t)row * ix.max_iv * 2, 2 * niv, nullptr, SB1_COLS, 0, 0,
+                               (int32_t)threadIdx.x, 64 * SB_WAVES},
+                    niv, 0, r0, a.seq_len};
   attend_single_bf16<D>(a, row, r0,
                         make_gen(rg, ix.cols + cb * ix.max_cols, max(0, min(ix.n_cols[cb], ix.max_cols)), r0, a.seq_len));
 }
@@ -1121,7 +1194,10 @@ SINGLE_KERNEL void attn_blocks_single_kernel(AttnArgs a, BlockIndex ix) {
   int32_t row, blk;
   work_item(a.hm, a.wo, nb, row, blk);
   const size_t cb = (size_t)row * nb + blk;
-  BlockRanges rg{ix.sel + cb * ix.max_sel, min(ix.n_sel[cb], ix.max_sel), 0, a.seq_len};
+  const int32_t ns = max(0, min(ix.n_sel[cb], ix.max_sel));
+  BlockRangesStaged rg{StagedList{ix.sel + cb * ix.max_sel, ns, nullptr, SB1_COLS, 0, 0, (int32_t)threadIdx.x,
+                                  64 * SB_WAVES},
+                       ns, 0, a.seq_len};
   attend_single_bf16<D>(a, row, blk * BLOCK, make_gen(rg, (const int32_t*)nullptr, 0, blk * BLOCK, a.seq_len));
 }
 
