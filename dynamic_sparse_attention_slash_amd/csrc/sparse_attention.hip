@@ -359,12 +359,16 @@ struct TileLds {
   static constexpr int RPI = 64 / UNITS;      // rows per buffer_load_dwordx4 ... lds
   static constexpr int INSTR = 16 / RPI;      // instructions per 16-row sub-block
   // Chunk swizzle of row r: an XOR-linear map of r's low four bits (table
-  // below, one nibble per r) under which the K reads (ds_read_b128, 16 rows
-  // at one logical chunk) and the V^T reads (ds_read_b64_tr_b16, 4 rows x 2
-  // chunks per 16 lanes) each touch distinct banks, with 32 or 64 banks and
-  // D = 64 or 128. The plain XOR by r conflicts 2-way on the V^T reads.
+  // below, one nibble per r) under which every operand read is free of bank
+  // conflicts, for D = 64 and 128. gfx950 LDS has 64 four-byte banks and, as
+  // measured with the bank-conflict counter, serves a ds_read_b128 in four
+  // passes of 16 lanes (each half-wave's lane quads q = l >> 2 split by the
+  // parity of q & 7: lanes 0-3, 12-15, 20-23, 24-27 form the first pass) and a
+  // ds_read_b64 / ds_read_b64_tr_b16 in two passes of 32 lanes. The K reads (16
+  // rows at one logical chunk per 16 lanes) and the V^T reads (4 rows x 2
+  // chunks per 16 lanes) touch distinct banks in every pass.
   __device__ static int swz(int r) {
-    return (int)((0xdb8e71249fca3560ull >> (4 * (r & 15))) & 15) & (UNITS - 1);
+    return (int)((0xae629d51bf738c40ull >> (4 * (r & 15))) & 15) & (UNITS - 1);
   }
   // byte offset of logical chunk c of row r
   __device__ static int off(int r, int c) { return r * ROW + 16 * (c ^ swz(r)); }
@@ -378,12 +382,25 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-// max of three floats in one instruction: fmaxf would first quiet each
-// operand (v_max_f32 x, x, x) under the IEEE mode the kernels run in
-__device__ __forceinline__ float max3f(float a, float b, float c) {
+// Max of three floats in one instruction: fmaxf would first quiet each
+// operand (v_max_f32 x, x, x) under the IEEE mode the kernels run in. The
+// compiler does not look inside the asm, so it would not put the wait states
+// that a VALU read of an MFMA result needs in front of it; `after` (not used by
+// the instruction) orders the asm behind max2v, a compiler-visible read of the
+// same MFMA result that does get them.
+__device__ __forceinline__ float max3f(float a, float b, float c, float after) {
   float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c), "v"(after));
   return r;
+}
+// max(a, b) for non-NaN inputs, as an instruction the compiler schedules
+// itself; pinf is +inf from opaque_inf(), which keeps the compiler from turning
+// the med3 into a quieting max
+__device__ __forceinline__ float max2v(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
+__device__ __forceinline__ float opaque_inf() {
+  float x;
+  asm volatile("v_mov_b32 %0, 0x7f800000" : "=v"(x));
+  return x;
 }
 
 // Row max over the four lane groups (lanes l, l^16, l^32, l^48 hold the same
@@ -474,6 +491,7 @@ __device__ void attend_panel(const uint16_t* __restrict__ qs, const uint16_t* __
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) rp1[qb] = q0 + 16 * qb + l16 + 1 - 4 * g;
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  const float pinf = opaque_inf();
 
   // loads of sub-block dw into this wave's quarter of a stage. Slots past a
   // range's end read the rows that follow (zeros past the slab) and slots past
@@ -578,9 +596,9 @@ __device__ void attend_panel(const uint16_t* __restrict__ qs, const uint16_t* __
     bool up_any = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      mx[qb] = max3f(max3f(st[0][qb][0], st[0][qb][1], st[0][qb][2]),
-                     max3f(st[0][qb][3], st[1][qb][0], st[1][qb][1]),
-                     max3f(st[1][qb][2], st[1][qb][3], st[1][qb][3]));
+      const float t = max2v(st[0][qb][0], st[0][qb][1], pinf);
+      mx[qb] = max3f(max3f(t, st[0][qb][2], st[0][qb][3], t), max3f(st[1][qb][0], st[1][qb][1], st[1][qb][2], t),
+                     st[1][qb][3], t);
       up_any |= mx[qb] > raise[qb];
     }
     if (__any(up_any)) {
@@ -832,6 +850,7 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) rp1[qb] = q0 + 16 * qb + l16 + 1 - 4 * g;
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  const float pinf = opaque_inf();
 
   auto issue_loads = [&](const Desc& dw, char* stage) {
     char* dst = stage + 16 * wave * L::ROW;
@@ -906,9 +925,9 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
     bool up_any = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      mx[qb] = max3f(max3f(st[0][qb][0], st[0][qb][1], st[0][qb][2]),
-                     max3f(st[0][qb][3], st[1][qb][0], st[1][qb][1]),
-                     max3f(st[1][qb][2], st[1][qb][3], st[1][qb][3]));
+      const float t = max2v(st[0][qb][0], st[0][qb][1], pinf);
+      mx[qb] = max3f(max3f(t, st[0][qb][2], st[0][qb][3], t), max3f(st[1][qb][0], st[1][qb][1], st[1][qb][2], t),
+                     st[1][qb][3], t);
       up_any |= mx[qb] > raise[qb];
     }
     if (__any(up_any)) {

@@ -350,6 +350,27 @@ def test_bs_end_to_end_small():
                 check_attention(oh[b, h], O.assemble(res["out"], n, D), f"bs b{b} h{h}")
 
 
+def test_repeat_launch_bitwise():
+    """Two launches on the same inputs give the same bits for every pattern: a
+    kernel that read an MFMA result before it is complete, or raced on LDS,
+    would change the lazy-max decisions and with them the last bits."""
+    say("repeat launch bitwise")
+    w = synthetic.BY_NAME["qwen2_7b_32k_b4_mixed_bf16"].scaled(batch=1, seq_len=8192, slash_topk=600,
+                                                                vertical_topk=100, topk=16, local_blocks=8)
+    x = synthetic.make_inputs(w)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    hp = x.heads
+    outs = []
+    for _ in range(2):
+        o = torch.zeros_like(q)
+        dsa.vertical_slash_sparse_attention(q, k, v, w.vertical_topk, w.slash_topk, heads=hp["vs"], out=o)
+        dsa.block_sparse_attention(q, k, v, w.topk, heads=hp["bs"], out=o)
+        dsa.streaming_attention(q, k, v, w.init_blocks, w.local_blocks, heads=hp["st"], out=o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_mixed_layer_small():
     """Three calls over head subsets fill one output, as a mixed layer does."""
     say("mixed layer small")
