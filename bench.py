@@ -214,6 +214,35 @@ def layer_flops(w, x, idx):
     return fl
 
 
+def stage_bytes(w, x, idx):
+    """Algorithmic HBM bytes of the memory-side stages (what each stage must
+    read and write once), for the fraction of HBM peak next to its time:
+    VS estimate: K of each involved kv head once per pass (two passes), the
+    window rows of Q, the v and s vectors; VS top-k: v and s in, the indices
+    out; VS index: the indices in, intervals, column lists and counts out;
+    BS pool: Q of the block-sparse heads and all of K in, the pooled rows out."""
+    n, D, B = w.seq_len, w.head_dim, w.batch
+    eb = 2 if w.dtype == "bf16" else 4
+    G = w.q_heads // w.kv_heads
+    nb = (n + 63) // 64
+    out = {}
+    if "vs" in idx:
+        hs = x.heads["vs"]
+        kv = {h // G for h in hs}
+        lq = min(w.last_q, n)
+        out["vs_estimate_ms"] = (2 * B * len(kv) * n * D * eb + B * len(hs) * lq * D * eb
+                                 + 2 * B * len(hs) * n * 4)
+        vk, sk = min(w.vertical_topk, n), min(w.slash_topk, n)
+        out["vs_topk_ms"] = B * len(hs) * (2 * n * 4 + (vk + sk) * 4)
+        iv, n_iv, cols, n_cols = idx["vs"]
+        out["vs_index_ms"] = (B * len(hs) * (vk + sk) * 4 + int(n_iv.sum()) * 8
+                              + int(n_cols.sum()) * 4 + n_cols.numel() * 4 + n_iv.numel() * 4)
+    if "bs" in idx:
+        hs = x.heads["bs"]
+        out["bs_pool_ms"] = B * (len(hs) + w.kv_heads) * (n * D * eb + nb * D * 4)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # CPU oracle on a bounded sample
 # ----------------------------------------------------------------------------
@@ -380,6 +409,10 @@ def run_layer(w, steps, warmup, with_cpu):
         "flops_dense_causal": dense, "density_vs_dense": f_total / dense,
         "stages_ms": st,
     }
+    sb = stage_bytes(w, x, idx)
+    res["stages_hbm"] = {k.replace("_ms", ""): {"bytes": v, "gbs": v / (st[k] * 1e-3) / 1e9,
+                                                "frac_hbm": v / (st[k] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+                         for k, v in sb.items() if k in st}
     if "vs" in flops and w.dtype == "bf16":
         ach = flops["vs"] / (st["vs_attention_ms"] * 1e-3) / 1e12
         res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -452,6 +485,8 @@ def main():
         "flops_per_pattern": prim["flops_per_pattern"],
         "density_vs_dense": prim["density_vs_dense"],
         "stages_ms": {k: round(v, 4) for k, v in prim["stages_ms"].items()},
+        "stages_hbm": {k: {kk: (round(vv, 4) if kk != "bytes" else vv) for kk, vv in v.items()}
+                       for k, v in prim["stages_hbm"].items()},
         "roofline": prim.get("roofline"),
     }
     if "cpu_baseline" in prim:
@@ -464,6 +499,8 @@ def main():
                             "pct_bf16_peak": round(100 * sec["tflops"] / PEAK_BF16_TFLOPS, 2),
                             "density_vs_dense": sec["density_vs_dense"],
                             "stages_ms": {k: round(v, 4) for k, v in sec["stages_ms"].items()},
+                            "stages_hbm": {k: {kk: (round(vv, 4) if kk != "bytes" else vv) for kk, vv in v.items()}
+                                           for k, v in sec["stages_hbm"].items()},
                             "roofline": sec.get("roofline")}
     print(json.dumps(res), flush=True)
 
