@@ -214,6 +214,26 @@ def layer_flops(w, x, idx):
     return fl
 
 
+KV_WINDOW, KV_KEEP = 256, 4096
+
+
+def kv_retention_timing(layer, reps):
+    """The step after prefill, outside the layer step: KV-retention scores of
+    every query head over the last 256 query rows and the 4096 kept keys per
+    head. Algorithmic bytes: K of every kv head once per pass (two passes:
+    softmax statistics, then scores), the scores written and read back by the
+    top-k, the kept indices written."""
+    w, q, k = layer.w, layer.q, layer.k
+    torch.cuda.synchronize()
+    ms = time_events(lambda: dsa.kv_retention(q, k, KV_WINDOW, KV_KEEP), reps)
+    n, D, B = w.seq_len, w.head_dim, w.batch
+    rows = B * w.q_heads
+    nbytes = 2 * B * w.kv_heads * n * D * 2 + 2 * rows * n * 4 + rows * min(KV_KEEP, n) * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kv_retention_ms": ms, "window": KV_WINDOW, "keep": KV_KEEP, "heads": w.q_heads,
+            "bytes": nbytes, "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+
+
 def stage_bytes(w, x, idx):
     """Algorithmic HBM bytes of the memory-side stages (what each stage must
     read and write once), for the fraction of HBM peak next to its time:
@@ -419,6 +439,8 @@ def run_layer(w, steps, warmup, with_cpu):
                            "frac": ach / PEAK_BF16_TFLOPS, "traffic": committed_traffic(w.name),
                            "kernel": DOMINANT, "flops_per_launch": flops["vs"],
                            "launch_ms": st["vs_attention_ms"]}
+    if w.dtype == "bf16":
+        res["after_prefill"] = kv_retention_timing(layer, reps=3)
     if with_cpu:
         log(f"[bench] {w.name}: cpu baseline (oracle, bounded sample)")
         res["cpu_baseline"] = cpu_baseline(layer, idx, f_total)
@@ -487,6 +509,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in prim["stages_ms"].items()},
         "stages_hbm": {k: {kk: (round(vv, 4) if kk != "bytes" else vv) for kk, vv in v.items()}
                        for k, v in prim["stages_hbm"].items()},
+        "after_prefill": prim.get("after_prefill"),
         "roofline": prim.get("roofline"),
     }
     if "cpu_baseline" in prim:

@@ -1,8 +1,9 @@
 """Dynamic sparse attention for the long-context prefill phase on MI355X.
 
 Vertical-slash, block-sparse and streaming (A-shape) heads, each as online
-sparse-index estimation followed by exact block-sparse attention, all in HIP
-kernels for gfx950 behind a C ABI (include/dsa.h). This package is the thin
+sparse-index estimation followed by exact block-sparse attention, and the
+KV-retention scores and kept keys that follow prefill, all in HIP kernels for
+gfx950 behind a C ABI (include/dsa.h). This package is the thin
 Python binding of that library; torch supplies device memory and streams.
 """
 from ._binding import (  # noqa: F401
@@ -12,6 +13,7 @@ from ._binding import (  # noqa: F401
     block_sparse_workspace_bytes,
     bs_pool,
     bs_select,
+    kv_retention,
     load,
     sparse_attention_blocks,
     sparse_attention_vs,

@@ -50,6 +50,8 @@ _SIGS = {
     "dsa_streaming_attention": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _i32, _i32, _f32, _ip, _i32, _vp], _i32),
     "dsa_vs_estimate": ([_vp, _vp, ctypes.POINTER(Shape), _i32, _f32, _ip, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "dsa_vs_estimate_workspace_bytes": ([ctypes.POINTER(Shape), _i32], _sz),
+    "dsa_kv_retention": ([_vp, _vp, ctypes.POINTER(Shape), _i32, _i32, _f32, _ip, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "dsa_kv_retention_workspace_bytes": ([ctypes.POINTER(Shape), _i32, _i32], _sz),
     "dsa_topk": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp], _i32),
     "dsa_topk_workspace_bytes": ([_i32, _i32, _i32], _sz),
     "dsa_vs_build_index": ([_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
@@ -227,6 +229,27 @@ def vs_estimate(q, k, *, last_q: int = 64, scale: Optional[float] = None,
     _call("dsa_vs_estimate", _dev(q, "q"), _dev(k, "k", q.dtype), ctypes.byref(sh), last_q,
           _scale(scale), ha, hn, vsc.data_ptr(), ssc.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q))
     return vsc, ssc
+
+
+def kv_retention(q, k, window: int, keep: int, *, scale: Optional[float] = None,
+                 heads: Optional[Sequence[int]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """KV-retention scores fp32 [batch * n_heads, seq_len] (softmax mass of each
+    key over the last `window` query rows) and the kept keys int32
+    [batch * n_heads, min(keep, seq_len)], ascending."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k must be [batch, heads, seq_len, head_dim]")
+    B, Hq, n, D = q.shape
+    sh = Shape(B, Hq, k.shape[1], n, D, _dtype_code(q))
+    ha, hn = _heads(heads)
+    nh = Hq if heads is None else hn
+    rows = B * nh
+    scores = torch.empty((rows, n), dtype=torch.float32, device=q.device)
+    kept = torch.empty((rows, max(0, min(keep, n))), dtype=torch.int32, device=q.device)
+    ws = _workspace(load().dsa_kv_retention_workspace_bytes(ctypes.byref(sh), keep, nh), q.device)
+    _call("dsa_kv_retention", _dev(q, "q"), _dev(k, "k", q.dtype), ctypes.byref(sh), window, keep,
+          _scale(scale), ha, hn, scores.data_ptr(), kept.data_ptr() if kept.numel() else None,
+          ws.data_ptr(), ws.numel(), _stream(q))
+    return scores, kept
 
 
 def topk(scores: torch.Tensor, k: int, forced_index: int = -1) -> torch.Tensor:

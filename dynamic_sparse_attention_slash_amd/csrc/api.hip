@@ -208,12 +208,52 @@ dsa_status dsa_vs_estimate(const void* q, const void* k, const dsa_shape* shape,
   a.q = q; a.k = k;
   a.seq_len = shape->seq_len; a.head_dim = shape->head_dim; a.dtype = shape->dtype;
   a.last_q = last_q; a.rows = rows;
+  a.win_start = a.seq_len - a.lq_eff(); a.add_v = 0; a.want_s = 1;
   a.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
   a.hm = hm;
   a.wo = make_work_order(hm);
   a.v_scores = v_scores; a.s_scores = s_scores;
   est_carve(a, workspace);
   return hip_status(launch_vs_estimate(a, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ KV retention
+size_t dsa_kv_retention_workspace_bytes(const dsa_shape* shape, int32_t keep, int32_t n_heads) {
+  if (check_shape(shape) != DSA_OK || n_heads < 0 || keep < 0) return 0;
+  const int32_t rows = shape->batch * n_heads, n = shape->seq_len;
+  const size_t est = est_workspace_bytes(rows, n);
+  const size_t tk = topk_workspace_bytes(rows, n, keep < n ? keep : n);
+  return est > tk ? est : tk;  // the estimator's partials are dead when the top-k runs
+}
+
+dsa_status dsa_kv_retention(const void* q, const void* k, const dsa_shape* shape, int32_t window,
+                            int32_t keep, float scale, const int32_t* heads, int32_t n_heads,
+                            float* scores, int32_t* kept, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !scores || window < 1 || keep < 0 || (keep > 0 && !kept)) return DSA_ERR_INVALID_ARG;
+  HeadMap hm;
+  if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  const int32_t rows = shape->batch * hm.n, n = shape->seq_len;
+  const size_t need = dsa_kv_retention_workspace_bytes(shape, keep, hm.n);
+  if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
+  if (rows == 0 || n == 0) return DSA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  EstArgs a;
+  a.q = q; a.k = k;
+  a.seq_len = n; a.head_dim = shape->head_dim; a.dtype = shape->dtype;
+  a.last_q = 64; a.rows = rows;
+  a.win_start = 0; a.add_v = 0; a.want_s = 0;
+  a.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
+  a.hm = hm;
+  a.wo = make_work_order(hm);
+  a.v_scores = scores; a.s_scores = nullptr;
+  est_carve(a, workspace);
+  hipError_t e = launch_window_column_scores(a, window, s);
+  const int32_t kk = keep < n ? keep : n;
+  if (e == hipSuccess && kk > 0) e = launch_topk_rows(scores, rows, n, kk, -1, kept, workspace, s);
+  return hip_status(e);
 }
 
 size_t dsa_topk_workspace_bytes(int32_t rows, int32_t n, int32_t k) {
@@ -298,6 +338,7 @@ dsa_status dsa_vertical_slash_sparse_attention(const void* q, const void* k, con
   ea.q = q; ea.k = k;
   ea.seq_len = n; ea.head_dim = shape->head_dim; ea.dtype = shape->dtype;
   ea.last_q = last_q; ea.rows = rows;
+  ea.win_start = ea.seq_len - ea.lq_eff(); ea.add_v = 0; ea.want_s = 1;
   ea.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
   ea.hm = hm;
   ea.wo = make_work_order(hm);

@@ -84,7 +84,10 @@ hipError_t launch_attention_stream(const AttnArgs& a, const StreamIndex& ix, hip
 constexpr int EST_CHUNK = 256;  // keys per estimator work-group
 struct EstArgs {
   const void* q; const void* k;
-  int32_t seq_len, head_dim, dtype, last_q;
+  int32_t seq_len, head_dim, dtype, last_q;  // last_q: window rows of this launch (<= 64)
+  int32_t win_start;   // sequence row of window row 0 (seq_len - lq_eff() for the last rows)
+  int32_t add_v;       // 0: write v, 1: add into v (window slices after the first)
+  int32_t want_s;      // 0: no slash scores (s_scores and s_part unused)
   int32_t rows;
   float scale_log2;
   HeadMap hm;
@@ -98,6 +101,9 @@ struct EstArgs {
 size_t est_workspace_bytes(int32_t rows, int32_t seq_len);
 void est_carve(EstArgs& a, void* ws);
 hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s);
+// v over a window of `window` rows ending at the last row, in slices of 64
+// rows (the first slice writes v, the others add), no slash scores
+hipError_t launch_window_column_scores(EstArgs a, int32_t window, hipStream_t s);
 
 // ---- top-k (topk.hip) ----
 // scratch of launch_topk_rows (0 when the rows are short enough for one pass)

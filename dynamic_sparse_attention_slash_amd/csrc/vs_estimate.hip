@@ -32,8 +32,8 @@ constexpr int C = EST_CHUNK;       // keys per work-group
 constexpr int SACC = C + 63;       // diagonal offsets one chunk touches
 
 struct Window {
-  int32_t n, lq;
-  __device__ int32_t pos(int32_t r) const { return n - lq + r; }  // sequence row of window row r
+  int32_t n, lq, start;
+  __device__ int32_t pos(int32_t r) const { return start + r; }  // sequence row of window row r
 };
 
 // S tile for 16 keys [j0, j0+16): lane holds key column j0 + l16 and window
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64) void est_stats_kernel(EstArgs a) {
   const int32_t nchunks = (a.seq_len + C - 1) / C;
   int32_t row, chunk;
   work_item(a.hm, a.wo, nchunks, row, chunk);
-  const Window w{a.seq_len, a.lq_eff()};
+  const Window w{a.seq_len, a.lq_eff(), a.win_start};
   const T* qs = static_cast<const T*>(a.q) + a.hm.q_slab(row, a.seq_len, D);
   const T* ks = static_cast<const T*>(a.k) + a.hm.kv_slab(row, a.seq_len, D);
   Tile<T, D> tile;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(64) void est_scores_kernel(EstArgs a) {
   int32_t row, chunk;
   work_item(a.hm, a.wo, nchunks, row, chunk);
   const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
-  const Window w{a.seq_len, a.lq_eff()};
+  const Window w{a.seq_len, a.lq_eff(), a.win_start};
   const T* qs = static_cast<const T*>(a.q) + a.hm.q_slab(row, a.seq_len, D);
   const T* ks = static_cast<const T*>(a.k) + a.hm.kv_slab(row, a.seq_len, D);
   Tile<T, D> tile;
@@ -265,8 +265,12 @@ __global__ __launch_bounds__(64) void est_scores_kernel(EstArgs a) {
           ptile[(16 * qb + 4 * g + i) * PS + 16 * sb + l16] = p;
         }
       colsum = xor_sum(xor_sum(colsum, 16), 32);
-      if (g == 0 && j0 + l16 < a.seq_len) vout[j0 + l16] = colsum;
+      if (g == 0 && j0 + l16 < a.seq_len) {
+        if (a.add_v) vout[j0 + l16] += colsum;
+        else vout[j0 + l16] = colsum;
+      }
     }
+    if (!a.want_s) continue;
     __syncthreads();
     // diagonal e = r - jj of the tile maps to chunk offset index
     // e + (C - 1) - (t0 - j_begin)
@@ -280,23 +284,24 @@ __global__ __launch_bounds__(64) void est_scores_kernel(EstArgs a) {
     }
     __syncthreads();
   }
+  if (!a.want_s) return;
   float* dst = a.s_part + ((size_t)row * nchunks + chunk) * SACC;
   for (int e = lane; e < SACC; e += 64) dst[e] = sacc[e];
 }
 
 // s[d] = sum over chunks c covering d (ascending c) of s_part[c][e_c(d)],
-// e_c(d) = d - (n - lq - (c*C + C - 1)).
+// e_c(d) = d - (start - (c*C + C - 1)), start = the window's first row.
 __global__ __launch_bounds__(256) void est_scombine_kernel(EstArgs a, int32_t nchunks) {
   const int32_t row = blockIdx.y;
   const int32_t d = blockIdx.x * 256 + threadIdx.x;
   if (d >= a.seq_len) return;
-  const int32_t n = a.seq_len, lq = a.lq_eff();
-  // keys of diagonal d: j in [n - lq - d, n - 1 - d] (clipped at 0)
-  const int32_t j_lo = max(0, n - lq - d), j_hi = n - 1 - d;
+  const int32_t n = a.seq_len, lq = a.lq_eff(), start = a.win_start;
+  // keys of diagonal d: j in [start - d, start + lq - 1 - d] (clipped at 0)
+  const int32_t j_lo = max(0, start - d), j_hi = start + lq - 1 - d;
   float sum = 0.f;
   const float* sp = a.s_part + (size_t)row * nchunks * SACC;
   for (int32_t c = j_lo / C; c <= j_hi / C; ++c) {
-    const int32_t e = d - (n - lq - (c * C + C - 1));
+    const int32_t e = d - (start - (c * C + C - 1));
     sum += sp[(size_t)c * SACC + e];
   }
   a.s_scores[(size_t)row * n + d] = sum;
@@ -335,8 +340,24 @@ hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(st, grid, dim3(64), 0, s, a);
   hipLaunchKernelGGL(est_combine_kernel, dim3(a.rows), dim3(64 * COMB_SPLIT), 0, s, a, nch);
   hipLaunchKernelGGL(sc, grid, dim3(64), 0, s, a);
-  hipLaunchKernelGGL(est_scombine_kernel, dim3((a.seq_len + 255) / 256, a.rows), dim3(256), 0, s, a, nch);
+  if (a.want_s)
+    hipLaunchKernelGGL(est_scombine_kernel, dim3((a.seq_len + 255) / 256, a.rows), dim3(256), 0, s, a, nch);
   return hipGetLastError();
+}
+
+hipError_t launch_window_column_scores(EstArgs a, int32_t window, hipStream_t s) {
+  const int32_t n = a.seq_len;
+  window = window < n ? window : n;
+  if (a.rows == 0 || n == 0 || window <= 0) return hipSuccess;
+  a.want_s = 0;
+  for (int32_t r0 = n - window; r0 < n; r0 += 64) {
+    a.win_start = r0;
+    a.last_q = n - r0 < 64 ? n - r0 : 64;
+    a.add_v = r0 > n - window;
+    const hipError_t e = launch_vs_estimate(a, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace dsa

@@ -204,6 +204,31 @@ dsa_status dsa_sparse_attention_blocks(
     float scale, const int32_t* heads, int32_t n_heads, const int32_t* sel,
     const int32_t* n_sel, int32_t max_sel, void* stream);
 
+/* ======================================================================
+ * After prefill: which keys to keep in the KV cache
+ * ====================================================================== */
+
+/* KV-retention scores and kept keys [Novita §2: per head, a key's score is the
+ * sum of its softmax probabilities over the window of the last queries (the
+ * PyramidKV score); the highest-scoring keys keep their KV cache entries]. For
+ * each listed head, with w = min(window, seq_len) and p[i][j] the causal
+ * softmax of query row i over keys j <= i:
+ *   scores[row][j] = sum over i in [seq_len - w, seq_len) of p[i][j]
+ * (the vertical score of dsa_vs_estimate over a window of w rows, computed in
+ * slices of 64 rows whose sums are added in ascending row order), and
+ * kept[row][0 .. min(keep, seq_len)) the top keys of scores[row] (no forced
+ * entry), ascending. window >= 1, keep >= 0. scores: device fp32
+ * [batch * n_heads][seq_len]; kept: device int32 [batch * n_heads]
+ * [min(keep, seq_len)] (may be NULL when keep == 0). workspace: at least
+ * dsa_kv_retention_workspace_bytes(...) bytes. */
+dsa_status dsa_kv_retention(const void* q, const void* k, const dsa_shape* shape,
+                            int32_t window, int32_t keep, float scale,
+                            const int32_t* heads, int32_t n_heads, float* scores,
+                            int32_t* kept, void* workspace, size_t workspace_bytes,
+                            void* stream);
+size_t dsa_kv_retention_workspace_bytes(const dsa_shape* shape, int32_t keep,
+                                        int32_t n_heads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,13 @@ R7  Streaming / A-shape [MInf usage listing, streaming_forward(init_num,
     (c < init_blocks or a - c < local_blocks); the local window counts the
     diagonal block.
 R8  GQA: query head h reads kv head h // (q_heads / kv_heads).
+R9  KV retention [Novita §2, the PyramidKV score; the formula itself is lost
+    from the page text]: a key's retention score is the sum of its softmax
+    probabilities over the window of the last ``window`` query rows (each row
+    normalised over its whole causal range, as in R2), rounded to float32;
+    per head the ``keep`` highest-scoring keys are kept (R3, no forced entry).
+    A window longer than the prompt is clamped to it. Not taken: also keeping
+    the window's own tokens whatever their score (the page does not say so).
 """
 from __future__ import annotations
 
@@ -185,6 +192,34 @@ def topk_indices(x, k: int, forced: Sequence[int] = ()) -> np.ndarray:
     # np.lexsort: the last key is the primary one.
     order = np.lexsort((np.arange(n), -key, ~is_forced))
     return np.sort(order[:k]).astype(np.int64)
+
+
+# ----------------------------------------------------------------------------
+# KV retention after prefill  [Novita §2; R9]
+# ----------------------------------------------------------------------------
+def kv_retention_scores(q: np.ndarray, k: np.ndarray, window: int, scale: float) -> np.ndarray:
+    """Retention score of every key of one query head, float64 [n]: the sum of
+    the key's softmax probabilities over the last min(window, n) query rows
+    [Novita §2: scores from the window of the last queries, each row's
+    probabilities p = exp(qk - rowmax) / l]."""
+    q = f64(q)
+    k = f64(k)
+    n = q.shape[0]
+    w = min(int(window), n)
+    S = np.zeros(n, dtype=np.float64)
+    for i in range(n - w, n):
+        lr = scale * (k[: i + 1] @ q[i])
+        e = np.exp(lr - lr.max())
+        S[: i + 1] += e / e.sum()
+    return S
+
+
+def kv_retention(q, k, window: int, keep: int, scale: float | None = None
+                 ) -> Tuple[np.ndarray, np.ndarray]:
+    """(float32 scores, kept keys ascending) of one query head (R9)."""
+    scale = default_scale(np.shape(q)[1]) if scale is None else scale
+    S32 = to_f32(kv_retention_scores(q, k, window, scale))
+    return S32, topk_indices(S32, keep)
 
 
 # ----------------------------------------------------------------------------

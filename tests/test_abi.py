@@ -108,6 +108,16 @@ def test_other_argument_errors(lib):
     assert lib.dsa_vs_estimate(P, P, ctypes.byref(sh), 64, 0.0, None, 0, P, P, P, 4, None) == WORKSPACE
     assert lib.dsa_sparse_attention_vs(P, P, P, P, ctypes.byref(sh), 0.0, None, 0, P, None, 1, P, P, 1, None) == INVALID
     assert lib.dsa_sparse_attention_blocks(P, P, P, P, ctypes.byref(sh), 0.0, None, 0, P, P, -1, None) == INVALID
+    # KV retention: window >= 1, keep >= 0, kept needed when keep > 0, workspace checked
+    kv = lambda win, keep, kept=P, ws=P, wsb=1 << 40, q=P: lib.dsa_kv_retention(
+        q, P, ctypes.byref(sh), win, keep, 0.0, None, 0, P, kept, ws, wsb, None)
+    assert kv(0, 4) == INVALID
+    assert kv(64, -1) == INVALID
+    assert kv(64, 4, kept=None) == INVALID
+    assert kv(64, 4, q=None) == INVALID
+    assert kv(64, 4, wsb=8) == WORKSPACE
+    assert lib.dsa_kv_retention_workspace_bytes(ctypes.byref(sh), 4, 4) > 0
+    assert lib.dsa_kv_retention_workspace_bytes(ctypes.byref(sh), -1, 4) == 0
     many = (ctypes.c_int32 * 300)(*range(300))
     big = shape(hq=300, hkv=300)
     assert lib.dsa_streaming_attention(P, P, P, P, ctypes.byref(big), 1, 1, 0.0, many, 300, None) == UNSUPPORTED

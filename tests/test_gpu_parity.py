@@ -350,6 +350,51 @@ def test_bs_end_to_end_small():
                 check_attention(oh[b, h], O.assemble(res["out"], n, D), f"bs b{b} h{h}")
 
 
+@pytest.mark.parametrize("n,D,dt,window,keep", [(1000, 128, "bf16", 256, 100), (777, 64, "f32", 64, 50),
+                                                 (300, 128, "bf16", 100, 300), (70, 128, "bf16", 500, 20),
+                                                 (5000, 128, "bf16", 130, 2000), (129, 64, "bf16", 1, 5),
+                                                 (400, 128, "bf16", 64, 0)])
+def test_kv_retention(n, D, dt, window, keep):
+    """Retention scores within the estimator bar of the oracle; kept keys
+    bit-exact against the oracle's top-k of the GPU's own scores."""
+    say(f"kv retention n={n} D={D} {dt} window={window} keep={keep}")
+    q, k, _ = rand_qkv(2, 4, 2, n, D, dt, seed=n + window, amp=2.0)
+    heads = [3, 1]
+    sc, kept = dsa.kv_retention(q, k, window, keep, heads=heads)
+    torch.cuda.synchronize()
+    assert kept.shape == (4, min(keep, n))
+    qh, kh = host64(q), host64(k)
+    for b in range(2):
+        for t, h in enumerate(heads):
+            row = b * 2 + t
+            S = O.kv_retention_scores(qh[b, h], kh[b, kvh(h, 4, 2)], window, 1.0 / math.sqrt(D))
+            g = sc[row].cpu().numpy()
+            check_scores(g, S, f"kv retention row {row}")
+            assert abs(float(g.astype(np.float64).sum()) - min(window, n)) < 1e-3 * min(window, n)
+            assert np.array_equal(kept[row].cpu().numpy(), O.topk_indices(g, keep))
+
+
+def test_kv_retention_128k_planted():
+    """At 128K with a 256-row window: scores of two heads against the oracle,
+    kept keys against the oracle's top-k of the GPU scores, and the planted
+    sink key (row 0, scaled up) is kept."""
+    say("kv retention 128K")
+    w = synthetic.BY_NAME["llama3_8b_128k_vs_bf16"].scaled(q_heads=4, kv_heads=1)
+    x = synthetic.make_inputs(w)
+    q, k = x.q.cuda(), x.k.cuda()
+    heads = [0, 3]
+    sc, kept = dsa.kv_retention(q, k, 256, 4096, heads=heads)
+    torch.cuda.synchronize()
+    qh, kh = host64(x.q), host64(x.k)
+    for t, h in enumerate(heads):
+        S = O.kv_retention_scores(qh[0, h], kh[0, 0], 256, 1.0 / math.sqrt(w.head_dim))
+        g = sc[t].cpu().numpy()
+        check_scores(g, S, f"kv retention 128K head {h}")
+        kt = kept[t].cpu().numpy()
+        assert np.array_equal(kt, O.topk_indices(g, 4096))
+        assert 0 in kt
+
+
 def test_repeat_launch_bitwise():
     """Two launches on the same inputs give the same bits for every pattern: a
     kernel that read an MFMA result before it is complete, or raced on LDS,

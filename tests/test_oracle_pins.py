@@ -154,6 +154,50 @@ def test_window_worked_example():
 
 
 # ---------------------------------------------------------------------------
+# KV-retention scores (the vertical score over a window of any length)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,window", [(1, 5), (9, 3), (70, 70), (150, 100), (200, 400)])
+def test_kv_retention_bruteforce(n, window):
+    q, k, _ = rnd(n, 6, 3 * n + window)
+    q *= 2.0
+    S = O.kv_retention_scores(q, k, window, 0.4)
+    bv, _ = bf_vs_scores(q.tolist(), k.tolist(), window, 0.4)
+    np.testing.assert_allclose(S, bv, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("n,window", [(300, 256), (1000, 130), (50, 1000)])
+def test_kv_retention_uniform_closed_form(n, window):
+    """q = 0: every row attends uniformly, so S[j] = sum over window rows
+    i >= j of 1/(i+1): a difference of harmonic numbers."""
+    k = np.random.default_rng(1).standard_normal((n, 8))
+    S = O.kv_retention_scores(np.zeros((n, 8)), k, window, 0.3)
+    w = min(window, n)
+    H = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+    want = np.array([H[n] - H[max(j, n - w)] for j in range(n)])
+    np.testing.assert_allclose(S, want, rtol=1e-12)
+    assert abs(S.sum() - w) < 1e-9
+
+
+def test_kv_retention_last_row_is_softmax():
+    """A window of one row is that row's causal softmax (scipy's)."""
+    from scipy.special import softmax
+    q, k, _ = rnd(500, 16, 11)
+    S = O.kv_retention_scores(q, k, 1, 0.25)
+    np.testing.assert_allclose(S, softmax(0.25 * (k @ q[-1])), rtol=1e-12)
+
+
+def test_kv_retention_keeps_heaviest_keys():
+    """Kept keys are the brute-force top-k of the float32 scores, and a key
+    made to dominate the window's attention is kept."""
+    q, k, _ = rnd(400, 16, 13)
+    u = q[-64:].mean(axis=0)
+    k[123] = 30.0 * u / (u @ u)   # mean window logit 30 * 0.25 = 7.5
+    S32, kept = O.kv_retention(q, k, 64, 20, 0.25)
+    assert S32.dtype == np.float32 and 123 in kept
+    assert list(kept) == bf_topk(S32.tolist(), 20)
+
+
+# ---------------------------------------------------------------------------
 # top-k
 # ---------------------------------------------------------------------------
 def test_topk_bruteforce_random():
