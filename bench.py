@@ -218,20 +218,41 @@ KV_WINDOW, KV_KEEP = 256, 4096
 
 
 def kv_retention_timing(layer, reps):
-    """The step after prefill, outside the layer step: KV-retention scores of
+    """The steps after prefill, outside the layer step: KV-retention scores of
     every query head over the last 256 query rows and the 4096 kept keys per
-    head. Algorithmic bytes: K of every kv head once per pass (two passes:
-    softmax statistics, then scores), the scores written and read back by the
-    top-k, the kept indices written."""
-    w, q, k = layer.w, layer.q, layer.k
+    head (algorithmic bytes: K of every kv head once per pass, two passes for
+    the softmax statistics and the scores; the scores written and read back by
+    the top-k; the kept indices), then one decode step over the kept keys and
+    one over the whole cache."""
+    w, q, k, v = layer.w, layer.q, layer.k, layer.v
     torch.cuda.synchronize()
     ms = time_events(lambda: dsa.kv_retention(q, k, KV_WINDOW, KV_KEEP), reps)
     n, D, B = w.seq_len, w.head_dim, w.batch
     rows = B * w.q_heads
     nbytes = 2 * B * w.kv_heads * n * D * 2 + 2 * rows * n * 4 + rows * min(KV_KEEP, n) * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"kv_retention_ms": ms, "window": KV_WINDOW, "keep": KV_KEEP, "heads": w.q_heads,
-            "bytes": nbytes, "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    out = {"kv_retention_ms": ms, "window": KV_WINDOW, "keep": KV_KEEP, "heads": w.q_heads,
+           "bytes": nbytes, "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    # One decode step after prefill: a new row per head over the kept keys, and
+    # over the whole cache. Bytes: the K and V rows read once (whole cache:
+    # once per kv head, the heads of a group share them in L2; kept keys: per
+    # head), the key lists, q and o.
+    _, kept = dsa.kv_retention(q, k, KV_WINDOW, KV_KEEP)
+    kk = kept.shape[1]
+    n_keys = torch.full((rows,), kk, dtype=torch.int32, device=q.device)
+    g = torch.Generator(device=q.device).manual_seed(7)
+    qd = torch.randn(B, w.q_heads, D, generator=g, device=q.device).to(q.dtype)
+    eb = 2 if w.dtype == "bf16" else 4
+    qo = 2 * rows * D * eb
+    ms_k = time_events(lambda: dsa.sparse_decode(qd, k, v, kept, n_keys), 20)
+    b_k = rows * kk * D * eb * 2 + rows * kk * 4 + qo
+    ms_a = time_events(lambda: dsa.sparse_decode(qd, k, v), 10)
+    b_a = 2 * B * w.kv_heads * n * D * eb + qo
+    for name, t, nb in (("decode_kept", ms_k, b_k), ("decode_all", ms_a, b_a)):
+        out[name] = {"ms": t, "keys_per_head": kk if name == "decode_kept" else n, "bytes": nb,
+                     "gbs": nb / (t * 1e-3) / 1e9, "frac_hbm": nb / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del kept, n_keys, qd
+    return out
 
 
 def stage_bytes(w, x, idx):

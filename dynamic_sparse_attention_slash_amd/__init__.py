@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     load,
     sparse_attention_blocks,
     sparse_attention_vs,
+    sparse_decode,
     streaming_attention,
     topk,
     vertical_slash_sparse_attention,

@@ -52,6 +52,8 @@ _SIGS = {
     "dsa_vs_estimate_workspace_bytes": ([ctypes.POINTER(Shape), _i32], _sz),
     "dsa_kv_retention": ([_vp, _vp, ctypes.POINTER(Shape), _i32, _i32, _f32, _ip, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "dsa_kv_retention_workspace_bytes": ([ctypes.POINTER(Shape), _i32, _i32], _sz),
+    "dsa_sparse_decode": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _f32, _ip, _i32, _vp, _i32, _vp, _vp, _sz, _vp], _i32),
+    "dsa_sparse_decode_workspace_bytes": ([ctypes.POINTER(Shape), _i32, _i32], _sz),
     "dsa_topk": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp], _i32),
     "dsa_topk_workspace_bytes": ([_i32, _i32, _i32], _sz),
     "dsa_vs_build_index": ([_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
@@ -250,6 +252,42 @@ def kv_retention(q, k, window: int, keep: int, *, scale: Optional[float] = None,
           _scale(scale), ha, hn, scores.data_ptr(), kept.data_ptr() if kept.numel() else None,
           ws.data_ptr(), ws.numel(), _stream(q))
     return scores, kept
+
+
+def sparse_decode(q, k, v, keys: Optional[torch.Tensor] = None, n_keys: Optional[torch.Tensor] = None, *,
+                  scale: Optional[float] = None, heads: Optional[Sequence[int]] = None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention of one new row per head over cached keys: q [batch,
+    q_heads, head_dim] (or [batch, q_heads, 1, head_dim]), k, v the cache
+    [batch, kv_heads, seq_len, head_dim]; keys int32 [batch * n_heads,
+    max_keys] with counts n_keys [batch * n_heads], or None for the whole
+    cache. Returns o shaped like q (listed heads written)."""
+    if k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("k, v must be [batch, kv_heads, seq_len, head_dim]")
+    B, Hkv, n, D = k.shape
+    if q.dim() == 4:
+        if q.shape[2] != 1:
+            raise ValueError("decode takes one query row per head")
+    elif q.dim() != 3:
+        raise ValueError("q must be [batch, q_heads, head_dim]")
+    Hq = q.shape[1]
+    sh = Shape(B, Hq, Hkv, n, D, _dtype_code(q))
+    ha, hn = _heads(heads)
+    nh = Hq if heads is None else hn
+    o = torch.zeros_like(q) if out is None else out
+    if keys is not None:
+        if keys.dtype != torch.int32 or n_keys is None or n_keys.dtype != torch.int32:
+            raise ValueError("keys and n_keys must be int32 tensors")
+        if keys.dim() != 2 or keys.shape[0] != B * nh or n_keys.numel() != B * nh:
+            raise ValueError("keys must be [batch * n_heads, max_keys], n_keys [batch * n_heads]")
+        kp, mk, nkp = _dev(keys, "keys"), keys.shape[1], _dev(n_keys, "n_keys")
+    else:
+        kp, mk, nkp = None, -1, None
+    ws = _workspace(load().dsa_sparse_decode_workspace_bytes(ctypes.byref(sh), mk, nh), q.device)
+    _call("dsa_sparse_decode", _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(o, "out"),
+          ctypes.byref(sh), _scale(scale), ha, hn, kp, max(mk, 0), nkp, ws.data_ptr(), ws.numel(),
+          _stream(q))
+    return o
 
 
 def topk(scores: torch.Tensor, k: int, forced_index: int = -1) -> torch.Tensor:

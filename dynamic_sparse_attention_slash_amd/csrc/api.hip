@@ -256,6 +256,39 @@ dsa_status dsa_kv_retention(const void* q, const void* k, const dsa_shape* shape
   return hip_status(e);
 }
 
+// ------------------------------------------------------------------ decode
+size_t dsa_sparse_decode_workspace_bytes(const dsa_shape* shape, int32_t max_keys, int32_t n_heads) {
+  if (check_shape(shape) != DSA_OK || n_heads < 0 || max_keys < -1) return 0;
+  const int32_t mk = max_keys < 0 ? shape->seq_len : max_keys;
+  return decode_workspace_bytes(shape->batch * n_heads, mk, shape->head_dim);
+}
+
+dsa_status dsa_sparse_decode(const void* q, const void* k, const void* v, void* o,
+                             const dsa_shape* shape, float scale, const int32_t* heads, int32_t n_heads,
+                             const int32_t* keys, int32_t max_keys, const int32_t* n_keys,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
+  if (keys && (max_keys < 0 || !n_keys)) return DSA_ERR_INVALID_ARG;
+  HeadMap hm;
+  if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  const int32_t rows = shape->batch * hm.n;
+  const size_t need = dsa_sparse_decode_workspace_bytes(shape, keys ? max_keys : -1, hm.n);
+  if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
+  if (rows == 0) return DSA_OK;
+  // an empty cache or empty lists still run: the rows come out as zeros
+  DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.n = shape->seq_len; a.head_dim = shape->head_dim; a.dtype = shape->dtype; a.rows = rows;
+  a.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
+  a.hm = hm;
+  a.wo = make_work_order(hm);
+  a.keys = keys; a.max_keys = keys ? max_keys : 0; a.n_keys = n_keys;
+  a.part = static_cast<float*>(workspace);
+  return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t dsa_topk_workspace_bytes(int32_t rows, int32_t n, int32_t k) {
   if (rows < 0 || n < 0 || k < 0) return 0;
   return topk_workspace_bytes(rows, n, k);

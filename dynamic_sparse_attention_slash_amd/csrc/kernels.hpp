@@ -105,6 +105,24 @@ hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s);
 // rows (the first slice writes v, the others add), no slash scores
 hipError_t launch_window_column_scores(EstArgs a, int32_t window, hipStream_t s);
 
+// ---- sparse decode (decode.hip) ----
+struct DecodeArgs {
+  const void* q; const void* k; const void* v; void* o;  // q, o: [batch][q_heads][1][D]
+  int32_t n, head_dim, dtype, rows;   // n: cached keys
+  int32_t splits, split_keys;         // set by launch_decode
+  int32_t bundles_per_batch;          // whole cache: head bundles per batch (set by launch_decode)
+  float scale_log2;
+  HeadMap hm;
+  WorkOrder wo;
+  const int32_t* keys;    // [rows][max_keys] cache positions, or NULL for all n
+  int32_t max_keys;
+  const int32_t* n_keys;  // [rows]
+  float* part;            // [rows][splits][2 + D]: (max, sum, output) per split
+};
+int32_t decode_splits(int32_t rows, int32_t max_keys, int32_t& split_keys);
+size_t decode_workspace_bytes(int32_t rows, int32_t max_keys, int32_t head_dim);
+hipError_t launch_decode(DecodeArgs a, hipStream_t s);
+
 // ---- top-k (topk.hip) ----
 // scratch of launch_topk_rows (0 when the rows are short enough for one pass)
 size_t topk_workspace_bytes(int32_t rows, int32_t n, int32_t k);

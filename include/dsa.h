@@ -229,6 +229,30 @@ dsa_status dsa_kv_retention(const void* q, const void* k, const dsa_shape* shape
 size_t dsa_kv_retention_workspace_bytes(const dsa_shape* shape, int32_t keep,
                                         int32_t n_heads);
 
+/* Sparse decode attention [Novita §2: decoding attends only to the KV entries
+ * a head kept; MInf §1: attention over a key set, other keys excluded]. One
+ * new query row per listed head attends over cached keys:
+ *   o[row] = sum over j in K(row) of softmax_j(scale * q[row] . k[j]) v[j]
+ * with K(row) = keys[row][0 .. n_keys[row]) (cache positions; entries are
+ * clamped into [0, seq_len) and should be distinct), or every cached key when
+ * keys is NULL. The decode row comes after the whole cache, so no causal cut
+ * applies; an empty key set gives zeros. Layout: q and o are device
+ * [batch][q_heads][head_dim] (one row per head), k and v the cache as
+ * [batch][kv_heads][seq_len][head_dim] with seq_len = cached keys; keys
+ * device int32 [batch * n_heads][max_keys], n_keys device int32
+ * [batch * n_heads]. Only listed heads of o are written. The list is cut into
+ * splits over work-groups whose partial (max, sum, output) are merged in split
+ * order, so results are bit-reproducible. workspace: at least
+ * dsa_sparse_decode_workspace_bytes(shape, max_keys, n_heads) bytes, with
+ * max_keys = -1 when keys is NULL. */
+dsa_status dsa_sparse_decode(const void* q, const void* k, const void* v, void* o,
+                             const dsa_shape* shape, float scale, const int32_t* heads,
+                             int32_t n_heads, const int32_t* keys, int32_t max_keys,
+                             const int32_t* n_keys, void* workspace, size_t workspace_bytes,
+                             void* stream);
+size_t dsa_sparse_decode_workspace_bytes(const dsa_shape* shape, int32_t max_keys,
+                                         int32_t n_heads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,11 @@ R7  Streaming / A-shape [MInf usage listing, streaming_forward(init_num,
     (c < init_blocks or a - c < local_blocks); the local window counts the
     diagonal block.
 R8  GQA: query head h reads kv head h // (q_heads / kv_heads).
+R10 Sparse decode [Novita §2: decoding uses only the kept KV entries; MInf §1]:
+    one new query row per head, placed after the whole cache, attends over a
+    set of cached key positions (every position when none is given) with the
+    softmax of R1; an empty set gives zeros. Each head has its own set (GQA
+    heads share the cache, not the set).
 R9  KV retention [Novita §2, the PyramidKV score; the formula itself is lost
     from the page text]: a key's retention score is the sum of its softmax
     probabilities over the window of the last ``window`` query rows (each row
@@ -212,6 +217,17 @@ def kv_retention_scores(q: np.ndarray, k: np.ndarray, window: int, scale: float)
         e = np.exp(lr - lr.max())
         S[: i + 1] += e / e.sum()
     return S
+
+
+def decode_attention(q_row, k, v, keys=None, scale: float | None = None) -> np.ndarray:
+    """One decode row over the cached keys ``keys`` (all when None), float64
+    [D] (R10): the masked attention of R1 for a row after the whole cache."""
+    k = f64(k)
+    v = f64(v)
+    n = k.shape[0]
+    scale = default_scale(k.shape[1]) if scale is None else scale
+    keys = np.arange(n) if keys is None else np.asarray(keys, dtype=np.int64)
+    return masked_attention(f64(q_row)[None, :], np.array([n]), keys, k, v, scale)[0]
 
 
 def kv_retention(q, k, window: int, keep: int, scale: float | None = None

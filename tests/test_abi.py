@@ -118,6 +118,15 @@ def test_other_argument_errors(lib):
     assert kv(64, 4, wsb=8) == WORKSPACE
     assert lib.dsa_kv_retention_workspace_bytes(ctypes.byref(sh), 4, 4) > 0
     assert lib.dsa_kv_retention_workspace_bytes(ctypes.byref(sh), -1, 4) == 0
+    # sparse decode: q/k/v/o required, a key list needs its counts and a width >= 0
+    dec = lambda keys=None, mk=0, nk=None, wsb=1 << 40, q=P: lib.dsa_sparse_decode(
+        q, P, P, P, ctypes.byref(sh), 0.0, None, 0, keys, mk, nk, P, wsb, None)
+    assert dec(q=None) == INVALID
+    assert dec(keys=P, mk=4, nk=None) == INVALID
+    assert dec(keys=P, mk=-1, nk=P) == INVALID
+    assert dec(wsb=8) == WORKSPACE
+    assert lib.dsa_sparse_decode_workspace_bytes(ctypes.byref(sh), -1, 4) > 0
+    assert lib.dsa_sparse_decode_workspace_bytes(ctypes.byref(sh), -2, 4) == 0
     many = (ctypes.c_int32 * 300)(*range(300))
     big = shape(hq=300, hkv=300)
     assert lib.dsa_streaming_attention(P, P, P, P, ctypes.byref(big), 1, 1, 0.0, many, 300, None) == UNSUPPORTED

@@ -395,6 +395,74 @@ def test_kv_retention_128k_planted():
         assert 0 in kt
 
 
+@pytest.mark.parametrize("n,D,dt,counts", [(10000, 128, "bf16", [0, 1, 7, 100, 5000, 257]),
+                                           (777, 64, "f32", [3, 777, 64, 0, 500, 31]),
+                                           (4096, 128, "bf16", None), (1, 64, "bf16", None),
+                                           (300, 128, "f32", None), (70000, 128, "bf16", None)])
+def test_sparse_decode(n, D, dt, counts):
+    """One decode row per listed head over a key list (or the whole cache)
+    against the oracle on the attention bar; unlisted heads stay zero."""
+    say(f"sparse decode n={n} D={D} {dt} counts={counts}")
+    B, Hq, Hkv, heads = 2, 4, 2, [3, 0, 2]
+    g = torch.Generator().manual_seed(n + D)
+    q = (torch.randn(B, Hq, D, generator=g) * 2.0).to(DT[dt]).cuda()
+    k = torch.randn(B, Hkv, n, D, generator=g).to(DT[dt]).cuda()
+    v = torch.randn(B, Hkv, n, D, generator=g).to(DT[dt]).cuda()
+    rng = np.random.default_rng(n)
+    lists = None
+    if counts is None:
+        o = dsa.sparse_decode(q, k, v, heads=heads)
+    else:
+        width = max(counts) + 3
+        keys = np.full((B * len(heads), width), -7, np.int32)   # entries past a count are never read
+        lists = []
+        for r, c in enumerate(counts):
+            sel = np.sort(rng.choice(n, size=min(c, n), replace=False)).astype(np.int32)
+            keys[r, : len(sel)] = sel
+            lists.append(sel)
+        n_keys = torch.tensor([len(x) for x in lists], dtype=torch.int32).cuda()
+        o = dsa.sparse_decode(q, k, v, torch.from_numpy(keys).cuda(), n_keys, heads=heads)
+    torch.cuda.synchronize()
+    qh, kh, vh, oh = host64(q), host64(k), host64(v), host64(o)
+    sc = 1.0 / math.sqrt(D)
+    for b in range(B):
+        for t, h in enumerate(heads):
+            r = b * len(heads) + t
+            want = O.decode_attention(qh[b, h], kh[b, kvh(h, Hq, Hkv)], vh[b, kvh(h, Hq, Hkv)],
+                                      None if lists is None else lists[r], sc)
+            check_attention(oh[b, h][None], want[None], f"decode b{b} h{h}")
+        assert not oh[b, 1].any()
+
+
+def test_decode_over_retained_keys_1m():
+    """The after-prefill chain at 1M tokens: retention scores over the last
+    256 rows keep 4096 keys per head, then a new row decodes over exactly
+    those keys; checked against the oracle (scores of the kept set, attention
+    over it), and decoding over all keys is checked too."""
+    say("decode over retained keys 1M")
+    w = synthetic.BY_NAME["llama3_8b_1m_mixed_bf16"].scaled(q_heads=4, kv_heads=1)
+    x = synthetic.make_inputs(w, device="cuda")
+    heads = [1, 2]
+    sc_, kept = dsa.kv_retention(x.q, x.k, 256, 4096, heads=heads)
+    g = torch.Generator().manual_seed(5)
+    qd = torch.randn(1, 4, w.head_dim, generator=g).to(torch.bfloat16).cuda()
+    n_keys = torch.full((2,), 4096, dtype=torch.int32, device="cuda")
+    o = dsa.sparse_decode(qd, x.k, x.v, kept, n_keys, heads=heads)
+    o_all = dsa.sparse_decode(qd, x.k, x.v, heads=heads)
+    torch.cuda.synchronize()
+    kh = x.k[0, 0].float().cpu().numpy().astype(np.float64)
+    vh = x.v[0, 0].float().cpu().numpy().astype(np.float64)
+    qh = host64(qd)
+    sc = 1.0 / math.sqrt(w.head_dim)
+    for t, h in enumerate(heads):
+        kt = kept[t].cpu().numpy()
+        assert np.array_equal(kt, O.topk_indices(sc_[t].cpu().numpy(), 4096))
+        want = O.decode_attention(qh[0, h], kh, vh, kt, sc)
+        check_attention(host64(o)[0, h][None], want[None], f"decode retained h{h}")
+        want_all = O.decode_attention(qh[0, h], kh, vh, None, sc)
+        check_attention(host64(o_all)[0, h][None], want_all[None], f"decode all h{h}")
+
+
 def test_repeat_launch_bitwise():
     """Two launches on the same inputs give the same bits for every pattern: a
     kernel that read an MFMA result before it is complete, or raced on LDS,

@@ -198,6 +198,37 @@ def test_kv_retention_keeps_heaviest_keys():
 
 
 # ---------------------------------------------------------------------------
+# sparse decode (one row after the whole cache)
+# ---------------------------------------------------------------------------
+def test_decode_bruteforce_and_sdpa():
+    """A key subset matches the pure-Python brute force; the whole cache
+    matches torch's scaled_dot_product_attention (float64, no mask)."""
+    q, k, v = rnd(300, 16, 21)
+    qd = 2.0 * q[0]
+    keys = np.array([0, 3, 17, 100, 101, 250, 299])
+    got = O.decode_attention(qd, k, v, keys, 0.3)
+    Q = np.vstack([k, qd[None, :]])                       # row 300 sees keys 0..299
+    bf = bf_attention(Q.tolist(), np.vstack([k, k[:1]]).tolist(), np.vstack([v, v[:1]]).tolist(), 0.3,
+                      lambda i, j: i == 300 and j in set(keys.tolist()))
+    np.testing.assert_allclose(got, bf[300], rtol=1e-12, atol=1e-14)
+    full = O.decode_attention(qd, k, v, None, 0.25)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(qd)[None, None, None], torch.tensor(k)[None, None], torch.tensor(v)[None, None],
+        scale=0.25)[0, 0, 0].numpy()
+    np.testing.assert_allclose(full, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_decode_closed_forms():
+    """One key gives its value row; q = 0 gives the mean of the listed
+    value rows; no key gives zeros."""
+    _, k, v = rnd(50, 8, 22)
+    np.testing.assert_allclose(O.decode_attention(np.ones(8), k, v, [7], 0.5), v[7], rtol=1e-15)
+    keys = [1, 4, 9, 30]
+    np.testing.assert_allclose(O.decode_attention(np.zeros(8), k, v, keys, 0.5), v[keys].mean(0), rtol=1e-13)
+    assert not O.decode_attention(np.ones(8), k, v, [], 0.5).any()
+
+
+# ---------------------------------------------------------------------------
 # top-k
 # ---------------------------------------------------------------------------
 def test_topk_bruteforce_random():
