@@ -70,7 +70,17 @@ struct Tile<uint16_t, D> {
       for (int s = 0; s < DS; ++s) acc = mfma_bf16(qop[qb][s], kop[s], acc);
       out[qb] = acc;
     }
-    mask(out, j0 + l16, w, scale_log2);
+    finish(out, j0, l16, w, scale_log2);
+  }
+  // scale, and mask only a step that reaches the window's first row (or a
+  // window of fewer than 64 rows): earlier keys precede every window row
+  __device__ static void finish(f32x4 (&x)[4], int32_t j0, int32_t l16, const Window& w, float scale_log2) {
+    if (j0 + 15 <= w.start && w.lq == 64) {
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) x[qb] *= scale_log2;
+    } else {
+      mask(x, j0 + l16, w, scale_log2);
+    }
   }
   __device__ static void mask(f32x4 (&x)[4], int32_t key, const Window& w, float scale_log2) {
     const int32_t g = threadIdx.x >> 4;
@@ -120,7 +130,7 @@ struct Tile<float, D> {
       for (int s = 0; s < DK; ++s) acc = mfma_f32(qop[qb][s], kop[s], acc);
       out[qb] = acc;
     }
-    Tile<uint16_t, D>::mask(out, j0 + l16, w, scale_log2);
+    Tile<uint16_t, D>::finish(out, j0, l16, w, scale_log2);
   }
 };
 
