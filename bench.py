@@ -5,7 +5,10 @@ A step runs the whole path for every head of the layer: vertical-slash heads
 (estimate, top-k, sparse format, attention), block-sparse heads (pooling,
 block selection, attention) and streaming heads (attention), each call over
 its head subset, all writing one output tensor, on one stream. Inputs are
-seeded synthetic tensors resident in HBM before timing starts.
+seeded synthetic tensors resident in HBM before timing starts. A layer with
+more than one pattern is also timed through the mixed call (the same index
+stages, then every head's attention in one launch) and reported as
+`one_launch`.
 
 Default workload: the 1M-token Llama-3-8B-shaped mixed layer (the named
 workload that runs every step of the path); the 128K layer is timed beside it.
@@ -126,7 +129,8 @@ class Layer:
         self.o = torch.zeros_like(self.q)
         all_vs = len(x.heads["vs"]) == w.q_heads
         self.vs_heads = None if all_vs else x.heads["vs"]
-        self.ws_vs = self.ws_bs = None
+        self.ws_vs = self.ws_bs = self.ws_mixed = None
+        self.patterns = synthetic.pattern_list(w)
         if x.heads["vs"]:
             nbytes = dsa.vertical_slash_workspace_bytes(self.q, self.k, w.vertical_topk, w.slash_topk,
                                                         self.vs_heads)
@@ -147,6 +151,19 @@ class Layer:
         if x.heads["st"]:
             dsa.streaming_attention(self.q, self.k, self.v, w.init_blocks, w.local_blocks,
                                     heads=x.heads["st"], out=self.o)
+
+    def one_launch(self):
+        """The same layer through the mixed call: every head's attention in one
+        launch (index stages as above)."""
+        w = self.w
+        if self.ws_mixed is None:
+            nbytes = dsa.mixed_workspace_bytes(self.q, self.k, self.patterns, w.vertical_topk,
+                                               w.slash_topk, w.topk)
+            self.ws_mixed = torch.empty(max(1, nbytes), dtype=torch.uint8, device=self.q.device)
+        return lambda: dsa.mixed_sparse_attention(
+            self.q, self.k, self.v, self.patterns, vertical_topk=w.vertical_topk, slash_topk=w.slash_topk,
+            topk=w.topk, init_blocks=w.init_blocks, local_blocks=w.local_blocks, last_q=w.last_q,
+            out=self.o, workspace=self.ws_mixed)
 
 
 def time_events(fn, reps):
@@ -450,6 +467,12 @@ def run_layer(w, steps, warmup, with_cpu):
         "flops_dense_causal": dense, "density_vs_dense": f_total / dense,
         "stages_ms": st,
     }
+    if sum(1 for p in ("vs", "bs", "st") if x.heads[p]) > 1:
+        one = layer.one_launch()
+        ms1 = time_events(one, steps)
+        res["one_launch"] = {"ms_per_layer": ms1, "tflops": f_total / (ms1 * 1e-3) / 1e12,
+                             "vs_three_calls": ms / ms1}
+        log(f"[bench] {w.name}: one-launch mixed layer {ms1:.3f} ms")
     sb = stage_bytes(w, x, idx)
     res["stages_hbm"] = {k.replace("_ms", ""): {"bytes": v, "gbs": v / (st[k] * 1e-3) / 1e9,
                                                 "frac_hbm": v / (st[k] * 1e-3) / 1e9 / PEAK_HBM_GBS}
@@ -531,6 +554,7 @@ def main():
         "stages_hbm": {k: {kk: (round(vv, 4) if kk != "bytes" else vv) for kk, vv in v.items()}
                        for k, v in prim["stages_hbm"].items()},
         "after_prefill": prim.get("after_prefill"),
+        "one_launch": prim.get("one_launch"),
         "roofline": prim.get("roofline"),
     }
     if "cpu_baseline" in prim:

@@ -1,7 +1,8 @@
 """Dynamic sparse attention for the long-context prefill phase on MI355X.
 
 Vertical-slash, block-sparse and streaming (A-shape) heads, each as online
-sparse-index estimation followed by exact block-sparse attention, and the
+sparse-index estimation followed by exact block-sparse attention (per pattern,
+or a whole mixed layer with one attention launch), and the
 KV-retention scores and kept keys that follow prefill, all in HIP kernels for
 gfx950 behind a C ABI (include/dsa.h). This package is the thin
 Python binding of that library; torch supplies device memory and streams.
@@ -15,7 +16,10 @@ from ._binding import (  # noqa: F401
     bs_select,
     kv_retention,
     load,
+    mixed_sparse_attention,
+    mixed_workspace_bytes,
     sparse_attention_blocks,
+    sparse_attention_mixed,
     sparse_attention_vs,
     sparse_decode,
     streaming_attention,

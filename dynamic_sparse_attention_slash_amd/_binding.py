@@ -62,6 +62,9 @@ _SIGS = {
     "dsa_bs_select_workspace_bytes": ([_i32, _i32], _sz),
     "dsa_sparse_attention_vs": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _f32, _ip, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp], _i32),
     "dsa_sparse_attention_blocks": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _f32, _ip, _i32, _vp, _vp, _i32, _vp], _i32),
+    "dsa_mixed_sparse_attention": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _ip, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp], _i32),
+    "dsa_mixed_sparse_attention_workspace_bytes": ([ctypes.POINTER(Shape), _ip, _i32, _i32, _i32], _sz),
+    "dsa_sparse_attention_mixed": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _f32, _ip, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp], _i32),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -209,6 +212,45 @@ def streaming_attention(q, k, v, init_blocks: int, local_blocks: int, *,
     ha, hn = _heads(heads)
     _call("dsa_streaming_attention", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
           ctypes.byref(sh), init_blocks, local_blocks, _scale(scale), ha, hn, _stream(q))
+    return o
+
+
+PATTERN_CODES = {None: -1, "vs": 0, "bs": 1, "st": 2}
+
+
+def _patterns(patterns: Sequence[Optional[str]], q_heads: int) -> ctypes.Array:
+    """Per-query-head pattern names ("vs", "bs", "st" or None) -> int32 array."""
+    if len(patterns) != q_heads:
+        raise ValueError(f"patterns must name one pattern per query head ({q_heads})")
+    try:
+        codes = [PATTERN_CODES[p] for p in patterns]
+    except KeyError as e:
+        raise ValueError(f"unknown pattern {e.args[0]!r}; use 'vs', 'bs', 'st' or None") from None
+    return (ctypes.c_int32 * q_heads)(*codes)
+
+
+def mixed_workspace_bytes(q, k, patterns: Sequence[Optional[str]], vertical_topk: int,
+                          slash_topk: int, topk: int) -> int:
+    sh = Shape(q.shape[0], q.shape[1], k.shape[1], q.shape[2], q.shape[3], _dtype_code(q))
+    return int(load().dsa_mixed_sparse_attention_workspace_bytes(
+        ctypes.byref(sh), _patterns(patterns, sh.q_heads), vertical_topk, slash_topk, topk))
+
+
+def mixed_sparse_attention(q, k, v, patterns: Sequence[Optional[str]], *, vertical_topk: int,
+                           slash_topk: int, topk: int, init_blocks: int, local_blocks: int,
+                           last_q: int = 64, scale: Optional[float] = None,
+                           out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A layer whose query head h follows patterns[h]; every head's attention
+    runs in one launch (heads with pattern None are left untouched in out)."""
+    sh = _shape_qkv(q, k, v)
+    o = _out_like(q, out)
+    pa = _patterns(patterns, sh.q_heads)
+    ws = _workspace(load().dsa_mixed_sparse_attention_workspace_bytes(
+        ctypes.byref(sh), pa, vertical_topk, slash_topk, topk), q.device, workspace)
+    _call("dsa_mixed_sparse_attention", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
+          ctypes.byref(sh), pa, vertical_topk, slash_topk, last_q, topk, init_blocks, local_blocks,
+          _scale(scale), ws.data_ptr(), ws.numel(), _stream(q))
     return o
 
 
@@ -371,4 +413,30 @@ def sparse_attention_blocks(q, k, v, sel, n_sel, *, scale: Optional[float] = Non
     _call("dsa_sparse_attention_blocks", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
           ctypes.byref(sh), _scale(scale), ha, hn, _dev(sel, "sel", torch.int32),
           _dev(n_sel, "n_sel", torch.int32), sel.shape[2], _stream(q))
+    return o
+
+
+def sparse_attention_mixed(q, k, v, patterns: Sequence[Optional[str]], *, vs_index=None, bs_index=None,
+                           init_blocks: int = 1, local_blocks: int = 1, scale: Optional[float] = None,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The one-launch attention over given indices: vs_index = (intervals,
+    n_intervals, cols, n_cols) for the VS heads in ascending order, bs_index =
+    (sel, n_sel) for the BS heads in ascending order."""
+    sh = _shape_qkv(q, k, v)
+    o = _out_like(q, out)
+    pa = _patterns(patterns, sh.q_heads)
+    iv = niv = cols = ncols = sel = nsel = None
+    max_iv = max_cols = max_sel = 0
+    if vs_index is not None:
+        intervals, n_intervals, c, nc = vs_index
+        iv, niv = _dev(intervals, "intervals", torch.int32), _dev(n_intervals, "n_intervals", torch.int32)
+        cols, ncols = _dev(c, "cols", torch.int32), _dev(nc, "n_cols", torch.int32)
+        max_iv, max_cols = intervals.shape[1], c.shape[2]
+    if bs_index is not None:
+        s_, ns = bs_index
+        sel, nsel = _dev(s_, "sel", torch.int32), _dev(ns, "n_sel", torch.int32)
+        max_sel = s_.shape[2]
+    _call("dsa_sparse_attention_mixed", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
+          ctypes.byref(sh), _scale(scale), pa, iv, niv, max_iv, cols, ncols, max_cols, sel, nsel,
+          max_sel, init_blocks, local_blocks, _stream(q))
     return o

@@ -153,6 +153,84 @@ hipError_t bs_select_rows(const float* qp, const float* kp, int32_t rows, int32_
   return hipSuccess;
 }
 
+
+// vertical-slash index of the heads of hm: scores, the two top-k, the sparse
+// format, into w (laid out by vs_layout for batch * hm.n rows)
+hipError_t vs_index_stages(const void* q, const void* k, const dsa_shape* shape, int32_t vk, int32_t sk,
+                           int32_t last_q, float scale, const HeadMap& hm, const VsWork& w, hipStream_t s) {
+  const int32_t rows = shape->batch * hm.n, n = shape->seq_len;
+  EstArgs ea;
+  ea.q = q; ea.k = k;
+  ea.seq_len = n; ea.head_dim = shape->head_dim; ea.dtype = shape->dtype;
+  ea.last_q = last_q; ea.rows = rows;
+  ea.win_start = ea.seq_len - ea.lq_eff(); ea.add_v = 0; ea.want_s = 1;
+  ea.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
+  ea.hm = hm;
+  ea.wo = make_work_order(hm);
+  ea.v_scores = w.v; ea.s_scores = w.s;
+  est_carve(ea, w.est);
+  hipError_t e = launch_vs_estimate(ea, s);
+  if (e == hipSuccess) e = launch_topk_rows(w.v, rows, n, vk, -1, w.V, w.tk, s);
+  if (e == hipSuccess) e = launch_topk_rows(w.s, rows, n, sk, 0, w.S, w.tk, s);
+  if (e == hipSuccess) e = launch_vs_build_index(w.V, vk, w.S, sk, rows, n, w.iv, w.n_iv, w.cols, w.n_cols, s);
+  return e;
+}
+
+// block-sparse index of the heads of hm: pooled Q and K, block logits and the
+// per-block top-k, into w (laid out by bs_layout for batch * hm.n rows)
+hipError_t bs_index_stages(const void* q, const void* k, const dsa_shape* shape, int32_t topk, float scale,
+                           const HeadMap& hm, const BsWork& w, hipStream_t s) {
+  const int32_t rows = shape->batch * hm.n, n = shape->seq_len, nb = nblocks(n), D = shape->head_dim;
+  // pooled K for every kv head the listed heads read
+  HeadMap kvm;
+  memset(&kvm, 0, sizeof(kvm));
+  kvm.q_heads = kvm.kv_heads = shape->kv_heads;
+  kvm.n = shape->kv_heads;
+  for (int32_t i = 0; i < kvm.n; ++i) kvm.h[i] = i;
+  hipError_t e = launch_pool(q, shape->dtype, n, D, rows, hm, w.qp, s);
+  if (e == hipSuccess) e = launch_pool(k, shape->dtype, n, D, shape->batch * kvm.n, kvm, w.kp, s);
+  if (e == hipSuccess)
+    e = bs_select_rows(w.qp, w.kp, rows, nb, D, eff_scale(scale, D), topk, true, hm, w.logits, false,
+                       w.sel, w.n_sel, s);
+  return e;
+}
+
+// patterns[q_heads] -> the map of every processed head (ascending), the maps
+// of the VS and BS heads and each head's pattern and position in its list
+dsa_status parse_patterns(const dsa_shape* shape, const int32_t* patterns, HeadMap& all, HeadMap& vs,
+                          HeadMap& bs, MixedIndex& ix) {
+  if (!patterns) return DSA_ERR_INVALID_ARG;
+  if (shape->q_heads > MAX_HEADS) return DSA_ERR_UNSUPPORTED;
+  int32_t lists[3][MAX_HEADS], counts[3] = {0, 0, 0}, listed[MAX_HEADS], n_listed = 0;
+  memset(&ix, 0, sizeof(ix));
+  for (int32_t h = 0; h < shape->q_heads; ++h) {
+    const int32_t p = patterns[h];
+    if (p == DSA_PATTERN_NONE) continue;
+    if (p != DSA_PATTERN_VS && p != DSA_PATTERN_BS && p != DSA_PATTERN_STREAM) return DSA_ERR_INVALID_ARG;
+    const int8_t kind = p == DSA_PATTERN_VS ? PAT_VS : p == DSA_PATTERN_BS ? PAT_BS : PAT_STREAM;
+    ix.kind[n_listed] = kind;
+    ix.slot[n_listed] = (int16_t)counts[kind];
+    lists[kind][counts[kind]++] = h;
+    listed[n_listed++] = h;
+  }
+  dsa_status st = make_map(shape->q_heads, shape->kv_heads, listed, n_listed, all);
+  if (st == DSA_OK) st = make_map(shape->q_heads, shape->kv_heads, lists[PAT_VS], counts[PAT_VS], vs);
+  if (st == DSA_OK) st = make_map(shape->q_heads, shape->kv_heads, lists[PAT_BS], counts[PAT_BS], bs);
+  ix.n_vs = counts[PAT_VS];
+  ix.n_bs = counts[PAT_BS];
+  return st;
+}
+
+size_t mixed_layout(const dsa_shape* shape, int32_t n_vs, int32_t n_bs, int32_t vk, int32_t sk, int32_t topk,
+                    void* base, VsWork* vw, BsWork* bw) {
+  const int32_t n = shape->seq_len;
+  const size_t vbytes = n_vs ? vs_layout(shape->batch * n_vs, n, vk, sk, nullptr, nullptr) : 0;
+  if (vw && n_vs) vs_layout(shape->batch * n_vs, n, vk, sk, base, vw);
+  char* bbase = base ? static_cast<char*>(base) + vbytes : nullptr;
+  const size_t bbytes = n_bs ? bs_layout(shape, shape->batch * n_bs, topk, nullptr, nullptr) : 0;
+  if (bw && n_bs) bs_layout(shape, shape->batch * n_bs, topk, bbase, bw);
+  return vbytes + bbytes;
+}
 }  // namespace
 
 namespace dsa {
@@ -167,6 +245,21 @@ WorkOrder make_work_order(const HeadMap& hm) {
       if (hm.h[t] / G == kv) wo.order[pos++] = (int16_t)t;
     if (pos > start) wo.gstart[wo.n_groups++] = (int16_t)start;
   }
+  wo.gstart[wo.n_groups] = (int16_t)pos;
+  return wo;
+}
+WorkOrder make_work_order(const HeadMap& hm, const int8_t* kind) {
+  WorkOrder wo;
+  memset(&wo, 0, sizeof(wo));
+  const int32_t G = hm.q_heads / hm.kv_heads;
+  int32_t pos = 0;
+  for (int8_t pat : {PAT_VS, PAT_BS, PAT_STREAM})
+    for (int32_t kv = 0; kv < hm.kv_heads; ++kv) {
+      const int32_t start = pos;
+      for (int32_t t = 0; t < hm.n; ++t)
+        if (kind[t] == pat && hm.h[t] / G == kv) wo.order[pos++] = (int16_t)t;
+      if (pos > start) wo.gstart[wo.n_groups++] = (int16_t)start;
+    }
   wo.gstart[wo.n_groups] = (int16_t)pos;
   return wo;
 }
@@ -367,20 +460,7 @@ dsa_status dsa_vertical_slash_sparse_attention(const void* q, const void* k, con
   VsWork w;
   vs_layout(rows, n, vk, sk, workspace, &w);
 
-  EstArgs ea;
-  ea.q = q; ea.k = k;
-  ea.seq_len = n; ea.head_dim = shape->head_dim; ea.dtype = shape->dtype;
-  ea.last_q = last_q; ea.rows = rows;
-  ea.win_start = ea.seq_len - ea.lq_eff(); ea.add_v = 0; ea.want_s = 1;
-  ea.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
-  ea.hm = hm;
-  ea.wo = make_work_order(hm);
-  ea.v_scores = w.v; ea.s_scores = w.s;
-  est_carve(ea, w.est);
-  hipError_t e = launch_vs_estimate(ea, s);
-  if (e == hipSuccess) e = launch_topk_rows(w.v, rows, n, vk, -1, w.V, w.tk, s);
-  if (e == hipSuccess) e = launch_topk_rows(w.s, rows, n, sk, 0, w.S, w.tk, s);
-  if (e == hipSuccess) e = launch_vs_build_index(w.V, vk, w.S, sk, rows, n, w.iv, w.n_iv, w.cols, w.n_cols, s);
+  hipError_t e = vs_index_stages(q, k, shape, vk, sk, last_q, scale, hm, w, s);
   if (e == hipSuccess) {
     AttnArgs a = attn_args(q, k, v, o, shape, scale, hm);
     e = launch_attention_vs(a, VsIndex{w.iv, w.n_iv, sk, w.cols, w.n_cols, vk}, s);
@@ -454,24 +534,14 @@ dsa_status dsa_block_sparse_attention(const void* q, const void* k, const void* 
   if (!q || !k || !v || !o || topk < 1) return DSA_ERR_INVALID_ARG;
   HeadMap hm;
   if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
-  const int32_t rows = shape->batch * hm.n, n = shape->seq_len, nb = nblocks(n), D = shape->head_dim;
+  const int32_t rows = shape->batch * hm.n, n = shape->seq_len, nb = nblocks(n);
   const size_t need = bs_layout(shape, rows, topk, nullptr, nullptr);
   if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
   if (rows == 0 || n == 0) return DSA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   BsWork w;
   bs_layout(shape, rows, topk, workspace, &w);
-  // pooled K for every kv head the listed heads read
-  HeadMap kvm;
-  memset(&kvm, 0, sizeof(kvm));
-  kvm.q_heads = kvm.kv_heads = shape->kv_heads;
-  kvm.n = shape->kv_heads;
-  for (int32_t i = 0; i < kvm.n; ++i) kvm.h[i] = i;
-  hipError_t e = launch_pool(q, shape->dtype, n, D, rows, hm, w.qp, s);
-  if (e == hipSuccess) e = launch_pool(k, shape->dtype, n, D, shape->batch * kvm.n, kvm, w.kp, s);
-  if (e == hipSuccess)
-    e = bs_select_rows(w.qp, w.kp, rows, nb, D, eff_scale(scale, D), topk, true, hm, w.logits, false,
-                       w.sel, w.n_sel, s);
+  hipError_t e = bs_index_stages(q, k, shape, topk, scale, hm, w, s);
   if (e == hipSuccess) {
     const int32_t ke = topk < nb ? topk : nb;
     e = launch_attention_blocks(attn_args(q, k, v, o, shape, scale, hm), BlockIndex{w.sel, w.n_sel, ke}, s);
@@ -492,6 +562,84 @@ dsa_status dsa_streaming_attention(const void* q, const void* k, const void* v, 
   if (a.rows == 0 || a.seq_len == 0) return DSA_OK;
   return hip_status(launch_attention_stream(a, StreamIndex{init_blocks, local_blocks},
                                             static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ mixed layer
+size_t dsa_mixed_sparse_attention_workspace_bytes(const dsa_shape* shape, const int32_t* patterns,
+                                                  int32_t vertical_topk, int32_t slash_topk, int32_t topk) {
+  if (check_shape(shape) != DSA_OK || vertical_topk < 0 || slash_topk < 1 || topk < 1) return 0;
+  HeadMap all, vs, bs;
+  MixedIndex ix;
+  if (parse_patterns(shape, patterns, all, vs, bs, ix) != DSA_OK) return 0;
+  const int32_t n = shape->seq_len;
+  return mixed_layout(shape, ix.n_vs, ix.n_bs, vertical_topk < n ? vertical_topk : n,
+                      slash_topk < n ? slash_topk : n, topk, nullptr, nullptr, nullptr);
+}
+
+dsa_status dsa_mixed_sparse_attention(const void* q, const void* k, const void* v, void* o,
+                                      const dsa_shape* shape, const int32_t* patterns, int32_t vertical_topk,
+                                      int32_t slash_topk, int32_t last_q, int32_t topk, int32_t init_blocks,
+                                      int32_t local_blocks, float scale, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
+  if (vertical_topk < 0 || slash_topk < 1 || topk < 1 || init_blocks < 0 || local_blocks < 1)
+    return DSA_ERR_INVALID_ARG;
+  if (last_q < 1 || last_q > 64) return DSA_ERR_UNSUPPORTED;
+  HeadMap all, vs, bs;
+  MixedIndex ix;
+  if ((st = parse_patterns(shape, patterns, all, vs, bs, ix)) != DSA_OK) return st;
+  const int32_t n = shape->seq_len, nb = nblocks(n);
+  const int32_t vk = vertical_topk < n ? vertical_topk : n;
+  const int32_t sk = slash_topk < n ? slash_topk : n;
+  const size_t need = mixed_layout(shape, ix.n_vs, ix.n_bs, vk, sk, topk, nullptr, nullptr, nullptr);
+  if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
+  if (shape->batch == 0 || all.n == 0 || n == 0) return DSA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  VsWork vw;
+  BsWork bw;
+  memset(&vw, 0, sizeof(vw));
+  memset(&bw, 0, sizeof(bw));
+  mixed_layout(shape, ix.n_vs, ix.n_bs, vk, sk, topk, workspace, &vw, &bw);
+  hipError_t e = hipSuccess;
+  if (ix.n_vs) e = vs_index_stages(q, k, shape, vk, sk, last_q, scale, vs, vw, s);
+  if (e == hipSuccess && ix.n_bs) e = bs_index_stages(q, k, shape, topk, scale, bs, bw, s);
+  if (e == hipSuccess) {
+    ix.vs = VsIndex{vw.iv, vw.n_iv, sk, vw.cols, vw.n_cols, vk};
+    ix.bs = BlockIndex{bw.sel, bw.n_sel, topk < nb ? topk : nb};
+    ix.st = StreamIndex{init_blocks, local_blocks};
+    AttnArgs a = attn_args(q, k, v, o, shape, scale, all);
+    a.wo = make_work_order(all, ix.kind);
+    e = launch_attention_mixed(a, ix, s);
+  }
+  return hip_status(e);
+}
+
+dsa_status dsa_sparse_attention_mixed(const void* q, const void* k, const void* v, void* o,
+                                      const dsa_shape* shape, float scale, const int32_t* patterns,
+                                      const int32_t* intervals, const int32_t* n_intervals, int32_t max_iv,
+                                      const int32_t* cols, const int32_t* n_cols, int32_t max_cols,
+                                      const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
+                                      int32_t init_blocks, int32_t local_blocks, void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !o || max_iv < 0 || max_cols < 0 || max_sel < 0 || init_blocks < 0 ||
+      local_blocks < 1)
+    return DSA_ERR_INVALID_ARG;
+  HeadMap all, vs, bs;
+  MixedIndex ix;
+  if ((st = parse_patterns(shape, patterns, all, vs, bs, ix)) != DSA_OK) return st;
+  if (ix.n_vs && (!n_intervals || !n_cols || (max_iv && !intervals) || (max_cols && !cols)))
+    return DSA_ERR_INVALID_ARG;
+  if (ix.n_bs && (!n_sel || (max_sel && !sel))) return DSA_ERR_INVALID_ARG;
+  if (shape->batch == 0 || all.n == 0 || shape->seq_len == 0) return DSA_OK;
+  ix.vs = VsIndex{intervals, n_intervals, max_iv, cols, n_cols, max_cols};
+  ix.bs = BlockIndex{sel, n_sel, max_sel};
+  ix.st = StreamIndex{init_blocks, local_blocks};
+  AttnArgs a = attn_args(q, k, v, o, shape, scale, all);
+  a.wo = make_work_order(all, ix.kind);
+  return hip_status(launch_attention_mixed(a, ix, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

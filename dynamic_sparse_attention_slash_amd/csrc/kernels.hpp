@@ -24,6 +24,7 @@ struct BlockIndex {    // explicit key-block lists
 struct StreamIndex {   // closed-form A-shape
   int32_t init_blocks, local_blocks;
 };
+enum : int8_t { PAT_VS = 0, PAT_BS = 1, PAT_STREAM = 2 };  // pattern of a head
 
 // Order of the attention work items (row, query block): batch, then the
 // groups of listed heads that share a kv head (kv-head order), then query
@@ -36,6 +37,9 @@ struct WorkOrder {
   int32_t n_groups;
 };
 WorkOrder make_work_order(const HeadMap& hm);
+// pattern by pattern (kind[t] of listed head t: vertical-slash, block-sparse,
+// streaming), each pattern's heads grouped by kv head as above
+WorkOrder make_work_order(const HeadMap& hm, const int8_t* kind);
 
 // Work-group -> (row, unit) for a grid of rows x units items, units visited
 // latest first. The hardware deals consecutive work-group ids round-robin over
@@ -79,6 +83,19 @@ struct AttnArgs {
 hipError_t launch_attention_vs(const AttnArgs& a, const VsIndex& ix, hipStream_t s);
 hipError_t launch_attention_blocks(const AttnArgs& a, const BlockIndex& ix, hipStream_t s);
 hipError_t launch_attention_stream(const AttnArgs& a, const StreamIndex& ix, hipStream_t s);
+
+// One launch over the heads of a mixed layer: listed head t (of a.hm) follows
+// pattern kind[t]; its rows in that pattern's index arrays are
+// b * (heads of that pattern) + slot[t]. bf16 work items follow a.wo.
+struct MixedIndex {
+  VsIndex vs;
+  BlockIndex bs;
+  StreamIndex st;
+  int32_t n_vs, n_bs;
+  int8_t kind[MAX_HEADS];
+  int16_t slot[MAX_HEADS];
+};
+hipError_t launch_attention_mixed(const AttnArgs& a, const MixedIndex& ix, hipStream_t s);
 
 // ---- vertical-slash estimate (vs_estimate.hip) ----
 constexpr int EST_CHUNK = 256;  // keys per estimator work-group

@@ -124,6 +124,39 @@ dsa_status dsa_streaming_attention(
     int32_t init_blocks, int32_t local_blocks, float scale, const int32_t* heads,
     int32_t n_heads, void* stream);
 
+/* Pattern of one query head in a mixed layer. */
+typedef enum {
+  DSA_PATTERN_NONE = -1, /* head not processed: its o rows are left untouched */
+  DSA_PATTERN_VS = 0,
+  DSA_PATTERN_BS = 1,
+  DSA_PATTERN_STREAM = 2
+} dsa_pattern;
+
+/* A layer whose heads follow different patterns [MInf §2.2: every head has
+ * one of the patterns, fixed offline; its sparse index is built online from
+ * the input]. patterns: HOST int32 [q_heads], a dsa_pattern per query head.
+ * Computes what dsa_vertical_slash_sparse_attention does for the VS heads,
+ * dsa_block_sparse_attention for the BS heads and dsa_streaming_attention for
+ * the streaming heads, each over its heads in ascending order, but the
+ * attention of all heads runs as one launch (work items pattern by pattern,
+ * each pattern's heads grouped by kv head). Output is bit-identical to those calls for
+ * the VS and BS heads; streaming heads run the one-block-per-work-group code
+ * (the streaming call runs two query blocks per work-group) and agree with it
+ * to rounding. Every argument is checked whatever the patterns:
+ * vertical_topk >= 0, slash_topk >= 1, last_q in [1, 64], topk >= 1,
+ * init_blocks >= 0, local_blocks >= 1; a pattern value outside the enum is
+ * DSA_ERR_INVALID_ARG. workspace: at least
+ * dsa_mixed_sparse_attention_workspace_bytes(...) bytes. */
+dsa_status dsa_mixed_sparse_attention(
+    const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
+    const int32_t* patterns, int32_t vertical_topk, int32_t slash_topk, int32_t last_q,
+    int32_t topk, int32_t init_blocks, int32_t local_blocks, float scale, void* workspace,
+    size_t workspace_bytes, void* stream);
+size_t dsa_mixed_sparse_attention_workspace_bytes(const dsa_shape* shape,
+                                                  const int32_t* patterns,
+                                                  int32_t vertical_topk, int32_t slash_topk,
+                                                  int32_t topk);
+
 /* ======================================================================
  * Stage calls: the same kernels the calls above run, exposed one by one.
  * ====================================================================== */
@@ -203,6 +236,20 @@ dsa_status dsa_sparse_attention_blocks(
     const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
     float scale, const int32_t* heads, int32_t n_heads, const int32_t* sel,
     const int32_t* n_sel, int32_t max_sel, void* stream);
+
+/* The attention launch of dsa_mixed_sparse_attention over given indices.
+ * patterns: HOST int32 [q_heads] as there. The VS heads, in ascending order,
+ * number t = 0 .. n_vs-1 and take rows b * n_vs + t of intervals, n_intervals,
+ * cols and n_cols (laid out as for dsa_sparse_attention_vs); the BS heads
+ * likewise take rows b * n_bs + t of sel and n_sel (as for
+ * dsa_sparse_attention_blocks). The index pointers of a pattern no head
+ * follows may be NULL. */
+dsa_status dsa_sparse_attention_mixed(
+    const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
+    float scale, const int32_t* patterns, const int32_t* intervals,
+    const int32_t* n_intervals, int32_t max_iv, const int32_t* cols, const int32_t* n_cols,
+    int32_t max_cols, const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
+    int32_t init_blocks, int32_t local_blocks, void* stream);
 
 /* ======================================================================
  * After prefill: which keys to keep in the KV cache

@@ -110,6 +110,15 @@ def head_patterns(w: Workload) -> Dict[str, List[int]]:
     return {"vs": sorted(vs), "bs": sorted(bs), "st": sorted(st)}
 
 
+def pattern_list(w: Workload) -> List[Optional[str]]:
+    """The same assignment as one pattern name per query head."""
+    out: List[Optional[str]] = [None] * w.q_heads
+    for pat, heads in head_patterns(w).items():
+        for h in heads:
+            out[h] = pat
+    return out
+
+
 @dataclass
 class Inputs:
     q: torch.Tensor

@@ -130,3 +130,39 @@ def test_other_argument_errors(lib):
     many = (ctypes.c_int32 * 300)(*range(300))
     big = shape(hq=300, hkv=300)
     assert lib.dsa_streaming_attention(P, P, P, P, ctypes.byref(big), 1, 1, 0.0, many, 300, None) == UNSUPPORTED
+
+
+def test_mixed_argument_errors(lib):
+    sh = shape(hq=4, hkv=2)
+    pats = lambda *p: (ctypes.c_int32 * len(p))(*p)
+    good = pats(0, 1, 2, -1)
+    mixed = lambda p=good, vk=8, sk=8, lq=64, tk=4, ib=1, lb=2, wsb=1 << 40, q=P: lib.dsa_mixed_sparse_attention(
+        q, P, P, P, ctypes.byref(sh), p, vk, sk, lq, tk, ib, lb, 0.0, P, wsb, None)
+    assert mixed(p=None) == INVALID
+    assert mixed(p=pats(0, 1, 3, -1)) == INVALID
+    assert mixed(p=pats(0, -2, 2, 1)) == INVALID
+    assert mixed(q=None) == INVALID
+    assert mixed(sk=0) == INVALID
+    assert mixed(tk=0) == INVALID
+    assert mixed(ib=-1) == INVALID
+    assert mixed(lb=0) == INVALID
+    assert mixed(lq=65) == UNSUPPORTED
+    assert mixed(wsb=8) == WORKSPACE
+    # no head processed: nothing to enqueue
+    assert mixed(p=pats(-1, -1, -1, -1), wsb=0) == OK
+    # workspace: the VS part for the VS heads plus the BS part for the BS heads
+    big = shape(hq=4, hkv=2, n=4096)
+    wm = lib.dsa_mixed_sparse_attention_workspace_bytes
+    vs1 = lib.dsa_vertical_slash_workspace_bytes(ctypes.byref(big), 64, 64, 1)
+    bs2 = lib.dsa_block_sparse_workspace_bytes(ctypes.byref(big), 8, 2)
+    assert wm(ctypes.byref(big), pats(0, 1, 1, 2), 64, 64, 8) == vs1 + bs2
+    assert wm(ctypes.byref(big), pats(2, 2, -1, 2), 64, 64, 8) == 0
+    assert wm(ctypes.byref(big), pats(2, 2, 5, 2), 64, 64, 8) == 0
+    assert wm(ctypes.byref(big), None, 64, 64, 8) == 0
+    # the stage call: index pointers required only for patterns some head follows
+    stage = lambda p, iv=P, niv=P, cols=P, ncols=P, sel=P, nsel=P: lib.dsa_sparse_attention_mixed(
+        P, P, P, P, ctypes.byref(sh), 0.0, p, iv, niv, 4, cols, ncols, 4, sel, nsel, 4, 1, 2, None)
+    assert stage(good, niv=None) == INVALID
+    assert stage(good, nsel=None) == INVALID
+    assert stage(pats(-1, -1, -1, -1), None, None, None, None, None, None) == OK
+    assert stage(pats(0, 1, 9, -1)) == INVALID

@@ -513,6 +513,73 @@ def test_mixed_layer_small():
         assert torch.equal(row_o[0, h], o[0, h])
 
 
+def _streaming_vs_oracle(o, q, k, v, heads, init_blocks, local_blocks, tag, blocks=None):
+    Hq, Hkv, n, D = q.shape[1], k.shape[1], q.shape[2], q.shape[3]
+    oh, qh, kh, vh = host64(o), host64(q), host64(k), host64(v)
+    for b in range(q.shape[0]):
+        for h in heads:
+            g = kvh(h, Hq, Hkv)
+            res = O.streaming_head(qh[b, h], kh[b, g], vh[b, g], init_blocks, local_blocks, blocks=blocks)
+            for a, ref in res["out"].items():
+                check_attention(oh[b, h, a * BLK: a * BLK + ref.shape[0]], ref, f"{tag} st b{b} h{h} block {a}")
+
+
+@pytest.mark.parametrize("D,dt,n,B", [(128, "bf16", 2048 + 37, 2), (64, "bf16", 1500, 1),
+                                      (64, "f32", 700, 2), (128, "bf16", 64, 1), (128, "bf16", 5, 2)])
+def test_mixed_one_launch(D, dt, n, B):
+    """The mixed layer as one attention launch: VS and BS heads bit-identical
+    to the per-pattern calls (which the oracle checks above), streaming heads
+    against the oracle, heads without a pattern left untouched."""
+    say(f"mixed one launch D={D} {dt} n={n} B={B}")
+    Hq, Hkv = 8, 2
+    q, k, v = rand_qkv(B, Hq, Hkv, n, D, dt, seed=100 + n)
+    pats = ["vs", "bs", "st", "vs", "st", None, "bs", "vs"]
+    vk, sk, tk, ib, lb = 40, 200, 6, 1, 3
+    hv = [h for h, p in enumerate(pats) if p == "vs"]
+    hb = [h for h, p in enumerate(pats) if p == "bs"]
+    hs = [h for h, p in enumerate(pats) if p == "st"]
+    o = torch.full_like(q, 7.0)
+    dsa.mixed_sparse_attention(q, k, v, pats, vertical_topk=vk, slash_topk=sk, topk=tk, init_blocks=ib,
+                               local_blocks=lb, out=o)
+    ref = torch.zeros_like(q)
+    dsa.vertical_slash_sparse_attention(q, k, v, vk, sk, heads=hv, out=ref)
+    dsa.block_sparse_attention(q, k, v, tk, heads=hb, out=ref)
+    dsa.streaming_attention(q, k, v, ib, lb, heads=hs, out=ref)
+    torch.cuda.synchronize()
+    for h in hv + hb:
+        assert torch.equal(o[:, h], ref[:, h]), h
+    assert (o[:, 5] == 7.0).all()
+    if dt == "f32":  # fp32 launches per pattern: the streaming kernel itself
+        for h in hs:
+            assert torch.equal(o[:, h], ref[:, h]), h
+    _streaming_vs_oracle(o, q, k, v, hs, ib, lb, "mixed")
+
+
+def test_sparse_attention_mixed_given_indices():
+    """The one-launch stage call over indices from the stage calls equals the
+    per-pattern stage calls bit for bit (VS, BS heads)."""
+    say("mixed given indices")
+    B, Hq, Hkv, n, D = 2, 6, 2, 1300, 128
+    q, k, v = rand_qkv(B, Hq, Hkv, n, D, "bf16", seed=5)
+    pats = ["st", "vs", "bs", "bs", "vs", "st"]
+    hv = [h for h, p in enumerate(pats) if p == "vs"]
+    hb = [h for h, p in enumerate(pats) if p == "bs"]
+    hs = [h for h, p in enumerate(pats) if p == "st"]
+    vg, sg = dsa.vs_estimate(q, k, heads=hv)
+    ix = dsa.vs_build_index(dsa.topk(vg, 30), dsa.topk(sg, 150, 0), n)
+    G = Hq // Hkv
+    kp = dsa.bs_pool(k)[torch.tensor([b * Hkv + h // G for b in range(B) for h in hb], device=q.device)]
+    sel, n_sel = dsa.bs_select(dsa.bs_pool(q, hb), kp.contiguous(), 5)
+    o = dsa.sparse_attention_mixed(q, k, v, pats, vs_index=ix, bs_index=(sel, n_sel), init_blocks=2,
+                                   local_blocks=4)
+    ref = dsa.sparse_attention_vs(q, k, v, *ix, heads=hv)
+    dsa.sparse_attention_blocks(q, k, v, sel, n_sel, heads=hb, out=ref)
+    torch.cuda.synchronize()
+    for h in hv + hb:
+        assert torch.equal(o[:, h], ref[:, h]), h
+    _streaming_vs_oracle(o, q, k, v, hs, 2, 4, "mixed stage")
+
+
 # ---------------------------------------------------------------------------
 # workload-shaped cases
 # ---------------------------------------------------------------------------
@@ -620,6 +687,25 @@ def _mixed_layer_sampled(w, checks, n_sample, seed):
     sc = 1 / math.sqrt(D)
     rng = np.random.default_rng(seed)
     blocks = sorted(set([0, 1, nb - 1] + rng.choice(nb, n_sample, replace=False).tolist()))
+    # the same layer as one attention launch: VS and BS heads bit for bit,
+    # streaming heads against the oracle on the sampled blocks
+    say("  one-launch layer")
+    o_one = dsa.mixed_sparse_attention(q, k, v, synthetic.pattern_list(w), vertical_topk=w.vertical_topk,
+                                       slash_topk=w.slash_topk, topk=w.topk, init_blocks=w.init_blocks,
+                                       local_blocks=w.local_blocks, last_q=w.last_q)
+    torch.cuda.synchronize()
+    for h in hv + hb:
+        assert torch.equal(o_one[:, h], o[:, h]), h
+    for b in range(w.batch):
+        for h in hs[:2]:
+            g = kvh(h, w.q_heads, w.kv_heads)
+            res = O.streaming_head(host64(q[b, h]), host64(k[b, g]), host64(v[b, g]), w.init_blocks,
+                                   w.local_blocks, blocks=blocks)
+            oh = host64(o_one[b, h])
+            for a, ref in res["out"].items():
+                check_attention(oh[a * BLK: a * BLK + ref.shape[0]], ref, f"one-launch st b{b} h{h} block {a}")
+    del o_one
+    torch.cuda.empty_cache()
     for pat, b, h in checks:
         assert h in x.heads[pat], (pat, h)
         g = kvh(h, w.q_heads, w.kv_heads)
