@@ -55,19 +55,24 @@ struct Tile<uint16_t, D> {
       for (int s = 0; s < DS; ++s) qop[qb][s] = src[s];
     }
   }
-  __device__ void scores(const uint16_t* ks, int32_t j0, const Window& w, float scale_log2,
-                         f32x4 (&out)[4]) const {
+  // K operands of the 16 keys from j0 (clamped into [0, n): a load past the
+  // end reads the last key, and its scores are never used)
+  struct KReg { u32x4 v[DS]; };
+  __device__ void load_k(const uint16_t* ks, int32_t j0, const Window& w, KReg& k) const {
     const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
-    int32_t key = min(j0 + l16, w.n - 1);
+    const int32_t key = min(j0 + l16, w.n - 1);
     const u32x4* src = reinterpret_cast<const u32x4*>(ks + (size_t)key * D + (D / 4) * g);
-    u32x4 kop[DS];
 #pragma unroll
-    for (int s = 0; s < DS; ++s) kop[s] = src[s];
+    for (int s = 0; s < DS; ++s) k.v[s] = src[s];
+  }
+  __device__ void scores_k(const KReg& k, int32_t j0, const Window& w, float scale_log2,
+                           f32x4 (&out)[4]) const {
+    const int32_t l16 = threadIdx.x & 15;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < DS; ++s) acc = mfma_bf16(qop[qb][s], kop[s], acc);
+      for (int s = 0; s < DS; ++s) acc = mfma_bf16(qop[qb][s], k.v[s], acc);
       out[qb] = acc;
     }
     finish(out, j0, l16, w, scale_log2);
@@ -112,30 +117,57 @@ struct Tile<float, D> {
       }
     }
   }
-  __device__ void scores(const float* ks, int32_t j0, const Window& w, float scale_log2,
-                         f32x4 (&out)[4]) const {
+  struct KReg { f32x4 v[DK / 4]; };
+  __device__ void load_k(const float* ks, int32_t j0, const Window& w, KReg& k) const {
     const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
-    int32_t key = min(j0 + l16, w.n - 1);
+    const int32_t key = min(j0 + l16, w.n - 1);
     const f32x4* src = reinterpret_cast<const f32x4*>(ks + (size_t)key * D + DK * g);
-    float kop[DK];
 #pragma unroll
-    for (int s = 0; s < DK / 4; ++s) {
-      f32x4 x = src[s];
-      kop[4 * s] = x[0]; kop[4 * s + 1] = x[1]; kop[4 * s + 2] = x[2]; kop[4 * s + 3] = x[3];
-    }
+    for (int s = 0; s < DK / 4; ++s) k.v[s] = src[s];
+  }
+  __device__ void scores_k(const KReg& k, int32_t j0, const Window& w, float scale_log2,
+                           f32x4 (&out)[4]) const {
+    const int32_t l16 = threadIdx.x & 15;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < DK; ++s) acc = mfma_f32(qop[qb][s], kop[s], acc);
+      for (int s = 0; s < DK; ++s) acc = mfma_f32(qop[qb][s], k.v[s / 4][s % 4], acc);
       out[qb] = acc;
     }
     Tile<uint16_t, D>::finish(out, j0, l16, w, scale_log2);
   }
 };
 
+// Scores of consecutive 16-key steps. bf16 loads the next step's K while the
+// current one computes (16 more VGPRs, still three waves per SIMD); fp32,
+// whose K operands are twice as wide, loads each step's K at its start.
 template <typename T, int D>
-__global__ __launch_bounds__(64) void est_stats_kernel(EstArgs a) {
+struct KStream {
+  static constexpr bool PREFETCH = sizeof(T) == 2;
+  typename Tile<T, D>::KReg kn;
+  __device__ KStream(const Tile<T, D>& tile, const T* ks, int32_t j_begin, const Window& w) {
+    if (PREFETCH) tile.load_k(ks, j_begin, w, kn);
+  }
+  __device__ void scores(const Tile<T, D>& tile, const T* ks, int32_t j0, const Window& w, float scale_log2,
+                         f32x4 (&x)[4]) {
+    if (PREFETCH) {
+      const typename Tile<T, D>::KReg kc = kn;
+      tile.load_k(ks, j0 + 16, w, kn);
+      tile.scores_k(kc, j0, w, scale_log2, x);
+    } else {
+      tile.load_k(ks, j0, w, kn);
+      tile.scores_k(kn, j0, w, scale_log2, x);
+    }
+  }
+};
+
+// bf16: three waves per SIMD, so the prefetched K costs no occupancy
+#define EST_KERNEL \
+  __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1, sizeof(T) == 2 ? 3 : 8)))
+
+template <typename T, int D>
+EST_KERNEL void est_stats_kernel(EstArgs a) {
   const int32_t nchunks = (a.seq_len + C - 1) / C;
   int32_t row, chunk;
   work_item(a.hm, a.wo, nchunks, row, chunk);
@@ -151,9 +183,10 @@ __global__ __launch_bounds__(64) void est_stats_kernel(EstArgs a) {
     for (int i = 0; i < 4; ++i) { m[qb][i] = NEG_BIG; z[qb][i] = 0.f; }
 
   const int32_t j_begin = chunk * C, j_end = min(a.seq_len, j_begin + C);
+  KStream<T, D> kst(tile, ks, j_begin, w);
   for (int32_t j0 = j_begin; j0 < j_end; j0 += 16) {
     f32x4 x[4];
-    tile.scores(ks, j0, w, a.scale_log2, x);
+    kst.scores(tile, ks, j0, w, a.scale_log2, x);
     // running (max, sum) with a deferred max: rescale only when a score
     // exceeds the current max by more than 2^8
     bool need = false;
@@ -237,7 +270,7 @@ __global__ __launch_bounds__(64 * COMB_SPLIT) void est_combine_kernel(EstArgs a,
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(64) void est_scores_kernel(EstArgs a) {
+EST_KERNEL void est_scores_kernel(EstArgs a) {
   constexpr int PS = 65;  // padded LDS row of the 64x64 probability tile
   __shared__ float ptile[64 * PS];
   __shared__ float sacc[SACC];
@@ -259,12 +292,13 @@ __global__ __launch_bounds__(64) void est_scores_kernel(EstArgs a) {
 
   float* vout = a.v_scores + (size_t)row * a.seq_len;
   const int32_t j_begin = chunk * C, j_end = min(a.seq_len, j_begin + C);
+  KStream<T, D> kst(tile, ks, j_begin, w);
   for (int32_t t0 = j_begin; t0 < j_end; t0 += 64) {
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
       const int32_t j0 = t0 + 16 * sb;
       f32x4 x[4];
-      tile.scores(ks, j0, w, a.scale_log2, x);
+      kst.scores(tile, ks, j0, w, a.scale_log2, x);
       float colsum = 0.f;
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb)
@@ -283,15 +317,26 @@ __global__ __launch_bounds__(64) void est_scores_kernel(EstArgs a) {
     if (!a.want_s) continue;
     __syncthreads();
     // diagonal e = r - jj of the tile maps to chunk offset index
-    // e + (C - 1) - (t0 - j_begin)
+    // e + (C - 1) - (t0 - j_begin). Lane l owns diagonals e1 = l - 63 (rows
+    // 0..l) and e2 = l + 1 (rows l+1..63): in row k both sit at column
+    // (k - l - 1) mod 64, so one 64-step sweep over the rows visits each
+    // element of both once, with the same trip count in every lane. Four
+    // interleaved partial sums per diagonal keep the reads in flight.
     const int32_t base = (C - 1) - (t0 - j_begin);
-    for (int32_t t = lane; t < 127; t += 64) {
-      const int32_t e = t - 63;
-      const int32_t r_lo = max(0, e), r_hi = min(63, 63 + e);
-      float sum = 0.f;
-      for (int32_t r = r_lo; r <= r_hi; ++r) sum += ptile[r * PS + (r - e)];
-      sacc[e + base] += sum;
+    float d1[4] = {0.f, 0.f, 0.f, 0.f}, d2[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int32_t k0 = 0; k0 < 64; k0 += 4) {
+#pragma unroll
+      for (int32_t u = 0; u < 4; ++u) {
+        const int32_t k = k0 + u;
+        const float v = ptile[k * PS + ((k - lane - 1) & 63)];
+        const float v1 = k <= lane ? v : 0.f;
+        d1[u] += v1;
+        d2[u] += v - v1;
+      }
     }
+    sacc[lane - 63 + base] += (d1[0] + d1[1]) + (d1[2] + d1[3]);
+    if (lane < 63) sacc[lane + 1 + base] += (d2[0] + d2[1]) + (d2[2] + d2[3]);
     __syncthreads();
   }
   if (!a.want_s) return;
