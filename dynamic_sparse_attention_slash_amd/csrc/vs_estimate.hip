@@ -19,8 +19,9 @@
 // Pass 2 (scores): recompute S, p = exp2(S*scale*log2e - F_r). Column sums are
 //   register sums plus two cross-lane steps (the loop runs key-major, so a
 //   key's scores stay in one lane column). Diagonal sums stage each 64x64 tile
-//   of p in LDS and add it along diagonals, one thread per diagonal, into a
-//   per-chunk accumulator: no atomics, fixed order, bit-reproducible.
+//   of p in LDS and add it along diagonals, each lane owning two diagonals
+//   that together take one element per tile row, into a per-chunk
+//   accumulator: no atomics, fixed order, bit-reproducible.
 // S-combine: s[d] adds the (at most two) chunk partials covering offset d in
 //   ascending chunk order.
 #include "kernels.hpp"
