@@ -38,7 +38,8 @@ struct Window {
 };
 
 // S tile for 16 keys [j0, j0+16): lane holds key column j0 + l16 and window
-// rows 16qb + 4g + i. Returns masked scores * scale_log2 (-inf when masked).
+// rows 16qb + 4g + i. Returns the unscaled scores, -inf where masked; the
+// consumers fold scale * log2(e) into one FMA per element.
 template <typename T, int D>
 struct Tile;
 
@@ -66,8 +67,7 @@ struct Tile<uint16_t, D> {
 #pragma unroll
     for (int s = 0; s < DS; ++s) k.v[s] = src[s];
   }
-  __device__ void scores_k(const KReg& k, int32_t j0, const Window& w, float scale_log2,
-                           f32x4 (&out)[4]) const {
+  __device__ void scores_k(const KReg& k, int32_t j0, const Window& w, f32x4 (&out)[4]) const {
     const int32_t l16 = threadIdx.x & 15;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
@@ -76,19 +76,14 @@ struct Tile<uint16_t, D> {
       for (int s = 0; s < DS; ++s) acc = mfma_bf16(qop[qb][s], k.v[s], acc);
       out[qb] = acc;
     }
-    finish(out, j0, l16, w, scale_log2);
+    finish(out, j0, l16, w);
   }
-  // scale, and mask only a step that reaches the window's first row (or a
-  // window of fewer than 64 rows): earlier keys precede every window row
-  __device__ static void finish(f32x4 (&x)[4], int32_t j0, int32_t l16, const Window& w, float scale_log2) {
-    if (j0 + 15 <= w.start && w.lq == 64) {
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) x[qb] *= scale_log2;
-    } else {
-      mask(x, j0 + l16, w, scale_log2);
-    }
+  // mask only a step that reaches the window's first row (or a window of
+  // fewer than 64 rows): earlier keys precede every window row
+  __device__ static void finish(f32x4 (&x)[4], int32_t j0, int32_t l16, const Window& w) {
+    if (!(j0 + 15 <= w.start && w.lq == 64)) mask(x, j0 + l16, w);
   }
-  __device__ static void mask(f32x4 (&x)[4], int32_t key, const Window& w, float scale_log2) {
+  __device__ static void mask(f32x4 (&x)[4], int32_t key, const Window& w) {
     const int32_t g = threadIdx.x >> 4;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
@@ -96,7 +91,7 @@ struct Tile<uint16_t, D> {
       for (int i = 0; i < 4; ++i) {
         int32_t r = 16 * qb + 4 * g + i;
         bool ok = r < w.lq && key <= w.pos(r);
-        x[qb][i] = ok ? x[qb][i] * scale_log2 : -INFINITY;
+        x[qb][i] = ok ? x[qb][i] : -INFINITY;
       }
   }
 };
@@ -126,8 +121,7 @@ struct Tile<float, D> {
 #pragma unroll
     for (int s = 0; s < DK / 4; ++s) k.v[s] = src[s];
   }
-  __device__ void scores_k(const KReg& k, int32_t j0, const Window& w, float scale_log2,
-                           f32x4 (&out)[4]) const {
+  __device__ void scores_k(const KReg& k, int32_t j0, const Window& w, f32x4 (&out)[4]) const {
     const int32_t l16 = threadIdx.x & 15;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
@@ -136,7 +130,7 @@ struct Tile<float, D> {
       for (int s = 0; s < DK; ++s) acc = mfma_f32(qop[qb][s], k.v[s / 4][s % 4], acc);
       out[qb] = acc;
     }
-    Tile<uint16_t, D>::finish(out, j0, l16, w, scale_log2);
+    Tile<uint16_t, D>::finish(out, j0, l16, w);
   }
 };
 
@@ -150,15 +144,14 @@ struct KStream {
   __device__ KStream(const Tile<T, D>& tile, const T* ks, int32_t j_begin, const Window& w) {
     if (PREFETCH) tile.load_k(ks, j_begin, w, kn);
   }
-  __device__ void scores(const Tile<T, D>& tile, const T* ks, int32_t j0, const Window& w, float scale_log2,
-                         f32x4 (&x)[4]) {
+  __device__ void scores(const Tile<T, D>& tile, const T* ks, int32_t j0, const Window& w, f32x4 (&x)[4]) {
     if (PREFETCH) {
       const typename Tile<T, D>::KReg kc = kn;
       tile.load_k(ks, j0 + 16, w, kn);
-      tile.scores_k(kc, j0, w, scale_log2, x);
+      tile.scores_k(kc, j0, w, x);
     } else {
       tile.load_k(ks, j0, w, kn);
-      tile.scores_k(kn, j0, w, scale_log2, x);
+      tile.scores_k(kn, j0, w, x);
     }
   }
 };
@@ -184,31 +177,38 @@ EST_KERNEL void est_stats_kernel(EstArgs a) {
     for (int i = 0; i < 4; ++i) { m[qb][i] = NEG_BIG; z[qb][i] = 0.f; }
 
   const int32_t j_begin = chunk * C, j_end = min(a.seq_len, j_begin + C);
+  const float sc = a.scale_log2;
   KStream<T, D> kst(tile, ks, j_begin, w);
   for (int32_t j0 = j_begin; j0 < j_end; j0 += 16) {
     f32x4 x[4];
-    kst.scores(tile, ks, j0, w, a.scale_log2, x);
-    // running (max, sum) with a deferred max: rescale only when a score
-    // exceeds the current max by more than 2^8
+    kst.scores(tile, ks, j0, w, x);
+    // running (max, sum) with a deferred max: d = x * scale * log2(e) - m in
+    // one FMA; the reference m is raised only when d exceeds 8 (then d = 0)
+    f32x4 d[4];
     bool need = false;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) need |= x[qb][i] > m[qb][i] + 8.f;
+      for (int i = 0; i < 4; ++i) {
+        d[qb][i] = __builtin_fmaf(x[qb][i], sc, -m[qb][i]);
+        need |= d[qb][i] > 8.f;
+      }
     if (__any(need)) {
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (x[qb][i] > m[qb][i] + 8.f) {
-            z[qb][i] *= fast_exp2(m[qb][i] - x[qb][i]);
-            m[qb][i] = x[qb][i];
+          if (d[qb][i] > 8.f) {
+            const float xs = x[qb][i] * sc;
+            z[qb][i] *= fast_exp2(m[qb][i] - xs);
+            m[qb][i] = xs;
+            d[qb][i] = 0.f;
           }
     }
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[qb][i] += fast_exp2(x[qb][i] - m[qb][i]);
+      for (int i = 0; i < 4; ++i) z[qb][i] += fast_exp2(d[qb][i]);
   }
   // merge the 16 key columns of each row (lanes with equal l >> 4)
 #pragma unroll
@@ -250,11 +250,24 @@ __global__ __launch_bounds__(64 * COMB_SPLIT) void est_combine_kernel(EstArgs a,
   const int32_t row = blockIdx.x, r = threadIdx.x & 63, part = threadIdx.x >> 6;
   const float* src = a.part_stats + (size_t)row * nchunks * 128 + 2 * r;
   float mm = NEG_BIG, zz = 0.f;
-  for (int32_t c = part; c < nchunks; c += COMB_SPLIT) {
-    const float mc = src[(size_t)c * 128], zc = src[(size_t)c * 128 + 1];
-    const float mn = fmaxf(mm, mc);
-    zz = zz * fast_exp2(mm - mn) + zc * fast_exp2(mc - mn);
-    mm = mn;
+  // eight chunks' loads in flight, then their merge in chunk order
+  constexpr int B = 8;
+  for (int32_t c0 = part; c0 < nchunks; c0 += B * COMB_SPLIT) {
+    float mc[B], zc[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int32_t c = c0 + u * COMB_SPLIT;
+      const bool ok = c < nchunks;
+      mc[u] = ok ? src[(size_t)c * 128] : NEG_BIG;
+      zc[u] = ok ? src[(size_t)c * 128 + 1] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      if (c0 + u * COMB_SPLIT >= nchunks) break;
+      const float mn = fmaxf(mm, mc[u]);
+      zz = zz * fast_exp2(mm - mn) + zc[u] * fast_exp2(mc[u] - mn);
+      mm = mn;
+    }
   }
   pm[part][r] = mm;
   pz[part][r] = zz;
@@ -270,7 +283,9 @@ __global__ __launch_bounds__(64 * COMB_SPLIT) void est_combine_kernel(EstArgs a,
   }
 }
 
-template <typename T, int D>
+// S: slash scores wanted (a.want_s); without them the probabilities never
+// go through LDS
+template <typename T, int D, bool S>
 EST_KERNEL void est_scores_kernel(EstArgs a) {
   constexpr int PS = 65;  // padded LDS row of the 64x64 probability tile
   __shared__ float ptile[64 * PS];
@@ -292,6 +307,7 @@ EST_KERNEL void est_scores_kernel(EstArgs a) {
   for (int e = lane; e < SACC; e += 64) sacc[e] = 0.f;
 
   float* vout = a.v_scores + (size_t)row * a.seq_len;
+  const float sc = a.scale_log2;
   const int32_t j_begin = chunk * C, j_end = min(a.seq_len, j_begin + C);
   KStream<T, D> kst(tile, ks, j_begin, w);
   for (int32_t t0 = j_begin; t0 < j_end; t0 += 64) {
@@ -299,15 +315,15 @@ EST_KERNEL void est_scores_kernel(EstArgs a) {
     for (int sb = 0; sb < 4; ++sb) {
       const int32_t j0 = t0 + 16 * sb;
       f32x4 x[4];
-      kst.scores(tile, ks, j0, w, a.scale_log2, x);
+      kst.scores(tile, ks, j0, w, x);
       float colsum = 0.f;
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float p = fast_exp2(x[qb][i] - F[qb][i]);
+          const float p = fast_exp2(__builtin_fmaf(x[qb][i], sc, -F[qb][i]));
           colsum += p;
-          ptile[(16 * qb + 4 * g + i) * PS + 16 * sb + l16] = p;
+          if (S) ptile[(16 * qb + 4 * g + i) * PS + 16 * sb + l16] = p;
         }
       colsum = xor_sum(xor_sum(colsum, 16), 32);
       if (g == 0 && j0 + l16 < a.seq_len) {
@@ -315,7 +331,7 @@ EST_KERNEL void est_scores_kernel(EstArgs a) {
         else vout[j0 + l16] = colsum;
       }
     }
-    if (!a.want_s) continue;
+    if (!S) continue;
     __syncthreads();
     // diagonal e = r - jj of the tile maps to chunk offset index
     // e + (C - 1) - (t0 - j_begin). Lane l owns diagonals e1 = l - 63 (rows
@@ -340,7 +356,7 @@ EST_KERNEL void est_scores_kernel(EstArgs a) {
     if (lane < 63) sacc[lane + 1 + base] += (d2[0] + d2[1]) + (d2[2] + d2[3]);
     __syncthreads();
   }
-  if (!a.want_s) return;
+  if (!S) return;
   float* dst = a.s_part + ((size_t)row * nchunks + chunk) * SACC;
   for (int e = lane; e < SACC; e += 64) dst[e] = sacc[e];
 }
@@ -391,8 +407,14 @@ hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)nch * a.rows));
   auto st = a.dtype == BF16 ? (a.head_dim == 64 ? est_stats_kernel<uint16_t, 64> : est_stats_kernel<uint16_t, 128>)
                             : (a.head_dim == 64 ? est_stats_kernel<float, 64> : est_stats_kernel<float, 128>);
-  auto sc = a.dtype == BF16 ? (a.head_dim == 64 ? est_scores_kernel<uint16_t, 64> : est_scores_kernel<uint16_t, 128>)
-                            : (a.head_dim == 64 ? est_scores_kernel<float, 64> : est_scores_kernel<float, 128>);
+  auto sc = a.want_s ? (a.dtype == BF16 ? (a.head_dim == 64 ? est_scores_kernel<uint16_t, 64, true>
+                                                             : est_scores_kernel<uint16_t, 128, true>)
+                                         : (a.head_dim == 64 ? est_scores_kernel<float, 64, true>
+                                                             : est_scores_kernel<float, 128, true>))
+                     : (a.dtype == BF16 ? (a.head_dim == 64 ? est_scores_kernel<uint16_t, 64, false>
+                                                             : est_scores_kernel<uint16_t, 128, false>)
+                                         : (a.head_dim == 64 ? est_scores_kernel<float, 64, false>
+                                                             : est_scores_kernel<float, 128, false>));
   hipLaunchKernelGGL(st, grid, dim3(64), 0, s, a);
   hipLaunchKernelGGL(est_combine_kernel, dim3(a.rows), dim3(64 * COMB_SPLIT), 0, s, a, nch);
   hipLaunchKernelGGL(sc, grid, dim3(64), 0, s, a);
