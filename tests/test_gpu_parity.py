@@ -484,6 +484,35 @@ def test_repeat_launch_bitwise():
     assert torch.equal(outs[0], outs[1])
 
 
+def test_layer_two_streams_bitwise():
+    """The block-sparse call on a second stream beside the other calls (the
+    benchmark's layer step) writes the same bits as the serial order."""
+    say("layer on two streams")
+    w = synthetic.BY_NAME["qwen2_7b_32k_b4_mixed_bf16"].scaled(batch=2, seq_len=4096 + 77, slash_topk=500,
+                                                                vertical_topk=60, topk=12, local_blocks=6)
+    x = synthetic.make_inputs(w)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    hp = x.heads
+    calls = [lambda o: dsa.vertical_slash_sparse_attention(q, k, v, w.vertical_topk, w.slash_topk, heads=hp["vs"], out=o),
+             lambda o: dsa.block_sparse_attention(q, k, v, w.topk, heads=hp["bs"], out=o),
+             lambda o: dsa.streaming_attention(q, k, v, w.init_blocks, w.local_blocks, heads=hp["st"], out=o)]
+    ref = torch.zeros_like(q)
+    for c in calls:
+        c(ref)
+    side = torch.cuda.Stream()
+    for _ in range(2):
+        o = torch.zeros_like(q)
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            calls[1](o)
+        calls[0](o)
+        calls[2](o)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref)
+
+
 def test_mixed_layer_small():
     """Three calls over head subsets fill one output, as a mixed layer does."""
     say("mixed layer small")
