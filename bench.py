@@ -16,6 +16,10 @@ stages, then every head's attention in one launch) and reported as
 Default workload: the 1M-token Llama-3-8B-shaped mixed layer (the named
 workload that runs every step of the path); the 128K layer is timed beside it.
 
+Per-stage times (`stages_ms`, and the after-prefill calls) time each call
+alone with HIP events after a 512 MiB write that leaves none of its inputs in
+the GPU's caches, averaged over the repetitions.
+
 Prints one JSON line. `value` is the effective TFLOP/s of the layer: the
 attention FLOPs of the computed key blocks (4 * head_dim * sum over query
 blocks of rows x keys, before the causal trim of the diagonal tile) divided by
@@ -188,8 +192,8 @@ class Layer:
 
 
 def time_events(fn, reps):
-    """Average ms per call of fn, HIP events on torch's current stream (the
-    stream every library call is enqueued on)."""
+    """Average ms per call of fn over back-to-back calls, HIP events on
+    torch's current stream (the stream every library call is enqueued on)."""
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fn()
@@ -201,6 +205,36 @@ def time_events(fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+FLUSH_BYTES = 512 << 20  # twice the 256 MB last-level (MALL) cache
+_flush_buf = None
+
+
+def flush_caches():
+    """Write 512 MiB so that no input of the next call is left in the GPU's
+    caches from the previous one."""
+    global _flush_buf
+    if _flush_buf is None:
+        _flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    _flush_buf.fill_(1)
+
+
+def time_stage(fn, reps):
+    """Average ms of one call of fn, each timed alone with HIP events on
+    torch's current stream after a cache flush (one untimed call first)."""
+    s = torch.cuda.current_stream()
+    fn()
+    ev = []
+    for _ in range(reps):
+        flush_caches()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        ev.append((e0, e1))
+    ev[-1][1].synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+
 def stages(layer, reps):
     """Each stage of the layer through the stage calls, timed alone; also
     returns the indices (for the FLOP accounting)."""
@@ -210,13 +244,13 @@ def stages(layer, reps):
     if x.heads["vs"]:
         hs = x.heads["vs"]
         vg, sg = dsa.vs_estimate(q, k, last_q=w.last_q, heads=hs)
-        t["vs_estimate_ms"] = time_events(lambda: dsa.vs_estimate(q, k, last_q=w.last_q, heads=hs), reps)
+        t["vs_estimate_ms"] = time_stage(lambda: dsa.vs_estimate(q, k, last_q=w.last_q, heads=hs), reps)
         V = dsa.topk(vg, w.vertical_topk)
         S = dsa.topk(sg, w.slash_topk, 0)
-        t["vs_topk_ms"] = time_events(lambda: (dsa.topk(vg, w.vertical_topk), dsa.topk(sg, w.slash_topk, 0)), reps)
+        t["vs_topk_ms"] = time_stage(lambda: (dsa.topk(vg, w.vertical_topk), dsa.topk(sg, w.slash_topk, 0)), reps)
         ix = dsa.vs_build_index(V, S, w.seq_len)
-        t["vs_index_ms"] = time_events(lambda: dsa.vs_build_index(V, S, w.seq_len), reps)
-        t["vs_attention_ms"] = time_events(lambda: dsa.sparse_attention_vs(q, k, v, *ix, heads=hs, out=o), reps)
+        t["vs_index_ms"] = time_stage(lambda: dsa.vs_build_index(V, S, w.seq_len), reps)
+        t["vs_attention_ms"] = time_stage(lambda: dsa.sparse_attention_vs(q, k, v, *ix, heads=hs, out=o), reps)
         idx["vs"] = ix
         del vg, sg
     if x.heads["bs"]:
@@ -225,16 +259,16 @@ def stages(layer, reps):
         sel_rows = torch.tensor([b * w.kv_heads + h // G for b in range(w.batch) for h in hs], device=q.device)
         qp = dsa.bs_pool(q, hs)
         kp_all = dsa.bs_pool(k)
-        t["bs_pool_ms"] = time_events(lambda: (dsa.bs_pool(q, hs), dsa.bs_pool(k)), reps)
+        t["bs_pool_ms"] = time_stage(lambda: (dsa.bs_pool(q, hs), dsa.bs_pool(k)), reps)
         kp = kp_all[sel_rows].contiguous()
         sel, n_sel = dsa.bs_select(qp, kp, w.topk)
-        t["bs_select_ms"] = time_events(lambda: dsa.bs_select(qp, kp, w.topk), reps)
-        t["bs_attention_ms"] = time_events(lambda: dsa.sparse_attention_blocks(q, k, v, sel, n_sel, heads=hs, out=o), reps)
+        t["bs_select_ms"] = time_stage(lambda: dsa.bs_select(qp, kp, w.topk), reps)
+        t["bs_attention_ms"] = time_stage(lambda: dsa.sparse_attention_blocks(q, k, v, sel, n_sel, heads=hs, out=o), reps)
         idx["bs"] = (sel, n_sel)
         del qp, kp, kp_all
     if x.heads["st"]:
         hs = x.heads["st"]
-        t["st_attention_ms"] = time_events(lambda: dsa.streaming_attention(q, k, v, w.init_blocks, w.local_blocks, heads=hs, out=o), reps)
+        t["st_attention_ms"] = time_stage(lambda: dsa.streaming_attention(q, k, v, w.init_blocks, w.local_blocks, heads=hs, out=o), reps)
     return t, idx
 
 
@@ -264,7 +298,7 @@ def kv_retention_timing(layer, reps):
     one over the whole cache."""
     w, q, k, v = layer.w, layer.q, layer.k, layer.v
     torch.cuda.synchronize()
-    ms = time_events(lambda: dsa.kv_retention(q, k, KV_WINDOW, KV_KEEP), reps)
+    ms = time_stage(lambda: dsa.kv_retention(q, k, KV_WINDOW, KV_KEEP), reps)
     n, D, B = w.seq_len, w.head_dim, w.batch
     rows = B * w.q_heads
     nbytes = 2 * B * w.kv_heads * n * D * 2 + 2 * rows * n * 4 + rows * min(KV_KEEP, n) * 4
@@ -282,9 +316,9 @@ def kv_retention_timing(layer, reps):
     qd = torch.randn(B, w.q_heads, D, generator=g, device=q.device).to(q.dtype)
     eb = 2 if w.dtype == "bf16" else 4
     qo = 2 * rows * D * eb
-    ms_k = time_events(lambda: dsa.sparse_decode(qd, k, v, kept, n_keys), 20)
+    ms_k = time_stage(lambda: dsa.sparse_decode(qd, k, v, kept, n_keys), 20)
     b_k = rows * kk * D * eb * 2 + rows * kk * 4 + qo
-    ms_a = time_events(lambda: dsa.sparse_decode(qd, k, v), 10)
+    ms_a = time_stage(lambda: dsa.sparse_decode(qd, k, v), 10)
     b_a = 2 * B * w.kv_heads * n * D * eb + qo
     for name, t, nb in (("decode_kept", ms_k, b_k), ("decode_all", ms_a, b_a)):
         out[name] = {"ms": t, "keys_per_head": kk if name == "decode_kept" else n, "bytes": nb,
