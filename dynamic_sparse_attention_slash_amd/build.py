@@ -24,13 +24,18 @@ FLAGS = [
 ]
 
 
+# per-source extra flags: the attention kernels take maxima of scores that are
+# finite or -inf, never NaN, and rely on NaN-free fmaxf for single v_max3_f32
+EXTRA = {"sparse_attention.hip": ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -382,25 +382,17 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-// Max of three floats in one instruction: fmaxf would first quiet each
-// operand (v_max_f32 x, x, x) under the IEEE mode the kernels run in. The
-// compiler does not look inside the asm, so it would not put the wait states
-// that a VALU read of an MFMA result needs in front of it; `after` (not used by
-// the instruction) orders the asm behind max2v, a compiler-visible read of the
-// same MFMA result that does get them.
-__device__ __forceinline__ float max3f(float a, float b, float c, float after) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c), "v"(after));
-  return r;
-}
-// max(a, b) for non-NaN inputs, as an instruction the compiler schedules
-// itself; pinf is +inf from opaque_inf(), which keeps the compiler from turning
-// the med3 into a quieting max
-__device__ __forceinline__ float max2v(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
-__device__ __forceinline__ float opaque_inf() {
-  float x;
-  asm volatile("v_mov_b32 %0, 0x7f800000" : "=v"(x));
-  return x;
+// Max of the eight scores a lane holds for query block qb of a 32-key tile.
+// This file is compiled without NaN semantics (-fno-honor-nans; a masked
+// score is -inf, never NaN), so fmaxf needs no operand quieting and the
+// compiler forms v_max3_f32 itself, with the wait states that a VALU read of
+// an MFMA result needs in front of it.
+template <int QB>
+__device__ __forceinline__ float tile_max(const f32x4 (&st)[2][QB], int qb) {
+  const float a = fmaxf(fmaxf(st[0][qb][0], st[0][qb][1]), st[0][qb][2]);
+  const float b = fmaxf(fmaxf(a, st[0][qb][3]), st[1][qb][0]);
+  const float c = fmaxf(fmaxf(b, st[1][qb][1]), st[1][qb][2]);
+  return fmaxf(c, st[1][qb][3]);
 }
 
 // Row max over the four lane groups (lanes l, l^16, l^32, l^48 hold the same
@@ -491,7 +483,6 @@ __device__ void attend_panel(const uint16_t* __restrict__ qs, const uint16_t* __
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) rp1[qb] = q0 + 16 * qb + l16 + 1 - 4 * g;
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-  const float pinf = opaque_inf();
 
   // loads of sub-block dw into this wave's quarter of a stage. Slots past a
   // range's end read the rows that follow (zeros past the slab) and slots past
@@ -596,9 +587,7 @@ __device__ void attend_panel(const uint16_t* __restrict__ qs, const uint16_t* __
     bool up_any = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float t = max2v(st[0][qb][0], st[0][qb][1], pinf);
-      mx[qb] = max3f(max3f(t, st[0][qb][2], st[0][qb][3], t), max3f(st[1][qb][0], st[1][qb][1], st[1][qb][2], t),
-                     st[1][qb][3], t);
+      mx[qb] = tile_max<2>(st, qb);
       up_any |= mx[qb] > raise[qb];
     }
     if (__any(up_any)) {
@@ -878,7 +867,6 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) rp1[qb] = q0 + 16 * qb + l16 + 1 - 4 * g;
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-  const float pinf = opaque_inf();
 
   auto issue_loads = [&](const Desc& dw, char* stage) {
     char* dst = stage + 16 * wave * L::ROW;
@@ -953,9 +941,7 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
     bool up_any = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float t = max2v(st[0][qb][0], st[0][qb][1], pinf);
-      mx[qb] = max3f(max3f(t, st[0][qb][2], st[0][qb][3], t), max3f(st[1][qb][0], st[1][qb][1], st[1][qb][2], t),
-                     st[1][qb][3], t);
+      mx[qb] = tile_max<2>(st, qb);
       up_any |= mx[qb] > raise[qb];
     }
     if (__any(up_any)) {
