@@ -16,8 +16,7 @@ by eye against the pages it follows. Sources, cited by page title and section:
   score keys over a window of the last queries, with the q start/end
   restriction.
 
-Readings taken where the pages are silent or garbled (each is repeated in
-DESIGN.md):
+Readings taken where the pages are silent or garbled:
 
 R1  Mask semantics [MInf §1]: the constant c of A(M) = softmax(QK^T/sqrt(d) -
     c(1-M)) is taken to infinity, so masked entries are excluded exactly. The

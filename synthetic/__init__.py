@@ -3,7 +3,7 @@
 This module only draws inputs. It holds none of the attention method's
 arithmetic, so both the GPU path and the CPU oracle may be fed from it.
 
-The recipe (also stated in the design doc):
+The recipe:
 
 * Base: Q, K, V ~ N(0, 1) i.i.d., drawn in float32 with a seeded
   ``torch.Generator`` on the generation device, then cast to the workload
