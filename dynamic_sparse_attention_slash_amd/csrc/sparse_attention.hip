@@ -894,21 +894,28 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
     __syncthreads();
     if (tt + 1 < ntiles) issue_loads(uniform_desc(desc, 2 * (tt + 1) + wave, cnt), nxt);
     const Desc d[2] = {uniform_desc(desc, 2 * tt, cnt), uniform_desc(desc, 2 * tt + 1, cnt)};
-    f32x4 st[2][2];
+    // K operands of both sub-blocks in one batch of LDS reads. The MFMA
+    // blocks run at raised wave priority, so that the other wave on the SIMD
+    // fills the gaps between them with its softmax work.
+    u32x4 kop[2][DS];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4 kop[DS];
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int s = 0; s < DS; ++s)
-        kop[s] = *reinterpret_cast<const u32x4*>(cur + koff[s] + s2 * 16 * L::ROW);
+        kop[s2][s] = *reinterpret_cast<const u32x4*>(cur + koff[s] + s2 * 16 * L::ROW);
+    f32x4 st[2][2];
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < DS; ++s) acc = mfma_bf16(kop[s], qop[qb][s], acc);
+        for (int s = 0; s < DS; ++s) acc = mfma_bf16(kop[s2][s], qop[qb][s], acc);
         st[s2][qb] = acc;
       }
-    }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     if ((d[0].b | d[1].b) & F_MASK) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -962,16 +969,22 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
     for (int qb = 0; qb < 2; ++qb)
       pop[qb] = u32x4{pack_bf16x2(st[0][qb][0], st[0][qb][1]), pack_bf16x2(st[0][qb][2], st[0][qb][3]),
                       pack_bf16x2(st[1][qb][0], st[1][qb][1]), pack_bf16x2(st[1][qb][2], st[1][qb][3])};
+    // V^T operands in one batch of transposing LDS reads, then the P.V MFMAs
+    u32x4 vop[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const u32x2 x0 = lds_read_tr16(cur + voff[db]);
       const u32x2 x1 = lds_read_tr16(cur + voff[db] + 16 * L::ROW);
-      const u32x4 aop = {x0[0], x0[1], x1[0], x1[1]};
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma_bf16(aop, pop[qb], oacc[db][qb]);
+      vop[db] = u32x4{x0[0], x0[1], x1[0], x1[1]};
     }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma_bf16(vop[db], pop[qb], oacc[db][qb]);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) oacc[DB][qb] = mfma_bf16(ones, pop[qb], oacc[DB][qb]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   while (true) {

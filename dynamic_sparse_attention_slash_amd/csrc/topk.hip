@@ -232,28 +232,147 @@ __host__ __device__ constexpr bool two_pass(int32_t n, int32_t kk) {
 
 // One work-group per (row, query block a): top min(topk, a+1) of
 // logits[row][a][0..a] with entry a forced. The candidates are read from
-// memory in every pass (the row stays in cache); LDS holds only the
-// histograms, which keeps eight work-groups resident per CU.
+// memory in every pass (the row stays in cache).
+//
+// Most rows take two reads. Read 1 counts the top FAST_BITS bits of every key
+// into LDS bins; a suffix scan over the bins finds the bin b that holds the
+// kk-th largest key and how many keys lie in higher bins (all of them are
+// kept). Read 2 collects the indices of those keys and the (key, index) pairs
+// of bin b in LDS. Each bin-b entry's rank among the bin-b entries, in the
+// rank order (larger key, then smaller index), decides whether it fills one
+// of the remaining places; the kk kept indices are then sorted ascending in
+// LDS. A row whose bin b holds more than FAST_CAND entries (many keys sharing
+// their top bits: constant or heavily tied rows), or with kk > FAST_KEEP,
+// takes the radix select above instead. Either way the result is the unique
+// exact top kk.
 constexpr int BLK_WAVES = 4;
+constexpr int FAST_BITS = 12, FAST_BINS = 1 << FAST_BITS;
+constexpr int FAST_CAND = 1024, FAST_KEEP = 1024;
+struct FastShared {
+  union {
+    uint32_t hist[FAST_BINS];
+    struct {
+      uint32_t ckey[FAST_CAND];
+      int32_t cidx[FAST_CAND];
+      int32_t keep[FAST_KEEP];
+    } l;
+  } u;
+  uint32_t wsum[BLK_WAVES];
+  uint32_t bin, above, in_bin, n_c, n_k;
+};
+union BlockTopkShared {
+  FastShared f;
+  SelectShared<BLK_WAVES, 2> r;
+};
+
 __global__ __launch_bounds__(BLK_WAVES * 64) void block_topk_kernel(const float* __restrict__ logits,
                                                                     int32_t nb, int32_t topk,
                                                                     int32_t* __restrict__ sel,
                                                                     int32_t* __restrict__ n_sel) {
-  __shared__ SelectShared<BLK_WAVES, 2> sh;
+  __shared__ BlockTopkShared sh;
+  constexpr int NT = BLK_WAVES * 64;
+  constexpr int PER = FAST_BINS / NT;  // bins per thread in the scan
   const int32_t a = blockIdx.x, row = blockIdx.y;
   const int32_t m = a + 1;
   const int32_t kk = min(topk, m);
   const int32_t kstride = min(topk, nb);
   const size_t cb = (size_t)row * nb + a;
   int32_t* o = sel + cb * kstride;
-  if (threadIdx.x == 0) n_sel[cb] = kk;
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) n_sel[cb] = kk;
   if (kk >= m) {
-    for (int32_t i = threadIdx.x; i < m; i += BLK_WAVES * 64) o[i] = i;
+    for (int32_t i = tid; i < m; i += NT) o[i] = i;
     return;
   }
-  GlobalSeg seg{logits + cb * nb, a, 0, 0, 0, (int32_t)(threadIdx.x & 63), 0};
+  GlobalSeg seg{logits + cb * nb, a, 0, 0, 0, lane, 0};
   wave_segment<BLK_WAVES>(m, seg.s0, seg.s1, seg.trips);
-  select_topk<BLK_WAVES, 2>(seg, kk, o, nullptr, sh);
+  FastShared& f = sh.f;
+
+  // read 1: bin counts of the top FAST_BITS key bits
+  for (int i = tid; i < FAST_BINS; i += NT) f.u.hist[i] = 0;
+  if (tid == 0) { f.n_c = 0; f.n_k = 0; }
+  __syncthreads();
+  seg.visit([&](int32_t, uint32_t key, bool valid) {
+    if (valid) atomicAdd(&f.u.hist[key >> (32 - FAST_BITS)], 1u);
+  });
+  __syncthreads();
+  // thread t owns bins [PER t, PER t + PER); suffix sums over the threads
+  uint32_t loc[PER], tsum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) { loc[j] = f.u.hist[PER * tid + j]; tsum += loc[j]; }
+  uint32_t s = tsum;  // inclusive suffix sum within the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t x = __shfl_down(s, d);
+    if (lane + d < 64) s += x;
+  }
+  if (lane == 0) f.wsum[wave] = s;
+  __syncthreads();
+  uint32_t higher = s - tsum;  // entries in bins above this thread's
+  for (int w = wave + 1; w < BLK_WAVES; ++w) higher += f.wsum[w];
+  if (higher < (uint32_t)kk && higher + tsum >= (uint32_t)kk) {
+    uint32_t acc = higher;
+    for (int j = PER - 1; j >= 0; --j) {
+      if (acc + loc[j] >= (uint32_t)kk) {
+        f.bin = (uint32_t)(PER * tid + j);
+        f.above = acc;
+        f.in_bin = loc[j];
+        break;
+      }
+      acc += loc[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t bin = f.bin, above = f.above, in_bin = f.in_bin;
+  if (in_bin > (uint32_t)FAST_CAND || kk > FAST_KEEP) {
+    __syncthreads();  // every thread has read the bin before the radix select reuses LDS
+    select_topk<BLK_WAVES, 2>(seg, kk, o, nullptr, sh.r);
+    return;
+  }
+
+  // read 2: keys above bin b are kept; bin b entries become candidates
+  seg.visit([&](int32_t j, uint32_t key, bool valid) {
+    const uint32_t hb = key >> (32 - FAST_BITS);
+    if (valid && hb > bin) {
+      f.u.l.keep[atomicAdd(&f.n_k, 1u)] = seg.index(j);
+    } else if (valid && hb == bin) {
+      const uint32_t p = atomicAdd(&f.n_c, 1u);
+      f.u.l.ckey[p] = key;
+      f.u.l.cidx[p] = seg.index(j);
+    }
+  });
+  __syncthreads();
+  // candidate c is kept when fewer than kk - above candidates rank before it
+  const uint32_t places = (uint32_t)kk - above;
+  for (uint32_t c = tid; c < in_bin; c += NT) {
+    const uint32_t kc = f.u.l.ckey[c];
+    const int32_t ic = f.u.l.cidx[c];
+    uint32_t rank = 0;
+    for (uint32_t e = 0; e < in_bin; ++e) {
+      const uint32_t ke = f.u.l.ckey[e];
+      rank += (ke > kc || (ke == kc && f.u.l.cidx[e] < ic)) ? 1u : 0u;
+    }
+    if (rank < places) f.u.l.keep[atomicAdd(&f.n_k, 1u)] = ic;
+  }
+  // ascending order: bitonic sort of the kk kept indices, padded to a power of two
+  int32_t P = 1;
+  while (P < kk) P <<= 1;
+  __syncthreads();
+  for (int32_t i = kk + tid; i < P; i += NT) f.u.l.keep[i] = 0x7fffffff;
+  __syncthreads();
+  for (int32_t size = 2; size <= P; size <<= 1) {
+    for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int32_t t = tid; t < (P >> 1); t += NT) {
+        const int32_t i = 2 * t - (t & (stride - 1));  // lower element of the pair
+        const int32_t jx = i + stride;
+        const bool up = (i & size) == 0;
+        const int32_t x = f.u.l.keep[i], y = f.u.l.keep[jx];
+        if ((x > y) == up) { f.u.l.keep[i] = y; f.u.l.keep[jx] = x; }
+      }
+      __syncthreads();
+    }
+  }
+  for (int32_t i = tid; i < kk; i += NT) o[i] = f.u.l.keep[i];
 }
 
 }  // namespace

@@ -274,6 +274,37 @@ def test_bs_pool_select(n, D, dt, topk):
     assert torch.equal(sel2, sel) and torch.equal(n_sel2, n_sel)
 
 
+@pytest.mark.parametrize("case", ["ties", "wide_topk", "few_values"])
+def test_bs_select_bin_and_radix_paths(case):
+    """Rows of 1100 blocks through both selection paths: all-equal logits (the
+    whole row shares one key bin, which the bin path ranks while the row holds
+    at most 1024 entries and the radix select takes beyond), a topk above 1024
+    (radix select), and logits with few distinct values (large tied bins).
+    Indices bit-exact against the oracle on the GPU's logits."""
+    say(f"bs_select paths case={case}")
+    nb, D = 1100, 64
+    g = torch.Generator(device="cuda").manual_seed(5)
+    kp = torch.randn(1, nb, D, generator=g, device="cuda")
+    qp = torch.randn(1, nb, D, generator=g, device="cuda")
+    topk = 40
+    if case == "ties":
+        qp.zero_()
+    elif case == "wide_topk":
+        topk = 1050
+    else:
+        qp = torch.randint(-1, 2, (1, nb, D), generator=g, device="cuda").float()
+        kp = torch.randint(-1, 2, (1, nb, D), generator=g, device="cuda").float()
+        topk = 300
+    sel, n_sel, lg = dsa.bs_select(qp, kp, topk, return_logits=True)
+    torch.cuda.synchronize()
+    Lg = lg[0].cpu().numpy()
+    want = O.block_select(Lg, topk)
+    s_h, n_h = sel[0].cpu().numpy(), n_sel[0].cpu().numpy()
+    for a in range(nb):
+        assert int(n_h[a]) == min(topk, a + 1)
+        assert np.array_equal(s_h[a, : int(n_h[a])], want[a]), (case, a)
+
+
 # ---------------------------------------------------------------------------
 # the three public calls end to end
 # ---------------------------------------------------------------------------
