@@ -248,6 +248,7 @@ __host__ __device__ constexpr bool two_pass(int32_t n, int32_t kk) {
 constexpr int BLK_WAVES = 4;
 constexpr int FAST_BITS = 12, FAST_BINS = 1 << FAST_BITS;
 constexpr int FAST_CAND = 1024, FAST_KEEP = 1024;
+constexpr int FAST_LOADS = 8;  // row loads in flight per thread
 struct FastShared {
   union {
     uint32_t hist[FAST_BINS];
@@ -284,17 +285,33 @@ __global__ __launch_bounds__(BLK_WAVES * 64) void block_topk_kernel(const float*
     for (int32_t i = tid; i < m; i += NT) o[i] = i;
     return;
   }
-  GlobalSeg seg{logits + cb * nb, a, 0, 0, 0, lane, 0};
+  const float* x = logits + cb * nb;
+  GlobalSeg seg{x, a, 0, 0, 0, lane, 0};
   wave_segment<BLK_WAVES>(m, seg.s0, seg.s1, seg.trips);
   FastShared& f = sh.f;
+  // the row's keys in any order, FAST_LOADS loads in flight per thread
+  auto each_key = [&](auto&& fn) {
+    constexpr int U = FAST_LOADS;
+    for (int32_t i0 = 0; i0 < m; i0 += U * NT) {
+      float xv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t i = i0 + u * NT + tid;
+        xv[u] = i < m ? x[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t i = i0 + u * NT + tid;
+        if (i < m) fn(i, i == a ? FORCED_KEY : score_key(xv[u]));
+      }
+    }
+  };
 
   // read 1: bin counts of the top FAST_BITS key bits
   for (int i = tid; i < FAST_BINS; i += NT) f.u.hist[i] = 0;
   if (tid == 0) { f.n_c = 0; f.n_k = 0; }
   __syncthreads();
-  seg.visit([&](int32_t, uint32_t key, bool valid) {
-    if (valid) atomicAdd(&f.u.hist[key >> (32 - FAST_BITS)], 1u);
-  });
+  each_key([&](int32_t, uint32_t key) { atomicAdd(&f.u.hist[key >> (32 - FAST_BITS)], 1u); });
   __syncthreads();
   // thread t owns bins [PER t, PER t + PER); suffix sums over the threads
   uint32_t loc[PER], tsum = 0;
@@ -331,14 +348,14 @@ __global__ __launch_bounds__(BLK_WAVES * 64) void block_topk_kernel(const float*
   }
 
   // read 2: keys above bin b are kept; bin b entries become candidates
-  seg.visit([&](int32_t j, uint32_t key, bool valid) {
+  each_key([&](int32_t i, uint32_t key) {
     const uint32_t hb = key >> (32 - FAST_BITS);
-    if (valid && hb > bin) {
-      f.u.l.keep[atomicAdd(&f.n_k, 1u)] = seg.index(j);
-    } else if (valid && hb == bin) {
+    if (hb > bin) {
+      f.u.l.keep[atomicAdd(&f.n_k, 1u)] = i;
+    } else if (hb == bin) {
       const uint32_t p = atomicAdd(&f.n_c, 1u);
       f.u.l.ckey[p] = key;
-      f.u.l.cidx[p] = seg.index(j);
+      f.u.l.cidx[p] = i;
     }
   });
   __syncthreads();
