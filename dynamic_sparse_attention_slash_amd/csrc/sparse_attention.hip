@@ -512,22 +512,27 @@ __device__ void attend_panel(const uint16_t* __restrict__ qs, const uint16_t* __
   auto half = [&](const char* cur, const PDesc& d0, const PDesc& d1) {
     const uint32_t m0 = (d0.vm >> (16 * blk)) & 0xffffu, m1 = (d1.vm >> (16 * blk)) & 0xffffu;
     if ((m0 | m1) == 0u) return;
-    // S^T = K Q^T
-    f32x4 st[2][2];
+    // S^T = K Q^T: K operands of both sub-blocks in one batch of LDS reads,
+    // the MFMAs at raised wave priority (as in the single-block kernel)
+    u32x4 kop[2][DS];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4 kop[DS];
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int s = 0; s < DS; ++s)
-        kop[s] = *reinterpret_cast<const u32x4*>(cur + koff[s] + s2 * 16 * L::ROW);
+        kop[s2][s] = *reinterpret_cast<const u32x4*>(cur + koff[s] + s2 * 16 * L::ROW);
+    f32x4 st[2][2];
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < DS; ++s) acc = mfma_bf16(kop[s], qop[qb][s], acc);
+        for (int s = 0; s < DS; ++s) acc = mfma_bf16(kop[s2][s], qop[qb][s], acc);
         st[s2][qb] = acc;
       }
-    }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     if ((m0 & m1) != 0xffffu || ((d0.f | d1.f) & (P_DIAG << blk))) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -610,16 +615,21 @@ __device__ void attend_panel(const uint16_t* __restrict__ qs, const uint16_t* __
       pop[qb] = u32x4{pack_bf16x2(st[0][qb][0], st[0][qb][1]), pack_bf16x2(st[0][qb][2], st[0][qb][3]),
                       pack_bf16x2(st[1][qb][0], st[1][qb][1]), pack_bf16x2(st[1][qb][2], st[1][qb][3])};
     // O^T += V^T P^T
+    u32x4 vop[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const u32x2 x0 = lds_read_tr16(cur + voff[db]);
       const u32x2 x1 = lds_read_tr16(cur + voff[db] + 16 * L::ROW);
-      const u32x4 aop = {x0[0], x0[1], x1[0], x1[1]};
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma_bf16(aop, pop[qb], oacc[db][qb]);
+      vop[db] = u32x4{x0[0], x0[1], x1[0], x1[1]};
     }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma_bf16(vop[db], pop[qb], oacc[db][qb]);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) oacc[DB][qb] = mfma_bf16(ones, pop[qb], oacc[DB][qb]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // one tile: wait for its loads, start the next tile's, compute both halves
