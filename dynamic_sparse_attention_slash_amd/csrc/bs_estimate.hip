@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64) void logits_kernel(const float* __restrict__ qp
     qa[b4] = q + (size_t)min(at * 64 + 16 * b4 + l16, nb - 1) * D + 8 * g;
     kc[b4] = k + (size_t)min(ct * 64 + 16 * b4 + l16, nb - 1) * D + 8 * g;
   }
-#pragma unroll 1
+#pragma unroll
   for (int s = 0; s < KS; ++s) {
     u32x4 ah[4], al[4];
 #pragma unroll
