@@ -75,6 +75,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
 
+// XOR swizzle of the 16-byte chunks of LDS row r (an XOR-linear map of r's
+// low four bits), under which 16 rows read at one logical chunk per 16 lanes
+// (ds_read_b128) and 4 rows x 2 chunks per 16 lanes (ds_read_b64 and its
+// transposing form) touch distinct banks in every pass of gfx950's LDS.
+// Chunk c of row r lives at chunk c ^ lds_chunk_swz(r) (masked to the row's
+// chunk count).
+__device__ __forceinline__ int lds_chunk_swz(int r) {
+  return (int)((0xae629d51bf738c40ull >> (4 * (r & 15))) & 15);
+}
+
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float NEG_BIG = -1.0e30f;  // finite "minus infinity" for running maxima
 

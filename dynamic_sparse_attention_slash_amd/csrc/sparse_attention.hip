@@ -367,9 +367,7 @@ struct TileLds {
   // ds_read_b64 / ds_read_b64_tr_b16 in two passes of 32 lanes. The K reads (16
   // rows at one logical chunk per 16 lanes) and the V^T reads (4 rows x 2
   // chunks per 16 lanes) touch distinct banks in every pass.
-  __device__ static int swz(int r) {
-    return (int)((0xae629d51bf738c40ull >> (4 * (r & 15))) & 15) & (UNITS - 1);
-  }
+  __device__ static int swz(int r) { return lds_chunk_swz(r) & (UNITS - 1); }
   // byte offset of logical chunk c of row r
   __device__ static int off(int r, int c) { return r * ROW + 16 * (c ^ swz(r)); }
 };

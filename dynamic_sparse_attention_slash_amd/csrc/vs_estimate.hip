@@ -156,6 +156,80 @@ struct KStream {
   }
 };
 
+// bf16 K of 16-key steps through a ring of KR_STAGES steps in LDS: each step
+// goes global -> LDS by DMA (buffer_load ... lds, no registers) two steps
+// before it is used, into its own stage array (12 KB per wave at D = 128, so
+// three waves per SIMD stay resident). Rows are stored with the swizzle the
+// attention tiles use, so the K operand reads are free of bank conflicts.
+// Rows past the head's slab read as zeros (buffer range check); their scores
+// are masked.
+constexpr int KR_STAGES = 3;
+template <int D>
+struct KRing {
+  static constexpr int ROW = D * 2;          // bytes per key
+  static constexpr int UNITS = ROW / 16;     // 16-byte chunks per key
+  static constexpr int STEP = 16 * ROW;      // bytes per 16-key step
+  static constexpr int INSTR = STEP / 1024;  // DMA instructions per step
+  static constexpr int RPI = 64 / UNITS;     // key rows per DMA instruction
+  static constexpr int DS = D / 32;
+  __amdgpu_buffer_rsrc_t rs;
+  int32_t ld_off[INSTR];  // byte offset of this lane's 16 bytes within a step
+  int32_t koff[DS];       // LDS offset of this lane's K operand of k-step s
+  __device__ KRing(const uint16_t* ks, int32_t n) {
+    const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+    rs = __builtin_amdgcn_make_buffer_rsrc((void*)ks, (short)0, (uint32_t)n * ROW, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < INSTR; ++k) {
+      const int32_t r = k * RPI + lane / UNITS;
+      ld_off[k] = r * ROW + 16 * ((lane % UNITS) ^ (lds_chunk_swz(r) & (UNITS - 1)));
+    }
+#pragma unroll
+    for (int s = 0; s < DS; ++s) koff[s] = l16 * ROW + 16 * (((D / 32) * g + s) ^ (lds_chunk_swz(l16) & (UNITS - 1)));
+  }
+  // keys [j0, j0 + 16) into stage: lane L of instruction k lands at byte
+  // k * 1024 + 16 L, i.e. row k * RPI + L / UNITS, chunk slot L % UNITS
+  __device__ void issue(int32_t j0, char* stage) const {
+#pragma unroll
+    for (int k = 0; k < INSTR; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + k * 1024), 16,
+                                               j0 * ROW + ld_off[k], 0, 0, 0);
+  }
+  // Waits until this lane's DMA of the current step (issued KR_STAGES - 1
+  // steps back) has landed, then reads the K operands. Every step issues
+  // exactly INSTR DMA loads, so at least INSTR * (KR_STAGES - 1) vector
+  // memory operations follow the current step's; loads completing in order,
+  // vmcnt of that count suffices (other loads and stores issued in between
+  // only make it stricter).
+  // The reads are one asm block that waits for its own results: the compiler
+  // cannot tell which stage an LDS DMA writes, and would otherwise drain
+  // every load in flight before each read.
+  __device__ void read(const char* stage, typename Tile<uint16_t, D>::KReg& k) const {
+    constexpr int ahead = INSTR * (KR_STAGES - 1);  // DMA loads issued after this step's
+    static_assert(ahead < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ahead);     // vmcnt(ahead), no expcnt / lgkmcnt wait
+    const uint32_t base = (uint32_t)(uintptr_t)stage;
+    if constexpr (DS == 4) {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %5\n\t"
+          "ds_read_b128 %2, %6\n\t"
+          "ds_read_b128 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k.v[0]), "=&v"(k.v[1]), "=&v"(k.v[2]), "=&v"(k.v[3])
+          : "v"(base + koff[0]), "v"(base + koff[1]), "v"(base + koff[2]), "v"(base + koff[3])
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %2\n\t"
+          "ds_read_b128 %1, %3\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k.v[0]), "=&v"(k.v[1])
+          : "v"(base + koff[0]), "v"(base + koff[1])
+          : "memory");
+    }
+  }
+};
+
 // bf16: three waves per SIMD, so the prefetched K costs no occupancy
 #define EST_KERNEL \
   __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1, sizeof(T) == 2 ? 3 : 8)))
@@ -178,10 +252,7 @@ EST_KERNEL void est_stats_kernel(EstArgs a) {
 
   const int32_t j_begin = chunk * C, j_end = min(a.seq_len, j_begin + C);
   const float sc = a.scale_log2;
-  KStream<T, D> kst(tile, ks, j_begin, w);
-  for (int32_t j0 = j_begin; j0 < j_end; j0 += 16) {
-    f32x4 x[4];
-    kst.scores(tile, ks, j0, w, x);
+  auto step = [&](const f32x4 (&x)[4]) {
     // running (max, sum) with a deferred max: d = x * scale * log2(e) - m in
     // one FMA; the reference m is raised only when d exceeds 8 (then d = 0)
     f32x4 d[4];
@@ -209,6 +280,39 @@ EST_KERNEL void est_stats_kernel(EstArgs a) {
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[qb][i] += fast_exp2(d[qb][i]);
+  };
+  if constexpr (sizeof(T) == 2) {
+    __shared__ __align__(16) char kr0[KRing<D>::STEP], kr1[KRing<D>::STEP], kr2[KRing<D>::STEP];
+    char* const stage[KR_STAGES] = {kr0, kr1, kr2};
+    const KRing<D> ring(ks, a.seq_len);
+    // every step issues its INSTR loads, past the chunk's end too (rows of
+    // the next chunk, or zeros past the slab, into stages never read), so
+    // that the wait count in ring.read is exact
+#pragma unroll
+    for (int u = 0; u < KR_STAGES - 1; ++u) ring.issue(j_begin + 16 * u, stage[u]);
+    for (int32_t t0 = j_begin; t0 < j_end; t0 += 16 * KR_STAGES) {
+#pragma unroll
+      for (int u = 0; u < KR_STAGES; ++u) {
+        const int32_t j0 = t0 + 16 * u;
+        // the stage of step u - 1 is consumed: refill it with step u + KR_STAGES - 1
+        ring.issue(j0 + 16 * (KR_STAGES - 1), stage[(u + KR_STAGES - 1) % KR_STAGES]);
+        if (j0 < j_end) {
+          typename Tile<T, D>::KReg kc;
+          ring.read(stage[u], kc);
+          f32x4 x[4];
+          tile.scores_k(kc, j0, w, x);
+          step(x);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // no DMA into LDS outlives the loop
+  } else {
+    KStream<T, D> kst(tile, ks, j_begin, w);
+    for (int32_t j0 = j_begin; j0 < j_end; j0 += 16) {
+      f32x4 x[4];
+      kst.scores(tile, ks, j0, w, x);
+      step(x);
+    }
   }
   // merge the 16 key columns of each row (lanes with equal l >> 4)
 #pragma unroll
@@ -283,6 +387,54 @@ __global__ __launch_bounds__(64 * COMB_SPLIT) void est_combine_kernel(EstArgs a,
   }
 }
 
+// Column sums of one chunk (no slash scores) with K through the LDS ring as
+// in the stats pass; the column-sum stores between the loads only make the
+// ring's fixed wait count conservative.
+template <int D>
+__device__ void ring_column_sums(const EstArgs& a, const Tile<uint16_t, D>& tile, const uint16_t* ks,
+                                 const Window& w, const float (&F)[4][4], float* vout, int32_t j_begin,
+                                 int32_t j_end) {
+  using T = uint16_t;
+  const int32_t g = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+  const float sc = a.scale_log2;
+  __shared__ __align__(16) char kr0[KRing<D>::STEP], kr1[KRing<D>::STEP], kr2[KRing<D>::STEP];
+  char* const stage[KR_STAGES] = {kr0, kr1, kr2};
+  const KRing<D> ring(ks, a.seq_len);
+  // the window slices after the first add into v: each step's earlier v
+  // is loaded together with its K, so that waiting for it never drains the
+  // loads issued after it
+  float vprev[KR_STAGES];
+  auto load_v = [&](int32_t j0) { return vout[min(j0 + l16, a.seq_len - 1)]; };
+#pragma unroll
+  for (int u = 0; u < KR_STAGES - 1; ++u) {
+    vprev[u] = a.add_v ? load_v(j_begin + 16 * u) : 0.f;
+    ring.issue(j_begin + 16 * u, stage[u]);
+  }
+  for (int32_t t0 = j_begin; t0 < j_end; t0 += 16 * KR_STAGES) {
+#pragma unroll
+    for (int u = 0; u < KR_STAGES; ++u) {
+      const int32_t j0 = t0 + 16 * u, jn = j0 + 16 * (KR_STAGES - 1);
+      const int un = (u + KR_STAGES - 1) % KR_STAGES;  // constant after unrolling
+      vprev[un] = a.add_v ? load_v(jn) : 0.f;
+      ring.issue(jn, stage[un]);
+      if (j0 < j_end) {
+        typename Tile<T, D>::KReg kc;
+        ring.read(stage[u], kc);
+        f32x4 x[4];
+        tile.scores_k(kc, j0, w, x);
+        float colsum = 0.f;
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) colsum += fast_exp2(__builtin_fmaf(x[qb][i], sc, -F[qb][i]));
+        colsum = xor_sum(xor_sum(colsum, 16), 32);
+        if (g == 0 && j0 + l16 < a.seq_len) vout[j0 + l16] = a.add_v ? vprev[u] + colsum : colsum;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA into LDS outlives the loop
+}
+
 // S: slash scores wanted (a.want_s); without them the probabilities never
 // go through LDS
 template <typename T, int D, bool S>
@@ -309,6 +461,10 @@ EST_KERNEL void est_scores_kernel(EstArgs a) {
   float* vout = a.v_scores + (size_t)row * a.seq_len;
   const float sc = a.scale_log2;
   const int32_t j_begin = chunk * C, j_end = min(a.seq_len, j_begin + C);
+  if constexpr (sizeof(T) == 2 && !S) {
+    ring_column_sums<D>(a, tile, ks, w, F, vout, j_begin, j_end);
+    return;
+  }
   KStream<T, D> kst(tile, ks, j_begin, w);
   for (int32_t t0 = j_begin; t0 < j_end; t0 += 64) {
 #pragma unroll
