@@ -7,7 +7,10 @@
 // -inf. Output indices are ascending.
 //
 // Method: scores map to order-preserving 32-bit keys (the forced entry gets
-// the maximum key, which no canonical float reaches). A 4-pass MSB-first radix
+// the maximum key, which no canonical float reaches). Whole rows and the
+// block lists first try a two-read select over 12-bit key bins (described at
+// select_bins below); rows it cannot take, and the chunk and merge passes of
+// long rows, use the radix select: a 4-pass MSB-first radix
 // select (8 bits per pass) finds the k-th largest key T and how many entries
 // equal to T must be kept (need_eq). Each pass counts digits into LDS
 // histograms, one copy per wave and lane group so that the few bins a float
@@ -42,15 +45,30 @@ struct SelectShared {
 // The keys of one wave's segment [s0, s1) of the candidates, visited in
 // ascending position order 64 at a time: visit(f) calls f(j, key, valid) for
 // position s0 + 64 j + lane, j < trips (trips is uniform over the wave).
+// The trips' loads are issued VISIT_LOADS at a time ahead of their callbacks
+// (which still run in trip order), so that a pass over a long segment is not
+// one memory latency per trip.
+constexpr int VISIT_LOADS = 8;
 struct GlobalSeg {
   const float* x; int32_t forced, s0, s1, trips, lane;
   int32_t base;  // index of x[0] in the output
   template <class F>
   __device__ __forceinline__ void visit(F&& f) const {
-    for (int32_t j = 0; j < trips; ++j) {
-      const int32_t i = s0 + 64 * j + lane;
-      const bool valid = i < s1;
-      f(j, valid ? (i == forced ? FORCED_KEY : score_key(x[i])) : 0u, valid);
+    for (int32_t j0 = 0; j0 < trips; j0 += VISIT_LOADS) {
+      float xv[VISIT_LOADS];
+#pragma unroll
+      for (int u = 0; u < VISIT_LOADS; ++u) {
+        const int32_t i = s0 + 64 * (j0 + u) + lane;
+        xv[u] = (j0 + u < trips && i < s1) ? x[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < VISIT_LOADS; ++u) {
+        const int32_t j = j0 + u;
+        if (j >= trips) break;
+        const int32_t i = s0 + 64 * j + lane;
+        const bool valid = i < s1;
+        f(j, valid ? (i == forced ? FORCED_KEY : score_key(xv[u])) : 0u, valid);
+      }
     }
   }
   __device__ __forceinline__ int32_t index(int32_t j) const { return base + s0 + 64 * j + lane; }
@@ -60,10 +78,20 @@ struct KeySeg {
   const uint32_t* keys; const int32_t* idx; int32_t s0, s1, trips, lane;
   template <class F>
   __device__ __forceinline__ void visit(F&& f) const {
-    for (int32_t j = 0; j < trips; ++j) {
-      const int32_t i = s0 + 64 * j + lane;
-      const bool valid = i < s1;
-      f(j, valid ? keys[i] : 0u, valid);
+    for (int32_t j0 = 0; j0 < trips; j0 += VISIT_LOADS) {
+      uint32_t kv[VISIT_LOADS];
+#pragma unroll
+      for (int u = 0; u < VISIT_LOADS; ++u) {
+        const int32_t i = s0 + 64 * (j0 + u) + lane;
+        kv[u] = (j0 + u < trips && i < s1) ? keys[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < VISIT_LOADS; ++u) {
+        const int32_t j = j0 + u;
+        if (j >= trips) break;
+        const int32_t i = s0 + 64 * j + lane;
+        f(j, i < s1 ? kv[u] : 0u, i < s1);
+      }
     }
   }
   __device__ __forceinline__ int32_t index(int32_t j) const { return idx[s0 + 64 * j + lane]; }
@@ -160,20 +188,188 @@ __device__ __forceinline__ void select_topk(const Seg& seg, int32_t kk, int32_t*
   });
 }
 
+// Two-read select. Read 1 counts the top BIN_BITS bits of every key into LDS
+// bins; a suffix scan over the bins finds the bin b that holds the kk-th
+// largest key and how many keys lie in higher bins (all of them are kept).
+// Read 2 collects those keys' indices and the (key, index) pairs of bin b in
+// LDS. Each bin-b entry's rank among the bin-b entries, in the rank order
+// (larger key, then smaller index), decides whether it fills one of the
+// remaining places; the kk kept entries are then sorted by index in LDS. A
+// row whose bin b holds more than CAND entries (many keys sharing their top
+// bits: constant or heavily tied rows), or with kk > KEEP, is left to the
+// radix select: the function then returns false having written nothing.
+// Either way the result is the unique exact top kk.
+constexpr int BIN_BITS = 12, BINS = 1 << BIN_BITS;
+constexpr int BIN_LOADS = 8;  // keys loaded ahead per thread
+template <int NW, int CAND, int KEEP, bool KEYS>
+struct BinShared {
+  union {
+    uint32_t hist[BINS];
+    struct {
+      uint32_t ckey[CAND];
+      int32_t cidx[CAND];
+      int32_t kidx[KEEP];
+      uint32_t kkey[KEYS ? KEEP : 1];
+    } l;
+  } u;
+  uint32_t wsum[NW];
+  uint32_t bin, above, in_bin, n_c, n_k;
+};
+
+// key_at(i) / idx_at(i): key and output index of entry i < m (visited in any
+// order, BIN_LOADS keys in flight per thread). Writes out[0..kk) ascending
+// (and their keys to out_key when KEYS).
+template <int NW, int CAND, int KEEP, bool KEYS, class KeyAt, class IdxAt>
+__device__ bool select_bins(KeyAt key_at, IdxAt idx_at, int32_t m, int32_t kk, int32_t* __restrict__ out,
+                            uint32_t* __restrict__ out_key, BinShared<NW, CAND, KEEP, KEYS>& f) {
+  constexpr int NT = NW * 64;
+  constexpr int PER = BINS / NT;  // bins per thread in the scan
+  static_assert(PER * NT == BINS, "bins per thread");
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto each_key = [&](auto&& fn) {
+    for (int32_t i0 = 0; i0 < m; i0 += BIN_LOADS * NT) {
+      uint32_t kv[BIN_LOADS];
+#pragma unroll
+      for (int u = 0; u < BIN_LOADS; ++u) {
+        const int32_t i = i0 + u * NT + tid;
+        kv[u] = i < m ? key_at(i) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < BIN_LOADS; ++u) {
+        const int32_t i = i0 + u * NT + tid;
+        if (i < m) fn(i, kv[u]);
+      }
+    }
+  };
+
+  // read 1: bin counts of the top BIN_BITS key bits
+  for (int i = tid; i < BINS; i += NT) f.u.hist[i] = 0;
+  if (tid == 0) { f.n_c = 0; f.n_k = 0; }
+  __syncthreads();
+  each_key([&](int32_t, uint32_t key) { atomicAdd(&f.u.hist[key >> (32 - BIN_BITS)], 1u); });
+  __syncthreads();
+  // thread t owns bins [PER t, PER t + PER); suffix sums over the threads
+  uint32_t loc[PER], tsum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) { loc[j] = f.u.hist[PER * tid + j]; tsum += loc[j]; }
+  uint32_t s = tsum;  // inclusive suffix sum within the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t x = __shfl_down(s, d);
+    if (lane + d < 64) s += x;
+  }
+  if (lane == 0) f.wsum[wave] = s;
+  __syncthreads();
+  uint32_t higher = s - tsum;  // entries in bins above this thread's
+  for (int w = wave + 1; w < NW; ++w) higher += f.wsum[w];
+  if (higher < (uint32_t)kk && higher + tsum >= (uint32_t)kk) {
+    uint32_t acc = higher;
+    for (int j = PER - 1; j >= 0; --j) {
+      if (acc + loc[j] >= (uint32_t)kk) {
+        f.bin = (uint32_t)(PER * tid + j);
+        f.above = acc;
+        f.in_bin = loc[j];
+        break;
+      }
+      acc += loc[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t bin = f.bin, above = f.above, in_bin = f.in_bin;
+  if (in_bin > (uint32_t)CAND || kk > KEEP) {
+    __syncthreads();  // every thread has read the bin before LDS is reused
+    return false;
+  }
+
+  // read 2: keys above bin b are kept; bin b entries become candidates
+  each_key([&](int32_t i, uint32_t key) {
+    const uint32_t hb = key >> (32 - BIN_BITS);
+    if (hb > bin) {
+      const uint32_t p = atomicAdd(&f.n_k, 1u);
+      f.u.l.kidx[p] = idx_at(i);
+      if (KEYS) f.u.l.kkey[p] = key;
+    } else if (hb == bin) {
+      const uint32_t p = atomicAdd(&f.n_c, 1u);
+      f.u.l.ckey[p] = key;
+      f.u.l.cidx[p] = idx_at(i);
+    }
+  });
+  __syncthreads();
+  // candidate c is kept when fewer than kk - above candidates rank before it
+  const uint32_t places = (uint32_t)kk - above;
+  for (uint32_t c = tid; c < in_bin; c += NT) {
+    const uint32_t kc = f.u.l.ckey[c];
+    const int32_t ic = f.u.l.cidx[c];
+    uint32_t rank = 0;
+    for (uint32_t e = 0; e < in_bin; ++e) {
+      const uint32_t ke = f.u.l.ckey[e];
+      rank += (ke > kc || (ke == kc && f.u.l.cidx[e] < ic)) ? 1u : 0u;
+    }
+    if (rank < places) {
+      const uint32_t p = atomicAdd(&f.n_k, 1u);
+      f.u.l.kidx[p] = ic;
+      if (KEYS) f.u.l.kkey[p] = kc;
+    }
+  }
+  // ascending indices: bitonic sort of the kk kept entries, padded to a power of two
+  int32_t P = 1;
+  while (P < kk) P <<= 1;
+  __syncthreads();
+  for (int32_t i = kk + tid; i < P; i += NT) f.u.l.kidx[i] = 0x7fffffff;
+  __syncthreads();
+  for (int32_t size = 2; size <= P; size <<= 1) {
+    for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int32_t t = tid; t < (P >> 1); t += NT) {
+        const int32_t i = 2 * t - (t & (stride - 1));  // lower element of the pair
+        const int32_t jx = i + stride;
+        const bool up = (i & size) == 0;
+        const int32_t x = f.u.l.kidx[i], y = f.u.l.kidx[jx];
+        if ((x > y) == up) {
+          f.u.l.kidx[i] = y;
+          f.u.l.kidx[jx] = x;
+          if (KEYS) {
+            const uint32_t kx = f.u.l.kkey[i];
+            f.u.l.kkey[i] = f.u.l.kkey[jx];
+            f.u.l.kkey[jx] = kx;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int32_t i = tid; i < kk; i += NT) {
+    out[i] = f.u.l.kidx[i];
+    if (KEYS) out_key[i] = f.u.l.kkey[i];
+  }
+  return true;
+}
+
+// Rows of up to two 64K chunks: one work-group per row, two-read select
+// (kk up to 8192). The chunk and merge passes of longer rows keep the radix
+// select: there the two-read select measured slower (its larger LDS keeps
+// one work-group per CU, and the merge candidates crowd into few bins).
+union RowTopkShared {
+  BinShared<16, 2048, 8192, false> f;
+  SelectShared<16, 2> r;
+};
 constexpr int ROW_WAVES = 16;
 __global__ __launch_bounds__(ROW_WAVES * 64) void topk_rows_kernel(const float* __restrict__ scores,
                                                                    int32_t n, int32_t kk, int32_t forced,
                                                                    int32_t* __restrict__ out) {
-  __shared__ SelectShared<ROW_WAVES, 2> sh;
+  __shared__ RowTopkShared sh;
   const int32_t row = blockIdx.x;
   int32_t* o = out + (size_t)row * kk;
   if (kk >= n) {
     for (int32_t i = threadIdx.x; i < n; i += ROW_WAVES * 64) o[i] = i;
     return;
   }
-  GlobalSeg seg{scores + (size_t)row * n, forced, 0, 0, 0, (int32_t)(threadIdx.x & 63), 0};
+  const float* x = scores + (size_t)row * n;
+  auto key_at = [&](int32_t i) { return i == forced ? FORCED_KEY : score_key(x[i]); };
+  auto idx_at = [](int32_t i) { return i; };
+  if (select_bins<ROW_WAVES>(key_at, idx_at, n, kk, o, (uint32_t*)nullptr, sh.f)) return;
+  GlobalSeg seg{x, forced, 0, 0, 0, (int32_t)(threadIdx.x & 63), 0};
   wave_segment<ROW_WAVES>(n, seg.s0, seg.s1, seg.trips);
-  select_topk<ROW_WAVES, 2>(seg, kk, o, nullptr, sh);
+  select_topk<ROW_WAVES, 2>(seg, kk, o, nullptr, sh.r);
 }
 
 // Long rows in two passes. Pass 1: every TOPK_CHUNK-long chunk of a row keeps
@@ -231,38 +427,11 @@ __host__ __device__ constexpr bool two_pass(int32_t n, int32_t kk) {
 }
 
 // One work-group per (row, query block a): top min(topk, a+1) of
-// logits[row][a][0..a] with entry a forced. The candidates are read from
-// memory in every pass (the row stays in cache).
-//
-// Most rows take two reads. Read 1 counts the top FAST_BITS bits of every key
-// into LDS bins; a suffix scan over the bins finds the bin b that holds the
-// kk-th largest key and how many keys lie in higher bins (all of them are
-// kept). Read 2 collects the indices of those keys and the (key, index) pairs
-// of bin b in LDS. Each bin-b entry's rank among the bin-b entries, in the
-// rank order (larger key, then smaller index), decides whether it fills one
-// of the remaining places; the kk kept indices are then sorted ascending in
-// LDS. A row whose bin b holds more than FAST_CAND entries (many keys sharing
-// their top bits: constant or heavily tied rows), or with kk > FAST_KEEP,
-// takes the radix select above instead. Either way the result is the unique
-// exact top kk.
+// logits[row][a][0..a] with entry a forced, by the two-read select (the
+// row stays in cache between the reads), else by the radix select.
 constexpr int BLK_WAVES = 4;
-constexpr int FAST_BITS = 12, FAST_BINS = 1 << FAST_BITS;
-constexpr int FAST_CAND = 1024, FAST_KEEP = 1024;
-constexpr int FAST_LOADS = 8;  // row loads in flight per thread
-struct FastShared {
-  union {
-    uint32_t hist[FAST_BINS];
-    struct {
-      uint32_t ckey[FAST_CAND];
-      int32_t cidx[FAST_CAND];
-      int32_t keep[FAST_KEEP];
-    } l;
-  } u;
-  uint32_t wsum[BLK_WAVES];
-  uint32_t bin, above, in_bin, n_c, n_k;
-};
 union BlockTopkShared {
-  FastShared f;
+  BinShared<BLK_WAVES, 1024, 1024, false> f;
   SelectShared<BLK_WAVES, 2> r;
 };
 
@@ -272,124 +441,24 @@ __global__ __launch_bounds__(BLK_WAVES * 64) void block_topk_kernel(const float*
                                                                     int32_t* __restrict__ n_sel) {
   __shared__ BlockTopkShared sh;
   constexpr int NT = BLK_WAVES * 64;
-  constexpr int PER = FAST_BINS / NT;  // bins per thread in the scan
   const int32_t a = blockIdx.x, row = blockIdx.y;
   const int32_t m = a + 1;
   const int32_t kk = min(topk, m);
   const int32_t kstride = min(topk, nb);
   const size_t cb = (size_t)row * nb + a;
   int32_t* o = sel + cb * kstride;
-  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) n_sel[cb] = kk;
+  if (threadIdx.x == 0) n_sel[cb] = kk;
   if (kk >= m) {
-    for (int32_t i = tid; i < m; i += NT) o[i] = i;
+    for (int32_t i = threadIdx.x; i < m; i += NT) o[i] = i;
     return;
   }
   const float* x = logits + cb * nb;
-  GlobalSeg seg{x, a, 0, 0, 0, lane, 0};
+  auto key_at = [&](int32_t i) { return i == a ? FORCED_KEY : score_key(x[i]); };
+  auto idx_at = [](int32_t i) { return i; };
+  if (select_bins<BLK_WAVES>(key_at, idx_at, m, kk, o, (uint32_t*)nullptr, sh.f)) return;
+  GlobalSeg seg{x, a, 0, 0, 0, (int32_t)(threadIdx.x & 63), 0};
   wave_segment<BLK_WAVES>(m, seg.s0, seg.s1, seg.trips);
-  FastShared& f = sh.f;
-  // the row's keys in any order, FAST_LOADS loads in flight per thread
-  auto each_key = [&](auto&& fn) {
-    constexpr int U = FAST_LOADS;
-    for (int32_t i0 = 0; i0 < m; i0 += U * NT) {
-      float xv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int32_t i = i0 + u * NT + tid;
-        xv[u] = i < m ? x[i] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int32_t i = i0 + u * NT + tid;
-        if (i < m) fn(i, i == a ? FORCED_KEY : score_key(xv[u]));
-      }
-    }
-  };
-
-  // read 1: bin counts of the top FAST_BITS key bits
-  for (int i = tid; i < FAST_BINS; i += NT) f.u.hist[i] = 0;
-  if (tid == 0) { f.n_c = 0; f.n_k = 0; }
-  __syncthreads();
-  each_key([&](int32_t, uint32_t key) { atomicAdd(&f.u.hist[key >> (32 - FAST_BITS)], 1u); });
-  __syncthreads();
-  // thread t owns bins [PER t, PER t + PER); suffix sums over the threads
-  uint32_t loc[PER], tsum = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) { loc[j] = f.u.hist[PER * tid + j]; tsum += loc[j]; }
-  uint32_t s = tsum;  // inclusive suffix sum within the wave
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t x = __shfl_down(s, d);
-    if (lane + d < 64) s += x;
-  }
-  if (lane == 0) f.wsum[wave] = s;
-  __syncthreads();
-  uint32_t higher = s - tsum;  // entries in bins above this thread's
-  for (int w = wave + 1; w < BLK_WAVES; ++w) higher += f.wsum[w];
-  if (higher < (uint32_t)kk && higher + tsum >= (uint32_t)kk) {
-    uint32_t acc = higher;
-    for (int j = PER - 1; j >= 0; --j) {
-      if (acc + loc[j] >= (uint32_t)kk) {
-        f.bin = (uint32_t)(PER * tid + j);
-        f.above = acc;
-        f.in_bin = loc[j];
-        break;
-      }
-      acc += loc[j];
-    }
-  }
-  __syncthreads();
-  const uint32_t bin = f.bin, above = f.above, in_bin = f.in_bin;
-  if (in_bin > (uint32_t)FAST_CAND || kk > FAST_KEEP) {
-    __syncthreads();  // every thread has read the bin before the radix select reuses LDS
-    select_topk<BLK_WAVES, 2>(seg, kk, o, nullptr, sh.r);
-    return;
-  }
-
-  // read 2: keys above bin b are kept; bin b entries become candidates
-  each_key([&](int32_t i, uint32_t key) {
-    const uint32_t hb = key >> (32 - FAST_BITS);
-    if (hb > bin) {
-      f.u.l.keep[atomicAdd(&f.n_k, 1u)] = i;
-    } else if (hb == bin) {
-      const uint32_t p = atomicAdd(&f.n_c, 1u);
-      f.u.l.ckey[p] = key;
-      f.u.l.cidx[p] = i;
-    }
-  });
-  __syncthreads();
-  // candidate c is kept when fewer than kk - above candidates rank before it
-  const uint32_t places = (uint32_t)kk - above;
-  for (uint32_t c = tid; c < in_bin; c += NT) {
-    const uint32_t kc = f.u.l.ckey[c];
-    const int32_t ic = f.u.l.cidx[c];
-    uint32_t rank = 0;
-    for (uint32_t e = 0; e < in_bin; ++e) {
-      const uint32_t ke = f.u.l.ckey[e];
-      rank += (ke > kc || (ke == kc && f.u.l.cidx[e] < ic)) ? 1u : 0u;
-    }
-    if (rank < places) f.u.l.keep[atomicAdd(&f.n_k, 1u)] = ic;
-  }
-  // ascending order: bitonic sort of the kk kept indices, padded to a power of two
-  int32_t P = 1;
-  while (P < kk) P <<= 1;
-  __syncthreads();
-  for (int32_t i = kk + tid; i < P; i += NT) f.u.l.keep[i] = 0x7fffffff;
-  __syncthreads();
-  for (int32_t size = 2; size <= P; size <<= 1) {
-    for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int32_t t = tid; t < (P >> 1); t += NT) {
-        const int32_t i = 2 * t - (t & (stride - 1));  // lower element of the pair
-        const int32_t jx = i + stride;
-        const bool up = (i & size) == 0;
-        const int32_t x = f.u.l.keep[i], y = f.u.l.keep[jx];
-        if ((x > y) == up) { f.u.l.keep[i] = y; f.u.l.keep[jx] = x; }
-      }
-      __syncthreads();
-    }
-  }
-  for (int32_t i = tid; i < kk; i += NT) o[i] = f.u.l.keep[i];
+  select_topk<BLK_WAVES, 2>(seg, kk, o, nullptr, sh.r);
 }
 
 }  // namespace
