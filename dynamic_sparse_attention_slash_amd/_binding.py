@@ -344,15 +344,16 @@ def topk(scores: torch.Tensor, k: int, forced_index: int = -1) -> torch.Tensor:
 
 
 def vs_build_index(V: torch.Tensor, S: torch.Tensor, seq_len: int):
-    """(intervals [rows, ns, 2], n_intervals [rows], cols [rows, nb, nv], n_cols [rows, nb])."""
+    """(intervals [rows, ns, 2], n_intervals [rows], cols [rows, nb, nv], n_cols [rows, nb]);
+    entries past the counts are left unwritten."""
     rows, nv = V.shape
     ns = S.shape[1]
     nb = (seq_len + BLOCK - 1) // BLOCK
     dev = V.device
-    iv = torch.zeros((rows, ns, 2), dtype=torch.int32, device=dev)
-    n_iv = torch.zeros((rows,), dtype=torch.int32, device=dev)
-    cols = torch.zeros((rows, nb, nv), dtype=torch.int32, device=dev)
-    n_cols = torch.zeros((rows, nb), dtype=torch.int32, device=dev)
+    iv = torch.empty((rows, ns, 2), dtype=torch.int32, device=dev)
+    n_iv = torch.empty((rows,), dtype=torch.int32, device=dev)
+    cols = torch.empty((rows, nb, nv), dtype=torch.int32, device=dev)
+    n_cols = torch.empty((rows, nb), dtype=torch.int32, device=dev)
     _call("dsa_vs_build_index", _dev(V, "V", torch.int32), nv, _dev(S, "S", torch.int32), ns, rows,
           seq_len, iv.data_ptr(), n_iv.data_ptr(), cols.data_ptr(), n_cols.data_ptr(), _stream(V))
     return iv, n_iv, cols, n_cols
@@ -371,13 +372,14 @@ def bs_pool(x: torch.Tensor, heads: Optional[Sequence[int]] = None) -> torch.Ten
 
 def bs_select(qp: torch.Tensor, kp: torch.Tensor, topk: int, *, scale: Optional[float] = None,
               return_logits: bool = False):
-    """(sel [rows, nb, min(topk, nb)], n_sel [rows, nb][, logits [rows, nb, nb]])."""
+    """(sel [rows, nb, min(topk, nb)], n_sel [rows, nb][, logits [rows, nb, nb]]); entries of
+    sel past n_sel are left unwritten."""
     rows, nb, D = qp.shape
     if kp.shape != qp.shape:
         raise ValueError("qp and kp must have equal shapes")
     ke = min(topk, nb)
-    sel = torch.zeros((rows, nb, ke), dtype=torch.int32, device=qp.device)
-    n_sel = torch.zeros((rows, nb), dtype=torch.int32, device=qp.device)
+    sel = torch.empty((rows, nb, ke), dtype=torch.int32, device=qp.device)
+    n_sel = torch.empty((rows, nb), dtype=torch.int32, device=qp.device)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if return_logits:
         lg = torch.full((rows, nb, nb), float("nan"), dtype=torch.float32, device=qp.device)

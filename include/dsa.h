@@ -192,7 +192,8 @@ size_t dsa_topk_workspace_bytes(int32_t rows, int32_t n, int32_t k);
  * ranges [max(0, 64a - d_hi), min(seq_len, 64a + 64 - d_lo)) of every interval
  * with d_lo < 64a + 64, and the columns cols [rows][nb][nv] (count in
  * n_cols [rows][nb]): the entries of V below min(seq_len, 64a + 64) that lie
- * in none of those ranges, ascending. All device int32 arrays. */
+ * in none of those ranges, ascending. All device int32 arrays; entries past
+ * n_intervals[row] and n_cols[row][a] are left unwritten. */
 dsa_status dsa_vs_build_index(const int32_t* V, int32_t nv, const int32_t* S, int32_t ns,
                               int32_t rows, int32_t seq_len, int32_t* intervals,
                               int32_t* n_intervals, int32_t* cols, int32_t* n_cols,
@@ -212,7 +213,8 @@ dsa_status dsa_bs_pool(const void* x, int32_t dtype, int32_t batch, int32_t x_he
  * within about 2^-16 relative of the exact dot); sel [rows][nb][min(topk, nb)]
  * receives the ascending
  * top-min(topk, a+1) blocks of L[a][0..a] with c = a forced and n_sel
- * [rows][nb] their count. logits: NULL, or device fp32 [rows][nb][nb] that
+ * [rows][nb] their count (entries of sel past the count are left unwritten).
+ * logits: NULL, or device fp32 [rows][nb][nb] that
  * receives L (entries c > a are left untouched). workspace: at least
  * dsa_bs_select_workspace_bytes(...) bytes. */
 dsa_status dsa_bs_select(const float* qp, const float* kp, int32_t rows, int32_t nb,
