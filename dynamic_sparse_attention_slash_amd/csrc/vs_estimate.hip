@@ -9,7 +9,7 @@
 // Atención: rowmax and l of a first pass turn a second pass into softmax
 // probabilities, restricted to the window's query rows.]
 //
-// Pass 1 (stats): per (row, chunk of 256 keys) one wave computes
+// Pass 1 (stats): per (row, chunk of EST_CHUNK keys) one wave computes
 //   S = Q_window K_chunk^T with MFMA (lane = one key column, 16 query rows) and
 //   keeps a running (max, sum) per query row; partials go to workspace.
 // Combine: per row, max / log-sum over the chunks -> F_r = m_r + log2 Z_r.
