@@ -216,28 +216,30 @@ struct BinShared {
   uint32_t bin, above, in_bin, n_c, n_k;
 };
 
-// key_at(i) / idx_at(i): key and output index of entry i < m (visited in any
-// order, BIN_LOADS keys in flight per thread). Writes out[0..kk) ascending
-// (and their keys to out_key when KEYS).
-template <int NW, int CAND, int KEEP, bool KEYS, class KeyAt, class IdxAt>
-__device__ bool select_bins(KeyAt key_at, IdxAt idx_at, int32_t m, int32_t kk, int32_t* __restrict__ out,
-                            uint32_t* __restrict__ out_key, BinShared<NW, CAND, KEEP, KEYS>& f) {
+// raw_at(i) loads entry i < m (as 32 bits), key_of(i, raw) maps it to its
+// key, idx_at(i) gives its output index. Entries are visited in any order,
+// BIN_LOADS loads issued before their keys are formed. Writes out[0..kk)
+// ascending (and their keys to out_key when KEYS).
+template <int NW, int CAND, int KEEP, bool KEYS, class RawAt, class KeyOf, class IdxAt>
+__device__ bool select_bins(RawAt raw_at, KeyOf key_of, IdxAt idx_at, int32_t m, int32_t kk,
+                            int32_t* __restrict__ out, uint32_t* __restrict__ out_key,
+                            BinShared<NW, CAND, KEEP, KEYS>& f) {
   constexpr int NT = NW * 64;
   constexpr int PER = BINS / NT;  // bins per thread in the scan
   static_assert(PER * NT == BINS, "bins per thread");
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   auto each_key = [&](auto&& fn) {
     for (int32_t i0 = 0; i0 < m; i0 += BIN_LOADS * NT) {
-      uint32_t kv[BIN_LOADS];
+      uint32_t rv[BIN_LOADS];
 #pragma unroll
       for (int u = 0; u < BIN_LOADS; ++u) {
         const int32_t i = i0 + u * NT + tid;
-        kv[u] = i < m ? key_at(i) : 0u;
+        rv[u] = i < m ? raw_at(i) : 0u;
       }
 #pragma unroll
       for (int u = 0; u < BIN_LOADS; ++u) {
         const int32_t i = i0 + u * NT + tid;
-        if (i < m) fn(i, kv[u]);
+        if (i < m) fn(i, key_of(i, rv[u]));
       }
     }
   };
@@ -364,9 +366,10 @@ __global__ __launch_bounds__(ROW_WAVES * 64) void topk_rows_kernel(const float* 
     return;
   }
   const float* x = scores + (size_t)row * n;
-  auto key_at = [&](int32_t i) { return i == forced ? FORCED_KEY : score_key(x[i]); };
+  auto raw_at = [&](int32_t i) { return __float_as_uint(x[i]); };
+  auto key_of = [&](int32_t i, uint32_t r) { return i == forced ? FORCED_KEY : score_key(__uint_as_float(r)); };
   auto idx_at = [](int32_t i) { return i; };
-  if (select_bins<ROW_WAVES>(key_at, idx_at, n, kk, o, (uint32_t*)nullptr, sh.f)) return;
+  if (select_bins<ROW_WAVES>(raw_at, key_of, idx_at, n, kk, o, (uint32_t*)nullptr, sh.f)) return;
   GlobalSeg seg{x, forced, 0, 0, 0, (int32_t)(threadIdx.x & 63), 0};
   wave_segment<ROW_WAVES>(n, seg.s0, seg.s1, seg.trips);
   select_topk<ROW_WAVES, 2>(seg, kk, o, nullptr, sh.r);
@@ -453,9 +456,10 @@ __global__ __launch_bounds__(BLK_WAVES * 64) void block_topk_kernel(const float*
     return;
   }
   const float* x = logits + cb * nb;
-  auto key_at = [&](int32_t i) { return i == a ? FORCED_KEY : score_key(x[i]); };
+  auto raw_at = [&](int32_t i) { return __float_as_uint(x[i]); };
+  auto key_of = [&](int32_t i, uint32_t r) { return i == a ? FORCED_KEY : score_key(__uint_as_float(r)); };
   auto idx_at = [](int32_t i) { return i; };
-  if (select_bins<BLK_WAVES>(key_at, idx_at, m, kk, o, (uint32_t*)nullptr, sh.f)) return;
+  if (select_bins<BLK_WAVES>(raw_at, key_of, idx_at, m, kk, o, (uint32_t*)nullptr, sh.f)) return;
   GlobalSeg seg{x, a, 0, 0, 0, (int32_t)(threadIdx.x & 63), 0};
   wave_segment<BLK_WAVES>(m, seg.s0, seg.s1, seg.trips);
   select_topk<BLK_WAVES, 2>(seg, kk, o, nullptr, sh.r);
