@@ -2,8 +2,9 @@
 // Head: mean-pool Q and K over blocks, score the block pairs, keep the top-k
 // key blocks per query block].
 //
-// pool_kernel: one work-group per (row, block): each thread sums 4 adjacent
-//   dims over a strided subset of the block's rows (coalesced 8/16-byte loads),
+// pool_kernel: one work-group per (row, block): each thread sums the 8 (bf16)
+//   or 4 (fp32) adjacent dims of one 16-byte load over a strided subset of the
+//   block's rows, all its loads of a whole block in flight at once,
 //   the partial sums meet in LDS in a fixed order, and the mean is written in
 //   fp32. HBM-bound: every input byte is read once.
 // logits_kernel: L[a][c] = scale * Qp[a] . Kp[c] for the causal triangle
@@ -21,29 +22,44 @@ constexpr int POOL_THREADS = 256;
 template <typename T, int D>
 __global__ __launch_bounds__(POOL_THREADS) void pool_kernel(const T* __restrict__ x, int32_t n,
                                                             HeadMap hm, float* __restrict__ out) {
-  constexpr int TPR = D / 4;                 // threads per row (4 dims each)
-  constexpr int RG = POOL_THREADS / TPR;     // row groups
+  constexpr int EPT = 16 / sizeof(T);         // dims per thread: one 16-byte load per row
+  constexpr int TPR = D / EPT;                // threads per row
+  constexpr int RG = POOL_THREADS / TPR;      // row groups
+  constexpr int RPT = BLOCK / RG;             // rows per thread in a whole block
   __shared__ float part[RG][D];
   const int32_t a = blockIdx.x, row = blockIdx.y;
   const int32_t nb = (n + BLOCK - 1) / BLOCK;
   const int32_t tid = threadIdx.x, dq = tid % TPR, rg = tid / TPR;
   const T* src = x + hm.q_slab(row, n, D);
   const int32_t r0 = a * BLOCK, r1 = min(n, r0 + BLOCK);
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int32_t r = r0 + rg; r < r1; r += RG) {
+  float acc[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
+  auto add_row = [&](const u32x4& w) {
     if constexpr (sizeof(T) == 2) {
-      u32x2 w = *reinterpret_cast<const u32x2*>(src + (size_t)r * D + 4 * dq);
-      acc[0] += bf16_bits_to_f32(w[0] & 0xffffu);
-      acc[1] += bf16_bits_to_f32(w[0] >> 16);
-      acc[2] += bf16_bits_to_f32(w[1] & 0xffffu);
-      acc[3] += bf16_bits_to_f32(w[1] >> 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_bits_to_f32(w[e] & 0xffffu);
+        acc[2 * e + 1] += bf16_bits_to_f32(w[e] >> 16);
+      }
     } else {
-      f32x4 w = *reinterpret_cast<const f32x4*>(src + (size_t)r * D + 4 * dq);
-      acc[0] += w[0]; acc[1] += w[1]; acc[2] += w[2]; acc[3] += w[3];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[e]);
     }
+  };
+  const u32x4* base = reinterpret_cast<const u32x4*>(src + (size_t)r0 * D + EPT * dq);
+  if (r1 - r0 == BLOCK) {
+    // a whole block: all of this thread's rows loaded before they are added
+    u32x4 w[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) w[k] = base[(size_t)(rg + RG * k) * (D / EPT)];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) add_row(w[k]);
+  } else {
+    for (int32_t r = rg; r < r1 - r0; r += RG) add_row(base[(size_t)r * (D / EPT)]);
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) part[rg][4 * dq + e] = acc[e];
+  for (int e = 0; e < EPT; ++e) part[rg][EPT * dq + e] = acc[e];
   __syncthreads();
   if (tid < D) {
     float s = 0.f;
