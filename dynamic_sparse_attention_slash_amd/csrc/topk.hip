@@ -227,6 +227,7 @@ __device__ bool select_bins(RawAt raw_at, KeyOf key_of, IdxAt idx_at, int32_t m,
   constexpr int NT = NW * 64;
   constexpr int PER = BINS / NT;  // bins per thread in the scan
   static_assert(PER * NT == BINS, "bins per thread");
+  if (kk > KEEP) return false;    // the kept entries would not fit
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   auto each_key = [&](auto&& fn) {
     for (int32_t i0 = 0; i0 < m; i0 += BIN_LOADS * NT) {
@@ -278,7 +279,7 @@ __device__ bool select_bins(RawAt raw_at, KeyOf key_of, IdxAt idx_at, int32_t m,
   }
   __syncthreads();
   const uint32_t bin = f.bin, above = f.above, in_bin = f.in_bin;
-  if (in_bin > (uint32_t)CAND || kk > KEEP) {
+  if (in_bin > (uint32_t)CAND) {
     __syncthreads();  // every thread has read the bin before LDS is reused
     return false;
   }
@@ -347,11 +348,17 @@ __device__ bool select_bins(RawAt raw_at, KeyOf key_of, IdxAt idx_at, int32_t m,
 }
 
 // Rows of up to two 64K chunks: one work-group per row, two-read select
-// (kk up to 8192). The chunk and merge passes of longer rows keep the radix
-// select: there the two-read select measured slower (its larger LDS keeps
-// one work-group per CU, and the merge candidates crowd into few bins).
+// (kk up to 8192). The merge pass of longer rows keeps the radix select:
+// there the two-read select measured slower (the merge candidates crowd
+// into few bins).
 union RowTopkShared {
   BinShared<16, 2048, 8192, false> f;
+  SelectShared<16, 2> r;
+};
+// per-chunk pass of long rows: the two-read select for lists of up to 1024
+// entries (with their keys, in 24 KB of LDS), the radix select beyond
+union ChunkTopkShared {
+  BinShared<16, 1024, 1024, true> f;
   SelectShared<16, 2> r;
 };
 constexpr int ROW_WAVES = 16;
@@ -386,7 +393,7 @@ __global__ __launch_bounds__(ROW_WAVES * 64) void topk_chunks_kernel(const float
                                                                      int32_t n, int32_t kk, int32_t forced,
                                                                      int32_t* __restrict__ cand_idx,
                                                                      uint32_t* __restrict__ cand_key) {
-  __shared__ SelectShared<ROW_WAVES, 2> sh;
+  __shared__ ChunkTopkShared sh;
   const int32_t c = blockIdx.x, row = blockIdx.y, nch = gridDim.x;
   const int32_t c0 = c * TOPK_CHUNK, m = min(TOPK_CHUNK, n - c0);
   const size_t off = ((size_t)row * nch + c) * kk;
@@ -401,9 +408,13 @@ __global__ __launch_bounds__(ROW_WAVES * 64) void topk_chunks_kernel(const float
     }
     return;
   }
+  auto raw_at = [&](int32_t i) { return __float_as_uint(x[i]); };
+  auto key_of = [&](int32_t i, uint32_t r) { return i == f ? FORCED_KEY : score_key(__uint_as_float(r)); };
+  auto idx_at = [&](int32_t i) { return c0 + i; };
+  if (select_bins<ROW_WAVES>(raw_at, key_of, idx_at, m, kk, oi, ok, sh.f)) return;
   GlobalSeg seg{x, f, 0, 0, 0, (int32_t)(threadIdx.x & 63), c0};
   wave_segment<ROW_WAVES>(m, seg.s0, seg.s1, seg.trips);
-  select_topk<ROW_WAVES, 2>(seg, kk, oi, ok, sh);
+  select_topk<ROW_WAVES, 2>(seg, kk, oi, ok, sh.r);
 }
 
 __global__ __launch_bounds__(ROW_WAVES * 64) void topk_merge_kernel(const int32_t* __restrict__ cand_idx,
