@@ -576,6 +576,29 @@ def test_mixed_layer_small():
         assert torch.equal(row_o[0, h], o[0, h])
 
 
+@pytest.mark.parametrize("n,D,dt", [(1, 128, "bf16"), (2, 64, "f32"), (63, 128, "bf16"), (64, 64, "bf16")])
+def test_one_block_layers(n, D, dt):
+    """Sequences of at most one 64-key block through the three public calls,
+    estimation included: every pattern's key set is then the whole causal
+    range (the forced diagonal offset, the forced diagonal block, the window
+    that holds the diagonal block), so each head equals dense causal attention;
+    a single token returns its own value row."""
+    say(f"one-block layer n={n} D={D} {dt}")
+    q, k, v = rand_qkv(1, 6, 2, n, D, dt, seed=40 + n)
+    o = torch.zeros_like(q)
+    dsa.vertical_slash_sparse_attention(q, k, v, 3, 2, heads=[0, 3], out=o)
+    dsa.block_sparse_attention(q, k, v, 1, heads=[1, 4], out=o)
+    dsa.streaming_attention(q, k, v, 0, 1, heads=[2, 5], out=o)
+    torch.cuda.synchronize()
+    oh, qh, kh, vh = host64(o), host64(q), host64(k), host64(v)
+    for h in range(6):
+        g = kvh(h, 6, 2)
+        ref = O.dense_causal_attention(qh[0, h], kh[0, g], vh[0, g], 1 / math.sqrt(D))
+        check_attention(oh[0, h], ref, f"h{h}")
+        if n == 1:
+            assert np.array_equal(oh[0, h, 0], vh[0, g, 0]), h
+
+
 def _streaming_vs_oracle(o, q, k, v, heads, init_blocks, local_blocks, tag, blocks=None):
     Hq, Hkv, n, D = q.shape[1], k.shape[1], q.shape[2], q.shape[3]
     oh, qh, kh, vh = host64(o), host64(q), host64(k), host64(v)
