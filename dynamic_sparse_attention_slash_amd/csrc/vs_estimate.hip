@@ -207,7 +207,8 @@ struct KRing {
     constexpr int ahead = INSTR * (KR_STAGES - 1);  // DMA loads issued after this step's
     static_assert(ahead < 16, "vmcnt field");
     __builtin_amdgcn_s_waitcnt(0x0F70 | ahead);     // vmcnt(ahead), no expcnt / lgkmcnt wait
-    const uint32_t base = (uint32_t)(uintptr_t)stage;
+    // the stage's LDS byte address (an address-space cast of the pointer)
+    const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)stage;
     if constexpr (DS == 4) {
       asm volatile(
           "ds_read_b128 %0, %4\n\t"
