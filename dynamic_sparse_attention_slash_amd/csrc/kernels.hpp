@@ -98,8 +98,9 @@ struct MixedIndex {
 hipError_t launch_attention_mixed(const AttnArgs& a, const MixedIndex& ix, hipStream_t s);
 
 // ---- vertical-slash estimate (vs_estimate.hip) ----
-// keys per estimator work-group: 1024 measured fastest at 128K-1M (each wave
-// loads its 64-row Q window once per chunk; 256: 12% slower at 1M)
+// keys per estimator work-group, at most: 1024 measured fastest at 128K-1M
+// (each wave loads its 64-row Q window once per chunk; 256: 12% slower at
+// 1M); smaller problems take 512 or 256 (est_chunk_keys)
 constexpr int EST_CHUNK = 1024;
 struct EstArgs {
   const void* q; const void* k;
@@ -114,9 +115,11 @@ struct EstArgs {
   float* v_scores; float* s_scores;       // [rows][seq_len]
   float* part_stats;  // [rows][nchunks][64][2]
   float* row_stats;   // [rows][64]
-  float* s_part;      // [rows][nchunks][EST_CHUNK + 63]
+  float* s_part;      // [rows][nchunks][chunk + 63]
+  int32_t chunk;      // keys per work-group (est_chunk_keys; set by est_carve)
   __host__ __device__ int32_t lq_eff() const { return last_q < seq_len ? last_q : seq_len; }
 };
+int32_t est_chunk_keys(int32_t rows, int32_t seq_len);
 size_t est_workspace_bytes(int32_t rows, int32_t seq_len);
 void est_carve(EstArgs& a, void* ws);
 hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s);

@@ -9,7 +9,7 @@
 // Atención: rowmax and l of a first pass turn a second pass into softmax
 // probabilities, restricted to the window's query rows.]
 //
-// Pass 1 (stats): per (row, chunk of EST_CHUNK keys) one wave computes
+// Pass 1 (stats): per (row, chunk of a.chunk keys) one wave computes
 //   S = Q_window K_chunk^T with MFMA (lane = one key column, 16 query rows) and
 //   keeps a running (max, sum) per query row; partials go to workspace.
 // Combine: per row, max / log-sum over the chunks -> F_r = m_r + log2 Z_r.
@@ -29,8 +29,7 @@
 namespace dsa {
 namespace {
 
-constexpr int C = EST_CHUNK;       // keys per work-group
-constexpr int SACC = C + 63;       // diagonal offsets one chunk touches
+constexpr int SACC_MAX = EST_CHUNK + 63;  // diagonal offsets the largest chunk touches
 
 struct Window {
   int32_t n, lq, start;
@@ -237,7 +236,7 @@ struct KRing {
 
 template <typename T, int D>
 EST_KERNEL void est_stats_kernel(EstArgs a) {
-  const int32_t nchunks = (a.seq_len + C - 1) / C;
+  const int32_t C = a.chunk, nchunks = (a.seq_len + C - 1) / C;
   int32_t row, chunk;
   work_item(a.hm, a.wo, nchunks, row, chunk);
   const Window w{a.seq_len, a.lq_eff(), a.win_start};
@@ -442,8 +441,8 @@ template <typename T, int D, bool S>
 EST_KERNEL void est_scores_kernel(EstArgs a) {
   constexpr int PS = 65;  // padded LDS row of the 64x64 probability tile
   __shared__ float ptile[64 * PS];
-  __shared__ float sacc[SACC];
-  const int32_t nchunks = (a.seq_len + C - 1) / C;
+  __shared__ float sacc[SACC_MAX];
+  const int32_t C = a.chunk, nchunks = (a.seq_len + C - 1) / C;
   int32_t row, chunk;
   work_item(a.hm, a.wo, nchunks, row, chunk);
   const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
@@ -457,6 +456,7 @@ EST_KERNEL void est_scores_kernel(EstArgs a) {
   for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) F[qb][i] = a.row_stats[(size_t)row * 64 + 16 * qb + 4 * g + i];
+  const int32_t SACC = C + 63;  // diagonal offsets this chunk touches
   for (int e = lane; e < SACC; e += 64) sacc[e] = 0.f;
 
   float* vout = a.v_scores + (size_t)row * a.seq_len;
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(256) void est_scombine_kernel(EstArgs a, int32_t nc
   const int32_t row = blockIdx.y;
   const int32_t d = blockIdx.x * 256 + threadIdx.x;
   if (d >= a.seq_len) return;
-  const int32_t n = a.seq_len, lq = a.lq_eff(), start = a.win_start;
+  const int32_t n = a.seq_len, lq = a.lq_eff(), start = a.win_start, C = a.chunk, SACC = C + 63;
   // keys of diagonal d: j in [start - d, start + lq - 1 - d] (clipped at 0)
   const int32_t j_lo = max(0, start - d), j_hi = start + lq - 1 - d;
   float sum = 0.f;
@@ -538,17 +538,26 @@ __global__ __launch_bounds__(256) void est_scombine_kernel(EstArgs a, int32_t nc
 
 }  // namespace
 
+int32_t est_chunk_keys(int32_t rows, int32_t seq_len) {
+  // the largest chunk that still gives about 2048 work-groups (two waves per SIMD)
+  for (int32_t cs = EST_CHUNK; cs > 256; cs /= 2)
+    if ((long long)rows * ((seq_len + cs - 1) / cs) >= 2048) return cs;
+  return 256;
+}
+
 size_t est_workspace_bytes(int32_t rows, int32_t seq_len) {
+  const int32_t C = est_chunk_keys(rows, seq_len);
   const size_t nch = (size_t)(seq_len + C - 1) / C;
   const size_t part = (size_t)rows * nch * 128 * sizeof(float);
   const size_t stats = (size_t)rows * 64 * sizeof(float);
-  const size_t spart = (size_t)rows * nch * SACC * sizeof(float);
+  const size_t spart = (size_t)rows * nch * (C + 63) * sizeof(float);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return al(part) + al(stats) + al(spart);
 }
 
 void est_carve(EstArgs& a, void* ws) {
-  const size_t nch = (size_t)(a.seq_len + C - 1) / C;
+  a.chunk = est_chunk_keys(a.rows, a.seq_len);
+  const size_t nch = (size_t)(a.seq_len + a.chunk - 1) / a.chunk;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char* p = static_cast<char*>(ws);
   a.part_stats = reinterpret_cast<float*>(p);
@@ -560,7 +569,7 @@ void est_carve(EstArgs& a, void* ws) {
 
 hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s) {
   if (a.rows == 0 || a.seq_len == 0) return hipSuccess;
-  const int32_t nch = (a.seq_len + C - 1) / C;
+  const int32_t nch = (a.seq_len + a.chunk - 1) / a.chunk;
   const dim3 grid((unsigned)((long long)nch * a.rows));
   auto st = a.dtype == BF16 ? (a.head_dim == 64 ? est_stats_kernel<uint16_t, 64> : est_stats_kernel<uint16_t, 128>)
                             : (a.head_dim == 64 ? est_stats_kernel<float, 64> : est_stats_kernel<float, 128>);
