@@ -125,7 +125,8 @@ size_t bs_layout(const dsa_shape* s, int32_t rows, int32_t topk, void* base, BsW
   const int32_t nb = nblocks(s->seq_len), D = s->head_dim;
   const int32_t ke = topk < nb ? topk : nb;
   float* qp = c.take<float>((size_t)rows * nb * D);
-  float* kp = c.take<float>((size_t)s->batch * s->kv_heads * nb * D);
+  // pooled K of every kv head the listed heads may read (none without rows)
+  float* kp = c.take<float>(rows ? (size_t)s->batch * s->kv_heads * nb * D : 0);
   float* lg = c.take<float>((size_t)(rows ? logit_rows_per_group(rows, nb) : 0) * nb * nb);
   int32_t* sel = c.take<int32_t>((size_t)rows * nb * ke);
   int32_t* n_sel = c.take<int32_t>((size_t)rows * nb);
