@@ -153,11 +153,12 @@ class Layer:
 
     def step(self, serial=False):
         """One layer. The block-sparse call (pooling, block selection,
-        attention) runs on a second stream beside the vertical-slash and
-        streaming calls, so its selection stages overlap the other heads'
-        work; the main stream waits for it before the step ends. The calls
-        write disjoint heads of one output with their own workspaces, so the
-        result is the same bits as the serial order (serial=True)."""
+        attention) runs on a second stream beside the streaming and
+        vertical-slash calls, so its selection stages overlap the other heads'
+        work (the streaming heads need no index and go first); the main stream
+        waits for it before the step ends. The calls write disjoint heads of
+        one output with their own workspaces, so the result is the same bits
+        as the serial order (serial=True)."""
         w, x = self.w, self.x
         side = x.heads["bs"] and (x.heads["vs"] or x.heads["st"]) and not serial
         main = torch.cuda.current_stream()
@@ -165,15 +166,15 @@ class Layer:
             self.side.wait_stream(main)
             with torch.cuda.stream(self.side):
                 self._bs()
+        if x.heads["st"]:
+            dsa.streaming_attention(self.q, self.k, self.v, w.init_blocks, w.local_blocks,
+                                    heads=x.heads["st"], out=self.o)
         if x.heads["vs"]:
             dsa.vertical_slash_sparse_attention(self.q, self.k, self.v, w.vertical_topk, w.slash_topk,
                                                 last_q=w.last_q, heads=self.vs_heads, out=self.o,
                                                 workspace=self.ws_vs)
         if x.heads["bs"] and not side:
             self._bs()
-        if x.heads["st"]:
-            dsa.streaming_attention(self.q, self.k, self.v, w.init_blocks, w.local_blocks,
-                                    heads=x.heads["st"], out=self.o)
         if side:
             main.wait_stream(self.side)
 
