@@ -93,6 +93,11 @@ struct VsWork {
   int32_t* cols; int32_t* n_cols; void* tk;
 };
 size_t vs_layout(int32_t rows, int32_t n, int32_t vk, int32_t sk, void* base, VsWork* w) {
+  // no rows or no tokens: nothing is launched, so no workspace is needed
+  if (rows == 0 || n == 0) {
+    if (w) *w = VsWork{};
+    return 0;
+  }
   Carver c{static_cast<char*>(base)};
   const int32_t nb = nblocks(n);
   void* est = c.take<char>(est_workspace_bytes(rows, n));

@@ -546,6 +546,7 @@ int32_t est_chunk_keys(int32_t rows, int32_t seq_len) {
 }
 
 size_t est_workspace_bytes(int32_t rows, int32_t seq_len) {
+  if (rows == 0 || seq_len == 0) return 0;  // nothing is launched
   const int32_t C = est_chunk_keys(rows, seq_len);
   const size_t nch = (size_t)(seq_len + C - 1) / C;
   const size_t part = (size_t)rows * nch * 128 * sizeof(float);

@@ -47,6 +47,11 @@
  *   128, an unknown dtype, last_q outside [1, 64], more than DSA_MAX_HEADS
  *   heads or a head slab (seq_len * head_dim * element size) of 2 GiB or more; DSA_ERR_WORKSPACE when workspace_bytes is below what the matching
  *   *_workspace_bytes call returns; DSA_ERR_HIP when a launch fails.
+ * Empty work. A prefill call (the three pattern calls, the mixed calls, the
+ *   stage calls, KV retention) with batch 0, seq_len 0 or no listed head
+ *   enqueues nothing, returns DSA_OK and needs no workspace (the matching
+ *   *_workspace_bytes call returns 0). The sparse decode step with an empty
+ *   cache or empty key lists still runs and writes zero rows.
  */
 #ifndef DSA_H
 #define DSA_H

@@ -71,6 +71,11 @@ def test_vs_argument_errors(lib):
     # nothing to do: zero batch or empty head list succeed without touching memory
     assert vs_call(lib, shape(b=0), ws=None, wsb=0) == OK
     assert vs_call(lib, shape(), heads=(ctypes.c_int32 * 1)(0), nh=0, ws=None, wsb=0) == OK
+    # an empty sequence: no workspace asked for, nothing enqueued
+    assert vs_call(lib, shape(n=0), ws=None, wsb=0) == OK
+    assert lib.dsa_vertical_slash_workspace_bytes(ctypes.byref(shape(n=0)), 8, 8, 4) == 0
+    assert lib.dsa_block_sparse_workspace_bytes(ctypes.byref(shape(n=0)), 4, 4) == 0
+    assert lib.dsa_vs_estimate(P, P, ctypes.byref(shape(n=0)), 64, 0.0, None, 0, P, P, None, 0, None) == OK
 
 
 def test_workspace_sizes(lib):
@@ -148,8 +153,11 @@ def test_mixed_argument_errors(lib):
     assert mixed(lb=0) == INVALID
     assert mixed(lq=65) == UNSUPPORTED
     assert mixed(wsb=8) == WORKSPACE
-    # no head processed: nothing to enqueue
+    # no head processed, or no tokens: nothing to enqueue
     assert mixed(p=pats(-1, -1, -1, -1), wsb=0) == OK
+    empty = shape(hq=4, hkv=2, n=0)
+    assert lib.dsa_mixed_sparse_attention(P, P, P, P, ctypes.byref(empty), good, 8, 8, 64, 4, 1, 2, 0.0,
+                                          None, 0, None) == OK
     # workspace: the VS part for the VS heads plus the BS part for the BS heads
     big = shape(hq=4, hkv=2, n=4096)
     wm = lib.dsa_mixed_sparse_attention_workspace_bytes
