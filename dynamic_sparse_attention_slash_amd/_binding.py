@@ -9,7 +9,6 @@ kernels. When the library is missing, import succeeds but every call raises
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional, Sequence, Tuple
 
@@ -126,6 +125,52 @@ def _shape_qkv(q, k, v) -> Shape:
         raise TypeError("q, k, v must share one dtype")
     B, Hq, n, D = q.shape
     return Shape(B, Hq, k.shape[1], n, D, _dtype_code(q))
+
+
+def _expect(name: str, t: torch.Tensor, shape: Tuple[int, ...]) -> None:
+    """The kernels read an index array as [rows, ...] of the call's extents
+    with no bound of their own: an array of any other shape is refused here."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_qk(q: torch.Tensor, k: torch.Tensor) -> None:
+    """q [B, Hq, n, D] and k [B, Hkv, n, D] with equal batch, seq_len and head_dim."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k must be [batch, heads, seq_len, head_dim]")
+    if q.shape[0] != k.shape[0] or q.shape[2:] != k.shape[2:]:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)}")
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must share one dtype")
+
+
+def _index_rows(sh: Shape, heads: Optional[Sequence[int]]) -> Tuple[int, int]:
+    """(rows, nb) of an explicit-index call: rows = batch * listed heads."""
+    nh = sh.q_heads if heads is None else len(heads)
+    return sh.batch * nh, (sh.seq_len + BLOCK - 1) // BLOCK
+
+
+def check_vs_index(sh: Shape, heads, intervals, n_intervals, cols, n_cols) -> None:
+    """Extents of a vertical-slash index for the call's rows: intervals
+    [rows, max_iv, 2], n_intervals [rows], cols [rows, nb, max_cols], n_cols
+    [rows, nb]."""
+    rows, nb = _index_rows(sh, heads)
+    if intervals.dim() != 3 or cols.dim() != 3:
+        raise ValueError("intervals must be [rows, max_iv, 2] and cols [rows, nb, max_cols]")
+    _expect("intervals", intervals, (rows, intervals.shape[1], 2))
+    _expect("n_intervals", n_intervals, (rows,))
+    _expect("cols", cols, (rows, nb, cols.shape[2]))
+    _expect("n_cols", n_cols, (rows, nb))
+
+
+def check_block_index(sh: Shape, heads, sel, n_sel) -> None:
+    """Extents of block lists for the call's rows: sel [rows, nb, max_sel],
+    n_sel [rows, nb]."""
+    rows, nb = _index_rows(sh, heads)
+    if sel.dim() != 3:
+        raise ValueError("sel must be [rows, nb, max_sel]")
+    _expect("sel", sel, (rows, nb, sel.shape[2]))
+    _expect("n_sel", n_sel, (rows, nb))
 
 
 def _heads(heads: Optional[Sequence[int]]) -> Tuple[Optional[ctypes.Array], int]:
@@ -260,8 +305,7 @@ def mixed_sparse_attention(q, k, v, patterns: Sequence[Optional[str]], *, vertic
 def vs_estimate(q, k, *, last_q: int = 64, scale: Optional[float] = None,
                 heads: Optional[Sequence[int]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Vertical and slash scores, fp32 [batch * n_heads, seq_len] each."""
-    if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("q, k must be [batch, heads, seq_len, head_dim]")
+    _check_qk(q, k)
     B, Hq, n, D = q.shape
     sh = Shape(B, Hq, k.shape[1], n, D, _dtype_code(q))
     ha, hn = _heads(heads)
@@ -280,8 +324,7 @@ def kv_retention(q, k, window: int, keep: int, *, scale: Optional[float] = None,
     """KV-retention scores fp32 [batch * n_heads, seq_len] (softmax mass of each
     key over the last `window` query rows) and the kept keys int32
     [batch * n_heads, min(keep, seq_len)], ascending."""
-    if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("q, k must be [batch, heads, seq_len, head_dim]")
+    _check_qk(q, k)
     B, Hq, n, D = q.shape
     sh = Shape(B, Hq, k.shape[1], n, D, _dtype_code(q))
     ha, hn = _heads(heads)
@@ -304,6 +347,10 @@ def sparse_decode(q, k, v, keys: Optional[torch.Tensor] = None, n_keys: Optional
     [batch, kv_heads, seq_len, head_dim]; keys int32 [batch * n_heads,
     max_keys] with counts n_keys [batch * n_heads], or None for the whole
     cache. Returns o shaped like q (listed heads written)."""
+    return _decode(q, k, v, keys, n_keys, scale, heads, out)
+
+
+def _decode(q, k, v, keys, n_keys, scale, heads, out) -> torch.Tensor:
     if k.dim() != 4 or v.shape != k.shape:
         raise ValueError("k, v must be [batch, kv_heads, seq_len, head_dim]")
     B, Hkv, n, D = k.shape
@@ -312,6 +359,8 @@ def sparse_decode(q, k, v, keys: Optional[torch.Tensor] = None, n_keys: Optional
             raise ValueError("decode takes one query row per head")
     elif q.dim() != 3:
         raise ValueError("q must be [batch, q_heads, head_dim]")
+    if q.shape[0] != B or q.shape[-1] != D:
+        raise ValueError(f"q{tuple(q.shape)} must match the cache's batch and head_dim {tuple(k.shape)}")
     Hq = q.shape[1]
     sh = Shape(B, Hq, Hkv, n, D, _dtype_code(q))
     ha, hn = _heads(heads)
@@ -380,15 +429,14 @@ def bs_select(qp: torch.Tensor, kp: torch.Tensor, topk: int, *, scale: Optional[
     ke = min(topk, nb)
     sel = torch.empty((rows, nb, ke), dtype=torch.int32, device=qp.device)
     n_sel = torch.empty((rows, nb), dtype=torch.int32, device=qp.device)
-    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if return_logits:
         lg = torch.full((rows, nb, nb), float("nan"), dtype=torch.float32, device=qp.device)
         _call("dsa_bs_select", _dev(qp, "qp", torch.float32), _dev(kp, "kp", torch.float32), rows, nb, D,
-              sc, topk, sel.data_ptr(), n_sel.data_ptr(), lg.data_ptr(), None, 0, _stream(qp))
+              _scale(scale), topk, sel.data_ptr(), n_sel.data_ptr(), lg.data_ptr(), None, 0, _stream(qp))
         return sel, n_sel, lg
     ws = _workspace(load().dsa_bs_select_workspace_bytes(rows, nb), qp.device)
     _call("dsa_bs_select", _dev(qp, "qp", torch.float32), _dev(kp, "kp", torch.float32), rows, nb, D,
-          sc, topk, sel.data_ptr(), n_sel.data_ptr(), None, ws.data_ptr(), ws.numel(), _stream(qp))
+          _scale(scale), topk, sel.data_ptr(), n_sel.data_ptr(), None, ws.data_ptr(), ws.numel(), _stream(qp))
     return sel, n_sel
 
 
@@ -396,6 +444,7 @@ def sparse_attention_vs(q, k, v, intervals, n_intervals, cols, n_cols, *,
                         scale: Optional[float] = None, heads: Optional[Sequence[int]] = None,
                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
     sh = _shape_qkv(q, k, v)
+    check_vs_index(sh, heads, intervals, n_intervals, cols, n_cols)
     o = _out_like(q, out)
     ha, hn = _heads(heads)
     _call("dsa_sparse_attention_vs", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
@@ -410,6 +459,7 @@ def sparse_attention_blocks(q, k, v, sel, n_sel, *, scale: Optional[float] = Non
                             heads: Optional[Sequence[int]] = None,
                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     sh = _shape_qkv(q, k, v)
+    check_block_index(sh, heads, sel, n_sel)
     o = _out_like(q, out)
     ha, hn = _heads(heads)
     _call("dsa_sparse_attention_blocks", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
@@ -425,8 +475,18 @@ def sparse_attention_mixed(q, k, v, patterns: Sequence[Optional[str]], *, vs_ind
     n_intervals, cols, n_cols) for the VS heads in ascending order, bs_index =
     (sel, n_sel) for the BS heads in ascending order."""
     sh = _shape_qkv(q, k, v)
-    o = _out_like(q, out)
     pa = _patterns(patterns, sh.q_heads)
+    n_vs = sum(1 for p in patterns if p == "vs")
+    n_bs = sum(1 for p in patterns if p == "bs")
+    if n_vs and vs_index is None:
+        raise ValueError("vs_index is required when a head follows the vertical-slash pattern")
+    if n_bs and bs_index is None:
+        raise ValueError("bs_index is required when a head follows the block-sparse pattern")
+    if vs_index is not None:
+        check_vs_index(sh, [0] * n_vs, *vs_index)
+    if bs_index is not None:
+        check_block_index(sh, [0] * n_bs, *bs_index)
+    o = _out_like(q, out)
     iv = niv = cols = ncols = sel = nsel = None
     max_iv = max_cols = max_sel = 0
     if vs_index is not None:

@@ -71,6 +71,12 @@ float eff_scale(float scale, int32_t head_dim) {
 
 int32_t nblocks(int32_t n) { return (n + BLOCK - 1) / BLOCK; }
 
+// A prefill call over no row or no token has nothing to read or write: its
+// data pointers may then be NULL (zero-size tensors have no address).
+bool no_work(const dsa_shape* s, int32_t listed_heads) {
+  return s->batch == 0 || s->seq_len == 0 || listed_heads == 0;
+}
+
 dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
 AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, const dsa_shape* s,
@@ -295,14 +301,14 @@ dsa_status dsa_vs_estimate(const void* q, const void* k, const dsa_shape* shape,
                            float* s_scores, void* workspace, size_t workspace_bytes, void* stream) {
   dsa_status st = check_shape(shape);
   if (st != DSA_OK) return st;
-  if (!q || !k || !v_scores || !s_scores) return DSA_ERR_INVALID_ARG;
   if (last_q < 1 || last_q > 64) return DSA_ERR_UNSUPPORTED;
   HeadMap hm;
   if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  if (no_work(shape, hm.n)) return DSA_OK;
+  if (!q || !k || !v_scores || !s_scores) return DSA_ERR_INVALID_ARG;
   const int32_t rows = shape->batch * hm.n;
   const size_t need = est_workspace_bytes(rows, shape->seq_len);
   if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
-  if (rows == 0 || shape->seq_len == 0) return DSA_OK;
   EstArgs a;
   a.q = q; a.k = k;
   a.seq_len = shape->seq_len; a.head_dim = shape->head_dim; a.dtype = shape->dtype;
@@ -331,13 +337,14 @@ dsa_status dsa_kv_retention(const void* q, const void* k, const dsa_shape* shape
                             void* stream) {
   dsa_status st = check_shape(shape);
   if (st != DSA_OK) return st;
-  if (!q || !k || !scores || window < 1 || keep < 0 || (keep > 0 && !kept)) return DSA_ERR_INVALID_ARG;
+  if (window < 1 || keep < 0) return DSA_ERR_INVALID_ARG;
   HeadMap hm;
   if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  if (no_work(shape, hm.n)) return DSA_OK;
+  if (!q || !k || !scores || (keep > 0 && !kept)) return DSA_ERR_INVALID_ARG;
   const int32_t rows = shape->batch * hm.n, n = shape->seq_len;
   const size_t need = dsa_kv_retention_workspace_bytes(shape, keep, hm.n);
   if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
-  if (rows == 0 || n == 0) return DSA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   EstArgs a;
   a.q = q; a.k = k;
@@ -368,14 +375,14 @@ dsa_status dsa_sparse_decode(const void* q, const void* k, const void* v, void* 
                              void* workspace, size_t workspace_bytes, void* stream) {
   dsa_status st = check_shape(shape);
   if (st != DSA_OK) return st;
-  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
-  if (keys && (max_keys < 0 || !n_keys)) return DSA_ERR_INVALID_ARG;
+  if (keys && max_keys < 0) return DSA_ERR_INVALID_ARG;
   HeadMap hm;
   if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
   const int32_t rows = shape->batch * hm.n;
+  if (rows == 0) return DSA_OK;  // no decode row: nothing read or written
+  if (!q || !k || !v || !o || (keys && !n_keys)) return DSA_ERR_INVALID_ARG;
   const size_t need = dsa_sparse_decode_workspace_bytes(shape, keys ? max_keys : -1, hm.n);
   if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
-  if (rows == 0) return DSA_OK;
   // an empty cache or empty lists still run: the rows come out as zeros
   DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
@@ -423,13 +430,13 @@ dsa_status dsa_sparse_attention_vs(const void* q, const void* k, const void* v, 
                                    const int32_t* n_cols, int32_t max_cols, void* stream) {
   dsa_status st = check_shape(shape);
   if (st != DSA_OK) return st;
-  if (!q || !k || !v || !o || !n_intervals || !n_cols || max_iv < 0 || max_cols < 0)
-    return DSA_ERR_INVALID_ARG;
-  if ((max_iv && !intervals) || (max_cols && !cols)) return DSA_ERR_INVALID_ARG;
+  if (max_iv < 0 || max_cols < 0) return DSA_ERR_INVALID_ARG;
   HeadMap hm;
   if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  if (no_work(shape, hm.n)) return DSA_OK;
+  if (!q || !k || !v || !o || !n_intervals || !n_cols) return DSA_ERR_INVALID_ARG;
+  if ((max_iv && !intervals) || (max_cols && !cols)) return DSA_ERR_INVALID_ARG;
   AttnArgs a = attn_args(q, k, v, o, shape, scale, hm);
-  if (a.rows == 0 || a.seq_len == 0) return DSA_OK;
   VsIndex ix{intervals, n_intervals, max_iv, cols, n_cols, max_cols};
   return hip_status(launch_attention_vs(a, ix, static_cast<hipStream_t>(stream)));
 }
@@ -451,17 +458,17 @@ dsa_status dsa_vertical_slash_sparse_attention(const void* q, const void* k, con
                                                void* stream) {
   dsa_status st = check_shape(shape);
   if (st != DSA_OK) return st;
-  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
   if (vertical_topk < 0 || slash_topk < 1) return DSA_ERR_INVALID_ARG;
   if (last_q < 1 || last_q > 64) return DSA_ERR_UNSUPPORTED;
   HeadMap hm;
   if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  if (no_work(shape, hm.n)) return DSA_OK;
+  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
   const int32_t rows = shape->batch * hm.n, n = shape->seq_len;
   const int32_t vk = vertical_topk < n ? vertical_topk : n;
   const int32_t sk = slash_topk < n ? slash_topk : n;
   const size_t need = vs_layout(rows, n, vk, sk, nullptr, nullptr);
   if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
-  if (rows == 0 || n == 0) return DSA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   VsWork w;
   vs_layout(rows, n, vk, sk, workspace, &w);
@@ -481,10 +488,11 @@ dsa_status dsa_bs_pool(const void* x, int32_t dtype, int32_t batch, int32_t x_he
   if (batch < 0 || x_heads <= 0 || seq_len < 0) return DSA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return DSA_ERR_UNSUPPORTED;
   if (dtype != DSA_BF16 && dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
-  if (!x || !out) return DSA_ERR_INVALID_ARG;
   HeadMap hm;
   dsa_status st = make_map(x_heads, x_heads, heads, n_heads, hm);
   if (st != DSA_OK) return st;
+  if (batch == 0 || seq_len == 0 || hm.n == 0) return DSA_OK;
+  if (!x || !out) return DSA_ERR_INVALID_ARG;
   return hip_status(launch_pool(x, dtype, seq_len, head_dim, batch * hm.n, hm, out,
                                 static_cast<hipStream_t>(stream)));
 }
@@ -517,11 +525,12 @@ dsa_status dsa_sparse_attention_blocks(const void* q, const void* k, const void*
                                        int32_t max_sel, void* stream) {
   dsa_status st = check_shape(shape);
   if (st != DSA_OK) return st;
-  if (!q || !k || !v || !o || !n_sel || max_sel < 0 || (max_sel && !sel)) return DSA_ERR_INVALID_ARG;
+  if (max_sel < 0) return DSA_ERR_INVALID_ARG;
   HeadMap hm;
   if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  if (no_work(shape, hm.n)) return DSA_OK;
+  if (!q || !k || !v || !o || !n_sel || (max_sel && !sel)) return DSA_ERR_INVALID_ARG;
   AttnArgs a = attn_args(q, k, v, o, shape, scale, hm);
-  if (a.rows == 0 || a.seq_len == 0) return DSA_OK;
   return hip_status(launch_attention_blocks(a, BlockIndex{sel, n_sel, max_sel},
                                             static_cast<hipStream_t>(stream)));
 }
@@ -537,13 +546,14 @@ dsa_status dsa_block_sparse_attention(const void* q, const void* k, const void* 
                                       size_t workspace_bytes, void* stream) {
   dsa_status st = check_shape(shape);
   if (st != DSA_OK) return st;
-  if (!q || !k || !v || !o || topk < 1) return DSA_ERR_INVALID_ARG;
+  if (topk < 1) return DSA_ERR_INVALID_ARG;
   HeadMap hm;
   if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  if (no_work(shape, hm.n)) return DSA_OK;
+  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
   const int32_t rows = shape->batch * hm.n, n = shape->seq_len, nb = nblocks(n);
   const size_t need = bs_layout(shape, rows, topk, nullptr, nullptr);
   if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
-  if (rows == 0 || n == 0) return DSA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   BsWork w;
   bs_layout(shape, rows, topk, workspace, &w);
@@ -561,11 +571,12 @@ dsa_status dsa_streaming_attention(const void* q, const void* k, const void* v, 
                                    float scale, const int32_t* heads, int32_t n_heads, void* stream) {
   dsa_status st = check_shape(shape);
   if (st != DSA_OK) return st;
-  if (!q || !k || !v || !o || init_blocks < 0 || local_blocks < 1) return DSA_ERR_INVALID_ARG;
+  if (init_blocks < 0 || local_blocks < 1) return DSA_ERR_INVALID_ARG;
   HeadMap hm;
   if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  if (no_work(shape, hm.n)) return DSA_OK;
+  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
   AttnArgs a = attn_args(q, k, v, o, shape, scale, hm);
-  if (a.rows == 0 || a.seq_len == 0) return DSA_OK;
   return hip_status(launch_attention_stream(a, StreamIndex{init_blocks, local_blocks},
                                             static_cast<hipStream_t>(stream)));
 }
@@ -589,19 +600,19 @@ dsa_status dsa_mixed_sparse_attention(const void* q, const void* k, const void* 
                                       size_t workspace_bytes, void* stream) {
   dsa_status st = check_shape(shape);
   if (st != DSA_OK) return st;
-  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
   if (vertical_topk < 0 || slash_topk < 1 || topk < 1 || init_blocks < 0 || local_blocks < 1)
     return DSA_ERR_INVALID_ARG;
   if (last_q < 1 || last_q > 64) return DSA_ERR_UNSUPPORTED;
   HeadMap all, vs, bs;
   MixedIndex ix;
   if ((st = parse_patterns(shape, patterns, all, vs, bs, ix)) != DSA_OK) return st;
+  if (no_work(shape, all.n)) return DSA_OK;
+  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
   const int32_t n = shape->seq_len, nb = nblocks(n);
   const int32_t vk = vertical_topk < n ? vertical_topk : n;
   const int32_t sk = slash_topk < n ? slash_topk : n;
   const size_t need = mixed_layout(shape, ix.n_vs, ix.n_bs, vk, sk, topk, nullptr, nullptr, nullptr);
   if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
-  if (shape->batch == 0 || all.n == 0 || n == 0) return DSA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   VsWork vw;
   BsWork bw;
@@ -630,16 +641,16 @@ dsa_status dsa_sparse_attention_mixed(const void* q, const void* k, const void* 
                                       int32_t init_blocks, int32_t local_blocks, void* stream) {
   dsa_status st = check_shape(shape);
   if (st != DSA_OK) return st;
-  if (!q || !k || !v || !o || max_iv < 0 || max_cols < 0 || max_sel < 0 || init_blocks < 0 ||
-      local_blocks < 1)
+  if (max_iv < 0 || max_cols < 0 || max_sel < 0 || init_blocks < 0 || local_blocks < 1)
     return DSA_ERR_INVALID_ARG;
   HeadMap all, vs, bs;
   MixedIndex ix;
   if ((st = parse_patterns(shape, patterns, all, vs, bs, ix)) != DSA_OK) return st;
+  if (no_work(shape, all.n)) return DSA_OK;
+  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
   if (ix.n_vs && (!n_intervals || !n_cols || (max_iv && !intervals) || (max_cols && !cols)))
     return DSA_ERR_INVALID_ARG;
   if (ix.n_bs && (!n_sel || (max_sel && !sel))) return DSA_ERR_INVALID_ARG;
-  if (shape->batch == 0 || all.n == 0 || shape->seq_len == 0) return DSA_OK;
   ix.vs = VsIndex{intervals, n_intervals, max_iv, cols, n_cols, max_cols};
   ix.bs = BlockIndex{sel, n_sel, max_sel};
   ix.st = StreamIndex{init_blocks, local_blocks};

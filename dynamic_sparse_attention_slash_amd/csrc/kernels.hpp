@@ -119,7 +119,7 @@ struct EstArgs {
   int32_t chunk;      // keys per work-group (est_chunk_keys; set by est_carve)
   __host__ __device__ int32_t lq_eff() const { return last_q < seq_len ? last_q : seq_len; }
 };
-int32_t est_chunk_keys(int32_t rows, int32_t seq_len);
+int32_t est_chunk_keys(int32_t seq_len);
 size_t est_workspace_bytes(int32_t rows, int32_t seq_len);
 void est_carve(EstArgs& a, void* ws);
 hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s);

@@ -65,7 +65,8 @@ struct BlockRanges {
   __device__ bool next(int32_t& lo, int32_t& hi) {
     while (t < n_sel) {
       int32_t c = sel[t++];
-      if (c < 0) continue;
+      // ids outside [0, nb) name no key block (and would overflow c * 64)
+      if (c < 0 || c > (n - 1) / BLOCK) continue;
       lo = c * BLOCK;
       hi = min(n, lo + BLOCK);
       if (lo < hi) return true;
@@ -720,7 +721,7 @@ struct BlockRangesStaged {
   __device__ bool next(int32_t& lo, int32_t& hi) {
     while (t < n_sel) {
       const int32_t c = sel.get(t++);
-      if (c < 0) continue;
+      if (c < 0 || c > (n - 1) / BLOCK) continue;  // outside [0, nb): no key block
       lo = c * BLOCK;
       hi = min(n, lo + BLOCK);
       if (lo < hi) return true;

@@ -538,16 +538,20 @@ __global__ __launch_bounds__(256) void est_scombine_kernel(EstArgs a, int32_t nc
 
 }  // namespace
 
-int32_t est_chunk_keys(int32_t rows, int32_t seq_len) {
-  // the largest chunk that still gives about 2048 work-groups (two waves per SIMD)
-  for (int32_t cs = EST_CHUNK; cs > 256; cs /= 2)
-    if ((long long)rows * ((seq_len + cs - 1) / cs) >= 2048) return cs;
+int32_t est_chunk_keys(int32_t seq_len) {
+  // The chunk fixes the fp32 summation order of the row statistics and the
+  // slash partials, so it depends on seq_len alone: a head's scores are then
+  // the same bits whatever batch or head list it is computed with. Long rows
+  // take the largest chunk (64+ chunks per row); shorter ones smaller chunks,
+  // so that few rows still spread over many work-groups.
+  if (seq_len >= 65536) return EST_CHUNK;
+  if (seq_len >= 16384) return 512;
   return 256;
 }
 
 size_t est_workspace_bytes(int32_t rows, int32_t seq_len) {
   if (rows == 0 || seq_len == 0) return 0;  // nothing is launched
-  const int32_t C = est_chunk_keys(rows, seq_len);
+  const int32_t C = est_chunk_keys(seq_len);
   const size_t nch = (size_t)(seq_len + C - 1) / C;
   const size_t part = (size_t)rows * nch * 128 * sizeof(float);
   const size_t stats = (size_t)rows * 64 * sizeof(float);
@@ -557,7 +561,7 @@ size_t est_workspace_bytes(int32_t rows, int32_t seq_len) {
 }
 
 void est_carve(EstArgs& a, void* ws) {
-  a.chunk = est_chunk_keys(a.rows, a.seq_len);
+  a.chunk = est_chunk_keys(a.seq_len);
   const size_t nch = (size_t)(a.seq_len + a.chunk - 1) / a.chunk;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char* p = static_cast<char*>(ws);

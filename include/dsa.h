@@ -50,8 +50,11 @@
  * Empty work. A prefill call (the three pattern calls, the mixed calls, the
  *   stage calls, KV retention) with batch 0, seq_len 0 or no listed head
  *   enqueues nothing, returns DSA_OK and needs no workspace (the matching
- *   *_workspace_bytes call returns 0). The sparse decode step with an empty
- *   cache or empty key lists still runs and writes zero rows.
+ *   *_workspace_bytes call returns 0); its data pointers are not read and may
+ *   be NULL (zero-size arrays have no address), while scalar arguments are
+ *   still checked. The sparse decode step with no decode row (batch 0 or no
+ *   listed head) likewise returns DSA_OK; with an empty cache or empty key
+ *   lists it still runs and writes zero rows.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -228,23 +231,38 @@ dsa_status dsa_bs_select(const float* qp, const float* kp, int32_t rows, int32_t
                          size_t workspace_bytes, void* stream);
 size_t dsa_bs_select_workspace_bytes(int32_t rows, int32_t nb);
 
-/* Attention over a vertical-slash index (as built by dsa_vs_build_index) for
- * the listed heads: row = b * n_heads + t indexes intervals [rows][max_iv][2],
- * n_intervals [rows], cols [rows][nb][max_cols] and n_cols [rows][nb]. */
+/* Attention under a given vertical-slash sparse format [MInf §1 Problem
+ * Formulation: exact attention with the entries outside the dynamic mask
+ * excluded; §2.2 Vertical-Slash Head: the slash and vertical indices drive a
+ * block-sparse computation]. Query block a attends, causally, to the key
+ * ranges its intervals cover and to its column list, exactly as in the
+ * dsa_vs_build_index description; every other key is excluded. For the listed
+ * heads, row = b * n_heads + t indexes intervals [rows][max_iv][2],
+ * n_intervals [rows], cols [rows][nb][max_cols] and n_cols [rows][nb] (device
+ * int32, as dsa_vs_build_index writes them; index values are clamped into
+ * [0, seq_len) before any key is read). The index arrays must hold rows
+ * entries of these extents: the kernel reads n_intervals[row] intervals and
+ * n_cols[row][a] columns of block a. Writes o for the listed heads. */
 dsa_status dsa_sparse_attention_vs(
     const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
     float scale, const int32_t* heads, int32_t n_heads, const int32_t* intervals,
     const int32_t* n_intervals, int32_t max_iv, const int32_t* cols, const int32_t* n_cols,
     int32_t max_cols, void* stream);
 
-/* Attention over explicit key-block lists: sel [rows][nb][max_sel] holds
- * n_sel [rows][nb] ascending distinct block ids per query block. */
+/* Attention over explicit key-block lists [MInf §1 Problem Formulation, with
+ * the mask given by whole 64-key blocks; §2.2 Block-Sparse Head: the selected
+ * blocks of each query block are computed, all others skipped]. Query block a
+ * attends, causally, to the keys of the blocks sel[row][a][0 .. n_sel[row][a])
+ * (device int32 [rows][nb][max_sel] and [rows][nb], ascending distinct ids;
+ * ids outside [0, nb) are skipped). Writes o for the listed heads. */
 dsa_status dsa_sparse_attention_blocks(
     const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
     float scale, const int32_t* heads, int32_t n_heads, const int32_t* sel,
     const int32_t* n_sel, int32_t max_sel, void* stream);
 
-/* The attention launch of dsa_mixed_sparse_attention over given indices.
+/* The attention launch of dsa_mixed_sparse_attention over given indices
+ * [MInf §1 Problem Formulation; §2.2: each head keeps its own pattern, whose
+ * index drives that head's block-sparse computation].
  * patterns: HOST int32 [q_heads] as there. The VS heads, in ascending order,
  * number t = 0 .. n_vs-1 and take rows b * n_vs + t of intervals, n_intervals,
  * cols and n_cols (laid out as for dsa_sparse_attention_vs); the BS heads
@@ -306,6 +324,7 @@ dsa_status dsa_sparse_decode(const void* q, const void* k, const void* v, void* 
                              void* stream);
 size_t dsa_sparse_decode_workspace_bytes(const dsa_shape* shape, int32_t max_keys,
                                          int32_t n_heads);
+
 
 #ifdef __cplusplus
 }

@@ -174,3 +174,103 @@ def test_mixed_argument_errors(lib):
     assert stage(good, nsel=None) == INVALID
     assert stage(pats(-1, -1, -1, -1), None, None, None, None, None, None) == OK
     assert stage(pats(0, 1, 9, -1)) == INVALID
+
+
+# ---- the binding refuses index arrays whose extents do not match the call ----
+# (meta tensors: the extents are checked before any pointer is taken, so these
+# run without a GPU; a correct call gets as far as the GPU-tensor check)
+def _meta(*shape, dtype=None):
+    import torch
+    return torch.empty(shape, dtype=dtype or torch.bfloat16, device="meta")
+
+
+def test_binding_rejects_mismatched_vs_index():
+    import torch
+    i32 = torch.int32
+    q, k, v = _meta(2, 4, 300, 64), _meta(2, 2, 300, 64), _meta(2, 2, 300, 64)
+    nb = 5
+    good = dict(intervals=_meta(8, 6, 2, dtype=i32), n_intervals=_meta(8, dtype=i32),
+                cols=_meta(8, nb, 7, dtype=i32), n_cols=_meta(8, nb, dtype=i32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dsa.sparse_attention_vs(q, k, v, **good)
+    bad = [("intervals", _meta(6, 6, 2, dtype=i32)),     # rows for another head list
+           ("intervals", _meta(8, 6, 3, dtype=i32)),
+           ("n_intervals", _meta(7, dtype=i32)),
+           ("cols", _meta(8, nb + 1, 7, dtype=i32)),     # index of another seq_len
+           ("n_cols", _meta(8, nb - 1, dtype=i32))]
+    for name, t in bad:
+        args = dict(good, **{name: t})
+        with pytest.raises(ValueError, match="must have shape"):
+            dsa.sparse_attention_vs(q, k, v, **args)
+    # with a head subset the rows are batch * len(heads)
+    sub = dict(intervals=_meta(2, 6, 2, dtype=i32), n_intervals=_meta(2, dtype=i32),
+               cols=_meta(2, nb, 7, dtype=i32), n_cols=_meta(2, nb, dtype=i32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dsa.sparse_attention_vs(q, k, v, heads=[3], **sub)
+    with pytest.raises(ValueError, match="must have shape"):
+        dsa.sparse_attention_vs(q, k, v, heads=[1, 3], **sub)
+
+
+def test_binding_rejects_mismatched_block_lists():
+    import torch
+    i32 = torch.int32
+    q, k, v = _meta(1, 4, 200, 128), _meta(1, 1, 200, 128), _meta(1, 1, 200, 128)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dsa.sparse_attention_blocks(q, k, v, _meta(4, 4, 3, dtype=i32), _meta(4, 4, dtype=i32))
+    for sel, n_sel in ((_meta(4, 3, 3, dtype=i32), _meta(4, 4, dtype=i32)),
+                       (_meta(5, 4, 3, dtype=i32), _meta(4, 4, dtype=i32)),
+                       (_meta(4, 4, 3, dtype=i32), _meta(4, 3, dtype=i32))):
+        with pytest.raises(ValueError, match="must have shape"):
+            dsa.sparse_attention_blocks(q, k, v, sel, n_sel)
+    # the one-launch call checks each pattern's index against that pattern's heads
+    pats = ["vs", "bs", "st", None]
+    vs_ix = (_meta(1, 4, 2, dtype=i32), _meta(1, dtype=i32), _meta(1, 4, 5, dtype=i32), _meta(1, 4, dtype=i32))
+    bs_ix = (_meta(1, 4, 3, dtype=i32), _meta(1, 4, dtype=i32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dsa.sparse_attention_mixed(q, k, v, pats, vs_index=vs_ix, bs_index=bs_ix)
+    with pytest.raises(ValueError, match="must have shape"):
+        dsa.sparse_attention_mixed(q, k, v, pats, vs_index=vs_ix, bs_index=(_meta(2, 4, 3, dtype=i32),
+                                                                            _meta(2, 4, dtype=i32)))
+    with pytest.raises(ValueError, match="required"):
+        dsa.sparse_attention_mixed(q, k, v, pats, vs_index=vs_ix)
+
+
+def test_binding_rejects_mismatched_q_k():
+    q = _meta(1, 4, 256, 64)
+    for k in (_meta(2, 2, 256, 64), _meta(1, 2, 255, 64), _meta(1, 2, 256, 128)):
+        with pytest.raises(ValueError, match="shape mismatch"):
+            dsa.vs_estimate(q, k)
+        with pytest.raises(ValueError, match="shape mismatch"):
+            dsa.kv_retention(q, k, 64, 8)
+    with pytest.raises(ValueError, match="batch and head_dim"):
+        dsa.sparse_decode(_meta(1, 4, 128), _meta(1, 2, 256, 64), _meta(1, 2, 256, 64))
+
+
+def test_empty_work_accepts_null_pointers(lib):
+    """batch 0 or seq_len 0: nothing is read, so NULL data pointers are fine
+    (zero-size tensors have no address); scalar arguments are still checked."""
+    for sh in (shape(b=0), shape(n=0)):
+        s = ctypes.byref(sh)
+        assert lib.dsa_vertical_slash_sparse_attention(None, None, None, None, s, 8, 8, 64, 0.0, None, 0,
+                                                       None, 0, None) == OK
+        assert lib.dsa_vertical_slash_sparse_attention(None, None, None, None, s, 8, 0, 64, 0.0, None, 0,
+                                                       None, 0, None) == INVALID
+        assert lib.dsa_block_sparse_attention(None, None, None, None, s, 4, 0.0, None, 0, None, 0, None) == OK
+        assert lib.dsa_streaming_attention(None, None, None, None, s, 1, 2, 0.0, None, 0, None) == OK
+        assert lib.dsa_streaming_attention(None, None, None, None, s, 1, 0, 0.0, None, 0, None) == INVALID
+        assert lib.dsa_vs_estimate(None, None, s, 64, 0.0, None, 0, None, None, None, 0, None) == OK
+        assert lib.dsa_kv_retention(None, None, s, 64, 8, 0.0, None, 0, None, None, None, 0, None) == OK
+        assert lib.dsa_sparse_attention_vs(None, None, None, None, s, 0.0, None, 0, None, None, 0, None, None,
+                                           0, None) == OK
+        assert lib.dsa_sparse_attention_blocks(None, None, None, None, s, 0.0, None, 0, None, None, 0,
+                                               None) == OK
+        pats = (ctypes.c_int32 * 4)(0, 1, 2, -1)
+        assert lib.dsa_mixed_sparse_attention(None, None, None, None, s, pats, 8, 8, 64, 4, 1, 2, 0.0, None,
+                                              0, None) == OK
+        assert lib.dsa_sparse_attention_mixed(None, None, None, None, s, 0.0, pats, None, None, 0, None, None,
+                                              0, None, None, 0, 1, 2, None) == OK
+    assert lib.dsa_bs_pool(None, 0, 0, 2, 100, 64, None, 0, None, None) == OK
+    assert lib.dsa_bs_pool(None, 0, 1, 2, 0, 64, None, 0, None, None) == OK
+    assert lib.dsa_sparse_decode(None, None, None, None, ctypes.byref(shape(b=0)), 0.0, None, 0, None, 0,
+                                 None, None, 0, None) == OK
+

@@ -62,6 +62,45 @@ def test_vs_estimate(n, D, dt, lq):
             check_scores(sg[row].cpu().numpy(), s, f"s row {row}")
 
 
+@pytest.mark.parametrize("n,dt", [(3000, "bf16"), (20000, "bf16"), (70000, "bf16"), (777, "f32")])
+def test_vs_estimate_same_bits_for_any_head_list(n, dt):
+    """A head's scores do not depend on the batch or head list of the call:
+    the key chunking (and so the fp32 summation order) depends on seq_len only."""
+    say(f"vs_estimate head-list independence n={n} {dt}")
+    q, k, _ = rand_qkv(2, 8, 2, n, 64, dt, seed=n, amp=2.0)
+    v_all, s_all = dsa.vs_estimate(q, k)
+    v_one, s_one = dsa.vs_estimate(q[1:2], k[1:2], heads=[5])
+    torch.cuda.synchronize()
+    assert torch.equal(v_one[0], v_all[8 + 5]) and torch.equal(s_one[0], s_all[8 + 5])
+
+
+def test_empty_calls_through_the_binding():
+    """batch 0 or seq_len 0 (zero-size tensors, whose data pointers are NULL)
+    return without work through every wrapper."""
+    say("empty calls")
+    for B, n in ((0, 256), (1, 0)):
+        q, k, v = rand_qkv(B, 4, 2, n, 64, "bf16", seed=1)
+        o = dsa.vertical_slash_sparse_attention(q, k, v, 8, 8)
+        o = dsa.block_sparse_attention(q, k, v, 4, out=o)
+        o = dsa.streaming_attention(q, k, v, 1, 2, out=o)
+        o = dsa.mixed_sparse_attention(q, k, v, ["vs", "bs", "st", None], vertical_topk=8, slash_topk=8,
+                                       topk=4, init_blocks=1, local_blocks=2, out=o)
+        assert o.shape == q.shape
+        vg, sg = dsa.vs_estimate(q, k)
+        sc, kept = dsa.kv_retention(q, k, 64, 8)
+        assert vg.numel() == sg.numel() == sc.numel() == kept.numel() == 0
+        assert dsa.bs_pool(q).numel() == 0
+        rows, nb = B * 4, (n + 63) // 64
+        i32 = dict(dtype=torch.int32, device="cuda")
+        dsa.sparse_attention_vs(q, k, v, torch.zeros(rows, 1, 2, **i32), torch.zeros(rows, **i32),
+                                torch.zeros(rows, nb, 1, **i32), torch.zeros(rows, nb, **i32), out=o)
+        dsa.sparse_attention_blocks(q, k, v, torch.zeros(rows, nb, 1, **i32), torch.zeros(rows, nb, **i32), out=o)
+    qd = torch.zeros(0, 4, 64, dtype=torch.bfloat16, device="cuda")
+    kd = torch.zeros(0, 2, 100, 64, dtype=torch.bfloat16, device="cuda")
+    assert dsa.sparse_decode(qd, kd, kd).numel() == 0
+    torch.cuda.synchronize()
+
+
 def test_vs_estimate_planted_structure_and_mass():
     w = synthetic.BY_NAME["llama3_8b_128k_vs_bf16"].scaled(seq_len=8192, q_heads=4, kv_heads=1,
                                                             slash_topk=512)
@@ -226,7 +265,10 @@ def test_attention_blocks_given_indices(n, D, dt):
 
 
 @pytest.mark.parametrize("n,D,dt,init,local", [(1000, 128, "bf16", 1, 2), (1000, 128, "bf16", 0, 1),
-                                               (64 * 9 + 5, 64, "f32", 2, 3), (500, 128, "bf16", 3, 64)])
+                                               (64 * 9 + 5, 64, "f32", 2, 3), (500, 128, "bf16", 3, 64),
+                                               # bf16 panels at head_dim 64: an even and an odd
+                                               # block count, windows crossing panel edges
+                                               (1000, 64, "bf16", 1, 3), (64 * 7 + 33, 64, "bf16", 2, 2)])
 def test_streaming(n, D, dt, init, local):
     say(f"streaming n={n} init={init} local={local}")
     q, k, v = rand_qkv(1, 4, 4, n, D, dt, seed=n + init, amp=2.0)
