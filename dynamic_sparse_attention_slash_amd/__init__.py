@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     sparse_attention_mixed,
     sparse_attention_vs,
     sparse_decode,
+    sparse_decode_noalloc,
     streaming_attention,
     topk,
     vertical_slash_sparse_attention,

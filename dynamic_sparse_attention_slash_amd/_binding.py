@@ -53,6 +53,7 @@ _SIGS = {
     "dsa_kv_retention_workspace_bytes": ([ctypes.POINTER(Shape), _i32, _i32], _sz),
     "dsa_sparse_decode": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _f32, _ip, _i32, _vp, _i32, _vp, _vp, _sz, _vp], _i32),
     "dsa_sparse_decode_workspace_bytes": ([ctypes.POINTER(Shape), _i32, _i32], _sz),
+    "dsa_sparse_decode_noalloc": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _f32, _ip, _i32, _vp, _i32, _vp, _vp], _i32),
     "dsa_topk": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp], _i32),
     "dsa_topk_workspace_bytes": ([_i32, _i32, _i32], _sz),
     "dsa_vs_build_index": ([_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
@@ -347,10 +348,20 @@ def sparse_decode(q, k, v, keys: Optional[torch.Tensor] = None, n_keys: Optional
     [batch, kv_heads, seq_len, head_dim]; keys int32 [batch * n_heads,
     max_keys] with counts n_keys [batch * n_heads], or None for the whole
     cache. Returns o shaped like q (listed heads written)."""
-    return _decode(q, k, v, keys, n_keys, scale, heads, out)
+    return _decode(q, k, v, keys, n_keys, scale, heads, out, False)
 
 
-def _decode(q, k, v, keys, n_keys, scale, heads, out) -> torch.Tensor:
+def sparse_decode_noalloc(q, k, v, keys: Optional[torch.Tensor] = None,
+                          n_keys: Optional[torch.Tensor] = None, *, scale: Optional[float] = None,
+                          heads: Optional[Sequence[int]] = None,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sparse_decode through the allocation-free entry point (split partials in
+    the library's static device scratch, no workspace). Pass `out` to keep the
+    call free of allocations on this side too."""
+    return _decode(q, k, v, keys, n_keys, scale, heads, out, True)
+
+
+def _decode(q, k, v, keys, n_keys, scale, heads, out, noalloc: bool) -> torch.Tensor:
     if k.dim() != 4 or v.shape != k.shape:
         raise ValueError("k, v must be [batch, kv_heads, seq_len, head_dim]")
     B, Hkv, n, D = k.shape
@@ -374,6 +385,10 @@ def _decode(q, k, v, keys, n_keys, scale, heads, out) -> torch.Tensor:
         kp, mk, nkp = _dev(keys, "keys"), keys.shape[1], _dev(n_keys, "n_keys")
     else:
         kp, mk, nkp = None, -1, None
+    if noalloc:
+        _call("dsa_sparse_decode_noalloc", _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+              _dev(o, "out"), ctypes.byref(sh), _scale(scale), ha, hn, kp, max(mk, 0), nkp, _stream(q))
+        return o
     ws = _workspace(load().dsa_sparse_decode_workspace_bytes(ctypes.byref(sh), mk, nh), q.device)
     _call("dsa_sparse_decode", _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(o, "out"),
           ctypes.byref(sh), _scale(scale), ha, hn, kp, max(mk, 0), nkp, ws.data_ptr(), ws.numel(),

@@ -369,10 +369,16 @@ size_t dsa_sparse_decode_workspace_bytes(const dsa_shape* shape, int32_t max_key
   return decode_workspace_bytes(shape->batch * n_heads, mk, shape->head_dim);
 }
 
-dsa_status dsa_sparse_decode(const void* q, const void* k, const void* v, void* o,
-                             const dsa_shape* shape, float scale, const int32_t* heads, int32_t n_heads,
-                             const int32_t* keys, int32_t max_keys, const int32_t* n_keys,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Decode step with its split partials in `workspace` (caller-owned, or the
+// static scratch; `scratch_bytes` is what it holds). Returns DSA_OK without
+// work when there is no decode row.
+dsa_status decode_call(const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
+                       float scale, const int32_t* heads, int32_t n_heads, const int32_t* keys,
+                       int32_t max_keys, const int32_t* n_keys, void* workspace, size_t workspace_bytes,
+                       bool static_scratch, void* stream) {
   dsa_status st = check_shape(shape);
   if (st != DSA_OK) return st;
   if (keys && max_keys < 0) return DSA_ERR_INVALID_ARG;
@@ -382,7 +388,17 @@ dsa_status dsa_sparse_decode(const void* q, const void* k, const void* v, void* 
   if (rows == 0) return DSA_OK;  // no decode row: nothing read or written
   if (!q || !k || !v || !o || (keys && !n_keys)) return DSA_ERR_INVALID_ARG;
   const size_t need = dsa_sparse_decode_workspace_bytes(shape, keys ? max_keys : -1, hm.n);
-  if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
+  if (static_scratch) {
+    // checked before the scratch is looked up: a refused call makes no HIP call
+    if (need > DSA_DECODE_NOALLOC_MAX_BYTES) return DSA_ERR_WORKSPACE;
+    float* p = nullptr;
+    size_t bytes = 0;
+    if (decode_static_scratch(&p, &bytes) != hipSuccess) return DSA_ERR_HIP;
+    if (bytes < need) return DSA_ERR_WORKSPACE;
+    workspace = p;
+  } else if (workspace_bytes < need || (need && !workspace)) {
+    return DSA_ERR_WORKSPACE;
+  }
   // an empty cache or empty lists still run: the rows come out as zeros
   DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
@@ -393,6 +409,25 @@ dsa_status dsa_sparse_decode(const void* q, const void* k, const void* v, void* 
   a.keys = keys; a.max_keys = keys ? max_keys : 0; a.n_keys = n_keys;
   a.part = static_cast<float*>(workspace);
   return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_sparse_decode(const void* q, const void* k, const void* v, void* o,
+                             const dsa_shape* shape, float scale, const int32_t* heads, int32_t n_heads,
+                             const int32_t* keys, int32_t max_keys, const int32_t* n_keys,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_call(q, k, v, o, shape, scale, heads, n_heads, keys, max_keys, n_keys, workspace,
+                     workspace_bytes, false, stream);
+}
+
+dsa_status dsa_sparse_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                                     const dsa_shape* shape, float scale, const int32_t* heads,
+                                     int32_t n_heads, const int32_t* keys, int32_t max_keys,
+                                     const int32_t* n_keys, void* stream) {
+  return decode_call(q, k, v, o, shape, scale, heads, n_heads, keys, max_keys, n_keys, nullptr, 0, true,
+                     stream);
 }
 
 size_t dsa_topk_workspace_bytes(int32_t rows, int32_t n, int32_t k) {

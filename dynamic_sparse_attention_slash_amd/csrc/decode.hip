@@ -22,10 +22,21 @@
 //
 // Whole-cache decode takes the heads of a kv group in bundles of up to four
 // rows per work-group, so every K and V row is read once for all of them.
+#include <mutex>
+
+#include "../../include/dsa.h"
 #include "kernels.hpp"
 
 namespace dsa {
 namespace {
+
+// Split partials of the allocation-free decode entry point: a fixed device
+// array (each GPU the library runs on holds its own copy for the life of the
+// process). Host code never passes this name to a kernel: it is a host-side
+// stand-in, not a device address; decode_static_scratch() looks the address
+// up once per device.
+static __device__ __align__(256) float scratch[DSA_DECODE_NOALLOC_MAX_BYTES / sizeof(float)];
+constexpr int MAX_DEVICES = 64;
 
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_WAVES = DEC_THREADS / 64;
@@ -251,6 +262,27 @@ size_t decode_workspace_bytes(int32_t rows, int32_t max_keys, int32_t head_dim) 
   int32_t sk;
   const int32_t splits = decode_splits(rows, max_keys, sk);
   return (size_t)rows * splits * (2 + head_dim) * sizeof(float);
+}
+
+hipError_t decode_static_scratch(float** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // with `dev` current: this device's copy of the array
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = static_cast<float*>(addr[dev]);
+  *bytes = sizeof(scratch);
+  return hipSuccess;
 }
 
 hipError_t launch_decode(DecodeArgs a, hipStream_t s) {

@@ -144,6 +144,9 @@ struct DecodeArgs {
 int32_t decode_splits(int32_t rows, int32_t max_keys, int32_t& split_keys);
 size_t decode_workspace_bytes(int32_t rows, int32_t max_keys, int32_t head_dim);
 hipError_t launch_decode(DecodeArgs a, hipStream_t s);
+// Device address (on the current device) and size of the static scratch that
+// the allocation-free decode entry point uses for its split partials.
+hipError_t decode_static_scratch(float** ptr, size_t* bytes);
 
 // ---- top-k (topk.hip) ----
 // scratch of launch_topk_rows (0 when the rows are short enough for one pass)

@@ -325,6 +325,27 @@ dsa_status dsa_sparse_decode(const void* q, const void* k, const void* v, void* 
 size_t dsa_sparse_decode_workspace_bytes(const dsa_shape* shape, int32_t max_keys,
                                          int32_t n_heads);
 
+/* Size of the static device scratch of dsa_sparse_decode_noalloc. */
+#define DSA_DECODE_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+
+/* dsa_sparse_decode for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, kernels and results, with the split partials in a fixed device
+ * array of the library instead of a workspace argument. Nothing is allocated
+ * and no allocating routine is called. The array is DSA_DECODE_NOALLOC_MAX_BYTES
+ * bytes, one copy per GPU, held until the process ends; its address is looked
+ * up on a device's first call (with that device current, which must be the
+ * device of `stream`). A call whose partials need more than that
+ * (dsa_sparse_decode_workspace_bytes(shape, max_keys, n_heads) >
+ * DSA_DECODE_NOALLOC_MAX_BYTES) returns DSA_ERR_WORKSPACE before any HIP call.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and must be serialised by the
+ * caller. Each call writes every partial it reads, so nothing carries over
+ * from the previous call's contents. */
+dsa_status dsa_sparse_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                                     const dsa_shape* shape, float scale, const int32_t* heads,
+                                     int32_t n_heads, const int32_t* keys, int32_t max_keys,
+                                     const int32_t* n_keys, void* stream);
 
 #ifdef __cplusplus
 }

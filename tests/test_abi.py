@@ -274,3 +274,18 @@ def test_empty_work_accepts_null_pointers(lib):
     assert lib.dsa_sparse_decode(None, None, None, None, ctypes.byref(shape(b=0)), 0.0, None, 0, None, 0,
                                  None, None, 0, None) == OK
 
+
+def test_noalloc_decode_argument_errors(lib):
+    """The allocation-free decode refuses, on the host, a call whose split
+    partials exceed its static scratch (no HIP call is made)."""
+    need = lib.dsa_sparse_decode_workspace_bytes(ctypes.byref(shape(b=200, hq=256, hkv=256, n=64)), -1, 256)
+    assert need > 16 << 20
+    big = shape(b=200, hq=256, hkv=256, n=64)
+    assert lib.dsa_sparse_decode_noalloc(P, P, P, P, ctypes.byref(big), 0.0, None, 0, None, 0, None,
+                                         None) == WORKSPACE
+    sh = shape()
+    assert lib.dsa_sparse_decode_noalloc(None, P, P, P, ctypes.byref(sh), 0.0, None, 0, None, 0, None,
+                                         None) == INVALID
+    assert lib.dsa_sparse_decode_noalloc(P, P, P, P, ctypes.byref(sh), 0.0, None, 0, P, -1, P, None) == INVALID
+    assert lib.dsa_sparse_decode_noalloc(None, None, None, None, ctypes.byref(shape(b=0)), 0.0, None, 0, None,
+                                         0, None, None) == OK
