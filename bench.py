@@ -42,12 +42,16 @@ from __future__ import annotations
 
 import argparse
 import csv
+import ctypes
 import glob
 import hashlib
 import json
 import math
 import os
+import re
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -63,6 +67,15 @@ BLK = 64
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
+# the pages' own figures (other hardware, other metrics): context only
+PAGES_CONTEXT = [
+    {"figure": "about 10x prefill speedup over dense attention", "hardware": "1x NVIDIA A100",
+     "workload": "million-token prompts", "source": "MInference 1.0 article, preface"},
+    {"figure": "18.95x attention decoding speedup", "hardware": "1x NVIDIA L40s 48GB",
+     "workload": "1M-token context", "source": "InfiniteHiP summary, introduction"},
+    {"figure": "about 1.58x serving throughput over vLLM 0.6.1", "hardware": "RTX 4090",
+     "workload": "4000 input / 500 output tokens", "source": "Novita AI KV-sparsity blog, results"},
+]
 ATTN_SRC = os.path.join(ROOT, "dynamic_sparse_attention_slash_amd", "csrc", "sparse_attention.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 DOMINANT = "attn_vs_single_kernel"
@@ -74,6 +87,69 @@ def log(*a):
 
 def source_hash(path=ATTN_SRC):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+# device facts and the clock under load
+# ----------------------------------------------------------------------------
+def device_info():
+    """Compute units and peak shader clock of device 0 from the HIP runtime
+    (hipDeviceAttributeMultiprocessorCount / hipDeviceAttributeClockRate)."""
+    info = {"name": torch.cuda.get_device_properties(0).name,
+            "gcn_arch": torch.cuda.get_device_properties(0).gcnArchName}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        for key, attr in (("compute_units", 63), ("peak_clock_mhz", 5)):
+            if hip.hipDeviceGetAttribute(ctypes.byref(val), attr, 0) == 0:
+                info[key] = val.value if key == "compute_units" else val.value / 1000.0
+    except OSError as e:
+        info["error"] = str(e)
+    if "compute_units" in info and "peak_clock_mhz" in info:
+        # dense bf16 MFMA: 4 SIMDs x 1024 FLOP per clock per CU
+        info["bf16_peak_tflops_at_peak_clock"] = info["compute_units"] * 4096 * info["peak_clock_mhz"] * 1e6 / 1e12
+    return info
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock with rocm-smi (a child process)
+    while the timed steps run."""
+
+    def __init__(self, period=0.3):
+        self.period, self.samples, self._stop = period, [], threading.Event()
+        self._thr = None
+
+    def _one(self):
+        try:
+            out = subprocess.run(["rocm-smi", "-d", "0", "--showclocks"], capture_output=True, text=True,
+                                 timeout=5).stdout
+        except (OSError, subprocess.SubprocessError):
+            return None
+        m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", out, re.I)
+        return float(m.group(1)) if m else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._one()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._thr = threading.Thread(target=self._run, daemon=True)
+        self._thr.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thr.join(timeout=10)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
+                "tool": "rocm-smi --showclocks (sclk), sampled during the timed steps"}
 
 
 # ----------------------------------------------------------------------------
@@ -357,6 +433,25 @@ def stage_bytes(w, x, idx):
     return out
 
 
+def bs_select_roofline(w, x, ms):
+    """Block select against its own roofline: D * nb * (nb + 1) FLOP per head
+    (one D-long dot per block pair of the causal triangle), each fp32 product
+    taken as three bf16 MFMA products, so the peak is a third of the bf16
+    MFMA peak; bytes are the pooled rows read, the logits written once and read
+    twice by the select, and the selections written."""
+    n, D, B = w.seq_len, w.head_dim, w.batch
+    nb = (n + BLK - 1) // BLK
+    rows = B * len(x.heads["bs"])
+    flops = float(D * nb * (nb + 1)) * rows
+    tri = nb * (nb + 1) // 2
+    nbytes = rows * (2 * nb * D * 4 + 3 * tri * 4 + nb * min(w.topk, nb) * 4 + nb * 4)
+    ach = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma (three bf16 products per fp32 product)", "flops": flops, "achieved": ach,
+            "peak": PEAK_BF16_TFLOPS / 3, "unit": "TFLOP/s", "frac": ach / (PEAK_BF16_TFLOPS / 3),
+            "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "ms": ms}
+
+
 # ----------------------------------------------------------------------------
 # CPU oracle on a bounded sample
 # ----------------------------------------------------------------------------
@@ -375,7 +470,44 @@ def _sampled_blocks(nb, rng, seconds, max_blocks, fn):
     return t_sum, rk_sum, done
 
 
-def cpu_baseline(layer, idx, flops_total, seconds=(12.0, 5.0, 1.0)):
+def cpu_baseline(layer, idx, flops_total, seconds=(12.0, 5.0, 1.0), full=False):
+    """The oracle on the host's cores: the whole layer (full=True; only for
+    layers it finishes in seconds), or a bounded sample scaled to the layer.
+    `cores` is the threads it actually kept busy: process CPU time over wall
+    time (numpy's BLAS threads; the oracle's own loops are serial)."""
+    c0, t0 = os.times(), time.perf_counter()
+    res = _cpu_full(layer) if full else _cpu_sampled(layer, idx, flops_total, seconds)
+    c1, wall = os.times(), time.perf_counter() - t0
+    cpu_s = (c1.user - c0.user) + (c1.system - c0.system)
+    res["value"] = flops_total / (res.pop("t_layer") ) / 1e12
+    res["cores"] = round(cpu_s / wall, 1) if wall > 0 else 1.0
+    res["affinity_cpus"] = len(os.sched_getaffinity(0))
+    res["wall_s"] = round(wall, 2)
+    return res
+
+
+def _cpu_full(layer):
+    """The oracle's three pipelines over every head of the layer."""
+    from oracle import dsa_oracle as O
+    w, x = layer.w, layer.x
+    f = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    q, k, v = f(layer.q), f(layer.k), f(layer.v)
+    t0 = time.perf_counter()
+    if x.heads["vs"]:
+        O.vertical_slash_sparse_attention(q, k, v, w.vertical_topk, w.slash_topk, last_q=w.last_q,
+                                          heads=x.heads["vs"])
+    if x.heads["bs"]:
+        O.block_sparse_attention(q, k, v, w.topk, heads=x.heads["bs"])
+    if x.heads["st"]:
+        O.streaming_attention(q, k, v, w.init_blocks, w.local_blocks, heads=x.heads["st"])
+    t = time.perf_counter() - t0
+    return {"unit": "TFLOP/s (effective, computed blocks)", "kind": "oracle", "t_layer": t,
+            "sample": "the whole layer: every head's estimate, selection and attention (float64 numpy "
+                      "oracle, not a tuned CPU implementation)",
+            "ms_per_layer": t * 1e3}
+
+
+def _cpu_sampled(layer, idx, flops_total, seconds):
     from oracle import dsa_oracle as O
     w, x = layer.w, layer.x
     n, D = w.seq_len, w.head_dim
@@ -437,9 +569,7 @@ def cpu_baseline(layer, idx, flops_total, seconds=(12.0, 5.0, 1.0)):
         rk = float((st_keys_per_block(n, w.init_blocks, w.local_blocks) * rows_per_block(n)).sum())
         t_total += t_att * rk / keys_s * w.batch * len(x.heads["st"])
         parts.append(f"one streaming head: attention of {nblk} sampled query blocks")
-    cores = len(os.sched_getaffinity(0))
-    return {"value": flops_total / t_total / 1e12, "unit": "TFLOP/s (effective, computed blocks)",
-            "cores": cores, "kind": "oracle",
+    return {"unit": "TFLOP/s (effective, computed blocks)", "kind": "oracle", "t_layer": t_total,
             "sample": "; ".join(parts) + "; times scaled to the whole layer by head count and by "
                       "row x key count (float64 numpy oracle, not a tuned CPU implementation)",
             "extrapolated_ms_per_layer": t_total * 1e3}
@@ -492,7 +622,7 @@ def committed_traffic(workload):
 
 
 # ----------------------------------------------------------------------------
-def run_layer(w, steps, warmup, with_cpu):
+def run_layer(w, steps, warmup, with_cpu, cpu_full=False, after_prefill=True, cpu_seconds=(12.0, 5.0, 1.0)):
     dev = torch.device("cuda:0")
     log(f"[bench] workload {w.name}: generating inputs on {dev}")
     x = synthetic.make_inputs(w, device=dev)
@@ -509,16 +639,21 @@ def run_layer(w, steps, warmup, with_cpu):
         layer.step()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(steps):
-        layer.step()
-    e1.record(s)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    with ClockSampler() as clk:
+        ev[0].record(s)
+        for i in range(steps):
+            layer.step()
+            ev[i + 1].record(s)
+        torch.cuda.synchronize()
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    ms = ev[0].elapsed_time(ev[-1]) / steps
     log(f"[bench] {w.name}: {ms:.3f} ms/layer; stages {st}")
     res = {
         "ms_per_layer": ms, "tflops": f_total / (ms * 1e-3) / 1e12,
+        "ms_per_layer_median": per_step[len(per_step) // 2], "ms_per_layer_min": per_step[0],
+        "dtype": w.dtype,
+        "clock_during_steps": clk.summary(),
         "flops_computed_blocks": f_total, "flops_per_pattern": flops,
         "flops_dense_causal": dense, "density_vs_dense": f_total / dense,
         "stages_ms": st,
@@ -534,20 +669,66 @@ def run_layer(w, steps, warmup, with_cpu):
     res["stages_hbm"] = {k.replace("_ms", ""): {"bytes": v, "gbs": v / (st[k] * 1e-3) / 1e9,
                                                 "frac_hbm": v / (st[k] * 1e-3) / 1e9 / PEAK_HBM_GBS}
                          for k, v in sb.items() if k in st}
-    if "vs" in flops and w.dtype == "bf16":
-        ach = flops["vs"] / (st["vs_attention_ms"] * 1e-3) / 1e12
-        res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / PEAK_BF16_TFLOPS, "traffic": committed_traffic(w.name),
-                           "kernel": DOMINANT, "flops_per_launch": flops["vs"],
-                           "launch_ms": st["vs_attention_ms"]}
-    if w.dtype == "bf16":
+    dom = "vs" if "vs" in flops else "bs" if "bs" in flops else None
+    if dom:
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        launch_ms = st[f"{dom}_attention_ms"]
+        ach = flops[dom] / (launch_ms * 1e-3) / 1e12
+        kernel = {("vs", "bf16"): DOMINANT, ("bs", "bf16"): "attn_blocks_single_kernel",
+                  ("vs", "f32"): "attn_vs_f32_kernel", ("bs", "f32"): "attn_blocks_f32_kernel"}[(dom, w.dtype)]
+        res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                           "frac": ach / peak,
+                           "traffic": committed_traffic(w.name) if kernel == DOMINANT else None,
+                           "kernel": kernel, "flops_per_launch": flops[dom], "launch_ms": launch_ms}
+    if "bs" in idx and "bs_select_ms" in st:
+        res["bs_select_roofline"] = bs_select_roofline(w, x, st["bs_select_ms"])
+    if w.dtype == "bf16" and after_prefill:
         res["after_prefill"] = kv_retention_timing(layer, reps=3)
     if with_cpu:
-        log(f"[bench] {w.name}: cpu baseline (oracle, bounded sample)")
-        res["cpu_baseline"] = cpu_baseline(layer, idx, f_total)
+        log(f"[bench] {w.name}: cpu baseline (oracle, {'whole layer' if cpu_full else 'bounded sample'})")
+        res["cpu_baseline"] = cpu_baseline(layer, idx, f_total, seconds=cpu_seconds, full=cpu_full)
     del layer, x, idx
     torch.cuda.empty_cache()
     return res
+
+
+# layers whose whole-layer oracle finishes in seconds (timed in full)
+FULL_ORACLE = ("vs_head_4k_f32", "bs_mha4_32k_bf16")
+
+
+def workload_config(w):
+    return {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+            "seq_len": w.seq_len, "head_dim": w.head_dim,
+            "heads_per_pattern": {p: len(hs) for p, hs in synthetic.head_patterns(w).items()},
+            "vertical_topk": w.vertical_topk, "slash_topk": w.slash_topk, "topk": w.topk,
+            "init_blocks": w.init_blocks, "local_blocks": w.local_blocks}
+
+
+def layer_record(r):
+    """The per-layer fields of the JSON line for one timed workload."""
+    peak = PEAK_BF16_TFLOPS if r["dtype"] == "bf16" else PEAK_F32_TFLOPS
+    out = {
+        "ms_per_layer": round(r["ms_per_layer"], 4),
+        "ms_per_layer_median": round(r["ms_per_layer_median"], 4),
+        "ms_per_layer_min": round(r["ms_per_layer_min"], 4),
+        "tflops": round(r["tflops"], 3),
+        "pct_peak": round(100 * r["tflops"] / peak, 2),
+        "peak_tflops": peak,
+        "clock_during_steps": r.get("clock_during_steps"),
+        "flops_computed_blocks": r["flops_computed_blocks"],
+        "flops_per_pattern": r["flops_per_pattern"],
+        "density_vs_dense": r["density_vs_dense"],
+        "stages_ms": {k: round(v, 4) for k, v in r["stages_ms"].items()},
+        "stages_hbm": {k: {kk: (round(vv, 4) if kk != "bytes" else vv) for kk, vv in v.items()}
+                       for k, v in r["stages_hbm"].items()},
+        "roofline": r.get("roofline"),
+    }
+    for key in ("bs_select_roofline", "after_prefill", "ms_per_layer_one_stream", "one_launch"):
+        if r.get(key) is not None:
+            out[key] = r[key]
+    if r["dtype"] == "bf16":
+        out["pct_bf16_peak"] = out["pct_peak"]
+    return out
 
 
 def main():
@@ -557,8 +738,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b_1m_mixed_bf16",
                     choices=[w.name for w in synthetic.WORKLOADS])
-    ap.add_argument("--secondary", default="llama3_8b_128k_vs_bf16",
-                    help="a second workload timed beside the first ('none' to skip)")
+    ap.add_argument("--secondary", default="all",
+                    help="workloads timed beside the first: 'all' (every other named workload), "
+                         "a comma-separated list, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-pmc", metavar="DIR")
@@ -588,7 +770,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = synthetic.BY_NAME[args.workload]
-    prim = run_layer(w, args.steps, args.warmup, not args.no_cpu_baseline)
+    dev_info = device_info()
+    log(f"[bench] device {dev_info}")
+    prim = run_layer(w, args.steps, args.warmup, not args.no_cpu_baseline,
+                     cpu_full=w.name in FULL_ORACLE)
     res = {
         "metric": "sparse prefill attention ms/layer + effective TFLOP/s (% bf16 peak) at 128K/1M",
         "value": round(prim["tflops"], 3),
@@ -597,37 +782,29 @@ def main():
         "ms_per_step": round(prim["ms_per_layer"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded; planted sink/slash structure)",
-        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
-                   "seq_len": w.seq_len, "head_dim": w.head_dim,
-                   "heads_per_pattern": {p: len(hs) for p, hs in synthetic.head_patterns(w).items()},
-                   "vertical_topk": w.vertical_topk, "slash_topk": w.slash_topk, "topk": w.topk,
-                   "init_blocks": w.init_blocks, "local_blocks": w.local_blocks},
-        "ms_per_layer": round(prim["ms_per_layer"], 4),
-        "pct_bf16_peak": round(100 * prim["tflops"] / PEAK_BF16_TFLOPS, 2),
-        "flops_computed_blocks": prim["flops_computed_blocks"],
-        "flops_per_pattern": prim["flops_per_pattern"],
-        "density_vs_dense": prim["density_vs_dense"],
-        "stages_ms": {k: round(v, 4) for k, v in prim["stages_ms"].items()},
-        "stages_hbm": {k: {kk: (round(vv, 4) if kk != "bytes" else vv) for kk, vv in v.items()}
-                       for k, v in prim["stages_hbm"].items()},
-        "after_prefill": prim.get("after_prefill"),
-        "ms_per_layer_one_stream": prim.get("ms_per_layer_one_stream"),
-        "one_launch": prim.get("one_launch"),
-        "roofline": prim.get("roofline"),
+        "config": workload_config(w),
+        "device": dev_info,
     }
+    res.update(layer_record(prim))
     if "cpu_baseline" in prim:
         res["cpu_baseline"] = prim["cpu_baseline"]
-    if args.secondary != "none" and args.secondary != w.name:
-        w2 = synthetic.BY_NAME[args.secondary]
-        sec = run_layer(w2, args.steps, args.warmup, False)
-        res["secondary"] = {"workload": w2.name, "ms_per_layer": round(sec["ms_per_layer"], 4),
-                            "tflops": round(sec["tflops"], 3),
-                            "pct_bf16_peak": round(100 * sec["tflops"] / PEAK_BF16_TFLOPS, 2),
-                            "density_vs_dense": sec["density_vs_dense"],
-                            "stages_ms": {k: round(v, 4) for k, v in sec["stages_ms"].items()},
-                            "stages_hbm": {k: {kk: (round(vv, 4) if kk != "bytes" else vv) for kk, vv in v.items()}
-                                           for k, v in sec["stages_hbm"].items()},
-                            "roofline": sec.get("roofline")}
+    res["pages_context"] = PAGES_CONTEXT
+    if args.secondary == "all":
+        names = [x.name for x in synthetic.WORKLOADS if x.name != w.name]
+    elif args.secondary == "none":
+        names = []
+    else:
+        names = [x for x in args.secondary.split(",") if x and x != w.name]
+    res["secondary"] = []
+    for name in names:
+        w2 = synthetic.BY_NAME[name]
+        sec = run_layer(w2, args.steps, args.warmup, not args.no_cpu_baseline,
+                        cpu_full=w2.name in FULL_ORACLE, after_prefill=False, cpu_seconds=(5.0, 3.0, 1.0))
+        rec = {"workload": w2.name, "config": workload_config(w2), "dtype": w2.dtype}
+        rec.update(layer_record(sec))
+        if "cpu_baseline" in sec:
+            rec["cpu_baseline"] = sec["cpu_baseline"]
+        res["secondary"].append(rec)
     print(json.dumps(res), flush=True)
 
 
