@@ -33,30 +33,42 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
+# host-side AddressSanitizer + UndefinedBehaviorSanitizer (device code is built
+# as usual): for checking the library's host code, argument validation above all
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def _compile(src: str, build_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = True, out: str = OUT, sanitize: bool = False) -> str:
+    """Compile every source and link ``out``. ``sanitize`` adds the host-side
+    sanitizers; such a library needs the sanitizer runtime loaded first (link
+    it into an executable built with the same -fsanitize flags)."""
+    build_dir = BUILD_DIR if out == OUT else out + ".build"
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
+    extra = SANITIZE if sanitize else []
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, build_dir, extra), srcs))
+    tmp = out + ".tmp"
+    link_extra = [*SANITIZE, "-Xarch_host", "-shared-libsan"] if sanitize else []
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
-    shutil.rmtree(BUILD_DIR, ignore_errors=True)
+    os.replace(tmp, out)
+    shutil.rmtree(build_dir, ignore_errors=True)
     if verbose:
-        print(f"built {OUT}", file=sys.stderr)
-    return OUT
+        print(f"built {out}", file=sys.stderr)
+    return out
 
 
 if __name__ == "__main__":

@@ -17,8 +17,11 @@ constexpr size_t LOGITS_BUDGET = (size_t)1 << 30;  // block-logit scratch per la
 
 size_t al(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
 
+// Lays out workspace regions from a base address. The base is NULL when only
+// the size is wanted, so addresses are formed as integers (pointer arithmetic
+// on NULL is undefined).
 struct Carver {
-  char* p;
+  uintptr_t p;
   size_t used = 0;
   template <typename T>
   T* take(size_t count) {
@@ -104,7 +107,7 @@ size_t vs_layout(int32_t rows, int32_t n, int32_t vk, int32_t sk, void* base, Vs
     if (w) *w = VsWork{};
     return 0;
   }
-  Carver c{static_cast<char*>(base)};
+  Carver c{reinterpret_cast<uintptr_t>(base)};
   const int32_t nb = nblocks(n);
   void* est = c.take<char>(est_workspace_bytes(rows, n));
   float* v = c.take<float>((size_t)rows * n);
@@ -132,7 +135,7 @@ int32_t logit_rows_per_group(int32_t rows, int32_t nb) {
 }
 struct BsWork { float* qp; float* kp; float* logits; int32_t* sel; int32_t* n_sel; };
 size_t bs_layout(const dsa_shape* s, int32_t rows, int32_t topk, void* base, BsWork* w) {
-  Carver c{static_cast<char*>(base)};
+  Carver c{reinterpret_cast<uintptr_t>(base)};
   const int32_t nb = nblocks(s->seq_len), D = s->head_dim;
   const int32_t ke = topk < nb ? topk : nb;
   float* qp = c.take<float>((size_t)rows * nb * D);
