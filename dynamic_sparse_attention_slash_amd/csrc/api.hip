@@ -329,7 +329,7 @@ dsa_status dsa_vs_estimate(const void* q, const void* k, const dsa_shape* shape,
 size_t dsa_kv_retention_workspace_bytes(const dsa_shape* shape, int32_t keep, int32_t n_heads) {
   if (check_shape(shape) != DSA_OK || n_heads < 0 || keep < 0) return 0;
   const int32_t rows = shape->batch * n_heads, n = shape->seq_len;
-  const size_t est = est_workspace_bytes(rows, n);
+  const size_t est = est_window_workspace_bytes(rows, n);
   const size_t tk = topk_workspace_bytes(rows, n, keep < n ? keep : n);
   return est > tk ? est : tk;  // the estimator's partials are dead when the top-k runs
 }
@@ -358,7 +358,7 @@ dsa_status dsa_kv_retention(const void* q, const void* k, const dsa_shape* shape
   a.hm = hm;
   a.wo = make_work_order(hm);
   a.v_scores = scores; a.s_scores = nullptr;
-  est_carve(a, workspace);
+  est_window_carve(a, workspace);
   hipError_t e = launch_window_column_scores(a, window, s);
   const int32_t kk = keep < n ? keep : n;
   if (e == hipSuccess && kk > 0) e = launch_topk_rows(scores, rows, n, kk, -1, kept, workspace, s);

@@ -124,7 +124,10 @@ size_t est_workspace_bytes(int32_t rows, int32_t seq_len);
 void est_carve(EstArgs& a, void* ws);
 hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s);
 // v over a window of `window` rows ending at the last row, in slices of 64
-// rows (the first slice writes v, the others add), no slash scores
+// rows, no slash scores; workspace from est_window_workspace_bytes, laid out
+// by est_window_carve
+size_t est_window_workspace_bytes(int32_t rows, int32_t seq_len);
+void est_window_carve(EstArgs& a, void* ws);
 hipError_t launch_window_column_scores(EstArgs a, int32_t window, hipStream_t s);
 
 // ---- sparse decode (decode.hip) ----

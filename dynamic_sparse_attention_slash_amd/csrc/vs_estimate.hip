@@ -30,6 +30,9 @@ namespace dsa {
 namespace {
 
 constexpr int SACC_MAX = EST_CHUNK + 63;  // diagonal offsets the largest chunk touches
+constexpr int WIN_WAVES = 4;              // window slices per work-group (column-score windows)
+
+__device__ __forceinline__ int32_t wave_lane() { return (int32_t)(threadIdx.x & 63); }
 
 struct Window {
   int32_t n, lq, start;
@@ -47,7 +50,7 @@ struct Tile<uint16_t, D> {
   static constexpr int DS = D / 32;
   u32x4 qop[4][DS];
   __device__ void load_q(const uint16_t* qs, const Window& w) {
-    const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+    const int32_t lane = wave_lane(), g = lane >> 4, l16 = lane & 15;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       int32_t r = min(16 * qb + l16, w.lq - 1);
@@ -60,14 +63,14 @@ struct Tile<uint16_t, D> {
   // end reads the last key, and its scores are never used)
   struct KReg { u32x4 v[DS]; };
   __device__ void load_k(const uint16_t* ks, int32_t j0, const Window& w, KReg& k) const {
-    const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+    const int32_t lane = wave_lane(), g = lane >> 4, l16 = lane & 15;
     const int32_t key = min(j0 + l16, w.n - 1);
     const u32x4* src = reinterpret_cast<const u32x4*>(ks + (size_t)key * D + (D / 4) * g);
 #pragma unroll
     for (int s = 0; s < DS; ++s) k.v[s] = src[s];
   }
   __device__ void scores_k(const KReg& k, int32_t j0, const Window& w, f32x4 (&out)[4]) const {
-    const int32_t l16 = threadIdx.x & 15;
+    const int32_t l16 = wave_lane() & 15;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -83,7 +86,7 @@ struct Tile<uint16_t, D> {
     if (!(j0 + 15 <= w.start && w.lq == 64)) mask(x, j0 + l16, w);
   }
   __device__ static void mask(f32x4 (&x)[4], int32_t key, const Window& w) {
-    const int32_t g = threadIdx.x >> 4;
+    const int32_t g = wave_lane() >> 4;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
@@ -100,7 +103,7 @@ struct Tile<float, D> {
   static constexpr int DK = D / 4;
   float qop[4][DK];
   __device__ void load_q(const float* qs, const Window& w) {
-    const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+    const int32_t lane = wave_lane(), g = lane >> 4, l16 = lane & 15;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       int32_t r = min(16 * qb + l16, w.lq - 1);
@@ -114,14 +117,14 @@ struct Tile<float, D> {
   }
   struct KReg { f32x4 v[DK / 4]; };
   __device__ void load_k(const float* ks, int32_t j0, const Window& w, KReg& k) const {
-    const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+    const int32_t lane = wave_lane(), g = lane >> 4, l16 = lane & 15;
     const int32_t key = min(j0 + l16, w.n - 1);
     const f32x4* src = reinterpret_cast<const f32x4*>(ks + (size_t)key * D + DK * g);
 #pragma unroll
     for (int s = 0; s < DK / 4; ++s) k.v[s] = src[s];
   }
   __device__ void scores_k(const KReg& k, int32_t j0, const Window& w, f32x4 (&out)[4]) const {
-    const int32_t l16 = threadIdx.x & 15;
+    const int32_t l16 = wave_lane() & 15;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -175,7 +178,7 @@ struct KRing {
   int32_t ld_off[INSTR];  // byte offset of this lane's 16 bytes within a step
   int32_t koff[DS];       // LDS offset of this lane's K operand of k-step s
   __device__ KRing(const uint16_t* ks, int32_t n) {
-    const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+    const int32_t lane = wave_lane(), g = lane >> 4, l16 = lane & 15;
     rs = __builtin_amdgcn_make_buffer_rsrc((void*)ks, (short)0, (uint32_t)n * ROW, 0x00020000);
 #pragma unroll
     for (int k = 0; k < INSTR; ++k) {
@@ -230,16 +233,32 @@ struct KRing {
   }
 };
 
-// bf16: three waves per SIMD, so the prefetched K costs no occupancy
-#define EST_KERNEL \
+// bf16: three waves per SIMD, so the prefetched K costs no occupancy.
+// MULTI: a work-group of up to WIN_WAVES waves, wave t taking window slice t
+// (64 rows from a.win_start + 64 t) over the same key chunk; each wave streams
+// K through its own ring, so the work-group's waves fetch each K line once
+// from memory and the other times from cache.
+#define EST_KERNEL_1 \
   __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1, sizeof(T) == 2 ? 3 : 8)))
+#define EST_WIN_KERNEL \
+  __global__ __launch_bounds__(64 * WIN_WAVES) __attribute__((amdgpu_waves_per_eu(3, 3)))
 
-template <typename T, int D>
-EST_KERNEL void est_stats_kernel(EstArgs a) {
+// The wave's window: the launch's (one wave) or its 64-row slice (MULTI)
+template <bool MULTI>
+__device__ __forceinline__ Window wave_window(const EstArgs& a, int32_t slice) {
+  if (!MULTI) return Window{a.seq_len, a.lq_eff(), a.win_start};
+  const int32_t start = a.win_start + 64 * slice;
+  return Window{a.seq_len, min(64, a.seq_len - start), start};
+}
+
+template <typename T, int D, bool MULTI>
+__device__ __forceinline__ void est_stats(const EstArgs& a) {
   const int32_t C = a.chunk, nchunks = (a.seq_len + C - 1) / C;
   int32_t row, chunk;
   work_item(a.hm, a.wo, nchunks, row, chunk);
-  const Window w{a.seq_len, a.lq_eff(), a.win_start};
+  const int32_t slice = MULTI ? __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6)) : 0;
+  const int32_t nsl = MULTI ? (int32_t)(blockDim.x >> 6) : 1;
+  const Window w = wave_window<MULTI>(a, slice);
   const T* qs = static_cast<const T*>(a.q) + a.hm.q_slab(row, a.seq_len, D);
   const T* ks = static_cast<const T*>(a.k) + a.hm.kv_slab(row, a.seq_len, D);
   Tile<T, D> tile;
@@ -255,16 +274,17 @@ EST_KERNEL void est_stats_kernel(EstArgs a) {
   auto step = [&](const f32x4 (&x)[4]) {
     // running (max, sum) with a deferred max: d = x * scale * log2(e) - m in
     // one FMA; the reference m is raised only when d exceeds 8 (then d = 0)
+    // one compare per step: the largest d against the margin (a v_max3 tree)
     f32x4 d[4];
-    bool need = false;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        d[qb][i] = __builtin_fmaf(x[qb][i], sc, -m[qb][i]);
-        need |= d[qb][i] > 8.f;
-      }
-    if (__any(need)) {
+      for (int i = 0; i < 4; ++i) d[qb][i] = __builtin_fmaf(x[qb][i], sc, -m[qb][i]);
+    const float dm = fmaxf(fmaxf(fmaxf(fmaxf(d[0][0], d[0][1]), fmaxf(d[0][2], d[0][3])),
+                                 fmaxf(fmaxf(d[1][0], d[1][1]), fmaxf(d[1][2], d[1][3]))),
+                           fmaxf(fmaxf(fmaxf(d[2][0], d[2][1]), fmaxf(d[2][2], d[2][3])),
+                                 fmaxf(fmaxf(d[3][0], d[3][1]), fmaxf(d[3][2], d[3][3]))));
+    if (__any(dm > 8.f)) {
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
@@ -282,8 +302,9 @@ EST_KERNEL void est_stats_kernel(EstArgs a) {
       for (int i = 0; i < 4; ++i) z[qb][i] += fast_exp2(d[qb][i]);
   };
   if constexpr (sizeof(T) == 2) {
-    __shared__ __align__(16) char kr0[KRing<D>::STEP], kr1[KRing<D>::STEP], kr2[KRing<D>::STEP];
-    char* const stage[KR_STAGES] = {kr0, kr1, kr2};
+    constexpr int NW = MULTI ? WIN_WAVES : 1;
+    __shared__ __align__(16) char kr0[NW][KRing<D>::STEP], kr1[NW][KRing<D>::STEP], kr2[NW][KRing<D>::STEP];
+    char* const stage[KR_STAGES] = {kr0[slice], kr1[slice], kr2[slice]};
     const KRing<D> ring(ks, a.seq_len);
     // every step issues its INSTR loads, past the chunk's end too (rows of
     // the next chunk, or zeros past the slab, into stages never read), so
@@ -330,9 +351,9 @@ EST_KERNEL void est_stats_kernel(EstArgs a) {
       m[qb][i] = mm;
       z[qb][i] = zz;
     }
-  const int32_t lane = threadIdx.x, g = lane >> 4;
+  const int32_t lane = wave_lane(), g = lane >> 4;
   if ((lane & 15) == 0) {
-    float* dst = a.part_stats + ((size_t)row * nchunks + chunk) * 64 * 2;
+    float* dst = a.part_stats + ((size_t)(row * nsl + slice) * nchunks + chunk) * 64 * 2;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
@@ -343,6 +364,11 @@ EST_KERNEL void est_stats_kernel(EstArgs a) {
       }
   }
 }
+
+template <typename T, int D>
+EST_KERNEL_1 void est_stats_kernel(EstArgs a) { est_stats<T, D, false>(a); }
+template <int D>
+EST_WIN_KERNEL void est_window_stats_kernel(EstArgs a) { est_stats<uint16_t, D, true>(a); }
 
 // F_r = m_r + log2(Z_r) over all chunks. One work-group per row: thread t
 // merges window row t % 64 over the chunks c = t / 64 (mod COMB_SPLIT) with a
@@ -389,25 +415,30 @@ __global__ __launch_bounds__(64 * COMB_SPLIT) void est_combine_kernel(EstArgs a,
 
 // Column sums of one chunk (no slash scores) with K through the LDS ring as
 // in the stats pass; the column-sum stores between the loads only make the
-// ring's fixed wait count conservative.
-template <int D>
+// ring's fixed wait count conservative. MULTI: each wave sums its window
+// slice into LDS, and after the chunk the work-group adds the slices in slice
+// order (a fixed order: the same bits on every run).
+template <int D, bool MULTI>
 __device__ void ring_column_sums(const EstArgs& a, const Tile<uint16_t, D>& tile, const uint16_t* ks,
                                  const Window& w, const float (&F)[4][4], float* vout, int32_t j_begin,
-                                 int32_t j_end) {
+                                 int32_t j_end, int32_t slice, int32_t nsl) {
   using T = uint16_t;
-  const int32_t g = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+  const int32_t g = wave_lane() >> 4, l16 = wave_lane() & 15;
   const float sc = a.scale_log2;
-  __shared__ __align__(16) char kr0[KRing<D>::STEP], kr1[KRing<D>::STEP], kr2[KRing<D>::STEP];
-  char* const stage[KR_STAGES] = {kr0, kr1, kr2};
+  constexpr int NW = MULTI ? WIN_WAVES : 1;
+  __shared__ __align__(16) char kr0[NW][KRing<D>::STEP], kr1[NW][KRing<D>::STEP], kr2[NW][KRing<D>::STEP];
+  __shared__ float cs[NW][MULTI ? EST_CHUNK : 1];
+  char* const stage[KR_STAGES] = {kr0[slice], kr1[slice], kr2[slice]};
   const KRing<D> ring(ks, a.seq_len);
-  // the window slices after the first add into v: each step's earlier v
-  // is loaded together with its K, so that waiting for it never drains the
-  // loads issued after it
+  // (one wave) the window slices after the first add into v: each step's
+  // earlier v is loaded together with its K, so that waiting for it never
+  // drains the loads issued after it
+  const bool add_here = !MULTI && a.add_v;
   float vprev[KR_STAGES];
   auto load_v = [&](int32_t j0) { return vout[min(j0 + l16, a.seq_len - 1)]; };
 #pragma unroll
   for (int u = 0; u < KR_STAGES - 1; ++u) {
-    vprev[u] = a.add_v ? load_v(j_begin + 16 * u) : 0.f;
+    vprev[u] = add_here ? load_v(j_begin + 16 * u) : 0.f;
     ring.issue(j_begin + 16 * u, stage[u]);
   }
   for (int32_t t0 = j_begin; t0 < j_end; t0 += 16 * KR_STAGES) {
@@ -415,7 +446,7 @@ __device__ void ring_column_sums(const EstArgs& a, const Tile<uint16_t, D>& tile
     for (int u = 0; u < KR_STAGES; ++u) {
       const int32_t j0 = t0 + 16 * u, jn = j0 + 16 * (KR_STAGES - 1);
       const int un = (u + KR_STAGES - 1) % KR_STAGES;  // constant after unrolling
-      vprev[un] = a.add_v ? load_v(jn) : 0.f;
+      vprev[un] = add_here ? load_v(jn) : 0.f;
       ring.issue(jn, stage[un]);
       if (j0 < j_end) {
         typename Tile<T, D>::KReg kc;
@@ -428,25 +459,42 @@ __device__ void ring_column_sums(const EstArgs& a, const Tile<uint16_t, D>& tile
 #pragma unroll
           for (int i = 0; i < 4; ++i) colsum += fast_exp2(__builtin_fmaf(x[qb][i], sc, -F[qb][i]));
         colsum = xor_sum(xor_sum(colsum, 16), 32);
-        if (g == 0 && j0 + l16 < a.seq_len) vout[j0 + l16] = a.add_v ? vprev[u] + colsum : colsum;
+        if (MULTI) {
+          if (g == 0) cs[slice][j0 - j_begin + l16] = colsum;
+        } else if (g == 0 && j0 + l16 < a.seq_len) {
+          vout[j0 + l16] = add_here ? vprev[u] + colsum : colsum;
+        }
       }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA into LDS outlives the loop
+  if constexpr (MULTI) {
+    __syncthreads();
+    for (int32_t jj = (int32_t)threadIdx.x; jj < j_end - j_begin; jj += 64 * nsl) {
+      float sum = 0.f;
+      for (int32_t t = 0; t < nsl; ++t) sum += cs[t][jj];
+      float* dst = vout + j_begin + jj;
+      *dst = a.add_v ? *dst + sum : sum;
+    }
+  }
 }
 
 // S: slash scores wanted (a.want_s); without them the probabilities never
 // go through LDS
-template <typename T, int D, bool S>
-EST_KERNEL void est_scores_kernel(EstArgs a) {
+template <typename T, int D, bool S, bool MULTI>
+__device__ __forceinline__ void est_scores(const EstArgs& a) {
+  static_assert(!(MULTI && S), "window slices: column scores only");
+  static_assert(!MULTI || sizeof(T) == 2, "window slices: bf16 only");
   constexpr int PS = 65;  // padded LDS row of the 64x64 probability tile
-  __shared__ float ptile[64 * PS];
-  __shared__ float sacc[SACC_MAX];
+  __shared__ float ptile[S ? 64 * PS : 1];
+  __shared__ float sacc[S ? SACC_MAX : 1];
   const int32_t C = a.chunk, nchunks = (a.seq_len + C - 1) / C;
   int32_t row, chunk;
   work_item(a.hm, a.wo, nchunks, row, chunk);
-  const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
-  const Window w{a.seq_len, a.lq_eff(), a.win_start};
+  const int32_t slice = MULTI ? __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6)) : 0;
+  const int32_t nsl = MULTI ? (int32_t)(blockDim.x >> 6) : 1;
+  const int32_t lane = wave_lane(), g = lane >> 4, l16 = lane & 15;
+  const Window w = wave_window<MULTI>(a, slice);
   const T* qs = static_cast<const T*>(a.q) + a.hm.q_slab(row, a.seq_len, D);
   const T* ks = static_cast<const T*>(a.k) + a.hm.kv_slab(row, a.seq_len, D);
   Tile<T, D> tile;
@@ -455,15 +503,16 @@ EST_KERNEL void est_scores_kernel(EstArgs a) {
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) F[qb][i] = a.row_stats[(size_t)row * 64 + 16 * qb + 4 * g + i];
+    for (int i = 0; i < 4; ++i) F[qb][i] = a.row_stats[(size_t)(row * nsl + slice) * 64 + 16 * qb + 4 * g + i];
   const int32_t SACC = C + 63;  // diagonal offsets this chunk touches
-  for (int e = lane; e < SACC; e += 64) sacc[e] = 0.f;
+  if (S)
+    for (int e = lane; e < SACC; e += 64) sacc[e] = 0.f;
 
   float* vout = a.v_scores + (size_t)row * a.seq_len;
   const float sc = a.scale_log2;
   const int32_t j_begin = chunk * C, j_end = min(a.seq_len, j_begin + C);
   if constexpr (sizeof(T) == 2 && !S) {
-    ring_column_sums<D>(a, tile, ks, w, F, vout, j_begin, j_end);
+    ring_column_sums<D, MULTI>(a, tile, ks, w, F, vout, j_begin, j_end, slice, nsl);
     return;
   }
   KStream<T, D> kst(tile, ks, j_begin, w);
@@ -517,6 +566,11 @@ EST_KERNEL void est_scores_kernel(EstArgs a) {
   float* dst = a.s_part + ((size_t)row * nchunks + chunk) * SACC;
   for (int e = lane; e < SACC; e += 64) dst[e] = sacc[e];
 }
+
+template <typename T, int D, bool S>
+EST_KERNEL_1 void est_scores_kernel(EstArgs a) { est_scores<T, D, S, false>(a); }
+template <int D>
+EST_WIN_KERNEL void est_window_scores_kernel(EstArgs a) { est_scores<uint16_t, D, false, true>(a); }
 
 // s[d] = sum over chunks c covering d (ascending c) of s_part[c][e_c(d)],
 // e_c(d) = d - (start - (c*C + C - 1)), start = the window's first row.
@@ -576,16 +630,13 @@ hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s) {
   if (a.rows == 0 || a.seq_len == 0) return hipSuccess;
   const int32_t nch = (a.seq_len + a.chunk - 1) / a.chunk;
   const dim3 grid((unsigned)((long long)nch * a.rows));
-  auto st = a.dtype == BF16 ? (a.head_dim == 64 ? est_stats_kernel<uint16_t, 64> : est_stats_kernel<uint16_t, 128>)
-                            : (a.head_dim == 64 ? est_stats_kernel<float, 64> : est_stats_kernel<float, 128>);
-  auto sc = a.want_s ? (a.dtype == BF16 ? (a.head_dim == 64 ? est_scores_kernel<uint16_t, 64, true>
-                                                             : est_scores_kernel<uint16_t, 128, true>)
-                                         : (a.head_dim == 64 ? est_scores_kernel<float, 64, true>
-                                                             : est_scores_kernel<float, 128, true>))
-                     : (a.dtype == BF16 ? (a.head_dim == 64 ? est_scores_kernel<uint16_t, 64, false>
-                                                             : est_scores_kernel<uint16_t, 128, false>)
-                                         : (a.head_dim == 64 ? est_scores_kernel<float, 64, false>
-                                                             : est_scores_kernel<float, 128, false>));
+  const bool bf = a.dtype == BF16, d64 = a.head_dim == 64;
+  auto st = bf ? (d64 ? est_stats_kernel<uint16_t, 64> : est_stats_kernel<uint16_t, 128>)
+               : (d64 ? est_stats_kernel<float, 64> : est_stats_kernel<float, 128>);
+  auto sc = a.want_s ? (bf ? (d64 ? est_scores_kernel<uint16_t, 64, true> : est_scores_kernel<uint16_t, 128, true>)
+                           : (d64 ? est_scores_kernel<float, 64, true> : est_scores_kernel<float, 128, true>))
+                     : (bf ? (d64 ? est_scores_kernel<uint16_t, 64, false> : est_scores_kernel<uint16_t, 128, false>)
+                           : (d64 ? est_scores_kernel<float, 64, false> : est_scores_kernel<float, 128, false>));
   hipLaunchKernelGGL(st, grid, dim3(64), 0, s, a);
   hipLaunchKernelGGL(est_combine_kernel, dim3(a.rows), dim3(64 * COMB_SPLIT), 0, s, a, nch);
   hipLaunchKernelGGL(sc, grid, dim3(64), 0, s, a);
@@ -594,16 +645,58 @@ hipError_t launch_vs_estimate(const EstArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+size_t est_window_workspace_bytes(int32_t rows, int32_t seq_len) {
+  if (rows == 0 || seq_len == 0) return 0;  // nothing is launched
+  const int32_t C = est_chunk_keys(seq_len);
+  const size_t nch = (size_t)(seq_len + C - 1) / C;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  // per (row, window slice of a launch): chunk partials and row statistics
+  return al((size_t)rows * WIN_WAVES * nch * 128 * sizeof(float)) +
+         al((size_t)rows * WIN_WAVES * 64 * sizeof(float));
+}
+
+void est_window_carve(EstArgs& a, void* ws) {
+  a.chunk = est_chunk_keys(a.seq_len);
+  const size_t nch = (size_t)(a.seq_len + a.chunk - 1) / a.chunk;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const uintptr_t p = reinterpret_cast<uintptr_t>(ws);
+  a.part_stats = reinterpret_cast<float*>(p);
+  a.row_stats = reinterpret_cast<float*>(p + al((size_t)a.rows * WIN_WAVES * nch * 128 * sizeof(float)));
+  a.s_part = nullptr;
+}
+
 hipError_t launch_window_column_scores(EstArgs a, int32_t window, hipStream_t s) {
   const int32_t n = a.seq_len;
   window = window < n ? window : n;
   if (a.rows == 0 || n == 0 || window <= 0) return hipSuccess;
   a.want_s = 0;
-  for (int32_t r0 = n - window; r0 < n; r0 += 64) {
-    a.win_start = r0;
-    a.last_q = n - r0 < 64 ? n - r0 : 64;
-    a.add_v = r0 > n - window;
-    const hipError_t e = launch_vs_estimate(a, s);
+  if (a.dtype != BF16) {
+    // fp32: one launch per 64-row slice (the first writes v, the others add)
+    for (int32_t r0 = n - window; r0 < n; r0 += 64) {
+      a.win_start = r0;
+      a.last_q = n - r0 < 64 ? n - r0 : 64;
+      a.add_v = r0 > n - window;
+      const hipError_t e = launch_vs_estimate(a, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  // bf16: up to WIN_WAVES slices per launch, one wave each
+  const int32_t nch = (n + a.chunk - 1) / a.chunk;
+  const dim3 grid((unsigned)((long long)nch * a.rows));
+  const bool d64 = a.head_dim == 64;
+  auto st = d64 ? est_window_stats_kernel<64> : est_window_stats_kernel<128>;
+  auto sc = d64 ? est_window_scores_kernel<64> : est_window_scores_kernel<128>;
+  const int32_t nslices = (window + 63) / 64;
+  for (int32_t s0 = 0; s0 < nslices; s0 += WIN_WAVES) {
+    const int32_t nsl = nslices - s0 < WIN_WAVES ? nslices - s0 : WIN_WAVES;
+    a.win_start = n - window + 64 * s0;
+    a.last_q = 64;
+    a.add_v = s0 > 0;
+    hipLaunchKernelGGL(st, grid, dim3(64 * nsl), 0, s, a);
+    hipLaunchKernelGGL(est_combine_kernel, dim3(a.rows * nsl), dim3(64 * COMB_SPLIT), 0, s, a, nch);
+    hipLaunchKernelGGL(sc, grid, dim3(64 * nsl), 0, s, a);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
