@@ -15,6 +15,10 @@ by eye against the pages it follows. Sources, cited by page title and section:
   blog), §2 "Modificación de Atención": softmax statistics (rowmax, l) reused to
   score keys over a window of the last queries, with the q start/end
   restriction.
+* [IHiP] InfiniteHiP summary (www.dtcms.com), section "模块化分层令牌剪枝算法"
+  (modular hierarchical token pruning): fixed-length chunks, the
+  highest-scoring token of each chunk, only the best chunks go on to the next
+  stage, stacked stages refine a block-sparse mask per query block.
 
 Readings taken where the pages are silent or garbled:
 
@@ -63,6 +67,23 @@ R9  KV retention [Novita §2, the PyramidKV score; the formula itself is lost
     per head the ``keep`` highest-scoring keys are kept (R3, no forced entry).
     A window longer than the prompt is clamped to it. Not taken: also keeping
     the window's own tokens whatever their score (the page does not say so).
+R11 Hierarchical chunk pruning [IHiP, modular hierarchical token pruning]: a
+    query vector sees the keys j < limit. A token's score is its logit
+    scale * q . k_j. Stage s has a chunk length c_s and a keep count k_s; the
+    lengths decrease and each divides the one before. Stage 1's candidates are
+    the chunks [x c_1, (x+1) c_1) that hold a visible key; stage s > 1 splits
+    each chunk kept by stage s-1 into chunks of c_s and takes those holding a
+    visible key. A candidate's score is the largest score of its visible
+    tokens (the chunk's highest-scoring token, found exactly); the k_s best
+    candidates are kept (R3), with the chunk holding key limit - 1 forced, so
+    the query's own neighbourhood is never pruned. The result is the last
+    stage's kept chunk ids, ascending. Decode: the query is the new row and
+    limit = n; the row then attends over the keys of the kept chunks (R10).
+    Prefill (an alternative block-sparse estimator): the query of block a is
+    its mean-pooled row (R6) and limit = min(n, 64 (a + 1)); with a last chunk
+    length of 64 the kept chunks are key blocks, attended as in R6. Not taken:
+    an approximate search for the highest-scoring token (the page says that it
+    is found in parallel and efficiently, not how).
 """
 from __future__ import annotations
 
@@ -327,6 +348,69 @@ def streaming_blocks(a: int, init_blocks: int, local_blocks: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# multi-stage hierarchical chunk pruning  [IHiP modular hierarchical token
+# pruning; R11]
+# ----------------------------------------------------------------------------
+def token_scores(q_vec, k, limit: int, scale: float) -> np.ndarray:
+    """scale * q . k_j of the visible keys j < limit, float64 [limit]."""
+    return scale * (f64(k)[:limit] @ f64(q_vec))
+
+
+def hier_prune(q_vec, k, limit: int, stages: Sequence[Tuple[int, int]], scale: float,
+               fine_max=None) -> np.ndarray:
+    """Chunk ids (of the last stage's length) kept by the stages, ascending.
+
+    ``stages``: (chunk length, keep count) per stage, outermost first.
+    ``fine_max`` (optional float32 [ceil(limit / 64)]): the largest token score
+    of every 64-key block, as another implementation computed it; a chunk's
+    score is then the largest of its blocks' values, which is the same
+    quantity, so the selection steps can be run on that implementation's
+    scores. Otherwise the token scores are computed here (float64).
+    """
+    if fine_max is None:
+        s = token_scores(q_vec, k, limit, scale)
+
+        def chunk_score(x, c):
+            return s[x * c: min(limit, (x + 1) * c)].max()
+    else:
+        fm = np.asarray(fine_max, dtype=np.float32)
+
+        def chunk_score(x, c):
+            return fm[x * c // BLOCK: (min(limit, (x + 1) * c) + BLOCK - 1) // BLOCK].max()
+
+    kept = None
+    prev_c = None
+    for c, keep in stages:
+        if kept is None:   # stage 1: every chunk holding a visible key
+            cand = list(range((limit + c - 1) // c))
+        else:              # the sub-chunks of the chunks the last stage kept
+            r = prev_c // c
+            cand = [y for x in kept for y in range(x * r, (x + 1) * r) if y * c < limit]
+        scores = np.array([chunk_score(x, c) for x in cand])
+        forced = cand.index((limit - 1) // c)
+        pick = topk_indices(scores, keep, forced=(forced,))
+        kept = [cand[i] for i in pick]
+        prev_c = c
+    return np.asarray(kept, dtype=np.int64)
+
+
+def chunks_to_keys(chunks: Sequence[int], c: int, limit: int) -> np.ndarray:
+    """Key positions (< limit) of the chunks of length c, ascending."""
+    parts = [np.arange(x * c, min(limit, (x + 1) * c)) for x in sorted(chunks)]
+    return np.concatenate(parts).astype(np.int64) if parts else np.zeros(0, np.int64)
+
+
+def hier_decode(q_row, k, v, stages, scale: float | None = None, fine_max=None) -> dict:
+    """Decode row over the keys the pruning keeps (R11, R10)."""
+    k, v = f64(k), f64(v)
+    n, D = k.shape
+    scale = default_scale(D) if scale is None else scale
+    chunks = hier_prune(q_row, k, n, stages, scale, fine_max)
+    keys = chunks_to_keys(chunks, stages[-1][0], n)
+    return dict(chunks=chunks, keys=keys, out=decode_attention(q_row, k, v, keys, scale))
+
+
+# ----------------------------------------------------------------------------
 # per-head pipelines (one query head; q [n, D], k/v its kv head [n, D])
 # ----------------------------------------------------------------------------
 def _attend_blocks(q, k, v, scale, block_keys, blocks=None) -> Dict[int, np.ndarray]:
@@ -377,6 +461,22 @@ def bs_head(q, k, v, topk: int, scale: float | None = None, blocks=None,
     sel = block_select(L32, topk)
     out = _attend_blocks(q, k, v, scale, lambda a: blocks_to_keys(sel[a], n), blocks)
     return dict(qp=qp, kp=kp, logits=L32, sel=sel, out=out)
+
+
+def hier_head(q, k, v, stages, scale: float | None = None, blocks=None, fine_max=None) -> dict:
+    """Prefill head with the hierarchical pruning as its block estimator
+    (R11): block a's query is its mean-pooled row, its keys those before its
+    end; the last stage's chunk length must be 64 (key blocks). ``fine_max``
+    (optional, float32 [nb][nb]) as in hier_prune, row a per query block."""
+    n, D = q.shape
+    assert stages[-1][0] == BLOCK
+    scale = default_scale(D) if scale is None else scale
+    qp = mean_pool(q)
+    sel = [hier_prune(qp[a], k, min(n, (a + 1) * BLOCK), stages, scale,
+                      None if fine_max is None else fine_max[a])
+           for a in range(num_blocks(n))]
+    out = _attend_blocks(q, k, v, scale, lambda a: blocks_to_keys(sel[a], n), blocks)
+    return dict(qp=qp, sel=sel, out=out)
 
 
 def streaming_head(q, k, v, init_blocks: int, local_blocks: int,

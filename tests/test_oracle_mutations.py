@@ -48,6 +48,16 @@ MUTATIONS = [
     ("decode row placed before the last key", "np.array([n]), keys, k, v, scale)",
      "np.array([n - 2]), keys, k, v, scale)"),
     ("default scale 1/D", "return 1.0 / math.sqrt(head_dim)", "return 1.0 / head_dim"),
+    ("pruning chunk score is the mean", "return s[x * c: min(limit, (x + 1) * c)].max()",
+     "return s[x * c: min(limit, (x + 1) * c)].mean()"),
+    ("pruning forced chunk dropped", "pick = topk_indices(scores, keep, forced=(forced,))",
+     "pick = topk_indices(scores, keep)"),
+    ("pruning later stages see every chunk",
+     "cand = [y for x in kept for y in range(x * r, (x + 1) * r) if y * c < limit]",
+     "cand = [y for y in range((limit + c - 1) // c)]"),
+    ("pruning stage limit taken from the whole cache", "cand = list(range((limit + c - 1) // c))",
+     "cand = list(range((len(k) + c - 1) // c))"),
+    ("pruning forces the first chunk", "forced = cand.index((limit - 1) // c)", "forced = 0"),
 ]
 
 

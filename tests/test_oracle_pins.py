@@ -469,3 +469,146 @@ def test_vs_structure_selects_sink():
     res = O.vs_head(x.q[0, 0], x.k[0, 0], x.v[0, 0], 64, 64, blocks=[])
     assert 0 in res["V"].tolist() and 0 in res["S"].tolist()
     assert abs(float(res["v"].astype(np.float64).sum()) - 64) < 1e-3
+
+
+# ---------------------------------------------------------------------------
+# hierarchical chunk pruning (R11)
+# ---------------------------------------------------------------------------
+def bf_hier(q, k, limit, stages, scale):
+    """The stages written out with explicit loops: token scores, chunk maxima
+    by scanning tokens, ranks by pairwise comparison (bf_topk)."""
+    s = [scale * sum(a * b for a, b in zip(q, k[j])) for j in range(limit)]
+    kept, prev = None, None
+    for c, keep in stages:
+        if kept is None:
+            cand = [x for x in range(limit) if x * c < limit]
+        else:
+            cand = []
+            for x in kept:
+                for y in range(x * (prev // c), (x + 1) * (prev // c)):
+                    if y * c < limit:
+                        cand.append(y)
+        scores = []
+        for x in cand:
+            best = -math.inf
+            for j in range(x * c, min(limit, (x + 1) * c)):
+                best = max(best, s[j])
+            scores.append(best)
+        forced = [i for i, x in enumerate(cand) if x * c <= limit - 1 < (x + 1) * c]
+        kept = [cand[i] for i in bf_topk(scores, keep, forced)]
+        prev = c
+    return sorted(kept)
+
+
+def test_hier_worked_examples():
+    """Hand-worked: 512 keys, scores are the keys' only entry (q = 1). Token 10
+    scores 5, token 300 scores 3, all others 0; key 511 lies in the forced
+    chunks. Keeping one 256-chunk keeps only the forced one (tokens 256..511),
+    whose best 64-chunk besides the forced one (7) is chunk 4 (token 300).
+    Keeping two 256-chunks lets chunk 0 (token 10) win the second slot."""
+    k = np.zeros((512, 1))
+    k[10, 0], k[300, 0] = 5.0, 3.0
+    q = np.ones(1)
+    assert O.hier_prune(q, k, 512, [(256, 1), (64, 2)], 1.0).tolist() == [4, 7]
+    assert O.hier_prune(q, k, 512, [(256, 2), (64, 2)], 1.0).tolist() == [0, 7]
+    # a visible limit cuts the candidates: keys below 300 only, key 299 forced
+    assert O.hier_prune(q, k, 300, [(256, 1), (64, 1)], 1.0).tolist() == [4]
+    assert O.hier_prune(q, k, 300, [(128, 2), (64, 2)], 1.0).tolist() == [0, 4]
+    # the chunk score is the chunk's largest token, not its mean: one token of
+    # 2.0 beats sixty-four tokens of 1.5
+    k2 = np.zeros((256, 1))
+    k2[0:64, 0] = 1.5
+    k2[100, 0] = 2.0
+    assert O.hier_prune(q, k2, 256, [(64, 2)], 1.0).tolist() == [1, 3]
+
+
+@pytest.mark.parametrize("limit,stages", [(300, [(64, 3)]), (1000, [(256, 2), (64, 3)]),
+                                          (1000, [(512, 1), (128, 3), (64, 2)]), (64, [(128, 1), (64, 1)]),
+                                          (777, [(256, 9), (64, 50)]), (450, [(192, 2), (64, 4)])])
+def test_hier_bruteforce(limit, stages):
+    r = np.random.default_rng(limit)
+    D = 4
+    k = r.standard_normal((limit + 37, D))
+    q = r.standard_normal(D)
+    k[r.integers(0, limit, 5)] *= 3.0      # a few dominant tokens
+    assert O.hier_prune(q, k, limit, stages, 0.5).tolist() == bf_hier(q, k, limit, stages, 0.5)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_hier_equals_flat_selection_when_outer_keeps_enough(seed):
+    """Closed form: with exact chunk maxima, two stages whose first keeps at
+    least as many chunks as the second select exactly the flat top-k of the
+    fine chunks (every chunk ranked above a selected fine chunk's parent holds
+    a fine chunk ranked above it). A mean instead of the max, or a dropped
+    forced chunk, breaks this."""
+    r = np.random.default_rng(seed)
+    limit = int(r.integers(200, 3000))
+    k = r.standard_normal((limit, 8))
+    q = r.standard_normal(8)
+    c1 = int(r.choice([128, 256, 512]))
+    k2 = int(r.integers(1, 12))
+    k1 = k2 + int(r.integers(0, 4))
+    hier = O.hier_prune(q, k, limit, [(c1, k1), (64, k2)], 0.3)
+    flat = O.hier_prune(q, k, limit, [(64, k2)], 0.3)
+    assert hier.tolist() == flat.tolist()
+    # and the flat selection is the top-k of the 64-key maxima (R3)
+    s = 0.3 * (k @ q)
+    m = np.array([s[x * 64: min(limit, x * 64 + 64)].max() for x in range((limit + 63) // 64)])
+    assert flat.tolist() == O.topk_indices(m, k2, forced=((limit - 1) // 64,)).tolist()
+
+
+def test_hier_properties():
+    """Keep-all keeps every visible chunk; the forced chunk survives even when
+    it scores lowest; each kept chunk lies inside a chunk every earlier stage
+    kept; a planted dominant token's chunks survive every stage."""
+    r = np.random.default_rng(3)
+    n = 4096
+    k = r.standard_normal((n, 16))
+    q = r.standard_normal(16)
+    assert O.hier_prune(q, k, n, [(1024, 4), (64, 64)], 1.0).tolist() == list(range(64))
+    k_low = k.copy()
+    k_low[n - 64:] = -10 * q / np.linalg.norm(q)      # the forced chunk scores lowest
+    res = O.hier_prune(q, k_low, n, [(1024, 1), (256, 1), (64, 1)], 1.0)
+    assert res.tolist() == [63]
+    k_pl = k.copy()
+    k_pl[1234] = 20 * q / np.linalg.norm(q)
+    st = [(1024, 2), (256, 2), (64, 2)]
+    res = O.hier_prune(q, k_pl, n, st, 1.0)
+    assert 1234 // 64 in res.tolist() and 63 in res.tolist()
+    for c, keep in [(1024, 2), (256, 2)]:
+        outer = set(O.hier_prune(q, k_pl, n, st[: [s[0] for s in st].index(c) + 1], 1.0).tolist())
+        assert all(x * 64 // c in outer for x in res.tolist())
+
+
+def test_hier_fine_max_route_agrees():
+    """The selection run on 64-key block maxima (rounded to float32) equals
+    the one on float64 token scores when no two candidates are within float32
+    rounding of each other (random Gaussian data)."""
+    r = np.random.default_rng(11)
+    n = 3000
+    k = r.standard_normal((n, 8))
+    q = r.standard_normal(8)
+    s = 0.25 * (k @ q)
+    fm = np.array([s[x * 64: min(n, x * 64 + 64)].max() for x in range((n + 63) // 64)], np.float32)
+    st = [(512, 3), (128, 4), (64, 5)]
+    assert O.hier_prune(q, k, n, st, 0.25).tolist() == O.hier_prune(q, k, n, st, 0.25, fine_max=fm).tolist()
+
+
+def test_hier_decode_and_head():
+    """Decode over the kept keys is R10's decode over exactly those keys, and
+    the prefill head attends each block over its kept key blocks (brute-force
+    attention with the element mask)."""
+    q, k, v = rnd(300, 8, 4)
+    res = O.hier_decode(q[5], k, v, [(128, 2), (64, 2)], 0.4)
+    keys = O.chunks_to_keys(res["chunks"], 64, 300)
+    assert set(keys.tolist()) == {j for x in res["chunks"].tolist() for j in range(x * 64, min(300, x * 64 + 64))}
+    np.testing.assert_allclose(res["out"], O.decode_attention(q[5], k, v, keys, 0.4), rtol=0, atol=1e-12)
+    st = [(128, 1), (64, 2)]
+    h = O.hier_head(q, k, v, st, 0.4)
+    qp = O.mean_pool(q)
+    for a, sel in enumerate(h["sel"]):
+        assert sel.tolist() == bf_hier(qp[a], k, min(300, 64 * (a + 1)), st, 0.4)
+    sets = {a: set(h["sel"][a].tolist()) for a in range(len(h["sel"]))}
+    bf = bf_attention(q.tolist(), k.tolist(), v.tolist(), 0.4,
+                      lambda i, j: j <= i and (j // 64) in sets[i // 64])
+    np.testing.assert_allclose(O.assemble(h["out"], 300, 8), bf, rtol=1e-10, atol=1e-12)
