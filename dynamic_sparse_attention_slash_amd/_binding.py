@@ -38,6 +38,14 @@ class Shape(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+PRUNE_MAX_STAGES = 4
+
+
+class PruneStages(ctypes.Structure):
+    _fields_ = [("n_stages", ctypes.c_int32), ("chunk", ctypes.c_int32 * PRUNE_MAX_STAGES),
+                ("keep", ctypes.c_int32 * PRUNE_MAX_STAGES)]
+
+
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _ip = ctypes.POINTER(ctypes.c_int32)
 _SIGS = {
@@ -65,6 +73,13 @@ _SIGS = {
     "dsa_mixed_sparse_attention": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _ip, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp], _i32),
     "dsa_mixed_sparse_attention_workspace_bytes": ([ctypes.POINTER(Shape), _ip, _i32, _i32, _i32], _sz),
     "dsa_sparse_attention_mixed": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), _f32, _ip, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp], _i32),
+    "dsa_hier_prune": ([_vp, _i32, _i32, _i32, _vp, ctypes.POINTER(Shape), ctypes.POINTER(PruneStages), _f32, _ip, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "dsa_hier_prune_workspace_bytes": ([ctypes.POINTER(Shape), _i32, _i32], _sz),
+    "dsa_chunks_to_keys": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
+    "dsa_hier_sparse_decode": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), ctypes.POINTER(PruneStages), _f32, _ip, _i32, _vp, _sz, _vp], _i32),
+    "dsa_hier_sparse_decode_workspace_bytes": ([ctypes.POINTER(Shape), ctypes.POINTER(PruneStages), _i32], _sz),
+    "dsa_hier_block_sparse_attention": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Shape), ctypes.POINTER(PruneStages), _f32, _ip, _i32, _vp, _sz, _vp], _i32),
+    "dsa_hier_block_sparse_workspace_bytes": ([ctypes.POINTER(Shape), ctypes.POINTER(PruneStages), _i32], _sz),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -516,4 +531,98 @@ def sparse_attention_mixed(q, k, v, patterns: Sequence[Optional[str]], *, vs_ind
     _call("dsa_sparse_attention_mixed", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
           ctypes.byref(sh), _scale(scale), pa, iv, niv, max_iv, cols, ncols, max_cols, sel, nsel,
           max_sel, init_blocks, local_blocks, _stream(q))
+    return o
+
+
+# ----------------------------------------------------------------------------
+# hierarchical chunk pruning
+# ----------------------------------------------------------------------------
+def _stages(stages: Sequence[Tuple[int, int]]) -> PruneStages:
+    """[(chunk length, keep count), ...] outermost first -> the C struct (the
+    library checks the values)."""
+    st = PruneStages()
+    st.n_stages = len(stages)
+    if not 1 <= len(stages) <= PRUNE_MAX_STAGES:
+        raise ValueError(f"1 to {PRUNE_MAX_STAGES} stages")
+    for i, (c, k) in enumerate(stages):
+        st.chunk[i], st.keep[i] = int(c), int(k)
+    return st
+
+
+def hier_prune(qu: torch.Tensor, k: torch.Tensor, stages: Sequence[Tuple[int, int]], *, q_heads: int,
+               heads: Optional[Sequence[int]] = None, unit_rows: int = 0, scale: Optional[float] = None,
+               return_block_max: bool = False):
+    """Pruning stages for query vectors qu [batch * n_heads, units, head_dim]
+    (bf16 or fp32) over the cache k [batch, kv_heads, seq_len, head_dim]:
+    (sel [rows, units, keep_last], n_sel [rows, units][, block_max
+    [rows, units, ceil(seq_len / 64)]]). Entries past the counts (and blocks a
+    unit does not see) are left unwritten."""
+    B, Hkv, n, D = k.shape
+    rows, units, Dq = qu.shape
+    ha, hn = _heads(heads)
+    nh = q_heads if heads is None else hn
+    if rows != B * nh or Dq != D:
+        raise ValueError(f"qu must be [batch * n_heads, units, head_dim] = [{B * nh}, *, {D}]")
+    sh = Shape(B, q_heads, Hkv, n, D, _dtype_code(k))
+    st = _stages(stages)
+    ks = stages[-1][1]
+    sel = torch.empty((rows, units, ks), dtype=torch.int32, device=k.device)
+    n_sel = torch.empty((rows, units), dtype=torch.int32, device=k.device)
+    bm, ws = None, None
+    if return_block_max:
+        bm = torch.full((rows, units, (n + BLOCK - 1) // BLOCK), float("nan"), dtype=torch.float32,
+                        device=k.device)
+    else:
+        ws = _workspace(load().dsa_hier_prune_workspace_bytes(ctypes.byref(sh), units, nh), k.device)
+    _call("dsa_hier_prune", _dev(qu, "qu"), _dtype_code(qu), units, unit_rows, _dev(k, "k"), ctypes.byref(sh),
+          ctypes.byref(st), _scale(scale), ha, hn, None if bm is None else bm.data_ptr(), sel.data_ptr(),
+          n_sel.data_ptr(), None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), _stream(k))
+    return (sel, n_sel, bm) if return_block_max else (sel, n_sel)
+
+
+def chunks_to_keys(sel: torch.Tensor, n_sel: torch.Tensor, chunk: int, seq_len: int):
+    """Key lists of kept chunks: (keys [rows, max_sel * chunk], n_keys [rows]); sel [rows, max_sel]."""
+    rows, max_sel = sel.shape
+    keys = torch.empty((rows, max_sel * chunk), dtype=torch.int32, device=sel.device)
+    n_keys = torch.empty((rows,), dtype=torch.int32, device=sel.device)
+    _call("dsa_chunks_to_keys", _dev(sel, "sel", torch.int32), _dev(n_sel, "n_sel", torch.int32), rows,
+          max_sel, chunk, seq_len, keys.data_ptr(), n_keys.data_ptr(), _stream(sel))
+    return keys, n_keys
+
+
+def hier_sparse_decode(q, k, v, stages: Sequence[Tuple[int, int]], *, scale: Optional[float] = None,
+                       heads: Optional[Sequence[int]] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode rows (q [batch, q_heads, head_dim]) over the keys the pruning
+    stages keep for them; k, v the cache [batch, kv_heads, seq_len, head_dim]."""
+    if k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("k, v must be [batch, kv_heads, seq_len, head_dim]")
+    B, Hkv, n, D = k.shape
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
+        raise ValueError("q must be [batch, q_heads, head_dim]")
+    sh = Shape(B, q.shape[1], Hkv, n, D, _dtype_code(q))
+    st = _stages(stages)
+    ha, hn = _heads(heads)
+    nh = q.shape[1] if heads is None else hn
+    o = torch.zeros_like(q) if out is None else out
+    ws = _workspace(load().dsa_hier_sparse_decode_workspace_bytes(ctypes.byref(sh), ctypes.byref(st), nh),
+                    q.device)
+    _call("dsa_hier_sparse_decode", _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(o, "out"),
+          ctypes.byref(sh), ctypes.byref(st), _scale(scale), ha, hn, ws.data_ptr(), ws.numel(), _stream(q))
+    return o
+
+
+def hier_block_sparse_attention(q, k, v, stages: Sequence[Tuple[int, int]], *, scale: Optional[float] = None,
+                                heads: Optional[Sequence[int]] = None,
+                                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Prefill heads whose key blocks the pruning stages choose (last chunk
+    length 64), q, k, v as in block_sparse_attention."""
+    sh = _shape_qkv(q, k, v)
+    st = _stages(stages)
+    o = _out_like(q, out)
+    ha, hn = _heads(heads)
+    nh = sh.q_heads if heads is None else hn
+    ws = _workspace(load().dsa_hier_block_sparse_workspace_bytes(ctypes.byref(sh), ctypes.byref(st), nh),
+                    q.device)
+    _call("dsa_hier_block_sparse_attention", _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
+          ctypes.byref(sh), ctypes.byref(st), _scale(scale), ha, hn, ws.data_ptr(), ws.numel(), _stream(q))
     return o

@@ -698,3 +698,191 @@ dsa_status dsa_sparse_attention_mixed(const void* q, const void* k, const void* 
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ hierarchical chunk pruning
+namespace {
+// Stage list checks: 1..4 stages, lengths multiples of 64, strictly
+// decreasing, each dividing the one before, keep >= 1; each stage's candidate
+// count (stage 1: the chunks of n keys; later: keep x sub-chunks per chunk)
+// at most DSA_PRUNE_MAX_CANDIDATES.
+dsa_status check_stages(const dsa_prune_stages* st, int32_t n) {
+  if (!st || st->n_stages < 1 || st->n_stages > DSA_PRUNE_MAX_STAGES) return DSA_ERR_INVALID_ARG;
+  for (int32_t s = 0; s < st->n_stages; ++s) {
+    const int32_t c = st->chunk[s];
+    if (c < 64 || c % 64 != 0 || st->keep[s] < 1) return DSA_ERR_INVALID_ARG;
+    if (s > 0 && (c >= st->chunk[s - 1] || st->chunk[s - 1] % c != 0)) return DSA_ERR_INVALID_ARG;
+  }
+  if (((int64_t)n + st->chunk[0] - 1) / st->chunk[0] > DSA_PRUNE_MAX_CANDIDATES) return DSA_ERR_UNSUPPORTED;
+  for (int32_t s = 1; s < st->n_stages; ++s)
+    if ((int64_t)st->keep[s - 1] * (st->chunk[s - 1] / st->chunk[s]) > DSA_PRUNE_MAX_CANDIDATES)
+      return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+PruneArgs prune_args(const void* qu, int32_t qu_dtype, int32_t qu_full, int32_t units, int32_t unit_rows,
+                     const void* k, const dsa_shape* shape, const dsa_prune_stages* st, float scale,
+                     const HeadMap& hm, float* fine, int32_t* sel, int32_t* n_sel) {
+  PruneArgs a;
+  a.qu = qu; a.qu_dtype = qu_dtype; a.qu_full = qu_full;
+  a.k = k; a.k_dtype = shape->dtype;
+  a.n = shape->seq_len; a.head_dim = shape->head_dim; a.units = units; a.rows = shape->batch * hm.n;
+  a.unit_rows = unit_rows;
+  a.scale = eff_scale(scale, shape->head_dim);
+  a.hm = hm;
+  a.wo = make_work_order(hm);
+  a.fine = fine;
+  a.nbf = nblocks(shape->seq_len);
+  a.ntiles = 0;
+  a.n_stages = st->n_stages;
+  for (int32_t s = 0; s < PR_MAX_STAGES; ++s) {
+    a.chunk_blocks[s] = s < st->n_stages ? st->chunk[s] / 64 : 1;
+    a.keep[s] = s < st->n_stages ? st->keep[s] : 1;
+  }
+  a.sel = sel; a.n_sel = n_sel;
+  a.max_sel = st->keep[st->n_stages - 1];
+  return a;
+}
+
+// workspace of the composite pruning calls: block maxima, chunk lists and
+// (decode) key lists and split partials, or (prefill) pooled queries
+struct HierWork { float* fine; int32_t* sel; int32_t* n_sel; int32_t* keys; int32_t* n_keys; float* part; float* qp; };
+size_t hier_layout(const dsa_shape* s, int32_t rows, const dsa_prune_stages* st, bool decode, void* base,
+                   HierWork* w) {
+  const int32_t n = s->seq_len, nb = nblocks(n), units = decode ? 1 : nb;
+  const int32_t ks = st->keep[st->n_stages - 1], c = st->chunk[st->n_stages - 1];
+  Carver cv{reinterpret_cast<uintptr_t>(base)};
+  HierWork h;
+  h.fine = cv.take<float>((size_t)rows * units * nb);
+  h.sel = cv.take<int32_t>((size_t)rows * units * ks);
+  h.n_sel = cv.take<int32_t>((size_t)rows * units);
+  h.keys = h.n_keys = nullptr;
+  h.part = h.qp = nullptr;
+  if (decode) {
+    const int32_t mk = (int32_t)std::min<int64_t>((int64_t)ks * c, (int64_t)INT32_MAX);
+    h.keys = cv.take<int32_t>((size_t)rows * ks * c);
+    h.n_keys = cv.take<int32_t>((size_t)rows);
+    h.part = cv.take<float>(decode_workspace_bytes(rows, mk, s->head_dim) / sizeof(float));
+  } else {
+    h.qp = cv.take<float>((size_t)rows * nb * s->head_dim);
+  }
+  if (w) *w = h;
+  return cv.used;
+}
+}  // namespace
+
+extern "C" {
+
+size_t dsa_hier_prune_workspace_bytes(const dsa_shape* shape, int32_t units, int32_t n_heads) {
+  if (check_shape(shape) != DSA_OK || units < 0 || n_heads < 0) return 0;
+  return al((size_t)shape->batch * n_heads * units * nblocks(shape->seq_len) * sizeof(float));
+}
+
+dsa_status dsa_hier_prune(const void* qu, int32_t qu_dtype, int32_t units, int32_t unit_rows, const void* k,
+                          const dsa_shape* shape, const dsa_prune_stages* stages, float scale,
+                          const int32_t* heads, int32_t n_heads, float* block_max, int32_t* sel, int32_t* n_sel,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if (units < 0 || unit_rows < 0) return DSA_ERR_INVALID_ARG;
+  if (qu_dtype != DSA_BF16 && qu_dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
+  if ((st = check_stages(stages, shape->seq_len)) != DSA_OK) return st;
+  HeadMap hm;
+  if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  if (no_work(shape, hm.n) || units == 0) return DSA_OK;
+  if (!qu || !k || !sel || !n_sel) return DSA_ERR_INVALID_ARG;
+  float* fine = block_max;
+  if (!fine) {
+    const size_t need = dsa_hier_prune_workspace_bytes(shape, units, hm.n);
+    if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
+    fine = static_cast<float*>(workspace);
+  }
+  const PruneArgs a = prune_args(qu, qu_dtype, 0, units, unit_rows, k, shape, stages, scale, hm, fine, sel, n_sel);
+  return hip_status(launch_prune(a, static_cast<hipStream_t>(stream)));
+}
+
+dsa_status dsa_chunks_to_keys(const int32_t* sel, const int32_t* n_sel, int32_t rows, int32_t max_sel,
+                              int32_t chunk, int32_t seq_len, int32_t* keys, int32_t* n_keys, void* stream) {
+  if (rows < 0 || max_sel < 0 || chunk < 1 || seq_len < 1) return DSA_ERR_INVALID_ARG;
+  if ((int64_t)max_sel * chunk > INT32_MAX) return DSA_ERR_UNSUPPORTED;
+  if (rows == 0 || max_sel == 0) return DSA_OK;
+  if (!sel || !n_sel || !keys || !n_keys) return DSA_ERR_INVALID_ARG;
+  return hip_status(launch_chunks_to_keys(sel, n_sel, rows, max_sel, chunk, seq_len, keys, n_keys,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_hier_sparse_decode_workspace_bytes(const dsa_shape* shape, const dsa_prune_stages* stages,
+                                              int32_t n_heads) {
+  if (check_shape(shape) != DSA_OK || n_heads < 0 || check_stages(stages, shape->seq_len) != DSA_OK) return 0;
+  return hier_layout(shape, shape->batch * n_heads, stages, true, nullptr, nullptr);
+}
+
+dsa_status dsa_hier_sparse_decode(const void* q, const void* k, const void* v, void* o, const dsa_shape* shape,
+                                  const dsa_prune_stages* stages, float scale, const int32_t* heads,
+                                  int32_t n_heads, void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if ((st = check_stages(stages, shape->seq_len)) != DSA_OK) return st;
+  if ((int64_t)stages->keep[stages->n_stages - 1] * stages->chunk[stages->n_stages - 1] > INT32_MAX)
+    return DSA_ERR_UNSUPPORTED;
+  HeadMap hm;
+  if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  const int32_t rows = shape->batch * hm.n;
+  if (rows == 0 || shape->seq_len == 0) return DSA_OK;  // no row, or nothing to prune (no key)
+  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
+  const size_t need = hier_layout(shape, rows, stages, true, nullptr, nullptr);
+  if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
+  HierWork w;
+  hier_layout(shape, rows, stages, true, workspace, &w);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const PruneArgs pa = prune_args(q, shape->dtype, 1, 1, 0, k, shape, stages, scale, hm, w.fine, w.sel, w.n_sel);
+  hipError_t e = launch_prune(pa, s);
+  const int32_t c = stages->chunk[stages->n_stages - 1];
+  if (e == hipSuccess)
+    e = launch_chunks_to_keys(w.sel, w.n_sel, rows, pa.max_sel, c, shape->seq_len, w.keys, w.n_keys, s);
+  if (e == hipSuccess) {
+    DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.n = shape->seq_len; a.head_dim = shape->head_dim; a.dtype = shape->dtype; a.rows = rows;
+    a.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
+    a.hm = hm;
+    a.wo = make_work_order(hm);
+    a.keys = w.keys; a.max_keys = pa.max_sel * c; a.n_keys = w.n_keys;
+    a.part = w.part;
+    e = launch_decode(a, s);
+  }
+  return hip_status(e);
+}
+
+size_t dsa_hier_block_sparse_workspace_bytes(const dsa_shape* shape, const dsa_prune_stages* stages,
+                                             int32_t n_heads) {
+  if (check_shape(shape) != DSA_OK || n_heads < 0 || check_stages(stages, shape->seq_len) != DSA_OK) return 0;
+  return hier_layout(shape, shape->batch * n_heads, stages, false, nullptr, nullptr);
+}
+
+dsa_status dsa_hier_block_sparse_attention(const void* q, const void* k, const void* v, void* o,
+                                           const dsa_shape* shape, const dsa_prune_stages* stages, float scale,
+                                           const int32_t* heads, int32_t n_heads, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  dsa_status st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if ((st = check_stages(stages, shape->seq_len)) != DSA_OK) return st;
+  if (stages->chunk[stages->n_stages - 1] != 64) return DSA_ERR_INVALID_ARG;  // key blocks
+  HeadMap hm;
+  if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
+  if (no_work(shape, hm.n)) return DSA_OK;
+  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
+  const int32_t rows = shape->batch * hm.n, n = shape->seq_len, nb = nblocks(n);
+  const size_t need = hier_layout(shape, rows, stages, false, nullptr, nullptr);
+  if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
+  HierWork w;
+  hier_layout(shape, rows, stages, false, workspace, &w);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_pool(q, shape->dtype, n, shape->head_dim, rows, hm, w.qp, s);
+  PruneArgs pa = prune_args(w.qp, DSA_F32, 0, nb, BLOCK, k, shape, stages, scale, hm, w.fine, w.sel, w.n_sel);
+  if (e == hipSuccess) e = launch_prune(pa, s);
+  if (e == hipSuccess)
+    e = launch_attention_blocks(attn_args(q, k, v, o, shape, scale, hm), BlockIndex{w.sel, w.n_sel, pa.max_sel}, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

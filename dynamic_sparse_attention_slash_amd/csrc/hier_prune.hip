@@ -1,0 +1,247 @@
+// Multi-stage hierarchical chunk pruning, gfx950.
+//
+// [InfiniteHiP summary, section "modular hierarchical token pruning": the keys
+// are cut into fixed-length chunks, the highest-scoring token of each chunk is
+// found in parallel, only the best chunks go on to the next stage, and stacked
+// stages refine the block-sparse mask of a query block.]
+//
+// A query vector (a decode row, or a query block's mean-pooled row) sees the
+// keys j < limit. A token's score is scale * q . k_j; a chunk's score is the
+// largest score among its visible tokens. Stage s keeps the keep[s] best chunks
+// of length chunk[s] among the sub-chunks of the chunks stage s-1 kept (stage
+// 1: all chunks), ranked as the rest of the library ranks (forced first, then
+// higher score, then lower id), with the chunk holding key limit - 1 forced.
+//
+// Two kernels:
+//   blockmax: the largest score of every 64-key block, per query vector. One
+//     lane per key holds the key's row as floats; a wave covers one 64-key
+//     block and takes its maximum with cross-lane steps. For one query vector
+//     per head (decode) it streams K once, memory-bound; for many (a query
+//     block each) it is VALU-bound, one FMA per key, dimension and vector.
+//   select: one work-group per query vector runs the stages. A chunk's score
+//     is the largest of its 64-key blocks' maxima (the same quantity). The
+//     keep[s] best of the m candidates are found as the keep[s]-th largest
+//     distinct 64-bit sort key (forced bit | order-preserving score bits |
+//     inverted id), built bit by bit from block-wide counts; the kept chunks
+//     are compacted in ascending id order, and their sub-chunks become the
+//     next stage's candidates in ascending order.
+// The chunk lists of a decode row expand to key lists for the sparse decode.
+#include "kernels.hpp"
+
+namespace dsa {
+namespace {
+
+constexpr int32_t PR_TILE = 256;  // keys per blockmax work-group (4 waves x 64)
+
+__device__ __forceinline__ int32_t unit_limit(const PruneArgs& a, int32_t u) {
+  return a.unit_rows > 0 ? min(a.n, (u + 1) * a.unit_rows) : a.n;
+}
+
+// unit vector element d as float
+template <typename TQ>
+__device__ __forceinline__ float qval(const TQ* p, int32_t d) {
+  if constexpr (sizeof(TQ) == 2) return bf16_bits_to_f32(p[d]);
+  else return p[d];
+}
+
+template <typename TK, typename TQ, int D>
+__global__ __launch_bounds__(PR_TILE) void prune_blockmax_kernel(PruneArgs a) {
+  int32_t row, tile;
+  work_item(a.hm, a.wo, a.ntiles, row, tile);
+  const int32_t tid = threadIdx.x, lane = tid & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t blk = tile * (PR_TILE / 64) + wave;  // this wave's 64-key block
+  if (blk * 64 >= a.n) return;                       // past the cache: no block
+  const int32_t j = blk * 64 + lane;
+  const TK* ks = static_cast<const TK*>(a.k) + a.hm.kv_slab(row, a.n, D);
+  // key j as floats (a lane past the end reads the last key; its score is masked)
+  float kf[D];
+  {
+    const TK* kr = ks + (size_t)min(j, a.n - 1) * D;
+    if constexpr (sizeof(TK) == 2) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(kr);
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        const u32x4 x = src[c];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          kf[8 * c + 2 * t] = __uint_as_float(x[t] << 16);
+          kf[8 * c + 2 * t + 1] = __uint_as_float(x[t] & 0xffff0000u);
+        }
+      }
+    } else {
+      const f32x4* src = reinterpret_cast<const f32x4*>(kr);
+#pragma unroll
+      for (int c = 0; c < D / 4; ++c) {
+        const f32x4 x = src[c];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kf[4 * c + t] = x[t];
+      }
+    }
+  }
+  // units that see no key of this block are skipped (prefill: unit u sees
+  // keys below (u + 1) * unit_rows)
+  const int32_t u_lo = a.unit_rows > 0 ? (blk * 64) / a.unit_rows : 0;
+  const TQ* qbase = static_cast<const TQ*>(a.qu) +
+                    (a.qu_full ? a.hm.q_slab(row, a.units, D) : (size_t)row * a.units * D);
+  float* out = a.fine + (size_t)row * a.units * a.nbf + blk;
+  for (int32_t u = u_lo; u < a.units; ++u) {
+    const int32_t limit = unit_limit(a, u);
+    const TQ* qv = qbase + (size_t)u * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) dot = __builtin_fmaf(kf[d], qval(qv, d), dot);
+    float x = j < limit ? dot * a.scale : -INFINITY;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x = xor_max(x, m);
+    if (lane == 0) out[(size_t)u * a.nbf] = x;
+  }
+}
+
+// order-preserving key of an fp32 score: NaN ranks as -inf, -0 as +0
+__device__ __forceinline__ uint32_t pr_score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int PR_THREADS = 256;
+
+// block-wide sum (all threads get it); red has PR_THREADS / 64 entries
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int w = 0; w < PR_THREADS / 64; ++w) s += red[w];
+  return s;
+}
+
+// exclusive prefix of v over the threads (in thread order); returns the total
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t& excl, uint32_t* buf) {
+  __syncthreads();
+  buf[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 1; off < PR_THREADS; off <<= 1) {
+    const uint32_t t = threadIdx.x >= (uint32_t)off ? buf[threadIdx.x - off] : 0u;
+    __syncthreads();
+    buf[threadIdx.x] += t;
+    __syncthreads();
+  }
+  excl = buf[threadIdx.x] - v;
+  return buf[PR_THREADS - 1];
+}
+
+__global__ __launch_bounds__(PR_THREADS) void prune_select_kernel(PruneArgs a) {
+  __shared__ uint64_t key[PR_MAX_CAND];
+  __shared__ int32_t cid[PR_MAX_CAND];
+  __shared__ int32_t kept[PR_MAX_CAND];
+  __shared__ uint32_t buf[PR_THREADS];
+  __shared__ uint32_t red[PR_THREADS / 64];
+  const int32_t u = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const int32_t limit = unit_limit(a, u);
+  const int32_t nvis = (limit + 63) / 64;  // visible 64-key blocks
+  const float* fm = a.fine + ((size_t)row * a.units + u) * a.nbf;
+  int32_t m = (nvis + a.chunk_blocks[0] - 1) / a.chunk_blocks[0];
+  for (int32_t i = tid; i < m; i += PR_THREADS) cid[i] = i;
+  int32_t nk = 0;
+  for (int32_t s = 0; s < a.n_stages; ++s) {
+    const int32_t cb = a.chunk_blocks[s];
+    const int32_t forced = (nvis - 1) / cb;
+    __syncthreads();
+    for (int32_t i = tid; i < m; i += PR_THREADS) {
+      const int32_t x = cid[i];
+      const int32_t b0 = x * cb, b1 = min(nvis, b0 + cb);
+      float best = -INFINITY;
+      for (int32_t b = b0; b < b1; ++b) best = fmaxf(best, fm[b]);
+      key[i] = x == forced ? ~0ull
+                           : ((uint64_t)pr_score_key(best) << 31) | (uint64_t)(0x7fffffff - x);
+    }
+    __syncthreads();
+    const int32_t keep = min(a.keep[s], m);
+    // the keep-th largest key: largest T with #{key >= T} >= keep
+    uint64_t T = 0;
+    if (keep < m) {
+      for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t t2 = T | (1ull << bit);
+        uint32_t c = 0;
+        for (int32_t i = tid; i < m; i += PR_THREADS) c += key[i] >= t2;
+        if (block_sum(c, red) >= (uint32_t)keep) T = t2;
+      }
+    }
+    // compact the kept candidates in ascending order (each thread a run)
+    const int32_t per = (m + PR_THREADS - 1) / PR_THREADS;
+    const int32_t i0 = min(m, tid * per), i1 = min(m, i0 + per);
+    uint32_t c = 0;
+    for (int32_t i = i0; i < i1; ++i) c += key[i] >= T;
+    uint32_t pos;
+    block_scan(c, pos, buf);
+    for (int32_t i = i0; i < i1; ++i)
+      if (key[i] >= T) kept[pos++] = cid[i];
+    nk = keep;
+    __syncthreads();
+    if (s + 1 < a.n_stages) {
+      // sub-chunks of the kept chunks, ascending; all but the last kept chunk
+      // (the forced one, the highest id) lie wholly below the limit
+      const int32_t r = cb / a.chunk_blocks[s + 1], cb2 = a.chunk_blocks[s + 1];
+      const int32_t last_vis = (nvis + cb2 - 1) / cb2;  // sub-chunk ids below this hold visible keys
+      m = (nk - 1) * r + (last_vis - kept[nk - 1] * r);
+      for (int32_t i = tid; i < nk * r; i += PR_THREADS) {
+        const int32_t y = kept[i / r] * r + i % r;
+        if (i < m) cid[i] = y;
+      }
+    }
+  }
+  int32_t* dst = a.sel + ((size_t)row * a.units + u) * a.max_sel;
+  for (int32_t i = tid; i < nk; i += PR_THREADS) dst[i] = kept[i];
+  if (tid == 0) a.n_sel[(size_t)row * a.units + u] = nk;
+}
+
+// keys[row][i * chunk + t] = sel[row][i] * chunk + t, for the n_sel[row]
+// chunks; n_keys = the keys below seq_len (only the last chunk can be cut).
+__global__ __launch_bounds__(256) void chunks_to_keys_kernel(const int32_t* __restrict__ sel,
+                                                             const int32_t* __restrict__ n_sel, int32_t max_sel,
+                                                             int32_t chunk, int32_t n, int32_t* __restrict__ keys,
+                                                             int32_t* __restrict__ n_keys) {
+  const int32_t row = blockIdx.y;
+  const int32_t cnt = min(n_sel[row], max_sel);
+  const int32_t total = cnt * chunk;
+  const int32_t* s = sel + (size_t)row * max_sel;
+  int32_t* k = keys + (size_t)row * max_sel * chunk;
+  for (int32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256)
+    k[i] = min(s[i / chunk] * chunk + i % chunk, n - 1);
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    n_keys[row] = cnt == 0 ? 0 : (cnt - 1) * chunk + min(chunk, n - s[cnt - 1] * chunk);
+}
+
+}  // namespace
+
+hipError_t launch_prune(PruneArgs a, hipStream_t s) {
+  if (a.rows == 0 || a.units == 0 || a.n == 0) return hipSuccess;
+  a.nbf = (a.n + 63) / 64;
+  a.ntiles = (a.n + PR_TILE - 1) / PR_TILE;
+  const bool kb = a.k_dtype == BF16, qb = a.qu_dtype == BF16, d64 = a.head_dim == 64;
+  auto bm = kb ? (qb ? (d64 ? prune_blockmax_kernel<uint16_t, uint16_t, 64> : prune_blockmax_kernel<uint16_t, uint16_t, 128>)
+                     : (d64 ? prune_blockmax_kernel<uint16_t, float, 64> : prune_blockmax_kernel<uint16_t, float, 128>))
+               : (qb ? (d64 ? prune_blockmax_kernel<float, uint16_t, 64> : prune_blockmax_kernel<float, uint16_t, 128>)
+                     : (d64 ? prune_blockmax_kernel<float, float, 64> : prune_blockmax_kernel<float, float, 128>));
+  hipLaunchKernelGGL(bm, dim3((unsigned)((long long)a.ntiles * a.rows)), dim3(PR_TILE), 0, s, a);
+  hipLaunchKernelGGL(prune_select_kernel, dim3(a.units, a.rows), dim3(PR_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunks_to_keys(const int32_t* sel, const int32_t* n_sel, int32_t rows, int32_t max_sel,
+                                 int32_t chunk, int32_t n, int32_t* keys, int32_t* n_keys, hipStream_t s) {
+  if (rows == 0 || max_sel == 0) return hipSuccess;
+  const long long blocks = ((long long)max_sel * chunk + 255) / 256;
+  const unsigned gx = (unsigned)(blocks < 64 ? blocks : 64);
+  hipLaunchKernelGGL(chunks_to_keys_kernel, dim3(gx, rows), dim3(256), 0, s, sel, n_sel, max_sel, chunk, n,
+                     keys, n_keys);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

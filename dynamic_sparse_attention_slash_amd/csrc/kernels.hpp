@@ -160,6 +160,33 @@ hipError_t launch_topk_rows(const float* scores, int32_t rows, int32_t n, int32_
 hipError_t launch_block_topk(const float* logits, int32_t rows, int32_t nb, int32_t topk,
                              int32_t* sel, int32_t* n_sel, hipStream_t s);
 
+// ---- hierarchical chunk pruning (hier_prune.hip) ----
+constexpr int32_t PR_MAX_STAGES = 4;
+constexpr int32_t PR_MAX_CAND = 4096;  // candidates of one stage
+struct PruneArgs {
+  // query vectors: qu_full ? [batch][q_heads][units][D] (rows map through hm)
+  //                        : [rows][units][D]
+  const void* qu; int32_t qu_dtype, qu_full;
+  const void* k; int32_t k_dtype;         // [batch][kv_heads][n][D]
+  int32_t n, head_dim, units, rows;
+  int32_t unit_rows;   // unit u sees keys < min(n, (u+1) unit_rows); 0: all n
+  float scale;
+  HeadMap hm;
+  WorkOrder wo;
+  float* fine;         // [rows][units][nbf]: largest score of each 64-key block
+  int32_t nbf, ntiles; // set by launch_prune
+  int32_t n_stages;
+  int32_t chunk_blocks[PR_MAX_STAGES];  // chunk lengths in 64-key blocks
+  int32_t keep[PR_MAX_STAGES];
+  int32_t* sel;        // [rows][units][max_sel] kept chunk ids of the last stage
+  int32_t* n_sel;      // [rows][units]
+  int32_t max_sel;
+};
+hipError_t launch_prune(PruneArgs a, hipStream_t s);
+// key lists of kept chunks: keys [rows][max_sel * chunk], n_keys [rows]
+hipError_t launch_chunks_to_keys(const int32_t* sel, const int32_t* n_sel, int32_t rows, int32_t max_sel,
+                                 int32_t chunk, int32_t n, int32_t* keys, int32_t* n_keys, hipStream_t s);
+
 // ---- vertical-slash index builder (vs_index.hip) ----
 hipError_t launch_vs_build_index(const int32_t* V, int32_t nv, const int32_t* S, int32_t ns,
                                  int32_t rows, int32_t seq_len, int32_t* iv, int32_t* n_iv,

@@ -347,6 +347,95 @@ dsa_status dsa_sparse_decode_noalloc(const void* q, const void* k, const void* v
                                      int32_t n_heads, const int32_t* keys, int32_t max_keys,
                                      const int32_t* n_keys, void* stream);
 
+/* ======================================================================
+ * Hierarchical chunk pruning [InfiniteHiP summary, section "modular
+ * hierarchical token pruning" (模块化分层令牌剪枝算法): the keys are cut into
+ * fixed-length chunks, the highest-scoring token of each chunk is found, only
+ * the best chunks go on to the next stage, and stacked stages refine the
+ * block-sparse mask of a query].
+ *
+ * A query vector sees the keys j < limit. A token's score is
+ * scale * q . k_j (scale <= 0: 1/sqrt(head_dim)); a chunk's score is the
+ * largest score of its visible tokens, found exactly. Stage s keeps the
+ * keep[s] best candidates of length chunk[s]: stage 1's candidates are the
+ * chunks of [0, limit), a later stage's the sub-chunks of the chunks the stage
+ * before kept that hold a visible key. Ranking: the chunk holding key
+ * limit - 1 first (forced), then higher score, then lower chunk id (-0 counts
+ * as +0, NaN as -inf). The result is the last stage's kept chunk ids,
+ * ascending, min(keep, candidates) of them.
+ * ====================================================================== */
+#define DSA_PRUNE_MAX_STAGES 4
+#define DSA_PRUNE_MAX_CANDIDATES 4096
+typedef struct {
+  int32_t n_stages;                     /* 1 .. DSA_PRUNE_MAX_STAGES */
+  int32_t chunk[DSA_PRUNE_MAX_STAGES];  /* keys per chunk: multiples of 64, strictly
+                                           decreasing, each dividing the one before */
+  int32_t keep[DSA_PRUNE_MAX_STAGES];   /* chunks kept by the stage, >= 1 */
+} dsa_prune_stages;
+/* Stage lists are checked on the host: a malformed list is
+ * DSA_ERR_INVALID_ARG; more than DSA_PRUNE_MAX_CANDIDATES candidates in a stage
+ * (stage 1: ceil(seq_len / chunk[0]); stage s: keep[s-1] * chunk[s-1] /
+ * chunk[s]) is DSA_ERR_UNSUPPORTED. */
+
+/* The pruning stages for explicit query vectors. qu: device
+ * [batch * n_heads][units][head_dim] (rows: batch-major, then listed heads),
+ * dtype qu_dtype (DSA_BF16 or DSA_F32); k: the device cache
+ * [batch][kv_heads][seq_len][head_dim] of shape->dtype; listed head h reads kv
+ * head h / (q_heads / kv_heads). Unit u of a row sees the keys
+ * j < min(seq_len, (u + 1) * unit_rows), or all seq_len keys when unit_rows is
+ * 0 (decode rows). Outputs: sel device int32 [rows][units][keep of the last
+ * stage] (entries past the count unwritten), n_sel [rows][units]; block_max
+ * (optional, device fp32 [rows][units][ceil(seq_len / 64)]) receives the
+ * largest token score of every visible 64-key block, which is what the stages
+ * rank (a chunk's score is the largest of its blocks'); blocks a unit does not
+ * see are unwritten. When block_max is NULL it lives in the workspace:
+ * dsa_hier_prune_workspace_bytes(shape, units, n_heads) bytes. */
+dsa_status dsa_hier_prune(const void* qu, int32_t qu_dtype, int32_t units, int32_t unit_rows,
+                          const void* k, const dsa_shape* shape, const dsa_prune_stages* stages,
+                          float scale, const int32_t* heads, int32_t n_heads, float* block_max,
+                          int32_t* sel, int32_t* n_sel, void* workspace, size_t workspace_bytes,
+                          void* stream);
+size_t dsa_hier_prune_workspace_bytes(const dsa_shape* shape, int32_t units, int32_t n_heads);
+
+/* Key lists of kept chunks, for dsa_sparse_decode: keys[r][i * chunk + t] =
+ * sel[r][i] * chunk + t for the n_sel[r] chunks of row r (ids ascending, as
+ * the pruning returns them), n_keys[r] = those keys below seq_len (only the
+ * last chunk can be cut). sel: device int32 [rows][max_sel]; keys: device
+ * int32 [rows][max_sel * chunk]. */
+dsa_status dsa_chunks_to_keys(const int32_t* sel, const int32_t* n_sel, int32_t rows,
+                              int32_t max_sel, int32_t chunk, int32_t seq_len, int32_t* keys,
+                              int32_t* n_keys, void* stream);
+
+/* Decode over pruned keys [InfiniteHiP summary: pruning for attention
+ * decoding; Novita §2: decoding attends only to the kept entries]: each listed
+ * head's new row (q, o as in dsa_sparse_decode) is the query vector, limit =
+ * seq_len; the stages select chunks, and the row attends over their keys with
+ * the softmax of dsa_sparse_decode. workspace: at least
+ * dsa_hier_sparse_decode_workspace_bytes(shape, stages, n_heads) bytes. */
+dsa_status dsa_hier_sparse_decode(const void* q, const void* k, const void* v, void* o,
+                                  const dsa_shape* shape, const dsa_prune_stages* stages, float scale,
+                                  const int32_t* heads, int32_t n_heads, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+size_t dsa_hier_sparse_decode_workspace_bytes(const dsa_shape* shape,
+                                              const dsa_prune_stages* stages, int32_t n_heads);
+
+/* Prefill heads with the pruning as their block estimator [InfiniteHiP
+ * summary: stages refine the block-sparse mask per query block; MInf §2.2
+ * Block-Sparse Head for the pooled query and the block attention]: query block
+ * a's query vector is its mean-pooled row, limit = min(seq_len, 64 (a + 1));
+ * the last stage's chunk length must be 64, so the kept chunks are key blocks;
+ * block a then attends over them, causally. Layout and head list as in
+ * dsa_block_sparse_attention. The block maxima take
+ * rows * nb * nb * 4 bytes of the workspace (nb = ceil(seq_len / 64)): this
+ * form is for contexts up to about 128K. workspace: at least
+ * dsa_hier_block_sparse_workspace_bytes(shape, stages, n_heads) bytes. */
+dsa_status dsa_hier_block_sparse_attention(const void* q, const void* k, const void* v, void* o,
+                                           const dsa_shape* shape, const dsa_prune_stages* stages,
+                                           float scale, const int32_t* heads, int32_t n_heads,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+size_t dsa_hier_block_sparse_workspace_bytes(const dsa_shape* shape,
+                                             const dsa_prune_stages* stages, int32_t n_heads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -289,3 +289,65 @@ def test_noalloc_decode_argument_errors(lib):
     assert lib.dsa_sparse_decode_noalloc(P, P, P, P, ctypes.byref(sh), 0.0, None, 0, P, -1, P, None) == INVALID
     assert lib.dsa_sparse_decode_noalloc(None, None, None, None, ctypes.byref(shape(b=0)), 0.0, None, 0, None,
                                          0, None, None) == OK
+
+
+def stages(*pairs):
+    return B._stages(list(pairs))
+
+
+def prune_call(lib, sh, st, units=0, unit_rows=0, qd=0, qu=P, sel=P):
+    # units = 0 by default: every check runs, and a call that passes them has
+    # no work, so nothing is launched
+    return lib.dsa_hier_prune(qu, qd, units, unit_rows, P, ctypes.byref(sh), ctypes.byref(st), 0.0, None, 0,
+                              P, sel, P, None, 0, None)
+
+
+def test_prune_stage_checks(lib):
+    """Stage lists are checked on the host: lengths multiples of 64, strictly
+    decreasing and nested, keep >= 1, at most 4 stages; candidate counts
+    capped at 4096 (unsupported beyond). No call here launches anything."""
+    sh = shape(n=1 << 20)
+    assert prune_call(lib, sh, stages((4096, 16), (512, 32), (64, 64))) == OK
+    assert prune_call(lib, sh, stages((4096, 16), (1000, 4))) == INVALID      # not a multiple of 64
+    assert prune_call(lib, sh, stages((512, 4), (512, 4))) == INVALID         # not decreasing
+    assert prune_call(lib, sh, stages((512, 4), (192, 4))) == INVALID         # does not divide
+    assert prune_call(lib, sh, stages((512, 0))) == INVALID                   # keep 0
+    assert prune_call(lib, sh, stages((32, 4))) == INVALID                    # below 64
+    st = stages((4096, 1))
+    st.n_stages = 5
+    assert prune_call(lib, sh, st) == INVALID
+    st.n_stages = 0
+    assert prune_call(lib, sh, st) == INVALID
+    assert prune_call(lib, sh, stages((128, 4))) == UNSUPPORTED               # 8192 stage-1 candidates
+    assert prune_call(lib, sh, stages((4096, 100), (64, 10))) == UNSUPPORTED  # 6400 stage-2 candidates
+    assert prune_call(lib, sh, stages((4096, 4)), qd=5) == UNSUPPORTED
+    assert prune_call(lib, sh, stages((4096, 4)), units=1, qu=None) == INVALID
+    assert prune_call(lib, sh, stages((4096, 4)), units=1, sel=None) == INVALID
+    assert prune_call(lib, sh, stages((4096, 4)), units=-1) == INVALID
+    assert prune_call(lib, sh, stages((4096, 4)), unit_rows=-1) == INVALID
+    assert prune_call(lib, sh, stages((4096, 4)), qu=None, sel=None) == OK   # no unit: nothing to do
+    assert lib.dsa_hier_prune(P, 0, 1, 0, P, ctypes.byref(sh), None, 0.0, None, 0, P, P, P, None, 0, None) == INVALID
+    # no block_max output and too small a workspace
+    assert lib.dsa_hier_prune(P, 0, 1, 0, P, ctypes.byref(sh), ctypes.byref(stages((4096, 4))), 0.0, None, 0,
+                              None, P, P, P, 16, None) == WORKSPACE
+
+
+def test_prune_composite_calls_checks(lib):
+    sh = shape(n=5000)
+    st = stages((1024, 2), (64, 8))
+    assert lib.dsa_hier_sparse_decode_workspace_bytes(ctypes.byref(sh), ctypes.byref(st), 4) > 0
+    assert lib.dsa_hier_block_sparse_workspace_bytes(ctypes.byref(sh), ctypes.byref(st), 4) > 0
+    assert lib.dsa_hier_sparse_decode_workspace_bytes(ctypes.byref(sh), None, 4) == 0
+    assert lib.dsa_hier_sparse_decode(P, P, P, P, ctypes.byref(sh), ctypes.byref(st), 0.0, None, 0, P, 8,
+                                      None) == WORKSPACE
+    assert lib.dsa_hier_sparse_decode(None, P, P, P, ctypes.byref(sh), ctypes.byref(st), 0.0, None, 0, P,
+                                      1 << 40, None) == INVALID
+    # the prefill form needs 64-key blocks at the last stage
+    st2 = stages((1024, 2), (128, 8))
+    assert lib.dsa_hier_block_sparse_attention(P, P, P, P, ctypes.byref(sh), ctypes.byref(st2), 0.0, None, 0,
+                                               P, 1 << 40, None) == INVALID
+    assert lib.dsa_hier_block_sparse_attention(P, P, P, P, ctypes.byref(shape(b=0)), ctypes.byref(st), 0.0,
+                                               None, 0, None, 0, None) == OK
+    assert lib.dsa_chunks_to_keys(P, P, 4, 8, 0, 100, P, P, None) == INVALID
+    assert lib.dsa_chunks_to_keys(P, P, 0, 8, 64, 100, P, P, None) == OK
+    assert lib.dsa_chunks_to_keys(None, P, 4, 8, 64, 100, P, P, None) == INVALID

@@ -912,3 +912,162 @@ def test_workload_llama_1m_mixed_every_head(h):
 def test_workload_qwen2_32k_b4_mixed_every_head(b, h):
     """The Qwen2-7B-shaped 32K layer, batch 4 (10 VS, 9 BS, 9 streaming heads), every (batch, head)."""
     _check_mixed_head(_WQW.name, b, h, 8, seed=8 + 28 * b + h)
+
+
+# ---------------------------------------------------------------------------
+# hierarchical chunk pruning
+# ---------------------------------------------------------------------------
+def _block_max_oracle(qv, kh, limit, scale):
+    """float64 largest token score of each visible 64-key block."""
+    s = O.token_scores(qv, kh, limit, scale)
+    return np.array([s[b * BLK: min(limit, (b + 1) * BLK)].max() for b in range((limit + BLK - 1) // BLK)])
+
+
+def _check_block_max(bm_gpu, qv, kh, limit, scale, tag):
+    """GPU block maxima within fp32 dot-product rounding of the float64 ones:
+    |error| <= 1e-4 * scale * |q| * max |k_j| over the block."""
+    ref = _block_max_oracle(qv, kh, limit, scale)
+    g = np.asarray(bm_gpu[: len(ref)], np.float64)
+    kn = np.linalg.norm(kh[:limit], axis=1)
+    kmax = np.array([kn[b * BLK: min(limit, (b + 1) * BLK)].max() for b in range(len(ref))])
+    bound = 1e-4 * scale * np.linalg.norm(qv) * kmax + 1e-6
+    bad = np.abs(g - ref) > bound
+    assert not bad.any(), (tag, np.flatnonzero(bad)[:5], g[bad][:5], ref[bad][:5])
+
+
+@pytest.mark.parametrize("n,D,dt,qdt,stages,unit_rows", [
+    (5000, 128, "bf16", "bf16", [(1024, 2), (256, 3), (64, 4)], 0),
+    (4096, 64, "f32", "f32", [(512, 3), (64, 5)], 0),
+    (777, 128, "bf16", "f32", [(256, 9), (64, 50)], 0),        # keep-all stages
+    (64, 128, "bf16", "bf16", [(128, 1), (64, 1)], 0),          # one block
+    (1, 64, "bf16", "bf16", [(64, 1)], 0),                      # one key
+    (70000, 128, "bf16", "bf16", [(4096, 4), (512, 8), (64, 16)], 0),
+    (1000, 128, "bf16", "f32", [(256, 2), (64, 3)], 64),        # prefill units (pooled blocks)
+    (64 * 9 + 5, 64, "f32", "f32", [(192, 1), (64, 2)], 64),
+])
+def test_hier_prune_stage_call(n, D, dt, qdt, stages, unit_rows):
+    """Block maxima against the float64 oracle; chunk ids bit-exact against the
+    oracle's stages on the GPU's own block maxima (GQA, a head subset)."""
+    say(f"hier prune n={n} D={D} {dt}/{qdt} stages={stages} unit_rows={unit_rows}")
+    B, Hq, Hkv, heads = 2, 4, 2, [3, 0]
+    g = torch.Generator().manual_seed(n + D)
+    k = torch.randn(B, Hkv, n, D, generator=g).to(DT[dt])
+    k[:, :, torch.randint(0, n, (5,), generator=g)] *= 4.0   # a few dominant keys
+    units = 1 if unit_rows == 0 else O.num_blocks(n)
+    qu = (torch.randn(B * len(heads), units, D, generator=g) * 0.7).to(DT[qdt])
+    sel, n_sel, bm = dsa.hier_prune(qu.cuda(), k.cuda(), stages, q_heads=Hq, heads=heads, unit_rows=unit_rows,
+                                    return_block_max=True)
+    torch.cuda.synchronize()
+    kh, quh = host64(k), host64(qu)
+    sc = 1 / math.sqrt(D)
+    sel, n_sel, bm = sel.cpu().numpy(), n_sel.cpu().numpy(), bm.cpu().numpy()
+    for b in range(B):
+        for t, h in enumerate(heads):
+            r = b * len(heads) + t
+            kk = kh[b, kvh(h, Hq, Hkv)]
+            for u in range(units):
+                limit = n if unit_rows == 0 else min(n, (u + 1) * unit_rows)
+                if u < 3 or u % 5 == 0 or u == units - 1:
+                    _check_block_max(bm[r, u], quh[r, u], kk, limit, sc, (r, u))
+                nv = O.num_blocks(limit)
+                want = O.hier_prune(quh[r, u], kk, limit, stages, sc, fine_max=bm[r, u, :nv])
+                assert int(n_sel[r, u]) == len(want), (r, u)
+                assert np.array_equal(sel[r, u, : len(want)], want), (r, u, sel[r, u, : len(want)], want)
+
+
+@pytest.mark.parametrize("n,D,dt,stages", [(5000, 128, "bf16", [(1024, 2), (256, 3), (64, 4)]),
+                                           (3000, 64, "f32", [(512, 2), (64, 3)]),
+                                           (100, 128, "bf16", [(128, 1), (64, 2)])])
+def test_hier_sparse_decode(n, D, dt, stages):
+    """Decode over pruned keys: the chunks equal the oracle's stages on the
+    GPU's block maxima, the key lists are those chunks' keys, and the output
+    matches the oracle's decode over them."""
+    say(f"hier decode n={n} D={D} {dt} stages={stages}")
+    B, Hq, Hkv, heads = 2, 4, 2, [2, 1, 3]
+    g = torch.Generator().manual_seed(n)
+    q = (torch.randn(B, Hq, D, generator=g) * 1.5).to(DT[dt]).cuda()
+    k = torch.randn(B, Hkv, n, D, generator=g).to(DT[dt]).cuda()
+    v = torch.randn(B, Hkv, n, D, generator=g).to(DT[dt]).cuda()
+    o = dsa.hier_sparse_decode(q, k, v, stages, heads=heads)
+    qu = q[:, heads].reshape(B * len(heads), 1, D).contiguous()
+    sel, n_sel, bm = dsa.hier_prune(qu, k, stages, q_heads=Hq, heads=heads, return_block_max=True)
+    keys, n_keys = dsa.chunks_to_keys(sel[:, 0].contiguous(), n_sel[:, 0].contiguous(), stages[-1][0], n)
+    o2 = dsa.sparse_decode(q, k, v, keys, n_keys, heads=heads)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)   # the composite call is the three stage calls
+    qh, kh, vh, oh = host64(q), host64(k), host64(v), host64(o)
+    sc = 1 / math.sqrt(D)
+    for b in range(B):
+        for t, h in enumerate(heads):
+            r = b * len(heads) + t
+            gk = kvh(h, Hq, Hkv)
+            res = O.hier_decode(qh[b, h], kh[b, gk], vh[b, gk], stages, sc,
+                                fine_max=bm[r, 0].cpu().numpy())
+            assert np.array_equal(sel[r, 0, : int(n_sel[r, 0])].cpu().numpy(), res["chunks"])
+            nk = int(n_keys[r])
+            assert np.array_equal(keys[r, :nk].cpu().numpy(), res["keys"])
+            check_attention(oh[b, h][None], res["out"][None], f"hier decode b{b} h{h}")
+        assert not oh[b, 0].any()
+
+
+@pytest.mark.parametrize("n,D,dt,stages", [(1000, 128, "bf16", [(256, 2), (64, 3)]),
+                                           (64 * 12 + 7, 64, "f32", [(384, 1), (128, 2), (64, 3)])])
+def test_hier_block_sparse_attention(n, D, dt, stages):
+    """Prefill heads with the pruning as block estimator: every query block
+    against the oracle (blocks chosen by the oracle's stages on the GPU's
+    block maxima of the pooled queries)."""
+    say(f"hier prefill n={n} D={D} {dt} stages={stages}")
+    q, k, v = rand_qkv(1, 4, 2, n, D, dt, seed=n, amp=1.5)
+    heads = [1, 2]
+    o = dsa.hier_block_sparse_attention(q, k, v, stages, heads=heads)
+    qp = dsa.bs_pool(q, heads)
+    sel, n_sel, bm = dsa.hier_prune(qp, k, stages, q_heads=4, heads=heads, unit_rows=BLK, return_block_max=True)
+    o2 = dsa.sparse_attention_blocks(q, k, v, sel, n_sel, heads=heads)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    qh, kh, vh, oh = host64(q), host64(k), host64(v), host64(o)
+    nb = O.num_blocks(n)
+    for t, h in enumerate(heads):
+        fm = np.full((nb, nb), np.nan, np.float32)
+        b_np = bm[t].cpu().numpy()
+        for a in range(nb):
+            fm[a, : a + 1] = b_np[a, : a + 1]
+        res = O.hier_head(qh[0, h], kh[0, kvh(h, 4, 2)], vh[0, kvh(h, 4, 2)], stages, 1 / math.sqrt(D),
+                          fine_max=fm)
+        for a in range(nb):
+            assert np.array_equal(sel[t, a, : int(n_sel[t, a])].cpu().numpy(), res["sel"][a]), (h, a)
+        check_attention(oh[0, h], O.assemble(res["out"], n, D), f"hier prefill h{h}")
+    assert float(np.abs(oh[0, 0]).max()) == 0.0
+
+
+HIER_DECODE_STAGES = [(4096, 16), (512, 32), (64, 64)]
+
+
+def test_hier_decode_1m_every_head():
+    """Decode after a 1M-token prefill (Llama-3-8B shape, 32 query heads):
+    every head's chunks against the oracle's stages on the GPU's block maxima,
+    four heads' block maxima against float64, every head's output against the
+    oracle's decode over its kept keys."""
+    w = synthetic.BY_NAME["llama3_8b_1m_mixed_bf16"]
+    say(f"hier decode 1M ({w.name})")
+    x = synthetic.make_inputs(w, device="cuda")
+    g = torch.Generator().manual_seed(21)
+    qd = torch.randn(1, w.q_heads, w.head_dim, generator=g).to(torch.bfloat16).cuda()
+    o = dsa.hier_sparse_decode(qd, x.k, x.v, HIER_DECODE_STAGES)
+    sel, n_sel, bm = dsa.hier_prune(qd.reshape(w.q_heads, 1, w.head_dim).contiguous(), x.k, HIER_DECODE_STAGES,
+                                    q_heads=w.q_heads, return_block_max=True)
+    torch.cuda.synchronize()
+    n, D = w.seq_len, w.head_dim
+    sc = 1 / math.sqrt(D)
+    qh, oh = host64(qd), host64(o)
+    bm_h, sel_h, ns_h = bm.cpu().numpy(), sel.cpu().numpy(), n_sel.cpu().numpy()
+    for kv in range(w.kv_heads):
+        kh = host64(x.k[0, kv])
+        vh = host64(x.v[0, kv])
+        for h in range(kv * (w.q_heads // w.kv_heads), (kv + 1) * (w.q_heads // w.kv_heads)):
+            if h % 8 == 0:
+                _check_block_max(bm_h[h, 0], qh[0, h], kh, n, sc, f"1M h{h}")
+            res = O.hier_decode(qh[0, h], kh, vh, HIER_DECODE_STAGES, sc, fine_max=bm_h[h, 0])
+            assert np.array_equal(sel_h[h, 0, : int(ns_h[h, 0])], res["chunks"]), h
+            check_attention(oh[0, h][None], res["out"][None], f"1M hier decode h{h}")
+        del kh, vh
