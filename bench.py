@@ -364,6 +364,17 @@ def layer_flops(w, x, idx):
 
 
 KV_WINDOW, KV_KEEP = 256, 4096
+# decode over pruned keys after prefill: 256 chunks of 4096 keys keep 16, their
+# 128 chunks of 512 keep 32, their 256 blocks of 64 keep 64 (4096 keys per
+# head, the retention budget); each stage keeps fewer chunks than the next, so
+# the hierarchy is not a flat selection
+HIER_DECODE_STAGES = [(4096, 16), (512, 32), (64, 64)]
+
+
+def hier_prefill_stages(topk):
+    """Pruning stages for a block-sparse layer with the same budget: topk key
+    blocks per query block after a 1024- and a 256-key stage."""
+    return [(1024, max(1, topk // 8)), (256, max(2, topk // 2)), (64, topk)]
 
 
 def kv_retention_timing(layer, reps):
@@ -400,8 +411,50 @@ def kv_retention_timing(layer, reps):
     for name, t, nb in (("decode_kept", ms_k, b_k), ("decode_all", ms_a, b_a)):
         out[name] = {"ms": t, "keys_per_head": kk if name == "decode_kept" else n, "bytes": nb,
                      "gbs": nb / (t * 1e-3) / 1e9, "frac_hbm": nb / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    del kept, n_keys, qd
+    # the retention passes are bound by their products and exponentials, not
+    # by memory: two passes of the window's rows against every key
+    wr = min(KV_WINDOW, n)
+    fl = 2 * 2.0 * rows * wr * n * D
+    out["compute"] = {"flops": fl, "exp": 2.0 * rows * wr * n, "tflops": fl / (ms * 1e-3) / 1e12,
+                      "frac_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    # decode over keys chosen per query by hierarchical chunk pruning: the
+    # block-maximum pass streams K once per kv head (the heads of a group share
+    # it in L2), then the decode reads the kept rows
+    ms_h = time_stage(lambda: dsa.hier_sparse_decode(qd, k, v, HIER_DECODE_STAGES), 10)
+    qu = qd.reshape(rows, 1, D).contiguous()
+    ms_p = time_stage(lambda: dsa.hier_prune(qu, k, HIER_DECODE_STAGES, q_heads=w.q_heads), 10)
+    kh = HIER_DECODE_STAGES[-1][0] * HIER_DECODE_STAGES[-1][1]
+    b_p = B * w.kv_heads * n * D * eb + rows * D * eb
+    b_h = b_p + rows * kh * D * eb * 2 + qo
+    out["hier_decode"] = {"stages": HIER_DECODE_STAGES, "ms": ms_h, "prune_ms": ms_p, "keys_per_head": kh,
+                          "bytes": b_h, "gbs": b_h / (ms_h * 1e-3) / 1e9,
+                          "frac_hbm": b_h / (ms_h * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "prune_bytes": b_p, "prune_frac_hbm": b_p / (ms_p * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "speedup_vs_decode_all": ms_a / ms_h}
+    del kept, n_keys, qd, qu
     return out
+
+
+def hier_prefill_timing(layer, reps):
+    """The block-sparse heads of a layer with the hierarchical pruning as their
+    block estimator (same key-block budget), beside the mean-pooled block
+    estimator; VALU-bound block maxima: one FMA per (query block, visible key,
+    dimension)."""
+    w, x = layer.w, layer.x
+    hb = x.heads["bs"]
+    st = hier_prefill_stages(w.topk)
+    ms = time_stage(lambda: dsa.hier_block_sparse_attention(layer.q, layer.k, layer.v, st, heads=hb,
+                                                           out=layer.o), reps)
+    ms_bs = time_stage(layer._bs, reps)
+    n, D, nb = w.seq_len, w.head_dim, (w.seq_len + 63) // 64
+    rows = w.batch * len(hb)
+    qp = dsa.bs_pool(layer.q, hb)
+    ms_p = time_stage(lambda: dsa.hier_prune(qp, layer.k, st, q_heads=w.q_heads, heads=hb, unit_rows=64), reps)
+    fma = rows * sum(min(n, 64 * (a + 1)) for a in range(nb)) * D
+    del qp
+    return {"stages": st, "ms": ms, "block_sparse_ms": ms_bs, "prune_ms": ms_p,
+            "prune_tflops": 2 * fma / (ms_p * 1e-3) / 1e12,
+            "prune_frac_f32_vector_peak": 2 * fma / (ms_p * 1e-3) / 1e12 / PEAK_F32_TFLOPS}
 
 
 def stage_bytes(w, x, idx):
@@ -684,6 +737,8 @@ def run_layer(w, steps, warmup, with_cpu, cpu_full=False, after_prefill=True, cp
         res["bs_select_roofline"] = bs_select_roofline(w, x, st["bs_select_ms"])
     if w.dtype == "bf16" and after_prefill:
         res["after_prefill"] = kv_retention_timing(layer, reps=3)
+    if w.dtype == "bf16" and x.heads["bs"] and w.seq_len <= 32768:
+        res["hier_prefill"] = hier_prefill_timing(layer, reps=3)
     if with_cpu:
         log(f"[bench] {w.name}: cpu baseline (oracle, {'whole layer' if cpu_full else 'bounded sample'})")
         res["cpu_baseline"] = cpu_baseline(layer, idx, f_total, seconds=cpu_seconds, full=cpu_full)
@@ -723,7 +778,7 @@ def layer_record(r):
                        for k, v in r["stages_hbm"].items()},
         "roofline": r.get("roofline"),
     }
-    for key in ("bs_select_roofline", "after_prefill", "ms_per_layer_one_stream", "one_launch"):
+    for key in ("bs_select_roofline", "after_prefill", "hier_prefill", "ms_per_layer_one_stream", "one_launch"):
         if r.get(key) is not None:
             out[key] = r[key]
     if r["dtype"] == "bf16":

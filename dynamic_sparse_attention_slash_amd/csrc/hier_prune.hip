@@ -98,6 +98,76 @@ __global__ __launch_bounds__(PR_TILE) void prune_blockmax_kernel(PruneArgs a) {
   }
 }
 
+// Decode rows (one query vector per head that sees the whole cache, bf16 q
+// and k): the heads of a kv group
+// share one pass over K. A work-group (four waves, 64 keys each) takes one
+// (batch, kv group, 256-key tile); for up to 16 heads at a time the scores
+// are one MFMA block per 16 keys, S^T = Q K^T (A = 16 query heads x 32 dims,
+// B = 32 dims x 16 keys, both read straight from memory: lane l holds 8 dims
+// of head / key l % 16), four MFMAs over the head dimension. In the output a
+// lane holds four heads' scores of one key; the block maximum is a per-lane
+// maximum over the four 16-key tiles and then over the 16 key lanes. bf16
+// products are exact in fp32, so this is the fp32 dot product up to the order
+// of its additions.
+template <int D>
+__global__ __launch_bounds__(PR_TILE) void prune_decode_blockmax_kernel(PruneArgs a) {
+  constexpr int DS = D / 32;
+  const int32_t ng = a.wo.n_groups;
+  const int32_t item = blockIdx.x;
+  const int32_t tile = item % a.ntiles, bg = item / a.ntiles;
+  const int32_t b = bg / ng, g = bg - b * ng;
+  const int32_t lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
+  const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+  const int32_t blk = tile * (PR_TILE / 64) + wave;
+  if (blk * 64 >= a.n) return;
+  const int32_t g0 = a.wo.gstart[g], gsize = a.wo.gstart[g + 1] - g0;
+  const int32_t kvh = a.hm.h[a.wo.order[g0]] / (a.hm.q_heads / a.hm.kv_heads);
+  const uint16_t* ks = static_cast<const uint16_t*>(a.k) + ((size_t)b * a.hm.kv_heads + kvh) * (size_t)a.n * D;
+  // B operands of the block's four 16-key tiles (keys past the end read the
+  // last key; their scores are masked)
+  u32x4 kop[4][DS];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int32_t key = min(blk * 64 + 16 * t + l16, a.n - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(ks + (size_t)key * D + 8 * grp);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) kop[t][s] = src[4 * s];
+  }
+  const uint16_t* qbase = static_cast<const uint16_t*>(a.qu);
+  for (int32_t h0 = 0; h0 < gsize; h0 += 16) {
+    // A operand: head h0 + l16 of the group (a lane past the group reads its
+    // first head; its rows are not written)
+    const int32_t t_head = a.wo.order[g0 + min(h0 + l16, gsize - 1)];
+    const size_t qrow = a.qu_full ? (size_t)b * a.hm.q_heads + a.hm.h[t_head] : (size_t)b * a.hm.n + t_head;
+    const u32x4* qsrc = reinterpret_cast<const u32x4*>(qbase + qrow * D + 8 * grp);
+    u32x4 qop[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qop[s] = qsrc[4 * s];
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) acc = mfma_bf16(qop[s], kop[t][s], acc);
+      const bool ok = blk * 64 + 16 * t + l16 < a.n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], ok ? acc[i] * a.scale : -INFINITY);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) mx[i] = xor_max(mx[i], m);
+    }
+    if (l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t hh = h0 + 4 * grp + i;
+        if (hh < gsize) a.fine[((size_t)b * a.hm.n + a.wo.order[g0 + hh]) * a.nbf + blk] = mx[i];
+      }
+    }
+  }
+}
+
 // order-preserving key of an fp32 score: NaN ranks as -inf, -0 as +0
 __device__ __forceinline__ uint32_t pr_score_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -229,7 +299,14 @@ hipError_t launch_prune(PruneArgs a, hipStream_t s) {
                      : (d64 ? prune_blockmax_kernel<uint16_t, float, 64> : prune_blockmax_kernel<uint16_t, float, 128>))
                : (qb ? (d64 ? prune_blockmax_kernel<float, uint16_t, 64> : prune_blockmax_kernel<float, uint16_t, 128>)
                      : (d64 ? prune_blockmax_kernel<float, float, 64> : prune_blockmax_kernel<float, float, 128>));
-  hipLaunchKernelGGL(bm, dim3((unsigned)((long long)a.ntiles * a.rows)), dim3(PR_TILE), 0, s, a);
+  if (a.units == 1 && a.unit_rows == 0 && kb && qb) {
+    // decode rows: one pass over K per kv group
+    auto dk = d64 ? prune_decode_blockmax_kernel<64> : prune_decode_blockmax_kernel<128>;
+    const long long items = (long long)(a.rows / a.hm.n) * a.wo.n_groups * a.ntiles;
+    hipLaunchKernelGGL(dk, dim3((unsigned)items), dim3(PR_TILE), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(bm, dim3((unsigned)((long long)a.ntiles * a.rows)), dim3(PR_TILE), 0, s, a);
+  }
   hipLaunchKernelGGL(prune_select_kernel, dim3(a.units, a.rows), dim3(PR_THREADS), 0, s, a);
   return hipGetLastError();
 }
