@@ -50,7 +50,10 @@ WorkOrder make_work_order(const HeadMap& hm, const int8_t* kind);
 // groups and unit positions (whose costs differ). A tail shorter than NUM_XCD
 // chunks keeps the identity mapping.
 constexpr int32_t NUM_XCD = 8;
-constexpr int32_t XCD_CHUNK = 32;
+#ifndef DSA_XCD_CHUNK
+#define DSA_XCD_CHUNK 32
+#endif
+constexpr int32_t XCD_CHUNK = DSA_XCD_CHUNK;
 __device__ __forceinline__ void work_item(const HeadMap& hm, const WorkOrder& wo, int32_t units,
                                           int32_t& row, int32_t& unit) {
   const int32_t N = gridDim.x, i = blockIdx.x;

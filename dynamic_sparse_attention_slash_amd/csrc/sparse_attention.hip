@@ -76,6 +76,7 @@ struct BlockRanges {
 };
 struct StreamRanges {
   int32_t a, init_blocks, local_blocks, t, n;
+  __device__ void stage_into(int32_t*) {}  // closed form: nothing staged
   __device__ bool next(int32_t& lo, int32_t& hi) {
     int32_t sink_end = min(init_blocks, a + 1);
     if (t == 0) {
@@ -729,35 +730,6 @@ struct BlockRangesStaged {
     return false;
   }
 };
-// Any of the three patterns behind one interface (the mixed-layer launch):
-// kind is the pattern of the work item's head, uniform over the work-group.
-// list holds the interval pairs (vertical-slash) or block ids (block-sparse);
-// the streaming window is closed-form. The per-pattern sources do the work.
-struct MixedRanges {
-  StagedList list;
-  int32_t kind, n_items, t, r0, n, init_blocks, local_blocks;
-  __device__ void stage_into(int32_t* buf) { list.buf = buf; }
-  __device__ bool next(int32_t& lo, int32_t& hi) {
-    bool r;
-    if (kind == PAT_VS) {
-      VsRangesStaged g{list, n_items, t, r0, n};
-      r = g.next(lo, hi);
-      list = g.iv;
-      t = g.t;
-    } else if (kind == PAT_BS) {
-      BlockRangesStaged g{list, n_items, t, n};
-      r = g.next(lo, hi);
-      list = g.sel;
-      t = g.t;
-    } else {
-      StreamRanges g{r0 / BLOCK, init_blocks, local_blocks, t, n};
-      r = g.next(lo, hi);
-      t = g.t;
-    }
-    return r;
-  }
-};
-
 constexpr int SB_WAVES = 2;
 constexpr int32_t SB1_CAP = 512;       // descriptors per refill
 constexpr int32_t SB1_COLS = 1024;     // column-list entries staged per refill
@@ -816,7 +788,25 @@ __device__ int32_t fill_single(DescGen<R>& gen, Desc* d, int32_t* lcols, int32_t
   return cnt;
 }
 
-template <int D, class R>
+// LDS of the single-block kernel: one object per head dimension, whatever
+// the key-range source, so that a kernel with several sources (the mixed
+// layer) holds it once.
+template <int D>
+struct SingleLds {
+  __align__(16) char ring0[TileLds<D>::HALF];
+  __align__(16) char ring1[TileLds<D>::HALF];
+  Desc desc[SB1_CAP];
+  int32_t lcols[SB1_COLS];
+};
+template <int D>
+__device__ __forceinline__ SingleLds<D>& single_lds() {
+  __shared__ SingleLds<D> lds;
+  return lds;
+}
+
+// SHARED: the LDS comes from single_lds (a kernel with several range
+// sources); otherwise it is declared here.
+template <int D, class R, bool SHARED = false>
 __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* __restrict__ ks,
                               const uint16_t* __restrict__ vs, uint16_t* __restrict__ os,
                               int32_t n, int32_t r0, float scale_log2, DescGen<R> gen) {
@@ -824,10 +814,26 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
   constexpr int DS = D / 32;
   constexpr int DB = D / 16;
   constexpr int NTH = 64 * SB_WAVES;
-  __shared__ __align__(16) char ring0[L::HALF];
-  __shared__ __align__(16) char ring1[L::HALF];
-  __shared__ Desc desc[SB1_CAP];
-  __shared__ int32_t lcols[SB1_COLS];
+  char* ring0;
+  char* ring1;
+  Desc* desc;
+  int32_t* lcols;
+  if constexpr (SHARED) {
+    SingleLds<D>& lds = single_lds<D>();
+    ring0 = lds.ring0;
+    ring1 = lds.ring1;
+    desc = lds.desc;
+    lcols = lds.lcols;
+  } else {
+    __shared__ __align__(16) char ring0_[L::HALF];
+    __shared__ __align__(16) char ring1_[L::HALF];
+    __shared__ Desc desc_[SB1_CAP];
+    __shared__ int32_t lcols_[SB1_COLS];
+    ring0 = ring0_;
+    ring1 = ring1_;
+    desc = desc_;
+    lcols = lcols_;
+  }
 
   const int32_t tid = threadIdx.x, lane = tid & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1219,11 +1225,11 @@ PANEL_KERNEL void attn_stream_bf16_kernel(AttnArgs a, StreamIndex ix) {
 
 #define SINGLE_KERNEL __global__ __launch_bounds__(64 * SB_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
-template <int D, class R>
+template <int D, class R, bool SHARED = false>
 __device__ __forceinline__ void attend_single_bf16(const AttnArgs& a, int32_t row, int32_t r0, DescGen<R> gen) {
   const size_t qoff = a.hm.q_slab(row, a.seq_len, D);
   const size_t kvoff = a.hm.kv_slab(row, a.seq_len, D);
-  attend_single<D, R>(static_cast<const uint16_t*>(a.q) + qoff, static_cast<const uint16_t*>(a.k) + kvoff,
+  attend_single<D, R, SHARED>(static_cast<const uint16_t*>(a.q) + qoff, static_cast<const uint16_t*>(a.k) + kvoff,
                       static_cast<const uint16_t*>(a.v) + kvoff, static_cast<uint16_t*>(a.o) + qoff,
                       a.seq_len, r0, a.scale_log2, gen);
 }
@@ -1257,7 +1263,9 @@ SINGLE_KERNEL void attn_blocks_single_kernel(AttnArgs a, BlockIndex ix) {
 }
 
 // All heads of a mixed layer in one grid: the work item's head picks its
-// pattern's key set; the attention code is the single-block kernel's.
+// pattern, and each pattern runs the single-block attention with its own
+// key-range source (the per-pattern kernels' sources), sharing one LDS
+// layout.
 template <int D>
 SINGLE_KERNEL void attn_mixed_single_kernel(AttnArgs a, MixedIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
@@ -1266,26 +1274,28 @@ SINGLE_KERNEL void attn_mixed_single_kernel(AttnArgs a, MixedIndex ix) {
   const int32_t r0 = blk * BLOCK;
   const int32_t t = row % a.hm.n, b = row / a.hm.n;
   const int32_t kind = ix.kind[t];
-  const int32_t* src = nullptr;
-  const int32_t* cols = nullptr;
-  int32_t n_items = 0, n_list = 0, n_cols = 0;
   if (kind == PAT_VS) {
     const int32_t prow = b * ix.n_vs + ix.slot[t];
     const size_t cb = (size_t)prow * nb + blk;
-    n_items = max(0, min(ix.vs.n_iv[prow], ix.vs.max_iv));
-    n_list = 2 * n_items;
-    src = ix.vs.iv + (size_t)prow * ix.vs.max_iv * 2;
-    cols = ix.vs.cols + cb * ix.vs.max_cols;
-    n_cols = max(0, min(ix.vs.n_cols[cb], ix.vs.max_cols));
+    const int32_t niv = max(0, min(ix.vs.n_iv[prow], ix.vs.max_iv));
+    VsRangesStaged rg{StagedList{ix.vs.iv + (size_t)prow * ix.vs.max_iv * 2, 2 * niv, nullptr, SB1_COLS, 0, 0,
+                                 (int32_t)threadIdx.x, 64 * SB_WAVES},
+                      niv, 0, r0, a.seq_len};
+    attend_single_bf16<D, VsRangesStaged, true>(a, row, r0,
+                          make_gen(rg, ix.vs.cols + cb * ix.vs.max_cols,
+                                   max(0, min(ix.vs.n_cols[cb], ix.vs.max_cols)), r0, a.seq_len));
   } else if (kind == PAT_BS) {
     const int32_t prow = b * ix.n_bs + ix.slot[t];
     const size_t cb = (size_t)prow * nb + blk;
-    n_items = n_list = max(0, min(ix.bs.n_sel[cb], ix.bs.max_sel));
-    src = ix.bs.sel + cb * ix.bs.max_sel;
+    const int32_t ns = max(0, min(ix.bs.n_sel[cb], ix.bs.max_sel));
+    BlockRangesStaged rg{StagedList{ix.bs.sel + cb * ix.bs.max_sel, ns, nullptr, SB1_COLS, 0, 0,
+                                    (int32_t)threadIdx.x, 64 * SB_WAVES},
+                         ns, 0, a.seq_len};
+    attend_single_bf16<D, BlockRangesStaged, true>(a, row, r0, make_gen(rg, (const int32_t*)nullptr, 0, r0, a.seq_len));
+  } else {
+    StreamRanges rg{blk, ix.st.init_blocks, ix.st.local_blocks, 0, a.seq_len};
+    attend_single_bf16<D, StreamRanges, true>(a, row, r0, make_gen(rg, (const int32_t*)nullptr, 0, r0, a.seq_len));
   }
-  MixedRanges rg{StagedList{src, n_list, nullptr, SB1_COLS, 0, 0, (int32_t)threadIdx.x, 64 * SB_WAVES},
-                 kind, n_items, 0, r0, a.seq_len, ix.st.init_blocks, ix.st.local_blocks};
-  attend_single_bf16<D>(a, row, r0, make_gen(rg, cols, n_cols, r0, a.seq_len));
 }
 
 // grid: rows x query blocks (or x panels of two blocks for the panel kernel)
