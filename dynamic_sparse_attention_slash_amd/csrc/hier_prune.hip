@@ -19,12 +19,15 @@
 //     per head (decode) it streams K once, memory-bound; for many (a query
 //     block each) it is VALU-bound, one FMA per key, dimension and vector.
 //   select: one work-group per query vector runs the stages. A chunk's score
-//     is the largest of its 64-key blocks' maxima (the same quantity). The
-//     keep[s] best of the m candidates are found as the keep[s]-th largest
-//     distinct 64-bit sort key (forced bit | order-preserving score bits |
-//     inverted id), built bit by bit from block-wide counts; the kept chunks
-//     are compacted in ascending id order, and their sub-chunks become the
-//     next stage's candidates in ascending order.
+//     is the largest of its 64-key blocks' maxima (the same quantity), taken
+//     over all (candidate, block) pairs in parallel with an LDS maximum on
+//     order-preserving keys. Each candidate gets a distinct 64-bit rank key
+//     (forced bit | score key | inverted id); the keep[s] best are those with
+//     fewer than keep[s] keys above them (one candidate per thread, up to 256
+//     candidates) or at least the keep[s]-th largest key, found bit by bit
+//     from block-wide counts; the kept chunks are compacted in ascending id
+//     order, and their sub-chunks become the next stage's candidates in
+//     ascending order.
 // The chunk lists of a decode row expand to key lists for the sparse decode.
 #include "kernels.hpp"
 
@@ -168,6 +171,79 @@ __global__ __launch_bounds__(PR_TILE) void prune_decode_blockmax_kernel(PruneArg
   }
 }
 
+// Pooled query blocks (units of 64 rows, fp32) against bf16 keys: one wave
+// per (row, 64-unit tile, 64-key block c), on the MFMA. Unit u sees the whole
+// block c when c <= u (keys below n), none of it otherwise. The fp32 unit
+// vector is split into bf16 hi + lo (x - hi - lo below 2^-17 |x|) and both
+// halves are multiplied with the bf16 keys (exact products, fp32
+// accumulation): S = Qu K^T as A = 16 units x 32 dims, B = 32 dims x 16 keys,
+// two MFMAs per k-step. A lane then holds four units' scores of one key; the
+// block maximum is a per-lane maximum over the block's four 16-key tiles and
+// then over the 16 key lanes.
+template <int D>
+__global__ __launch_bounds__(64) void prune_prefill_blockmax_kernel(PruneArgs a) {
+  constexpr int DS = D / 32;
+  const int32_t c = blockIdx.x, ut = blockIdx.y, row = blockIdx.z;
+  if (c > 64 * ut + 63) return;  // no unit of the tile sees this block
+  const int32_t lane = threadIdx.x, l16 = lane & 15, grp = lane >> 4;
+  const uint16_t* ks = static_cast<const uint16_t*>(a.k) + a.hm.kv_slab(row, a.n, D);
+  u32x4 kop[4][DS];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int32_t key = min(c * 64 + 16 * t + l16, a.n - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(ks + (size_t)key * D + 8 * grp);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) kop[t][s] = src[4 * s];
+  }
+  const float* qrow = static_cast<const float*>(a.qu) + (size_t)row * a.units * D;
+  float* out = a.fine + (size_t)row * a.units * a.nbf + c;
+#pragma unroll 1
+  for (int ub = 0; ub < 4; ++ub) {
+    const int32_t u0 = 64 * ut + 16 * ub;
+    if (u0 >= a.units || u0 + 15 < c) continue;  // units past the end, or all before block c
+    // A operands: unit u0 + l16, dims 8 grp + 32 s .. + 7, split into hi / lo
+    const float* qv = qrow + (size_t)min(u0 + l16, a.units - 1) * D + 8 * grp;
+    u32x4 ah[DS], al[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(qv + 32 * s);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(qv + 32 * s + 4);
+      const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+        ah[s][e] = h;
+        al[s][e] = pack_bf16x2(x[2 * e] - __uint_as_float(h << 16), x[2 * e + 1] - __uint_as_float(h & 0xffff0000u));
+      }
+    }
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        acc = mfma_bf16(ah[s], kop[t][s], acc);
+        acc = mfma_bf16(al[s], kop[t][s], acc);
+      }
+      const bool ok = c * 64 + 16 * t + l16 < a.n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], ok ? acc[i] * a.scale : -INFINITY);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) mx[i] = xor_max(mx[i], m);
+    }
+    if (l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t u = u0 + 4 * grp + i;
+        if (u < a.units && c <= u) out[(size_t)u * a.nbf] = mx[i];
+      }
+    }
+  }
+}
+
 // order-preserving key of an fp32 score: NaN ranks as -inf, -0 as +0
 __device__ __forceinline__ uint32_t pr_score_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -206,10 +282,14 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t& excl, uint3
   return buf[PR_THREADS - 1];
 }
 
+// CAP: candidates one stage may hold (the host picks the smallest instance
+// that fits the stage list, so small lists leave room for more work-groups).
+template <int CAP>
 __global__ __launch_bounds__(PR_THREADS) void prune_select_kernel(PruneArgs a) {
-  __shared__ uint64_t key[PR_MAX_CAND];
-  __shared__ int32_t cid[PR_MAX_CAND];
-  __shared__ int32_t kept[PR_MAX_CAND];
+  __shared__ uint64_t key[CAP];
+  __shared__ uint32_t sk[CAP];  // a candidate's score key, then its kept flag
+  __shared__ int32_t cid[CAP];
+  __shared__ int32_t kept[CAP];
   __shared__ uint32_t buf[PR_THREADS];
   __shared__ uint32_t red[PR_THREADS / 64];
   const int32_t u = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
@@ -223,35 +303,51 @@ __global__ __launch_bounds__(PR_THREADS) void prune_select_kernel(PruneArgs a) {
     const int32_t cb = a.chunk_blocks[s];
     const int32_t forced = (nvis - 1) / cb;
     __syncthreads();
-    for (int32_t i = tid; i < m; i += PR_THREADS) {
-      const int32_t x = cid[i];
-      const int32_t b0 = x * cb, b1 = min(nvis, b0 + cb);
-      float best = -INFINITY;
-      for (int32_t b = b0; b < b1; ++b) best = fmaxf(best, fm[b]);
-      key[i] = x == forced ? ~0ull
-                           : ((uint64_t)pr_score_key(best) << 31) | (uint64_t)(0x7fffffff - x);
+    for (int32_t i = tid; i < m; i += PR_THREADS) sk[i] = 0u;  // below every score key
+    __syncthreads();
+    // a candidate's score is its largest block maximum: every (candidate,
+    // block) pair in parallel (consecutive pairs read consecutive blocks),
+    // combined by an LDS maximum on order-preserving keys
+    for (int32_t p = tid; p < m * cb; p += PR_THREADS) {
+      const int32_t i = p / cb, b = cid[i] * cb + (p - i * cb);
+      if (b < nvis) atomicMax(&sk[i], pr_score_key(fm[b]));
     }
     __syncthreads();
+    for (int32_t i = tid; i < m; i += PR_THREADS)
+      key[i] = cid[i] == forced ? ~0ull : ((uint64_t)sk[i] << 31) | (uint64_t)(0x7fffffff - cid[i]);
+    __syncthreads();
     const int32_t keep = min(a.keep[s], m);
-    // the keep-th largest key: largest T with #{key >= T} >= keep
-    uint64_t T = 0;
-    if (keep < m) {
+    if (keep >= m) {
+      for (int32_t i = tid; i < m; i += PR_THREADS) sk[i] = 1u;
+    } else if (m <= PR_THREADS) {
+      // one candidate per thread: kept iff fewer than keep keys rank above it
+      if (tid < m) {
+        const uint64_t kt = key[tid];
+        int32_t r = 0;
+        for (int32_t j = 0; j < m; ++j) r += key[j] > kt;
+        sk[tid] = r < keep ? 1u : 0u;
+      }
+    } else {
+      // the keep-th largest key: largest T with #{key >= T} >= keep
+      uint64_t T = 0;
       for (int bit = 63; bit >= 0; --bit) {
         const uint64_t t2 = T | (1ull << bit);
         uint32_t c = 0;
         for (int32_t i = tid; i < m; i += PR_THREADS) c += key[i] >= t2;
         if (block_sum(c, red) >= (uint32_t)keep) T = t2;
       }
+      for (int32_t i = tid; i < m; i += PR_THREADS) sk[i] = key[i] >= T ? 1u : 0u;
     }
+    __syncthreads();
     // compact the kept candidates in ascending order (each thread a run)
     const int32_t per = (m + PR_THREADS - 1) / PR_THREADS;
     const int32_t i0 = min(m, tid * per), i1 = min(m, i0 + per);
     uint32_t c = 0;
-    for (int32_t i = i0; i < i1; ++i) c += key[i] >= T;
+    for (int32_t i = i0; i < i1; ++i) c += sk[i];
     uint32_t pos;
     block_scan(c, pos, buf);
     for (int32_t i = i0; i < i1; ++i)
-      if (key[i] >= T) kept[pos++] = cid[i];
+      if (sk[i]) kept[pos++] = cid[i];
     nk = keep;
     __syncthreads();
     if (s + 1 < a.n_stages) {
@@ -299,7 +395,11 @@ hipError_t launch_prune(PruneArgs a, hipStream_t s) {
                      : (d64 ? prune_blockmax_kernel<uint16_t, float, 64> : prune_blockmax_kernel<uint16_t, float, 128>))
                : (qb ? (d64 ? prune_blockmax_kernel<float, uint16_t, 64> : prune_blockmax_kernel<float, uint16_t, 128>)
                      : (d64 ? prune_blockmax_kernel<float, float, 64> : prune_blockmax_kernel<float, float, 128>));
-  if (a.units == 1 && a.unit_rows == 0 && kb && qb) {
+  if (a.unit_rows == BLOCK && kb && !qb && !a.qu_full) {
+    // pooled query blocks against bf16 keys: block maxima on the MFMA
+    auto pk = d64 ? prune_prefill_blockmax_kernel<64> : prune_prefill_blockmax_kernel<128>;
+    hipLaunchKernelGGL(pk, dim3(a.nbf, (a.units + 63) / 64, a.rows), dim3(64), 0, s, a);
+  } else if (a.units == 1 && a.unit_rows == 0 && kb && qb) {
     // decode rows: one pass over K per kv group
     auto dk = d64 ? prune_decode_blockmax_kernel<64> : prune_decode_blockmax_kernel<128>;
     const long long items = (long long)(a.rows / a.hm.n) * a.wo.n_groups * a.ntiles;
@@ -307,7 +407,14 @@ hipError_t launch_prune(PruneArgs a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL(bm, dim3((unsigned)((long long)a.ntiles * a.rows)), dim3(PR_TILE), 0, s, a);
   }
-  hipLaunchKernelGGL(prune_select_kernel, dim3(a.units, a.rows), dim3(PR_THREADS), 0, s, a);
+  // the largest candidate count of any stage picks the select's LDS size
+  int64_t cand = (a.nbf + a.chunk_blocks[0] - 1) / a.chunk_blocks[0];
+  for (int32_t st = 1; st < a.n_stages; ++st) {
+    const int64_t c2 = (int64_t)a.keep[st - 1] * (a.chunk_blocks[st - 1] / a.chunk_blocks[st]);
+    cand = c2 > cand ? c2 : cand;
+  }
+  hipLaunchKernelGGL(cand <= 1024 ? prune_select_kernel<1024> : prune_select_kernel<PR_MAX_CAND>,
+                     dim3(a.units, a.rows), dim3(PR_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
