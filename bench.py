@@ -438,8 +438,10 @@ def kv_retention_timing(layer, reps):
 def hier_prefill_timing(layer, reps):
     """The block-sparse heads of a layer with the hierarchical pruning as their
     block estimator (same key-block budget), beside the mean-pooled block
-    estimator; VALU-bound block maxima: one FMA per (query block, visible key,
-    dimension)."""
+    estimator. The pruning's block maxima score every visible key against
+    every query block's pooled row: 2·D FLOP per pair, two bf16 MFMA products
+    per fp32 product (the pooled row's hi and lo halves), so its peak is half
+    the bf16 peak."""
     w, x = layer.w, layer.x
     hb = x.heads["bs"]
     st = hier_prefill_stages(w.topk)
@@ -453,8 +455,9 @@ def hier_prefill_timing(layer, reps):
     fma = rows * sum(min(n, 64 * (a + 1)) for a in range(nb)) * D
     del qp
     return {"stages": st, "ms": ms, "block_sparse_ms": ms_bs, "prune_ms": ms_p,
-            "prune_tflops": 2 * fma / (ms_p * 1e-3) / 1e12,
-            "prune_frac_f32_vector_peak": 2 * fma / (ms_p * 1e-3) / 1e12 / PEAK_F32_TFLOPS}
+            "prune_flops": 2 * fma, "prune_tflops": 2 * fma / (ms_p * 1e-3) / 1e12,
+            "prune_peak_tflops": PEAK_BF16_TFLOPS / 2,
+            "prune_frac": 2 * fma / (ms_p * 1e-3) / 1e12 / (PEAK_BF16_TFLOPS / 2)}
 
 
 def stage_bytes(w, x, idx):
