@@ -115,6 +115,8 @@ class ClockSampler:
     """Samples the GPU's current shader clock with rocm-smi (a child process)
     while the timed steps run."""
 
+    enabled = True  # --no-clock: no child processes (e.g. under a counter profiler)
+
     def __init__(self, period=0.3):
         self.period, self.samples, self._stop = period, [], threading.Event()
         self._thr = None
@@ -136,13 +138,15 @@ class ClockSampler:
             self._stop.wait(self.period)
 
     def __enter__(self):
-        self._thr = threading.Thread(target=self._run, daemon=True)
-        self._thr.start()
+        if ClockSampler.enabled:
+            self._thr = threading.Thread(target=self._run, daemon=True)
+            self._thr.start()
         return self
 
     def __exit__(self, *exc):
         self._stop.set()
-        self._thr.join(timeout=10)
+        if self._thr is not None:
+            self._thr.join(timeout=10)
 
     def summary(self):
         if not self.samples:
@@ -801,10 +805,13 @@ def main():
                          "a comma-separated list, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="do not sample the clock with rocm-smi child processes")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--record", action="store_true",
                     help="with --summarize-pmc: store the summary for --workload in the traffic file")
     args = ap.parse_args()
+    ClockSampler.enabled = not args.no_clock
     if args.summarize_pmc:
         summ = summarize_pmc(args.summarize_pmc, args.copy_probe or 1024)
         summ["workload"] = args.workload
