@@ -1071,3 +1071,42 @@ def test_hier_decode_1m_every_head():
             assert np.array_equal(sel_h[h, 0, : int(ns_h[h, 0])], res["chunks"]), h
             check_attention(oh[0, h][None], res["out"][None], f"1M hier decode h{h}")
         del kh, vh
+
+
+def test_hier_prefill_qwen2_32k_b4_sampled():
+    """The pruning as block estimator on the Qwen2-shaped 32K batch-4 layer's
+    block-sparse heads at full size, with the benchmark's stages: every
+    (batch, head)'s chunk ids bit-exact against the oracle's stages on the
+    GPU's block maxima for sampled query blocks, block maxima of those blocks
+    against float64, and their attention against the oracle."""
+    w = synthetic.BY_NAME["qwen2_7b_32k_b4_mixed_bf16"]
+    say(f"hier prefill {w.name}")
+    x = synthetic.make_inputs(w, device="cuda")
+    hb = x.heads["bs"]
+    st = [(1024, max(1, w.topk // 8)), (256, max(2, w.topk // 2)), (64, w.topk)]
+    o = dsa.hier_block_sparse_attention(x.q, x.k, x.v, st, heads=hb)
+    qp = dsa.bs_pool(x.q, hb)
+    sel, n_sel, bm = dsa.hier_prune(qp, x.k, st, q_heads=w.q_heads, heads=hb, unit_rows=BLK, return_block_max=True)
+    torch.cuda.synchronize()
+    n, D = w.seq_len, w.head_dim
+    nb = O.num_blocks(n)
+    sc = 1 / math.sqrt(D)
+    rng = np.random.default_rng(31)
+    for b in range(w.batch):
+        for t, h in enumerate(hb):
+            r = b * len(hb) + t
+            g = kvh(h, w.q_heads, w.kv_heads)
+            kh, vh = host64(x.k[b, g]), host64(x.v[b, g])
+            qh = host64(x.q[b, h])
+            qpo = O.mean_pool(qh)
+            blocks = sorted(set([0, nb - 1] + rng.choice(nb, 3, replace=False).tolist()))
+            bm_r = bm[r].cpu().numpy()
+            for a in blocks:
+                limit = min(n, BLK * (a + 1))
+                _check_block_max(bm_r[a], qpo[a], kh, limit, sc, (b, h, a))
+                want = O.hier_prune(qpo[a], kh, limit, st, sc, fine_max=bm_r[a, : a + 1])
+                assert int(n_sel[r, a]) == len(want), (b, h, a)
+                assert np.array_equal(sel[r, a, : len(want)].cpu().numpy(), want), (b, h, a)
+                rows = np.arange(a * BLK, min(n, (a + 1) * BLK))
+                ref = O.masked_attention(qh[rows], rows, O.blocks_to_keys(want, n), kh, vh, sc)
+                check_attention(host64(o[b, h, a * BLK: a * BLK + len(rows)]), ref, f"hier prefill b{b} h{h} a{a}")
