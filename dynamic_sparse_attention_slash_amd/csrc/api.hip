@@ -389,7 +389,9 @@ dsa_status decode_call(const void* q, const void* k, const void* v, void* o, con
   if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
   const int32_t rows = shape->batch * hm.n;
   if (rows == 0) return DSA_OK;  // no decode row: nothing read or written
-  if (!q || !k || !v || !o || (keys && !n_keys)) return DSA_ERR_INVALID_ARG;
+  // an empty cache reads no key or value (the pointers of empty tensors may be NULL)
+  const bool has_kv = shape->seq_len > 0;
+  if (!q || !o || (has_kv && (!k || !v)) || (keys && !n_keys)) return DSA_ERR_INVALID_ARG;
   const size_t need = dsa_sparse_decode_workspace_bytes(shape, keys ? max_keys : -1, hm.n);
   if (static_scratch) {
     // checked before the scratch is looked up: a refused call makes no HIP call
@@ -827,29 +829,33 @@ dsa_status dsa_hier_sparse_decode(const void* q, const void* k, const void* v, v
   HeadMap hm;
   if ((st = make_map(shape->q_heads, shape->kv_heads, heads, n_heads, hm)) != DSA_OK) return st;
   const int32_t rows = shape->batch * hm.n;
-  if (rows == 0 || shape->seq_len == 0) return DSA_OK;  // no row, or nothing to prune (no key)
-  if (!q || !k || !v || !o) return DSA_ERR_INVALID_ARG;
+  if (rows == 0) return DSA_OK;  // no decode row: nothing read or written
+  if (!q || !o || (shape->seq_len > 0 && (!k || !v))) return DSA_ERR_INVALID_ARG;
   const size_t need = hier_layout(shape, rows, stages, true, nullptr, nullptr);
   if (workspace_bytes < need || (need && !workspace)) return DSA_ERR_WORKSPACE;
   HierWork w;
   hier_layout(shape, rows, stages, true, workspace, &w);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const PruneArgs pa = prune_args(q, shape->dtype, 1, 1, 0, k, shape, stages, scale, hm, w.fine, w.sel, w.n_sel);
-  hipError_t e = launch_prune(pa, s);
   const int32_t c = stages->chunk[stages->n_stages - 1];
-  if (e == hipSuccess)
-    e = launch_chunks_to_keys(w.sel, w.n_sel, rows, pa.max_sel, c, shape->seq_len, w.keys, w.n_keys, s);
-  if (e == hipSuccess) {
-    DecodeArgs a;
-    a.q = q; a.k = k; a.v = v; a.o = o;
-    a.n = shape->seq_len; a.head_dim = shape->head_dim; a.dtype = shape->dtype; a.rows = rows;
-    a.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
-    a.hm = hm;
-    a.wo = make_work_order(hm);
+  hipError_t e = hipSuccess;
+  DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.n = shape->seq_len; a.head_dim = shape->head_dim; a.dtype = shape->dtype; a.rows = rows;
+  a.scale_log2 = eff_scale(scale, shape->head_dim) * LOG2E;
+  a.hm = hm;
+  a.wo = make_work_order(hm);
+  a.part = w.part;
+  if (shape->seq_len == 0) {
+    // an empty cache: nothing to prune, the rows come out as zeros (as in dsa_sparse_decode)
+    a.keys = nullptr; a.max_keys = 0; a.n_keys = nullptr;
+  } else {
+    e = launch_prune(pa, s);
+    if (e == hipSuccess)
+      e = launch_chunks_to_keys(w.sel, w.n_sel, rows, pa.max_sel, c, shape->seq_len, w.keys, w.n_keys, s);
     a.keys = w.keys; a.max_keys = pa.max_sel * c; a.n_keys = w.n_keys;
-    a.part = w.part;
-    e = launch_decode(a, s);
   }
+  if (e == hipSuccess) e = launch_decode(a, s);
   return hip_status(e);
 }
 

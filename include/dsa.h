@@ -308,7 +308,9 @@ size_t dsa_kv_retention_workspace_bytes(const dsa_shape* shape, int32_t keep,
  * with K(row) = keys[row][0 .. n_keys[row]) (cache positions; entries are
  * clamped into [0, seq_len) and should be distinct), or every cached key when
  * keys is NULL. The decode row comes after the whole cache, so no causal cut
- * applies; an empty key set gives zeros. Layout: q and o are device
+ * applies; an empty key set gives zeros, and so does an empty cache
+ * (seq_len 0: every list counts as empty, and k and v, which are not read,
+ * may be NULL). Layout: q and o are device
  * [batch][q_heads][head_dim] (one row per head), k and v the cache as
  * [batch][kv_heads][seq_len][head_dim] with seq_len = cached keys; keys
  * device int32 [batch * n_heads][max_keys], n_keys device int32
@@ -410,7 +412,8 @@ dsa_status dsa_chunks_to_keys(const int32_t* sel, const int32_t* n_sel, int32_t 
  * decoding; Novita §2: decoding attends only to the kept entries]: each listed
  * head's new row (q, o as in dsa_sparse_decode) is the query vector, limit =
  * seq_len; the stages select chunks, and the row attends over their keys with
- * the softmax of dsa_sparse_decode. workspace: at least
+ * the softmax of dsa_sparse_decode (an empty cache gives zero rows, as there).
+ * workspace: at least
  * dsa_hier_sparse_decode_workspace_bytes(shape, stages, n_heads) bytes. */
 dsa_status dsa_hier_sparse_decode(const void* q, const void* k, const void* v, void* o,
                                   const dsa_shape* shape, const dsa_prune_stages* stages, float scale,

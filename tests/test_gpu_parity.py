@@ -98,6 +98,14 @@ def test_empty_calls_through_the_binding():
     qd = torch.zeros(0, 4, 64, dtype=torch.bfloat16, device="cuda")
     kd = torch.zeros(0, 2, 100, 64, dtype=torch.bfloat16, device="cuda")
     assert dsa.sparse_decode(qd, kd, kd).numel() == 0
+    assert dsa.hier_sparse_decode(qd, kd, kd, [(128, 1), (64, 1)]).numel() == 0
+    # an empty cache: every decode row comes out as zeros
+    q1 = torch.randn(2, 4, 64, device="cuda").to(torch.bfloat16)
+    k0 = torch.zeros(2, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    for out in (dsa.sparse_decode(q1, k0, k0, out=torch.full_like(q1, 3.0)),
+                dsa.hier_sparse_decode(q1, k0, k0, [(128, 1), (64, 1)], out=torch.full_like(q1, 3.0))):
+        torch.cuda.synchronize()
+        assert not out.float().any()
     torch.cuda.synchronize()
 
 
