@@ -985,6 +985,7 @@ def test_hier_prune_stage_call(n, D, dt, qdt, stages, unit_rows):
 
 @pytest.mark.parametrize("n,D,dt,stages", [(5000, 128, "bf16", [(1024, 2), (256, 3), (64, 4)]),
                                            (3000, 64, "f32", [(512, 2), (64, 3)]),
+                                           (2000, 64, "bf16", [(512, 2), (128, 3), (64, 5)]),
                                            (100, 128, "bf16", [(128, 1), (64, 2)])])
 def test_hier_sparse_decode(n, D, dt, stages):
     """Decode over pruned keys: the chunks equal the oracle's stages on the
@@ -1019,7 +1020,8 @@ def test_hier_sparse_decode(n, D, dt, stages):
 
 
 @pytest.mark.parametrize("n,D,dt,stages", [(1000, 128, "bf16", [(256, 2), (64, 3)]),
-                                           (64 * 12 + 7, 64, "f32", [(384, 1), (128, 2), (64, 3)])])
+                                           (64 * 12 + 7, 64, "f32", [(384, 1), (128, 2), (64, 3)]),
+                                           (64 * 70 + 9, 64, "bf16", [(1024, 1), (256, 2), (64, 6)])])
 def test_hier_block_sparse_attention(n, D, dt, stages):
     """Prefill heads with the pruning as block estimator: every query block
     against the oracle (blocks chosen by the oracle's stages on the GPU's
