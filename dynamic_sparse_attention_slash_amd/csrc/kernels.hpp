@@ -155,7 +155,8 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t s);
 hipError_t decode_static_scratch(float** ptr, size_t* bytes);
 
 // ---- top-k (topk.hip) ----
-// scratch of launch_topk_rows (0 when the rows are short enough for one pass)
+// scratch of launch_topk_rows (0 when one work-group per row selects: rows
+// shorter than 64K entries)
 size_t topk_workspace_bytes(int32_t rows, int32_t n, int32_t k);
 hipError_t launch_topk_rows(const float* scores, int32_t rows, int32_t n, int32_t k,
                             int32_t forced, int32_t* out, void* ws, hipStream_t s);

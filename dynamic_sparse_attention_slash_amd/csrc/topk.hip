@@ -7,19 +7,25 @@
 // -inf. Output indices are ascending.
 //
 // Method: scores map to order-preserving 32-bit keys (the forced entry gets
-// the maximum key, which no canonical float reaches). Whole rows and the
-// block lists first try a two-read select over 12-bit key bins (described at
-// select_bins below); rows it cannot take, and the chunk and merge passes of
-// long rows, use the radix select: a 4-pass MSB-first radix
-// select (8 bits per pass) finds the k-th largest key T and how many entries
-// equal to T must be kept (need_eq). Each pass counts digits into LDS
-// histograms, one copy per wave and lane group so that the few bins a float
-// exponent range fills are not hit by a whole wave at once; the bin holding
-// the k-th largest key comes from a parallel suffix scan over the 256 bins.
-// A compaction pass then walks the entries in index order, each wave owning
-// one contiguous segment (which it also visits in the counting passes): an entry is kept when key > T, or key == T and fewer
-// than need_eq equal keys precede it. Ballot prefix counts give each kept
-// entry its output slot, so the result comes out ascending with no sort.
+// the maximum key, which no canonical float reaches). Rows shorter than 64K
+// entries and the block lists are selected by one work-group each, which
+// first tries a two-read select over 12-bit key bins (described at
+// select_bins below); rows it cannot take use the radix select: a 4-pass
+// MSB-first radix select (8 bits per pass) finds the k-th largest key T and
+// how many entries equal to T must be kept (need_eq). Each pass counts
+// digits into LDS histograms, one copy per wave and lane group so that the
+// few bins a float exponent range fills are not hit by a whole wave at once;
+// the bin holding the k-th largest key comes from a parallel suffix scan over
+// the 256 bins. A compaction pass then walks the entries in index order, each
+// wave owning one contiguous segment (which it also visits in the counting
+// passes): an entry is kept when key > T, or key == T and fewer than need_eq
+// equal keys precede it. Ballot prefix counts give each kept entry its output
+// slot, so the result comes out ascending with no sort.
+// Rows of 64K entries or more spread the same steps over many work-groups
+// (the row-parallel passes further down): row histograms in global memory
+// give T 12 + 12 + 8 bits at a time, then every 16K-entry chunk of the row
+// counts and writes its kept entries at offsets summed from the earlier
+// chunks' counts.
 #include "kernels.hpp"
 
 namespace dsa {
@@ -72,29 +78,6 @@ struct GlobalSeg {
     }
   }
   __device__ __forceinline__ int32_t index(int32_t j) const { return base + s0 + 64 * j + lane; }
-};
-// Candidates given as (key, index) lists, keys already mapped.
-struct KeySeg {
-  const uint32_t* keys; const int32_t* idx; int32_t s0, s1, trips, lane;
-  template <class F>
-  __device__ __forceinline__ void visit(F&& f) const {
-    for (int32_t j0 = 0; j0 < trips; j0 += VISIT_LOADS) {
-      uint32_t kv[VISIT_LOADS];
-#pragma unroll
-      for (int u = 0; u < VISIT_LOADS; ++u) {
-        const int32_t i = s0 + 64 * (j0 + u) + lane;
-        kv[u] = (j0 + u < trips && i < s1) ? keys[i] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < VISIT_LOADS; ++u) {
-        const int32_t j = j0 + u;
-        if (j >= trips) break;
-        const int32_t i = s0 + 64 * j + lane;
-        f(j, i < s1 ? kv[u] : 0u, i < s1);
-      }
-    }
-  }
-  __device__ __forceinline__ int32_t index(int32_t j) const { return idx[s0 + 64 * j + lane]; }
 };
 // Wave w's segment of m candidates: [w * seg, (w + 1) * seg) clipped to m.
 template <int NW>
@@ -347,18 +330,10 @@ __device__ bool select_bins(RawAt raw_at, KeyOf key_of, IdxAt idx_at, int32_t m,
   return true;
 }
 
-// Rows of up to two 64K chunks: one work-group per row, two-read select
-// (kk up to 8192). The merge pass of longer rows keeps the radix select:
-// there the two-read select measured slower (the merge candidates crowd
-// into few bins).
+// Rows shorter than RP_MIN_N: one work-group per row, two-read select (kk up
+// to 8192), else the radix select.
 union RowTopkShared {
   BinShared<16, 2048, 8192, false> f;
-  SelectShared<16, 2> r;
-};
-// per-chunk pass of long rows: the two-read select for lists of up to 1024
-// entries (with their keys, in 24 KB of LDS), the radix select beyond
-union ChunkTopkShared {
-  BinShared<16, 1024, 1024, true> f;
   SelectShared<16, 2> r;
 };
 constexpr int ROW_WAVES = 16;
@@ -382,63 +357,224 @@ __global__ __launch_bounds__(ROW_WAVES * 64) void topk_rows_kernel(const float* 
   select_topk<ROW_WAVES, 2>(seg, kk, o, nullptr, sh.r);
 }
 
-// Long rows in two passes. Pass 1: every TOPK_CHUNK-long chunk of a row keeps
-// its own top kk (indices and keys, ascending) in the workspace; the row's
-// top kk are among them, since an entry's rank inside its chunk is at most its
-// rank in the row. Pass 2: one work-group per row selects the top kk of the
-// candidates, which lie in index order, so ties and the output order are those
-// of the single pass.
-constexpr int32_t TOPK_CHUNK = 65536;
-__global__ __launch_bounds__(ROW_WAVES * 64) void topk_chunks_kernel(const float* __restrict__ scores,
-                                                                     int32_t n, int32_t kk, int32_t forced,
-                                                                     int32_t* __restrict__ cand_idx,
-                                                                     uint32_t* __restrict__ cand_key) {
-  __shared__ ChunkTopkShared sh;
-  const int32_t c = blockIdx.x, row = blockIdx.y, nch = gridDim.x;
-  const int32_t c0 = c * TOPK_CHUNK, m = min(TOPK_CHUNK, n - c0);
-  const size_t off = ((size_t)row * nch + c) * kk;
-  int32_t* oi = cand_idx + off;
-  uint32_t* ok = cand_key + off;
-  const float* x = scores + (size_t)row * n + c0;
-  const int32_t f = (forced >= c0 && forced < c0 + m) ? forced - c0 : -1;
-  if (kk >= m) {
-    for (int32_t i = threadIdx.x; i < m; i += ROW_WAVES * 64) {
-      oi[i] = c0 + i;
-      ok[i] = i == f ? FORCED_KEY : score_key(x[i]);
+// Long rows, row-parallel: every RP_CHUNK-long chunk of a row is one
+// work-group of each pass.
+//   Passes 1-3 find the row's kk-th largest key K exactly, 12 + 12 + 8 bits at
+//   a time: each pass adds the bins of the keys that share K's bits found so
+//   far to a row histogram, whose suffix scan then gives the next bits of K and
+//   how many keys lie above them.
+//   Pass 4 counts, per chunk, the keys above K (gt) and equal to K (eq).
+//   Pass 5 writes each chunk's kept entries, in index order, straight to the
+//   output: every key above K, and keys equal to K while fewer than
+//   need = kk - (keys above K in the row) of them precede it in the row. The
+//   chunk's first output slot is the earlier chunks' gt plus min(need, their
+//   eq). This is the rank order (larger key, then smaller index) and the
+//   output comes out ascending, as in the other selects.
+constexpr int32_t RP_CHUNK = 16384;
+constexpr int RP_WAVES = 4;
+constexpr int RP_BINS2 = 256;  // last level: key bits 7-0
+
+__host__ __device__ constexpr int32_t rp_chunks(int32_t n) { return (n + RP_CHUNK - 1) / RP_CHUNK; }
+// Rows of at least RP_MIN_N entries take the row-parallel select (measured: at
+// 32K entries one work-group per row is faster, from 64K on the row-parallel
+// passes are)
+constexpr int32_t RP_MIN_N = 65536;
+__host__ __device__ constexpr bool row_parallel(int32_t n, int32_t kk) {
+  return n >= RP_MIN_N && kk < n;
+}
+
+// workspace, per row: the three level histograms and (K, keys above K), then
+// (gt, eq) per chunk and wave
+constexpr int32_t RP_HIST_WORDS = 2 * BINS + RP_BINS2 + 2;
+__host__ __device__ constexpr size_t rp_bytes(int32_t rows, int32_t nch) {
+  return (size_t)rows * ((size_t)RP_HIST_WORDS + 2 * RP_WAVES * (size_t)nch) * sizeof(uint32_t);
+}
+
+// Over an NB-bin histogram h (global), the bin holding the r-th largest entry
+// (1 <= r <= total) and the number of entries in the bins above it, for every
+// thread of the work-group. Thread t owns bins [PER t, PER t + PER).
+template <int NW, int NB>
+__device__ void boundary_bin(const uint32_t* __restrict__ h, uint32_t r, uint32_t* wsum, uint32_t* res,
+                             uint32_t& bin, uint32_t& above) {
+  constexpr int NT = NW * 64, PER = NB / NT;
+  static_assert(PER * NT == NB, "bins per thread");
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t loc[PER], tsum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) { loc[j] = h[PER * tid + j]; tsum += loc[j]; }
+  uint32_t s = tsum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t x = __shfl_down(s, d);
+    if (lane + d < 64) s += x;
+  }
+  if (lane == 0) wsum[wave] = s;
+  __syncthreads();
+  uint32_t higher = s - tsum;
+  for (int v = wave + 1; v < NW; ++v) higher += wsum[v];
+  if (higher < r && higher + tsum >= r) {
+    uint32_t acc = higher;
+    for (int j = PER - 1; j >= 0; --j) {
+      if (acc + loc[j] >= r) { res[0] = (uint32_t)(PER * tid + j); res[1] = acc; break; }
+      acc += loc[j];
     }
-    return;
   }
-  auto raw_at = [&](int32_t i) { return __float_as_uint(x[i]); };
-  auto key_of = [&](int32_t i, uint32_t r) { return i == f ? FORCED_KEY : score_key(__uint_as_float(r)); };
-  auto idx_at = [&](int32_t i) { return c0 + i; };
-  if (select_bins<ROW_WAVES>(raw_at, key_of, idx_at, m, kk, oi, ok, sh.f)) return;
-  GlobalSeg seg{x, f, 0, 0, 0, (int32_t)(threadIdx.x & 63), c0};
-  wave_segment<ROW_WAVES>(m, seg.s0, seg.s1, seg.trips);
-  select_topk<ROW_WAVES, 2>(seg, kk, oi, ok, sh.r);
+  __syncthreads();
+  bin = res[0];
+  above = res[1];
+  __syncthreads();  // res and wsum are reused
 }
 
-__global__ __launch_bounds__(ROW_WAVES * 64) void topk_merge_kernel(const int32_t* __restrict__ cand_idx,
-                                                                    const uint32_t* __restrict__ cand_key,
-                                                                    int32_t n, int32_t nch, int32_t kk,
-                                                                    int32_t* __restrict__ out) {
-  __shared__ SelectShared<ROW_WAVES, 2> sh;
-  const int32_t row = blockIdx.x;
-  const int32_t m_last = n - (nch - 1) * TOPK_CHUNK;
-  const int32_t m = (nch - 1) * kk + min(kk, m_last);  // candidates, contiguous
-  const size_t off = (size_t)row * nch * kk;
+struct RpBound { uint32_t key, above; };  // K, keys above K in the row (passes >= LEVEL)
+
+// K's bits known before pass LEVEL (LEVEL 0: none; 1: bits 31-20; 2: bits 31-8;
+// 3: all) and the count of keys above them.
+template <int LEVEL>
+__device__ RpBound rp_bound(const uint32_t* __restrict__ hr, int32_t kk, uint32_t* wsum, uint32_t* res) {
+  RpBound b{0u, 0u};
+  if (LEVEL >= 1) {
+    uint32_t b0, a0;
+    boundary_bin<RP_WAVES, BINS>(hr, (uint32_t)kk, wsum, res, b0, a0);
+    b.key = b0 << 20;
+    b.above = a0;
+  }
+  if (LEVEL >= 2) {
+    uint32_t b1, a1;
+    boundary_bin<RP_WAVES, BINS>(hr + BINS, (uint32_t)kk - b.above, wsum, res, b1, a1);
+    b.key |= b1 << 8;
+    b.above += a1;
+  }
+  if (LEVEL >= 3) {
+    uint32_t b2, a2;
+    boundary_bin<RP_WAVES, RP_BINS2>(hr + 2 * BINS, (uint32_t)kk - b.above, wsum, res, b2, a2);
+    b.key |= b2;
+    b.above += a2;
+  }
+  return b;
+}
+
+__global__ __launch_bounds__(256) void rp_zero_kernel(uint32_t* __restrict__ p, int32_t words) {
+  for (int32_t i = blockIdx.x * 256 + threadIdx.x; i < words; i += gridDim.x * 256) p[i] = 0u;
+}
+
+// Pass LEVEL + 1 (LEVEL 0, 1, 2): histogram of the next bits of the keys that
+// share K's known bits.
+template <int LEVEL>
+__global__ __launch_bounds__(RP_WAVES * 64) void rp_hist_kernel(const float* __restrict__ scores, int32_t n,
+                                                                 int32_t kk, int32_t forced, uint32_t* __restrict__ ws) {
+  constexpr int NT = RP_WAVES * 64;
+  constexpr int NB = LEVEL == 2 ? RP_BINS2 : BINS;
+  __shared__ uint32_t h[NB];
+  __shared__ uint32_t wsum[RP_WAVES], res[2];
+  const int32_t c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const int32_t c0 = c * RP_CHUNK, m = min(RP_CHUNK, n - c0), f = forced - c0;
+  uint32_t* hr = ws + (size_t)row * RP_HIST_WORDS;
+  const RpBound b = rp_bound<LEVEL>(hr, kk, wsum, res);
+  for (int i = tid; i < NB; i += NT) h[i] = 0u;
+  __syncthreads();
+  const float* x = scores + (size_t)row * n + c0;
+  for (int32_t i0 = 0; i0 < m; i0 += BIN_LOADS * NT) {
+    float v[BIN_LOADS];
+#pragma unroll
+    for (int u = 0; u < BIN_LOADS; ++u) {
+      const int32_t i = i0 + u * NT + tid;
+      v[u] = i < m ? x[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < BIN_LOADS; ++u) {
+      const int32_t i = i0 + u * NT + tid;
+      if (i >= m) continue;
+      const uint32_t key = i == f ? FORCED_KEY : score_key(v[u]);
+      if (LEVEL == 0) atomicAdd(&h[key >> 20], 1u);
+      else if (LEVEL == 1) { if ((key >> 20) == (b.key >> 20)) atomicAdd(&h[(key >> 8) & (BINS - 1)], 1u); }
+      else if ((key >> 8) == (b.key >> 8)) atomicAdd(&h[key & (RP_BINS2 - 1)], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* ho = hr + LEVEL * BINS;
+  for (int i = tid; i < NB; i += NT)
+    if (h[i]) atomicAdd(&ho[i], h[i]);
+}
+
+// K and the number of keys above it, once per row, for passes 4 and 5.
+__global__ __launch_bounds__(RP_WAVES * 64) void rp_bound_kernel(int32_t kk, uint32_t* __restrict__ ws) {
+  __shared__ uint32_t wsum[RP_WAVES], res[2];
+  uint32_t* hr = ws + (size_t)blockIdx.x * RP_HIST_WORDS;
+  const RpBound b = rp_bound<3>(hr, kk, wsum, res);
+  if (threadIdx.x == 0) {
+    hr[2 * BINS + RP_BINS2] = b.key;
+    hr[2 * BINS + RP_BINS2 + 1] = b.above;
+  }
+}
+
+// Pass 4: keys above K and equal to K in each wave's segment of each chunk.
+__global__ __launch_bounds__(RP_WAVES * 64) void rp_count_kernel(const float* __restrict__ scores, int32_t n,
+                                                                  int32_t forced, const uint32_t* __restrict__ ws,
+                                                                  uint32_t* __restrict__ cnt) {
+  const int32_t c = blockIdx.x, row = blockIdx.y, nch = gridDim.x;
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t c0 = c * RP_CHUNK, m = min(RP_CHUNK, n - c0);
+  const uint32_t K = ws[(size_t)row * RP_HIST_WORDS + 2 * BINS + RP_BINS2];
+  GlobalSeg seg{scores + (size_t)row * n + c0, forced - c0, 0, 0, 0, lane, c0};
+  wave_segment<RP_WAVES>(m, seg.s0, seg.s1, seg.trips);
+  uint32_t gt = 0, eq = 0;
+  seg.visit([&](int32_t, uint32_t key, bool valid) {
+    gt += __popcll(__ballot(valid && key > K));
+    eq += __popcll(__ballot(valid && key == K));
+  });
+  if (lane == 0) {
+    uint32_t* cc = cnt + (((size_t)row * nch + c) * RP_WAVES + wave) * 2;
+    cc[0] = gt;
+    cc[1] = eq;
+  }
+}
+
+// Pass 5: each chunk's kept entries to the output, ascending.
+__global__ __launch_bounds__(RP_WAVES * 64) void rp_write_kernel(const float* __restrict__ scores, int32_t n,
+                                                                  int32_t kk, int32_t forced, const uint32_t* __restrict__ ws,
+                                                                  const uint32_t* __restrict__ cnt,
+                                                                  int32_t* __restrict__ out) {
+  constexpr int NT = RP_WAVES * 64;
+  __shared__ uint32_t pre[RP_WAVES][2];
+  const int32_t c = blockIdx.x, row = blockIdx.y, nch = gridDim.x;
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t c0 = c * RP_CHUNK, m = min(RP_CHUNK, n - c0);
+  const uint32_t* hb = ws + (size_t)row * RP_HIST_WORDS + 2 * BINS + RP_BINS2;
+  const uint32_t K = hb[0], need = (uint32_t)kk - hb[1];
+  // keys above K (G) and equal to K (E) in the earlier chunks, and in this
+  // chunk's earlier waves
+  const uint32_t* cr = cnt + (size_t)row * nch * RP_WAVES * 2;
+  uint32_t g = 0, e = 0;
+  for (int32_t j = tid; j < c * RP_WAVES; j += NT) { g += cr[2 * j]; e += cr[2 * j + 1]; }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) { g += __shfl_xor(g, d); e += __shfl_xor(e, d); }
+  if (lane == 0) { pre[wave][0] = g; pre[wave][1] = e; }
+  __syncthreads();
+  uint32_t G = 0, E = 0, gt_before = 0, eq_before = 0;
+  for (int v = 0; v < RP_WAVES; ++v) { G += pre[v][0]; E += pre[v][1]; }
+  for (int v = 0; v < wave; ++v) {
+    gt_before += cr[2 * (c * RP_WAVES + v)];
+    eq_before += cr[2 * (c * RP_WAVES + v) + 1];
+  }
+  GlobalSeg seg{scores + (size_t)row * n + c0, forced - c0, 0, 0, 0, lane, c0};
+  wave_segment<RP_WAVES>(m, seg.s0, seg.s1, seg.trips);
+  uint32_t eq_seen = E + eq_before;  // keys equal to K before this wave's segment
+  uint32_t pos = G + min(need, E) + gt_before + min(need - min(need, E), eq_before);
   int32_t* o = out + (size_t)row * kk;
-  if (kk >= m) {
-    for (int32_t i = threadIdx.x; i < m; i += ROW_WAVES * 64) o[i] = cand_idx[off + i];
-    return;
-  }
-  KeySeg seg{cand_key + off, cand_idx + off, 0, 0, 0, (int32_t)(threadIdx.x & 63)};
-  wave_segment<ROW_WAVES>(m, seg.s0, seg.s1, seg.trips);
-  select_topk<ROW_WAVES, 2>(seg, kk, o, nullptr, sh);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  seg.visit([&](int32_t j, uint32_t key, bool valid) {
+    const bool is_eq = valid && key == K;
+    const uint64_t eq_mask = __ballot(is_eq);
+    const uint32_t eq_rank = eq_seen + __popcll(eq_mask & lt_mask);
+    const bool keep = valid && (key > K || (is_eq && eq_rank < need));
+    const uint64_t keep_mask = __ballot(keep);
+    const uint32_t slot = pos + __popcll(keep_mask & lt_mask);
+    if (keep && slot < (uint32_t)kk) o[slot] = seg.index(j);
+    pos += __popcll(keep_mask);
+    eq_seen += __popcll(eq_mask);
+  });
 }
 
-__host__ __device__ constexpr bool two_pass(int32_t n, int32_t kk) {
-  return n > 2 * TOPK_CHUNK && kk <= TOPK_CHUNK / 4;
-}
 
 // One work-group per (row, query block a): top min(topk, a+1) of
 // logits[row][a][0..a] with entry a forced, by the two-read select (the
@@ -480,27 +616,30 @@ __global__ __launch_bounds__(BLK_WAVES * 64) void block_topk_kernel(const float*
 
 size_t topk_workspace_bytes(int32_t rows, int32_t n, int32_t k) {
   const int32_t kk = k < n ? k : n;
-  if (rows <= 0 || !two_pass(n, kk)) return 0;
-  const size_t nch = (size_t)(n + TOPK_CHUNK - 1) / TOPK_CHUNK;
-  return (size_t)rows * nch * kk * (sizeof(int32_t) + sizeof(uint32_t));
+  if (rows <= 0 || !row_parallel(n, kk)) return 0;
+  return rp_bytes(rows, rp_chunks(n));
 }
 
 hipError_t launch_topk_rows(const float* scores, int32_t rows, int32_t n, int32_t k,
                             int32_t forced, int32_t* out, void* ws, hipStream_t s) {
   const int32_t kk = k < n ? k : n;
   if (rows == 0 || kk == 0) return hipSuccess;
-  if (!two_pass(n, kk)) {
-    hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(ROW_WAVES * 64), 0, s, scores, n, kk,
-                       forced, out);
+  if (row_parallel(n, kk)) {
+    const int32_t nch = rp_chunks(n);
+    uint32_t* hist = static_cast<uint32_t*>(ws);
+    uint32_t* cnt = hist + (size_t)rows * RP_HIST_WORDS;
+    const int32_t words = rows * RP_HIST_WORDS;
+    const dim3 grid(nch, rows), block(RP_WAVES * 64);
+    hipLaunchKernelGGL(rp_zero_kernel, dim3(min((words + 255) / 256, 1024)), dim3(256), 0, s, hist, words);
+    hipLaunchKernelGGL(rp_hist_kernel<0>, grid, block, 0, s, scores, n, kk, forced, hist);
+    hipLaunchKernelGGL(rp_hist_kernel<1>, grid, block, 0, s, scores, n, kk, forced, hist);
+    hipLaunchKernelGGL(rp_hist_kernel<2>, grid, block, 0, s, scores, n, kk, forced, hist);
+    hipLaunchKernelGGL(rp_bound_kernel, dim3(rows), block, 0, s, kk, hist);
+    hipLaunchKernelGGL(rp_count_kernel, grid, block, 0, s, scores, n, forced, hist, cnt);
+    hipLaunchKernelGGL(rp_write_kernel, grid, block, 0, s, scores, n, kk, forced, hist, cnt, out);
     return hipGetLastError();
   }
-  const int32_t nch = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
-  int32_t* cand_idx = static_cast<int32_t*>(ws);
-  uint32_t* cand_key = reinterpret_cast<uint32_t*>(cand_idx + (size_t)rows * nch * kk);
-  hipLaunchKernelGGL(topk_chunks_kernel, dim3(nch, rows), dim3(ROW_WAVES * 64), 0, s, scores, n, kk,
-                     forced, cand_idx, cand_key);
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(ROW_WAVES * 64), 0, s, cand_idx, cand_key,
-                     n, nch, kk, out);
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(ROW_WAVES * 64), 0, s, scores, n, kk, forced, out);
   return hipGetLastError();
 }
 

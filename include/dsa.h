@@ -185,8 +185,8 @@ size_t dsa_vs_estimate_workspace_bytes(const dsa_shape* shape, int32_t n_heads);
  * blocks]. scores: device [rows][n]; out: device int32 [rows][min(k, n)],
  * ascending. forced_index in [-1, n): the entry ranked first in every row
  * (-1: none). k >= 0. workspace: device memory of at least
- * dsa_topk_workspace_bytes(rows, n, k) bytes (0 for rows short enough to be
- * selected in one pass; NULL is then accepted). */
+ * dsa_topk_workspace_bytes(rows, n, k) bytes (0 for rows shorter than 65536
+ * entries, which one work-group each selects; NULL is then accepted). */
 dsa_status dsa_topk(const float* scores, int32_t rows, int32_t n, int32_t k,
                     int32_t forced_index, int32_t* out, void* workspace,
                     size_t workspace_bytes, void* stream);

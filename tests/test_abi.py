@@ -88,10 +88,15 @@ def test_workspace_sizes(lib):
     assert lib.dsa_vertical_slash_workspace_bytes(ctypes.byref(shape(d=96)), 1, 1, 1) == 0
     assert lib.dsa_block_sparse_workspace_bytes(ctypes.byref(sh), 8, 4) > 0
     assert lib.dsa_bs_select_workspace_bytes(3, 512) == 3 * 512 * 512 * 4
-    # top-k: one pass (no scratch) for short rows, candidates of 64K chunks for long ones
-    assert lib.dsa_topk_workspace_bytes(4, 131072, 1000) == 0
-    assert lib.dsa_topk_workspace_bytes(2, 1 << 20, 1000) == 2 * 16 * 1000 * 8
-    assert lib.dsa_topk_workspace_bytes(2, 1 << 20, 20000) == 0
+    # top-k: no scratch for rows shorter than 65536 entries (one work-group
+    # each); longer rows: per row three key histograms (4096 + 4096 + 256
+    # bins), K and its count, and (above K, equal to K) per 16K-entry chunk
+    # and wave
+    assert lib.dsa_topk_workspace_bytes(4, 65535, 1000) == 0
+    assert lib.dsa_topk_workspace_bytes(4, 65536, 65536) == 0   # k >= n: every index
+    assert lib.dsa_topk_workspace_bytes(4, 131072, 1000) == 4 * (8450 + 8 * 8) * 4
+    assert lib.dsa_topk_workspace_bytes(2, 1 << 20, 20000) == 2 * (8450 + 8 * 64) * 4
+    assert lib.dsa_topk_workspace_bytes(1, 70000, 5) == (8450 + 8 * 5) * 4
 
 
 def test_other_argument_errors(lib):

@@ -143,9 +143,11 @@ def _special_scores(rows, n, seed):
 @pytest.mark.parametrize("n,k,forced", [(100, 7, -1), (100, 7, 0), (100, 100, -1), (100, 150, 0),
                                         (1, 1, 0), (5000, 256, 0), (5000, 1, -1), (131072, 6096, 0),
                                         (131072, 1000, -1), (4097, 4096, 4096),
-                                        # rows longer than two 64K chunks take the two-pass path
-                                        (200001, 1000, 200000), (300000, 6096, 0),
-                                        (1 << 20, 6096, 123457), (1 << 20, 1000, -1)])
+                                        # rows of 64K entries or more take the row-parallel path
+                                        (200001, 1000, 200000), (300000, 6096, 0), (70000, 16384, 5),
+                                        (1 << 20, 6096, 123457), (1 << 20, 1000, -1),
+                                        # k above 16384: one work-group per row, or chunks + merge
+                                        (70000, 20000, 7), (300000, 17000, -1)])
 def test_topk(n, k, forced):
     say(f"topk n={n} k={k} forced={forced}")
     x = _special_scores(3, n, n + k)
@@ -153,6 +155,24 @@ def test_topk(n, k, forced):
     for r in range(3):
         want = O.topk_indices(x[r], k, [forced] if forced >= 0 else [])
         assert np.array_equal(out[r], want), (r, out[r][:10], want[:10])
+
+
+@pytest.mark.parametrize("n,k,forced", [(100000, 8000, -1), (100000, 16384, 99999), (65536, 7000, 3)])
+def test_topk_ties_across_chunks(n, k, forced):
+    # the k-th largest key is an exact tie shared by entries in many 16K-entry
+    # chunks: the tied entries kept are the first ones in index order, across
+    # chunk boundaries (rows of 64K entries or more are selected row-parallel)
+    say(f"topk ties across chunks n={n} k={k} forced={forced}")
+    r = np.random.default_rng(n + k)
+    x = -np.abs(r.standard_normal((2, n))).astype(np.float32) - 1.0
+    x[:, ::10] = 0.0
+    pos = r.choice(n, size=(3000,), replace=False)
+    x[0, pos] = np.abs(r.standard_normal(3000)).astype(np.float32) + 0.5
+    x[1, pos[:200]] = 1.0                      # ties above the boundary too
+    out = dsa.topk(torch.from_numpy(x).cuda(), k, forced).cpu().numpy()
+    for row in range(2):
+        want = O.topk_indices(x[row], k, [forced] if forced >= 0 else [])
+        assert np.array_equal(out[row], want), (row, out[row][:10], want[:10])
 
 
 @pytest.mark.parametrize("n", [70000, 300000])
