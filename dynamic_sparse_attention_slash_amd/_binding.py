@@ -459,12 +459,13 @@ def bs_select(qp: torch.Tensor, kp: torch.Tensor, topk: int, *, scale: Optional[
     ke = min(topk, nb)
     sel = torch.empty((rows, nb, ke), dtype=torch.int32, device=qp.device)
     n_sel = torch.empty((rows, nb), dtype=torch.int32, device=qp.device)
+    ws = _workspace(load().dsa_bs_select_workspace_bytes(rows, nb), qp.device)
     if return_logits:
         lg = torch.full((rows, nb, nb), float("nan"), dtype=torch.float32, device=qp.device)
         _call("dsa_bs_select", _dev(qp, "qp", torch.float32), _dev(kp, "kp", torch.float32), rows, nb, D,
-              _scale(scale), topk, sel.data_ptr(), n_sel.data_ptr(), lg.data_ptr(), None, 0, _stream(qp))
+              _scale(scale), topk, sel.data_ptr(), n_sel.data_ptr(), lg.data_ptr(), ws.data_ptr(), ws.numel(),
+              _stream(qp))
         return sel, n_sel, lg
-    ws = _workspace(load().dsa_bs_select_workspace_bytes(rows, nb), qp.device)
     _call("dsa_bs_select", _dev(qp, "qp", torch.float32), _dev(kp, "kp", torch.float32), rows, nb, D,
           _scale(scale), topk, sel.data_ptr(), n_sel.data_ptr(), None, ws.data_ptr(), ws.numel(), _stream(qp))
     return sel, n_sel

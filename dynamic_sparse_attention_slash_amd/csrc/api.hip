@@ -133,34 +133,49 @@ int32_t logit_rows_per_group(int32_t rows, int32_t nb) {
   if (g > (size_t)rows) g = (size_t)rows;
   return (int32_t)g;
 }
-struct BsWork { float* qp; float* kp; float* logits; int32_t* sel; int32_t* n_sel; };
+struct BsWork { float* qp; float* kp; float* logits; uint16_t* split; int32_t* sel; int32_t* n_sel; };
 size_t bs_layout(const dsa_shape* s, int32_t rows, int32_t topk, void* base, BsWork* w) {
   Carver c{reinterpret_cast<uintptr_t>(base)};
   const int32_t nb = nblocks(s->seq_len), D = s->head_dim;
   const int32_t ke = topk < nb ? topk : nb;
+  const int32_t grp = rows ? logit_rows_per_group(rows, nb) : 0;
   float* qp = c.take<float>((size_t)rows * nb * D);
   // pooled K of every kv head the listed heads may read (none without rows)
   float* kp = c.take<float>(rows ? (size_t)s->batch * s->kv_heads * nb * D : 0);
-  float* lg = c.take<float>((size_t)(rows ? logit_rows_per_group(rows, nb) : 0) * nb * nb);
+  float* lg = c.take<float>((size_t)grp * nb * nb);
+  uint16_t* split = c.take<uint16_t>(block_split_elems(grp, nb, D));
   int32_t* sel = c.take<int32_t>((size_t)rows * nb * ke);
   int32_t* n_sel = c.take<int32_t>((size_t)rows * nb);
-  if (w) *w = BsWork{qp, kp, lg, sel, n_sel};
+  if (w) *w = BsWork{qp, kp, lg, split, sel, n_sel};
+  return c.used;
+}
+
+// scratch of dsa_bs_select: the logits of one group of rows (unless the
+// caller takes them all) and that group's bf16 splits (sized for the largest
+// head dimension)
+struct BsSelectScratch { float* logits; uint16_t* split; };
+size_t bs_select_scratch(int32_t rows, int32_t nb, bool with_logits, void* base, BsSelectScratch* w) {
+  Carver c{reinterpret_cast<uintptr_t>(base)};
+  const int32_t grp = logit_rows_per_group(rows, nb);
+  float* lg = c.take<float>(with_logits ? (size_t)grp * nb * nb : 0);
+  uint16_t* split = c.take<uint16_t>(block_split_elems(grp, nb, 128));
+  if (w) *w = BsSelectScratch{lg, split};
   return c.used;
 }
 
 // block logits + per-block top-k, in groups of rows bounded by the scratch size
 hipError_t bs_select_rows(const float* qp, const float* kp, int32_t rows, int32_t nb, int32_t D,
                           float scale, int32_t topk, bool kv_map, const HeadMap& hm,
-                          float* logits, bool logits_full, int32_t* sel, int32_t* n_sel,
+                          float* logits, bool logits_full, uint16_t* split, int32_t* sel, int32_t* n_sel,
                           hipStream_t st) {
   const int32_t ke = topk < nb ? topk : nb;
-  const int32_t grp = logits_full ? rows : logit_rows_per_group(rows, nb);
+  const int32_t grp = logit_rows_per_group(rows, nb);
   for (int32_t r0 = 0; r0 < rows; r0 += grp) {
     const int32_t nr = rows - r0 < grp ? rows - r0 : grp;
     float* lg = logits_full ? logits + (size_t)r0 * nb * nb : logits;
     const float* kpr = kv_map ? kp : kp + (size_t)r0 * nb * D;
     hipError_t e = launch_block_logits(qp + (size_t)r0 * nb * D, kpr, r0, nr, nb, D, scale,
-                                       kv_map, hm, lg, st);
+                                       kv_map, hm, split, lg, st);
     if (e != hipSuccess) return e;
     e = launch_block_topk(lg, nr, nb, topk, sel + (size_t)r0 * nb * ke, n_sel + (size_t)r0 * nb, st);
     if (e != hipSuccess) return e;
@@ -206,7 +221,7 @@ hipError_t bs_index_stages(const void* q, const void* k, const dsa_shape* shape,
   if (e == hipSuccess) e = launch_pool(k, shape->dtype, n, D, shape->batch * kvm.n, kvm, w.kp, s);
   if (e == hipSuccess)
     e = bs_select_rows(w.qp, w.kp, rows, nb, D, eff_scale(scale, D), topk, true, hm, w.logits, false,
-                       w.sel, w.n_sel, s);
+                       w.split, w.sel, w.n_sel, s);
   return e;
 }
 
@@ -539,7 +554,7 @@ dsa_status dsa_bs_pool(const void* x, int32_t dtype, int32_t batch, int32_t x_he
 
 size_t dsa_bs_select_workspace_bytes(int32_t rows, int32_t nb) {
   if (rows <= 0 || nb <= 0) return 0;
-  return (size_t)logit_rows_per_group(rows, nb) * nb * nb * sizeof(float);
+  return bs_select_scratch(rows, nb, true, nullptr, nullptr);
 }
 
 dsa_status dsa_bs_select(const float* qp, const float* kp, int32_t rows, int32_t nb, int32_t head_dim,
@@ -549,12 +564,14 @@ dsa_status dsa_bs_select(const float* qp, const float* kp, int32_t rows, int32_t
   if (head_dim != 64 && head_dim != 128) return DSA_ERR_UNSUPPORTED;
   if (rows == 0 || nb == 0) return DSA_OK;
   if (!qp || !kp || !sel || !n_sel) return DSA_ERR_INVALID_ARG;
-  if (!logits && (workspace_bytes < dsa_bs_select_workspace_bytes(rows, nb) || !workspace))
+  if (!workspace || workspace_bytes < bs_select_scratch(rows, nb, !logits, nullptr, nullptr))
     return DSA_ERR_WORKSPACE;
   HeadMap hm;
   memset(&hm, 0, sizeof(hm));
+  BsSelectScratch w;
+  bs_select_scratch(rows, nb, !logits, workspace, &w);
   hipError_t e = bs_select_rows(qp, kp, rows, nb, head_dim, eff_scale(scale, head_dim), topk, false, hm,
-                                logits ? logits : static_cast<float*>(workspace), logits != nullptr,
+                                logits ? logits : w.logits, logits != nullptr, w.split,
                                 sel, n_sel, static_cast<hipStream_t>(stream));
   return hip_status(e);
 }

@@ -204,8 +204,13 @@ hipError_t launch_pool(const void* x, int32_t dtype, int32_t seq_len, int32_t he
 // data. kp: with kv_map false it points at row0's data too (row r scores
 // against kp row r); with kv_map true it is the whole pooled-K array
 // [batch * kv_heads][nb][dim] and row r reads kp row b * kv_heads + kv head.
+// split: scratch of block_split_elems(rows, nb, head_dim) bf16 values (the
+// hi / lo splits of the rows' pooled Q and K).
 hipError_t launch_block_logits(const float* qp, const float* kp, int32_t row0, int32_t rows,
                                int32_t nb, int32_t head_dim, float scale, bool kv_map,
-                               const HeadMap& hm, float* logits, hipStream_t s);
+                               const HeadMap& hm, uint16_t* split, float* logits, hipStream_t s);
+inline size_t block_split_elems(int32_t rows, int32_t nb, int32_t head_dim) {
+  return (size_t)4 * rows * nb * head_dim;
+}
 
 }  // namespace dsa

@@ -223,8 +223,9 @@ dsa_status dsa_bs_pool(const void* x, int32_t dtype, int32_t batch, int32_t x_he
  * top-min(topk, a+1) blocks of L[a][0..a] with c = a forced and n_sel
  * [rows][nb] their count (entries of sel past the count are left unwritten).
  * logits: NULL, or device fp32 [rows][nb][nb] that
- * receives L (entries c > a are left untouched). workspace: at least
- * dsa_bs_select_workspace_bytes(...) bytes. */
+ * receives L (entries c > a are left untouched). workspace: device memory of
+ * at least dsa_bs_select_workspace_bytes(rows, nb) bytes, also when logits is
+ * given (it then holds only the bf16 splits of qp and kp). */
 dsa_status dsa_bs_select(const float* qp, const float* kp, int32_t rows, int32_t nb,
                          int32_t head_dim, float scale, int32_t topk, int32_t* sel,
                          int32_t* n_sel, float* logits, void* workspace,

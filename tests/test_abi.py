@@ -87,7 +87,9 @@ def test_workspace_sizes(lib):
     assert w4 >= 4 * 64 * 256 * 4
     assert lib.dsa_vertical_slash_workspace_bytes(ctypes.byref(shape(d=96)), 1, 1, 1) == 0
     assert lib.dsa_block_sparse_workspace_bytes(ctypes.byref(sh), 8, 4) > 0
-    assert lib.dsa_bs_select_workspace_bytes(3, 512) == 3 * 512 * 512 * 4
+    # block select: one group's fp32 logits plus its bf16 hi / lo splits of the
+    # pooled Q and K (four arrays, sized for head_dim 128)
+    assert lib.dsa_bs_select_workspace_bytes(3, 512) == 3 * 512 * 512 * 4 + 4 * 3 * 512 * 128 * 2
     # top-k: no scratch for rows shorter than 65536 entries (one work-group
     # each); longer rows: per row three key histograms (4096 + 4096 + 256
     # bins), K and its count, and (above K, equal to K) per 16K-entry chunk
