@@ -453,8 +453,8 @@ __device__ RpBound rp_bound(const uint32_t* __restrict__ hr, int32_t kk, uint32_
   return b;
 }
 
-__global__ __launch_bounds__(256) void rp_zero_kernel(uint32_t* __restrict__ p, int32_t words) {
-  for (int32_t i = blockIdx.x * 256 + threadIdx.x; i < words; i += gridDim.x * 256) p[i] = 0u;
+__global__ __launch_bounds__(256) void rp_zero_kernel(uint32_t* __restrict__ p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256) p[i] = 0u;
 }
 
 // Pass LEVEL + 1 (LEVEL 0, 1, 2): histogram of the next bits of the keys that
@@ -628,9 +628,10 @@ hipError_t launch_topk_rows(const float* scores, int32_t rows, int32_t n, int32_
     const int32_t nch = rp_chunks(n);
     uint32_t* hist = static_cast<uint32_t*>(ws);
     uint32_t* cnt = hist + (size_t)rows * RP_HIST_WORDS;
-    const int32_t words = rows * RP_HIST_WORDS;
+    const size_t words = (size_t)rows * RP_HIST_WORDS;
     const dim3 grid(nch, rows), block(RP_WAVES * 64);
-    hipLaunchKernelGGL(rp_zero_kernel, dim3(min((words + 255) / 256, 1024)), dim3(256), 0, s, hist, words);
+    hipLaunchKernelGGL(rp_zero_kernel, dim3((unsigned)std::min<size_t>((words + 255) / 256, 1024)), dim3(256), 0, s,
+                       hist, words);
     hipLaunchKernelGGL(rp_hist_kernel<0>, grid, block, 0, s, scores, n, kk, forced, hist);
     hipLaunchKernelGGL(rp_hist_kernel<1>, grid, block, 0, s, scores, n, kk, forced, hist);
     hipLaunchKernelGGL(rp_hist_kernel<2>, grid, block, 0, s, scores, n, kk, forced, hist);
