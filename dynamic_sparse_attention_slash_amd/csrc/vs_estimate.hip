@@ -18,10 +18,11 @@
 // a chunk of K is fetched from memory once per group.
 // Pass 2 (scores): recompute S, p = exp2(S*scale*log2e - F_r). Column sums are
 //   register sums plus two cross-lane steps (the loop runs key-major, so a
-//   key's scores stay in one lane column). Diagonal sums stage each 64x64 tile
-//   of p in LDS and add it along diagonals, each lane owning two diagonals
-//   that together take one element per tile row, into a per-chunk
-//   accumulator: no atomics, fixed order, bit-reproducible.
+//   key's scores stay in one lane column). Diagonal sums: per 32-key half
+//   tile, each p goes to LDS at the row of its diagonal (a skewed tile whose
+//   unused slots stay zero), each lane adds up whole rows, and a diagonal
+//   still open at the half tile's end moves on to the lane that owns it in
+//   the next one: no atomics, fixed order, bit-reproducible.
 // S-combine: s[d] adds the (at most two) chunk partials covering offset d in
 //   ascending chunk order.
 #include "kernels.hpp"
@@ -29,7 +30,12 @@
 namespace dsa {
 namespace {
 
-constexpr int SACC_MAX = EST_CHUNK + 63;  // diagonal offsets the largest chunk touches
+// Skewed probability tile of one 32-key half tile (64 window rows x 32 keys):
+// element (r, c) sits at row r - c + 31 (its diagonal), column c. Rows 0..94
+// hold the 95 diagonals, row 95 stays zero. Row stride 34 floats: the 64-bit
+// row reads are free of bank conflicts, and the whole tile (13 KB) leaves
+// room for three one-wave work-groups per SIMD.
+constexpr int DG_ROWS = 96, DG_STRIDE = 34;
 constexpr int WIN_WAVES = 4;              // window slices per work-group (column-score windows)
 
 __device__ __forceinline__ int32_t wave_lane() { return (int32_t)(threadIdx.x & 63); }
@@ -85,14 +91,16 @@ struct Tile<uint16_t, D> {
   __device__ static void finish(f32x4 (&x)[4], int32_t j0, int32_t l16, const Window& w) {
     if (!(j0 + 15 <= w.start && w.lq == 64)) mask(x, j0 + l16, w);
   }
+  // row r = 16 qb + 4 g + i is kept when r < lq and key <= start + r, i.e.
+  // when lo <= 16 qb + i < hi for the lane values below (no per-row registers)
   __device__ static void mask(f32x4 (&x)[4], int32_t key, const Window& w) {
-    const int32_t g = wave_lane() >> 4;
+    const int32_t g4 = 4 * (wave_lane() >> 4);
+    const int32_t lo = key - w.start - g4, hi = w.lq - g4;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int32_t r = 16 * qb + 4 * g + i;
-        bool ok = r < w.lq && key <= w.pos(r);
+        const bool ok = 16 * qb + i >= lo && 16 * qb + i < hi;
         x[qb][i] = ok ? x[qb][i] : -INFINITY;
       }
   }
@@ -139,9 +147,9 @@ struct Tile<float, D> {
 // Scores of consecutive 16-key steps. bf16 loads the next step's K while the
 // current one computes (16 more VGPRs, still three waves per SIMD); fp32,
 // whose K operands are twice as wide, loads each step's K at its start.
-template <typename T, int D>
+template <typename T, int D, bool PF = sizeof(T) == 2>
 struct KStream {
-  static constexpr bool PREFETCH = sizeof(T) == 2;
+  static constexpr bool PREFETCH = PF;
   typename Tile<T, D>::KReg kn;
   __device__ KStream(const Tile<T, D>& tile, const T* ks, int32_t j_begin, const Window& w) {
     if (PREFETCH) tile.load_k(ks, j_begin, w, kn);
@@ -485,9 +493,7 @@ template <typename T, int D, bool S, bool MULTI>
 __device__ __forceinline__ void est_scores(const EstArgs& a) {
   static_assert(!(MULTI && S), "window slices: column scores only");
   static_assert(!MULTI || sizeof(T) == 2, "window slices: bf16 only");
-  constexpr int PS = 65;  // padded LDS row of the 64x64 probability tile
-  __shared__ float ptile[S ? 64 * PS : 1];
-  __shared__ float sacc[S ? SACC_MAX : 1];
+  __shared__ __align__(16) float dtile[S ? DG_ROWS * DG_STRIDE : 1];
   const int32_t C = a.chunk, nchunks = (a.seq_len + C - 1) / C;
   int32_t row, chunk;
   work_item(a.hm, a.wo, nchunks, row, chunk);
@@ -504,9 +510,6 @@ __device__ __forceinline__ void est_scores(const EstArgs& a) {
   for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) F[qb][i] = a.row_stats[(size_t)(row * nsl + slice) * 64 + 16 * qb + 4 * g + i];
-  const int32_t SACC = C + 63;  // diagonal offsets this chunk touches
-  if (S)
-    for (int e = lane; e < SACC; e += 64) sacc[e] = 0.f;
 
   float* vout = a.v_scores + (size_t)row * a.seq_len;
   const float sc = a.scale_log2;
@@ -515,11 +518,30 @@ __device__ __forceinline__ void est_scores(const EstArgs& a) {
     ring_column_sums<D, MULTI>(a, tile, ks, w, F, vout, j_begin, j_end, slice, nsl);
     return;
   }
-  KStream<T, D> kst(tile, ks, j_begin, w);
-  for (int32_t t0 = j_begin; t0 < j_end; t0 += 64) {
+  // The chunk's partial diagonal sums: entry (C - 1) - (J - j_begin) + e holds
+  // the diagonal with r - c = e in the half tile starting at key J, i.e. the
+  // entry of (window row r, key j) is r - j + j_begin + C - 1, in [0, C + 63).
+  float* const spart = S ? a.s_part + ((size_t)row * nchunks + chunk) * (C + 63) : nullptr;
+  // write slot of this lane's (r, c) = (16 qb + 4 g + i, 16 sb + l16): the
+  // lane part (4 g - l16 + 15) * DG_STRIDE + l16 (never negative) plus the
+  // constant (16 (qb - sb) + i + 16) * DG_STRIDE + 16 sb
+  const int32_t wlane = (4 * g - l16 + 15) * DG_STRIDE + l16;
+  // lane l sums diagonal e = l - 31 (row l) into da and, for l < 31, diagonal
+  // e = l + 33 (row l + 64) into db; the other lanes read the zero row
+  const float* const rda = dtile + lane * DG_STRIDE;
+  const float* const rdb = dtile + (lane < 31 ? lane + 64 : DG_ROWS - 1) * DG_STRIDE;
+  float da = 0.f, db = 0.f;
+  if (S) {
+    // slots no (r, c) maps to are never written: zero them once
+    for (int32_t e = lane; e < DG_ROWS * DG_STRIDE; e += 64) dtile[e] = 0.f;
+    __syncthreads();
+  }
+  KStream<T, D, (sizeof(T) == 2 && !(S && D == 128))> kst(tile, ks, j_begin, w);
+  int32_t h0 = j_begin;
+  for (; h0 < j_end; h0 += 32) {
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      const int32_t j0 = t0 + 16 * sb;
+    for (int sb = 0; sb < 2; ++sb) {
+      const int32_t j0 = h0 + 16 * sb;
       f32x4 x[4];
       kst.scores(tile, ks, j0, w, x);
       float colsum = 0.f;
@@ -529,7 +551,7 @@ __device__ __forceinline__ void est_scores(const EstArgs& a) {
         for (int i = 0; i < 4; ++i) {
           const float p = fast_exp2(__builtin_fmaf(x[qb][i], sc, -F[qb][i]));
           colsum += p;
-          if (S) ptile[(16 * qb + 4 * g + i) * PS + 16 * sb + l16] = p;
+          if (S) dtile[wlane + (16 * (qb - sb) + i + 16) * DG_STRIDE + 16 * sb] = p;
         }
       colsum = xor_sum(xor_sum(colsum, 16), 32);
       if (g == 0 && j0 + l16 < a.seq_len) {
@@ -539,32 +561,37 @@ __device__ __forceinline__ void est_scores(const EstArgs& a) {
     }
     if (!S) continue;
     __syncthreads();
-    // diagonal e = r - jj of the tile maps to chunk offset index
-    // e + (C - 1) - (t0 - j_begin). Lane l owns diagonals e1 = l - 63 (rows
-    // 0..l) and e2 = l + 1 (rows l+1..63): in row k both sit at column
-    // (k - l - 1) mod 64, so one 64-step sweep over the rows visits each
-    // element of both once, with the same trip count in every lane. Four
-    // interleaved partial sums per diagonal keep the reads in flight.
-    const int32_t base = (C - 1) - (t0 - j_begin);
-    float d1[4] = {0.f, 0.f, 0.f, 0.f}, d2[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int32_t k0 = 0; k0 < 64; k0 += 4) {
+    float sa[2] = {0.f, 0.f}, sbv[2] = {0.f, 0.f};
 #pragma unroll
-      for (int32_t u = 0; u < 4; ++u) {
-        const int32_t k = k0 + u;
-        const float v = ptile[k * PS + ((k - lane - 1) & 63)];
-        const float v1 = k <= lane ? v : 0.f;
-        d1[u] += v1;
-        d2[u] += v - v1;
-      }
+    for (int c = 0; c < 32; c += 2) {
+      const float2 va = *reinterpret_cast<const float2*>(rda + c);
+      const float2 vb = *reinterpret_cast<const float2*>(rdb + c);
+      sa[(c >> 1) & 1] += va.x + va.y;
+      sbv[(c >> 1) & 1] += vb.x + vb.y;
     }
-    sacc[lane - 63 + base] += (d1[0] + d1[1]) + (d1[2] + d1[3]);
-    if (lane < 63) sacc[lane + 1 + base] += (d2[0] + d2[1]) + (d2[2] + d2[3]);
+    da += sa[0] + sa[1];
+    db += sbv[0] + sbv[1];
     __syncthreads();
+    // diagonals e in [32, 63] end in this half tile: e = l + 33 (lanes < 31)
+    // and e = 32 (lane 63, its da)
+    const int32_t base = (C - 1) - (h0 - j_begin);
+    if (lane < 31) spart[base + lane + 33] = db;
+    if (lane == 63) spart[base + 32] = da;
+    // e <= 31 continues as e + 32 in the next half tile: lane l's da (e = l - 31)
+    // becomes da of lane l + 32 (l < 32) or db of lane l - 32 (l >= 32)
+    const float moved = __shfl_xor(da, 32, 64);
+    da = lane >= 32 ? moved : 0.f;
+    db = lane < 31 ? moved : 0.f;
   }
   if (!S) return;
-  float* dst = a.s_part + ((size_t)row * nchunks + chunk) * SACC;
-  for (int e = lane; e < SACC; e += 64) dst[e] = sacc[e];
+  // diagonals still open, in the frame of the half tile after the last:
+  // da of lanes >= 32 (e = l - 31), db of lanes < 31 (e = l + 33)
+  const int32_t base = (C - 1) - (h0 - j_begin);
+  if (lane >= 32) spart[base + lane - 31] = da;
+  if (lane < 31) spart[base + lane + 33] = db;
+  // a short last chunk leaves the entries below base + 1 untouched (no key
+  // of this chunk lies on them): zero them, as a full chunk would have
+  for (int32_t e = lane; e <= base; e += 64) spart[e] = 0.f;
 }
 
 template <typename T, int D, bool S>
