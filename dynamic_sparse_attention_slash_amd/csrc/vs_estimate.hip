@@ -166,15 +166,19 @@ struct KStream {
   }
 };
 
-// bf16 K of 16-key steps through a ring of KR_STAGES steps in LDS: each step
-// goes global -> LDS by DMA (buffer_load ... lds, no registers) two steps
-// before it is used, into its own stage array (12 KB per wave at D = 128, so
-// three waves per SIMD stay resident). Rows are stored with the swizzle the
-// attention tiles use, so the K operand reads are free of bank conflicts.
-// Rows past the head's slab read as zeros (buffer range check); their scores
-// are masked.
+// bf16 K of 16-key steps through a ring of NS steps in LDS: each step goes
+// global -> LDS by DMA (buffer_load ... lds, no registers) NS - 1 steps
+// before it is used, into its own stage array (4 KB per step at D = 128).
+// Rows are stored with the swizzle the attention tiles use, so the K operand
+// reads are free of bank conflicts. Rows past the head's slab read as zeros
+// (buffer range check); their scores are masked. One-wave work-groups take
+// three stages (12 KB per wave: three waves per SIMD stay resident).
 constexpr int KR_STAGES = 3;
-template <int D>
+// The window column-sum work-groups (four waves, each with its own ring and
+// the chunk's per-slice column sums) take two stages: 48 KB of LDS instead
+// of 64 KB, so three work-groups per CU, three waves per SIMD.
+constexpr int WIN_RING_STAGES = 2;
+template <int D, int NS = KR_STAGES>
 struct KRing {
   static constexpr int ROW = D * 2;          // bytes per key
   static constexpr int UNITS = ROW / 16;     // 16-byte chunks per key
@@ -204,9 +208,9 @@ struct KRing {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + k * 1024), 16,
                                                j0 * ROW + ld_off[k], 0, 0, 0);
   }
-  // Waits until this lane's DMA of the current step (issued KR_STAGES - 1
-  // steps back) has landed, then reads the K operands. Every step issues
-  // exactly INSTR DMA loads, so at least INSTR * (KR_STAGES - 1) vector
+  // Waits until this lane's DMA of the current step (issued NS - 1 steps
+  // back) has landed, then reads the K operands. Every step issues
+  // exactly INSTR DMA loads, so at least INSTR * (NS - 1) vector
   // memory operations follow the current step's; loads completing in order,
   // vmcnt of that count suffices (other loads and stores issued in between
   // only make it stricter).
@@ -214,7 +218,7 @@ struct KRing {
   // cannot tell which stage an LDS DMA writes, and would otherwise drain
   // every load in flight before each read.
   __device__ void read(const char* stage, typename Tile<uint16_t, D>::KReg& k) const {
-    constexpr int ahead = INSTR * (KR_STAGES - 1);  // DMA loads issued after this step's
+    constexpr int ahead = INSTR * (NS - 1);  // DMA loads issued after this step's
     static_assert(ahead < 16, "vmcnt field");
     __builtin_amdgcn_s_waitcnt(0x0F70 | ahead);     // vmcnt(ahead), no expcnt / lgkmcnt wait
     // the stage's LDS byte address (an address-space cast of the pointer)
@@ -434,26 +438,28 @@ __device__ void ring_column_sums(const EstArgs& a, const Tile<uint16_t, D>& tile
   const int32_t g = wave_lane() >> 4, l16 = wave_lane() & 15;
   const float sc = a.scale_log2;
   constexpr int NW = MULTI ? WIN_WAVES : 1;
-  __shared__ __align__(16) char kr0[NW][KRing<D>::STEP], kr1[NW][KRing<D>::STEP], kr2[NW][KRing<D>::STEP];
+  constexpr int NS = MULTI ? WIN_RING_STAGES : KR_STAGES;
+  constexpr int STEP = KRing<D, NS>::STEP;
+  __shared__ __align__(16) char kr0[NW][STEP], kr1[NW][STEP], kr2[NS > 2 ? NW : 1][NS > 2 ? STEP : 16];
   __shared__ float cs[NW][MULTI ? EST_CHUNK : 1];
-  char* const stage[KR_STAGES] = {kr0[slice], kr1[slice], kr2[slice]};
-  const KRing<D> ring(ks, a.seq_len);
+  char* const stage[3] = {kr0[slice], kr1[slice], kr2[NS > 2 ? slice : 0]};
+  const KRing<D, NS> ring(ks, a.seq_len);
   // (one wave) the window slices after the first add into v: each step's
   // earlier v is loaded together with its K, so that waiting for it never
   // drains the loads issued after it
   const bool add_here = !MULTI && a.add_v;
-  float vprev[KR_STAGES];
+  float vprev[NS];
   auto load_v = [&](int32_t j0) { return vout[min(j0 + l16, a.seq_len - 1)]; };
 #pragma unroll
-  for (int u = 0; u < KR_STAGES - 1; ++u) {
+  for (int u = 0; u < NS - 1; ++u) {
     vprev[u] = add_here ? load_v(j_begin + 16 * u) : 0.f;
     ring.issue(j_begin + 16 * u, stage[u]);
   }
-  for (int32_t t0 = j_begin; t0 < j_end; t0 += 16 * KR_STAGES) {
+  for (int32_t t0 = j_begin; t0 < j_end; t0 += 16 * NS) {
 #pragma unroll
-    for (int u = 0; u < KR_STAGES; ++u) {
-      const int32_t j0 = t0 + 16 * u, jn = j0 + 16 * (KR_STAGES - 1);
-      const int un = (u + KR_STAGES - 1) % KR_STAGES;  // constant after unrolling
+    for (int u = 0; u < NS; ++u) {
+      const int32_t j0 = t0 + 16 * u, jn = j0 + 16 * (NS - 1);
+      const int un = (u + NS - 1) % NS;  // constant after unrolling
       vprev[un] = add_here ? load_v(jn) : 0.f;
       ring.issue(jn, stage[un]);
       if (j0 < j_end) {
