@@ -103,7 +103,7 @@ hipError_t launch_attention_mixed(const AttnArgs& a, const MixedIndex& ix, hipSt
 // ---- vertical-slash estimate (vs_estimate.hip) ----
 // keys per estimator work-group, at most: 1024 measured fastest at 128K-1M
 // (each wave loads its 64-row Q window once per chunk; 256: 12% slower at
-// 1M); smaller problems take 512 or 256 (est_chunk_keys)
+// 1M); shorter rows take 512 down to 64 (est_chunk_keys)
 constexpr int EST_CHUNK = 1024;
 struct EstArgs {
   const void* q; const void* k;

@@ -1033,15 +1033,27 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
 
 // ---------------------------------------------------------------------------
 // fp32 kernel (MFMA 16x16x4 f32: one k value per lane, so V needs no transpose)
+//
+// F32_WAVES waves share a query block: they fill the descriptor array
+// together (the generator's state is the same in every wave) and wave w takes
+// the sub-block pairs w, w + F32_WAVES, ...; at the end the waves' partial
+// (max, sum, O) meet in LDS and wave 0 merges them in wave order. A short
+// sequence has few query blocks, so one wave per block would leave most of
+// the chip idle; more than 256 VGPRs per wave allow one wave per SIMD, so
+// four waves per work-group.
 // ---------------------------------------------------------------------------
+constexpr int F32_WAVES = 4;
 template <int D, class R>
 __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict__ ks,
                            const float* __restrict__ vs, float* __restrict__ os, int32_t n,
                            int32_t r0, float scale_log2, DescGen<R> gen) {
   constexpr int DK = D / 4;   // k-steps of Q.K; lane group g holds dims DK*g .. DK*g + DK-1
   constexpr int DB = D / 16;
+  constexpr int MW = DB * 16 + 8;  // merged floats per lane: O, max, sum
   __shared__ Desc desc[SB_CAP];
-  const int32_t lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+  __shared__ float mbuf[(F32_WAVES - 1) * MW * 64];
+  const int32_t lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
   const int32_t* cols = gen.cols;
 
   float qop[4][DK];
@@ -1065,10 +1077,10 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
 
   while (true) {
     __syncthreads();
-    const int32_t cnt = gen.fill(desc, lane, 64);
+    const int32_t cnt = gen.fill(desc, (int32_t)threadIdx.x, 64 * F32_WAVES);
     if (cnt == 0) break;
     __syncthreads();
-    for (int32_t t = 0; t < cnt; t += 2) {
+    for (int32_t t = 2 * wave; t < cnt; t += 2 * F32_WAVES) {
       const Desc d[2] = {uniform_desc(desc, t, cnt), uniform_desc(desc, t + 1, cnt)};
       f32x4 st[2][4];
 #pragma unroll
@@ -1124,6 +1136,44 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
     }
   }
 
+  // Every lane's state covers the same query columns in every wave (the max
+  // is per column, the sums and O per lane), so the merge is lane by lane:
+  // element e of a lane at mbuf[(w - 1) * MW * 64 + e * 64 + lane].
+  if (wave > 0) {
+    float* dst = mbuf + (size_t)(wave - 1) * MW * 64 + lane;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      dst[qb * 64] = m[qb];
+      dst[(4 + qb) * 64] = lsum[qb];
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(8 + 16 * db + 4 * qb + i) * 64] = oacc[db][qb][i];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  for (int32_t w = 1; w < F32_WAVES; ++w) {
+    const float* src = mbuf + (size_t)(w - 1) * MW * 64 + lane;
+    float a0[4], a1[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const float mw = src[qb * 64], mx = fmaxf(m[qb], mw);
+      a0[qb] = fast_exp2(m[qb] - mx);
+      a1[qb] = fast_exp2(mw - mx);
+      m[qb] = mx;
+      lsum[qb] = lsum[qb] * a0[qb] + src[(4 + qb) * 64] * a1[qb];
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          oacc[db][qb][i] = oacc[db][qb][i] * a0[qb] + src[(8 + 16 * db + 4 * qb + i) * 64] * a1[qb];
+  }
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
     float lt = xor_sum(xor_sum(lsum[qb], 16), 32);
@@ -1139,7 +1189,7 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
 
 // ---------------------------------------------------------------------------
 // kernels per index mode
-// fp32: one work-group (one wave) per (row, query block)
+// fp32: one work-group (F32_WAVES waves) per (row, query block)
 // bf16: one work-group (four waves) per (row, panel of two query blocks)
 // ---------------------------------------------------------------------------
 template <class R>
@@ -1177,7 +1227,7 @@ __device__ __forceinline__ int32_t num_blocks(int32_t n) { return (n + BLOCK - 1
 __device__ __forceinline__ int32_t num_panels(int32_t n) { return (num_blocks(n) + PANEL - 1) / PANEL; }
 
 template <int D>
-__global__ __launch_bounds__(64) void attn_vs_f32_kernel(AttnArgs a, VsIndex ix) {
+__global__ __launch_bounds__(64 * F32_WAVES) void attn_vs_f32_kernel(AttnArgs a, VsIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
   work_item(a.hm, a.wo, nb, row, blk);
@@ -1189,7 +1239,7 @@ __global__ __launch_bounds__(64) void attn_vs_f32_kernel(AttnArgs a, VsIndex ix)
 }
 
 template <int D>
-__global__ __launch_bounds__(64) void attn_blocks_f32_kernel(AttnArgs a, BlockIndex ix) {
+__global__ __launch_bounds__(64 * F32_WAVES) void attn_blocks_f32_kernel(AttnArgs a, BlockIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
   work_item(a.hm, a.wo, nb, row, blk);
@@ -1199,7 +1249,7 @@ __global__ __launch_bounds__(64) void attn_blocks_f32_kernel(AttnArgs a, BlockIn
 }
 
 template <int D>
-__global__ __launch_bounds__(64) void attn_stream_f32_kernel(AttnArgs a, StreamIndex ix) {
+__global__ __launch_bounds__(64 * F32_WAVES) void attn_stream_f32_kernel(AttnArgs a, StreamIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
   work_item(a.hm, a.wo, nb, row, blk);
@@ -1319,8 +1369,8 @@ hipError_t launch_attention_vs(const AttnArgs& a, const VsIndex& ix, hipStream_t
     hipLaunchKernelGGL(a.head_dim == 64 ? attn_vs_single_kernel<64> : attn_vs_single_kernel<128>, grid,
                        dim3(64 * SB_WAVES), 0, s, a, ix);
   else
-    hipLaunchKernelGGL(a.head_dim == 64 ? attn_vs_f32_kernel<64> : attn_vs_f32_kernel<128>, grid, dim3(64), 0,
-                       s, a, ix);
+    hipLaunchKernelGGL(a.head_dim == 64 ? attn_vs_f32_kernel<64> : attn_vs_f32_kernel<128>, grid,
+                       dim3(64 * F32_WAVES), 0, s, a, ix);
   return hipGetLastError();
 }
 
@@ -1332,7 +1382,7 @@ hipError_t launch_attention_blocks(const AttnArgs& a, const BlockIndex& ix, hipS
                        dim3(64 * SB_WAVES), 0, s, a, ix);
   else
     hipLaunchKernelGGL(a.head_dim == 64 ? attn_blocks_f32_kernel<64> : attn_blocks_f32_kernel<128>, grid,
-                       dim3(64), 0, s, a, ix);
+                       dim3(64 * F32_WAVES), 0, s, a, ix);
   return hipGetLastError();
 }
 
@@ -1376,7 +1426,7 @@ hipError_t launch_attention_stream(const AttnArgs& a, const StreamIndex& ix, hip
                        dim3(64 * PANEL_WAVES), 0, s, a, ix);
   else
     hipLaunchKernelGGL(a.head_dim == 64 ? attn_stream_f32_kernel<64> : attn_stream_f32_kernel<128>, grid,
-                       dim3(64), 0, s, a, ix);
+                       dim3(64 * F32_WAVES), 0, s, a, ix);
   return hipGetLastError();
 }
 

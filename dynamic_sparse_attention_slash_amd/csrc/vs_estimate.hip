@@ -630,10 +630,12 @@ int32_t est_chunk_keys(int32_t seq_len) {
   // slash partials, so it depends on seq_len alone: a head's scores are then
   // the same bits whatever batch or head list it is computed with. Long rows
   // take the largest chunk (64+ chunks per row); shorter ones smaller chunks,
-  // so that few rows still spread over many work-groups.
+  // down to 64 keys, so that a row still spreads over about 64 work-groups.
   if (seq_len >= 65536) return EST_CHUNK;
-  if (seq_len >= 16384) return 512;
-  return 256;
+  if (seq_len >= 32768) return 512;
+  if (seq_len >= 16384) return 256;
+  if (seq_len >= 8192) return 128;
+  return 64;
 }
 
 size_t est_workspace_bytes(int32_t rows, int32_t seq_len) {
