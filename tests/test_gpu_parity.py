@@ -292,6 +292,34 @@ def test_attention_blocks_given_indices(n, D, dt):
             check_attention(oh[b, h], O.assemble(ref, n, D), f"b{b} h{h}")
 
 
+def test_attention_blocks_f32_long_rows():
+    """fp32 query blocks with more than 1024 key sub-blocks: every key block up
+    to the diagonal is listed, so the last query blocks of a 19211-token head
+    hold up to 1201 sub-blocks, more than one refill of the descriptor array
+    that the work-group's four waves share and split. Sampled query blocks
+    (both sides of the 1024-sub-block line, the ragged last one) against the
+    oracle; every output row finite."""
+    n, D = 64 * 300 + 11, 64
+    say(f"attention_blocks f32 long rows n={n}")
+    q, k, v = rand_qkv(1, 1, 1, n, D, "f32", seed=77)
+    nb = O.num_blocks(n)
+    sel = np.zeros((1, nb, nb), np.int32)
+    nsel = np.zeros((1, nb), np.int32)
+    for a in range(nb):
+        sel[0, a, : a + 1] = np.arange(a + 1)
+        nsel[0, a] = a + 1
+    o = dsa.sparse_attention_blocks(q, k, v, torch.from_numpy(sel).cuda(), torch.from_numpy(nsel).cuda())
+    torch.cuda.synchronize()
+    oh = host64(o)
+    assert np.isfinite(oh).all()
+    blocks = [0, 1, 200, 255, 256, 257, 299, 300]
+    ref = O._attend_blocks(host64(q)[0, 0], host64(k)[0, 0], host64(v)[0, 0], 1 / math.sqrt(D),
+                           lambda a: O.blocks_to_keys(np.arange(a + 1), n), blocks=blocks)
+    for a in blocks:
+        rows = slice(a * 64, min(n, (a + 1) * 64))
+        check_attention(oh[0, 0, rows], ref[a], f"block {a}")
+
+
 @pytest.mark.parametrize("n,D,dt,init,local", [(1000, 128, "bf16", 1, 2), (1000, 128, "bf16", 0, 1),
                                                (64 * 9 + 5, 64, "f32", 2, 3), (500, 128, "bf16", 3, 64),
                                                # bf16 panels at head_dim 64: an even and an odd
