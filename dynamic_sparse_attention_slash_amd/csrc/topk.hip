@@ -10,7 +10,8 @@
 // the maximum key, which no canonical float reaches). Rows shorter than 64K
 // entries and the block lists are selected by one work-group each, which
 // first tries a two-read select over 12-bit key bins (described at
-// select_bins below); rows it cannot take use the radix select: a 4-pass
+// select_bins below; its kept entries come out in index order from an LDS
+// bitmap); rows it cannot take use the radix select: a 4-pass
 // MSB-first radix select (8 bits per pass) finds the k-th largest key T and
 // how many entries equal to T must be kept (need_eq). Each pass counts
 // digits into LDS histograms, one copy per wave and lane group so that the
@@ -184,6 +185,7 @@ __device__ __forceinline__ void select_topk(const Seg& seg, int32_t kk, int32_t*
 // Either way the result is the unique exact top kk.
 constexpr int BIN_BITS = 12, BINS = 1 << BIN_BITS;
 constexpr int BIN_LOADS = 8;  // keys loaded ahead per thread
+constexpr int BM_WORDS = 2048;  // kept-entry bitmap: rows of up to 65536 entries
 template <int NW, int CAND, int KEEP, bool KEYS>
 struct BinShared {
   union {
@@ -191,7 +193,10 @@ struct BinShared {
     struct {
       uint32_t ckey[CAND];
       int32_t cidx[CAND];
-      int32_t kidx[KEEP];
+      union {
+        int32_t kidx[KEEP];
+        uint32_t bm[BM_WORDS];  // bit i: entry i kept
+      };
       uint32_t kkey[KEYS ? KEEP : 1];
     } l;
   } u;
@@ -200,9 +205,12 @@ struct BinShared {
 };
 
 // raw_at(i) loads entry i < m (as 32 bits), key_of(i, raw) maps it to its
-// key, idx_at(i) gives its output index. Entries are visited in any order,
-// BIN_LOADS loads issued before their keys are formed. Writes out[0..kk)
-// ascending (and their keys to out_key when KEYS).
+// key, idx_at(i) gives its output index (distinct values in [0, m)). Entries
+// are visited in any order, BIN_LOADS loads issued before their keys are
+// formed. Writes out[0..kk) ascending (and their keys to out_key when KEYS).
+// Without keys and for rows of up to 32 * BM_WORDS entries, the kept
+// entries are marked in an LDS bitmap and written out in index order by a
+// popcount prefix sum; otherwise they are gathered and bitonic-sorted.
 template <int NW, int CAND, int KEEP, bool KEYS, class RawAt, class KeyOf, class IdxAt>
 __device__ bool select_bins(RawAt raw_at, KeyOf key_of, IdxAt idx_at, int32_t m, int32_t kk,
                             int32_t* __restrict__ out, uint32_t* __restrict__ out_key,
@@ -266,14 +274,29 @@ __device__ bool select_bins(RawAt raw_at, KeyOf key_of, IdxAt idx_at, int32_t m,
     __syncthreads();  // every thread has read the bin before LDS is reused
     return false;
   }
+  const bool use_bm = !KEYS && m <= 32 * BM_WORDS;
+  const int32_t nw = (m + 31) >> 5;
+  if (use_bm) {
+    // the bitmap may overlay the bin counts, which every thread copied to
+    // registers before the barrier above
+    for (int32_t i = tid; i < nw; i += NT) f.u.l.bm[i] = 0u;
+    __syncthreads();
+  }
+  auto keep = [&](int32_t ix, uint32_t key) {
+    if (use_bm) {
+      atomicOr(&f.u.l.bm[ix >> 5], 1u << (ix & 31));
+    } else {
+      const uint32_t p = atomicAdd(&f.n_k, 1u);
+      f.u.l.kidx[p] = ix;
+      if (KEYS) f.u.l.kkey[p] = key;
+    }
+  };
 
   // read 2: keys above bin b are kept; bin b entries become candidates
   each_key([&](int32_t i, uint32_t key) {
     const uint32_t hb = key >> (32 - BIN_BITS);
     if (hb > bin) {
-      const uint32_t p = atomicAdd(&f.n_k, 1u);
-      f.u.l.kidx[p] = idx_at(i);
-      if (KEYS) f.u.l.kkey[p] = key;
+      keep(idx_at(i), key);
     } else if (hb == bin) {
       const uint32_t p = atomicAdd(&f.n_c, 1u);
       f.u.l.ckey[p] = key;
@@ -291,11 +314,33 @@ __device__ bool select_bins(RawAt raw_at, KeyOf key_of, IdxAt idx_at, int32_t m,
       const uint32_t ke = f.u.l.ckey[e];
       rank += (ke > kc || (ke == kc && f.u.l.cidx[e] < ic)) ? 1u : 0u;
     }
-    if (rank < places) {
-      const uint32_t p = atomicAdd(&f.n_k, 1u);
-      f.u.l.kidx[p] = ic;
-      if (KEYS) f.u.l.kkey[p] = kc;
+    if (rank < places) keep(ic, kc);
+  }
+  if (use_bm) {
+    // thread t owns bitmap words [wpt t, wpt t + wpt); its set bits go out
+    // after those of the threads before it (block prefix of the popcounts)
+    __syncthreads();
+    const int32_t wpt = (nw + NT - 1) / NT, w0 = tid * wpt, w1 = min(nw, w0 + wpt);
+    uint32_t cnt = 0;
+    for (int32_t wi = w0; wi < w1; ++wi) cnt += __popc(f.u.l.bm[wi]);
+    uint32_t sc = cnt;  // inclusive prefix within the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t x = __shfl_up(sc, d);
+      if (lane >= d) sc += x;
     }
+    if (lane == 63) f.wsum[wave] = sc;
+    __syncthreads();
+    uint32_t pos = sc - cnt;
+    for (int w = 0; w < wave; ++w) pos += f.wsum[w];
+    for (int32_t wi = w0; wi < w1; ++wi) {
+      uint32_t b = f.u.l.bm[wi];
+      while (b) {
+        out[pos++] = 32 * wi + __builtin_ctz(b);
+        b &= b - 1u;
+      }
+    }
+    return true;
   }
   // ascending indices: bitonic sort of the kk kept entries, padded to a power of two
   int32_t P = 1;
