@@ -191,8 +191,9 @@ struct BinShared {
   union {
     uint32_t hist[BINS];
     struct {
-      uint32_t ckey[CAND];
-      int32_t cidx[CAND];
+      // boundary-bin candidates as (key << 32 | ~index): a larger value
+      // ranks first (larger key, then smaller index)
+      alignas(16) uint64_t cand[CAND];
       union {
         int32_t kidx[KEEP];
         uint32_t bm[BM_WORDS];  // bit i: entry i kept
@@ -299,22 +300,21 @@ __device__ bool select_bins(RawAt raw_at, KeyOf key_of, IdxAt idx_at, int32_t m,
       keep(idx_at(i), key);
     } else if (hb == bin) {
       const uint32_t p = atomicAdd(&f.n_c, 1u);
-      f.u.l.ckey[p] = key;
-      f.u.l.cidx[p] = idx_at(i);
+      f.u.l.cand[p] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)idx_at(i);
     }
   });
   __syncthreads();
   // candidate c is kept when fewer than kk - above candidates rank before it
   const uint32_t places = (uint32_t)kk - above;
   for (uint32_t c = tid; c < in_bin; c += NT) {
-    const uint32_t kc = f.u.l.ckey[c];
-    const int32_t ic = f.u.l.cidx[c];
-    uint32_t rank = 0;
-    for (uint32_t e = 0; e < in_bin; ++e) {
-      const uint32_t ke = f.u.l.ckey[e];
-      rank += (ke > kc || (ke == kc && f.u.l.cidx[e] < ic)) ? 1u : 0u;
+    const uint64_t cc = f.u.l.cand[c];
+    uint32_t rank = 0, e = 0;
+    for (; e + 1 < in_bin; e += 2) {  // two candidates per 16-byte LDS read
+      const uint64_t* pe = &f.u.l.cand[e];
+      rank += (pe[0] > cc ? 1u : 0u) + (pe[1] > cc ? 1u : 0u);
     }
-    if (rank < places) keep(ic, kc);
+    if (e < in_bin) rank += f.u.l.cand[e] > cc ? 1u : 0u;
+    if (rank < places) keep((int32_t)~(uint32_t)cc, (uint32_t)(cc >> 32));
   }
   if (use_bm) {
     // thread t owns bitmap words [wpt t, wpt t + wpt); its set bits go out
