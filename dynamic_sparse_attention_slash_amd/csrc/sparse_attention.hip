@@ -516,21 +516,23 @@ __device__ void attend_panel(const uint16_t* __restrict__ qs, const uint16_t* __
     // the MFMAs at raised wave priority (as in the single-block kernel)
     u32x4 kop[2][DS];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+    for (int s = 0; s < DS; ++s)
 #pragma unroll
-      for (int s = 0; s < DS; ++s)
+      for (int s2 = 0; s2 < 2; ++s2)
         kop[s2][s] = *reinterpret_cast<const u32x4*>(cur + koff[s] + s2 * 16 * L::ROW);
     f32x4 st[2][2];
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < 2; ++qb) st[s2][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_s_setprio(1);
+    // k-step major: the four accumulator chains interleave
 #pragma unroll
-        for (int s = 0; s < DS; ++s) acc = mfma_bf16(kop[s2][s], qop[qb][s], acc);
-        st[s2][qb] = acc;
-      }
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) st[s2][qb] = mfma_bf16(kop[s2][s], qop[qb][s], st[s2][qb]);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if ((m0 & m1) != 0xffffu || ((d0.f | d1.f) & (P_DIAG << blk))) {
@@ -914,21 +916,23 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
     // fills the gaps between them with its softmax work.
     u32x4 kop[2][DS];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+    for (int s = 0; s < DS; ++s)
 #pragma unroll
-      for (int s = 0; s < DS; ++s)
+      for (int s2 = 0; s2 < 2; ++s2)
         kop[s2][s] = *reinterpret_cast<const u32x4*>(cur + koff[s] + s2 * 16 * L::ROW);
     f32x4 st[2][2];
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < 2; ++qb) st[s2][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_s_setprio(1);
+    // k-step major: the four accumulator chains interleave
 #pragma unroll
-        for (int s = 0; s < DS; ++s) acc = mfma_bf16(kop[s2][s], qop[qb][s], acc);
-        st[s2][qb] = acc;
-      }
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) st[s2][qb] = mfma_bf16(kop[s2][s], qop[qb][s], st[s2][qb]);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if ((d[0].b | d[1].b) & F_MASK) {
