@@ -143,6 +143,10 @@ def _special_scores(rows, n, seed):
 @pytest.mark.parametrize("n,k,forced", [(100, 7, -1), (100, 7, 0), (100, 100, -1), (100, 150, 0),
                                         (1, 1, 0), (5000, 256, 0), (5000, 1, -1), (131072, 6096, 0),
                                         (131072, 1000, -1), (4097, 4096, 4096),
+                                        # one work-group per row: many kept entries written from
+                                        # the bitmap (up to its 65535-entry rows), and k above its
+                                        # 8192 kept entries (radix select)
+                                        (65535, 8192, 65534), (30000, 3000, 0), (50000, 9000, -1),
                                         # rows of 64K entries or more take the row-parallel path
                                         (200001, 1000, 200000), (300000, 6096, 0), (70000, 16384, 5),
                                         (1 << 20, 6096, 123457), (1 << 20, 1000, -1),
