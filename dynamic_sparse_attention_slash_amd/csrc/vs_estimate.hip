@@ -612,13 +612,18 @@ __global__ __launch_bounds__(256) void est_scombine_kernel(EstArgs a, int32_t nc
   const int32_t d = blockIdx.x * 256 + threadIdx.x;
   if (d >= a.seq_len) return;
   const int32_t n = a.seq_len, lq = a.lq_eff(), start = a.win_start, C = a.chunk, SACC = C + 63;
+  const int32_t cs = __builtin_ctz((uint32_t)C);  // the chunk is a power of two
   // keys of diagonal d: j in [start - d, start + lq - 1 - d] (clipped at 0)
   const int32_t j_lo = max(0, start - d), j_hi = start + lq - 1 - d;
-  float sum = 0.f;
+  // a diagonal spans lq <= 64 <= C keys: at most two chunks, both loaded
+  // before the add (in chunk order, as always)
   const float* sp = a.s_part + (size_t)row * nchunks * SACC;
-  for (int32_t c = j_lo / C; c <= j_hi / C; ++c) {
-    const int32_t e = d - (start - (c * C + C - 1));
-    sum += sp[(size_t)c * SACC + e];
+  const int32_t c0 = j_lo >> cs, c1 = j_hi >> cs;
+  float sum = 0.f;
+  if (c0 <= c1) {
+    const float x0 = sp[(size_t)c0 * SACC + d - (start - (c0 * C + C - 1))];
+    const float x1 = c1 > c0 ? sp[(size_t)c1 * SACC + d - (start - (c1 * C + C - 1))] : 0.f;
+    sum = c1 > c0 ? x0 + x1 : x0;
   }
   a.s_scores[(size_t)row * n + d] = sum;
 }
