@@ -1039,12 +1039,16 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
 // fp32 kernel (MFMA 16x16x4 f32: one k value per lane, so V needs no transpose)
 //
 // F32_WAVES waves share a query block: they fill the descriptor array
-// together (the generator's state is the same in every wave) and wave w takes
-// the sub-block pairs w, w + F32_WAVES, ...; at the end the waves' partial
-// (max, sum, O) meet in LDS and wave 0 merges them in wave order. A short
-// sequence has few query blocks, so one wave per block would leave most of
-// the chip idle; more than 256 VGPRs per wave allow one wave per SIMD, so
-// four waves per work-group.
+// together (the generator's state is the same in every wave). At D = 64 every
+// wave holds all 64 queries and wave w takes the sub-block pairs w,
+// w + F32_WAVES, ...; at D = 128 (where 64 queries of Q and O would not fit
+// the registers) waves 0 and 2 hold queries 0-31, waves 1 and 3 queries
+// 32-63, and each pair splits the sub-block pairs two ways. At the end the
+// partial (max, sum, O) of the waves of a query group meet in LDS and the
+// group's first wave merges them in wave order. A short sequence has few
+// query blocks, so one wave per block would leave most of the chip idle; more
+// than 256 VGPRs per wave allow one wave per SIMD, so four waves per
+// work-group.
 // ---------------------------------------------------------------------------
 constexpr int F32_WAVES = 4;
 template <int D, class R>
@@ -1053,17 +1057,25 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
                            int32_t r0, float scale_log2, DescGen<R> gen) {
   constexpr int DK = D / 4;   // k-steps of Q.K; lane group g holds dims DK*g .. DK*g + DK-1
   constexpr int DB = D / 16;
-  constexpr int MW = DB * 16 + 8;  // merged floats per lane: O, max, sum
+  // 16-query blocks per wave: a wave's Q and O take 2 * QPW * D / 4 VGPRs per
+  // lane, so at D = 128 the waves split the 64 queries in two halves and the
+  // keys two ways instead of four
+  constexpr int QPW = D >= 128 ? 2 : 4;
+  constexpr int QH = 4 / QPW;            // query groups of the work-group
+  constexpr int KW = F32_WAVES / QH;     // waves splitting the keys of a group
+  constexpr int MW = DB * 4 * QPW + 2 * QPW;  // merged floats per lane: max, sum, O
   __shared__ Desc desc[SB_CAP];
-  __shared__ float mbuf[(F32_WAVES - 1) * MW * 64];
+  __shared__ float mbuf[(F32_WAVES - QH) * MW * 64];
   const int32_t lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+  const int32_t qh = wave % QH, kw = wave / QH;
+  const int32_t q0 = r0 + 16 * QPW * qh;   // first query of this wave
   const int32_t* cols = gen.cols;
 
-  float qop[4][DK];
+  float qop[QPW][DK];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    int32_t row = min(r0 + 16 * qb + l16, n - 1);
+  for (int qb = 0; qb < QPW; ++qb) {
+    int32_t row = min(q0 + 16 * qb + l16, n - 1);
     const f32x4* src = reinterpret_cast<const f32x4*>(qs + (size_t)row * D + DK * g);
 #pragma unroll
     for (int s = 0; s < DK / 4; ++s) {
@@ -1071,22 +1083,23 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
       qop[qb][4 * s] = x[0]; qop[qb][4 * s + 1] = x[1]; qop[qb][4 * s + 2] = x[2]; qop[qb][4 * s + 3] = x[3];
     }
   }
-  f32x4 oacc[DB][4];
+  f32x4 oacc[DB][QPW];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[4] = {NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
-  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < QPW; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[QPW], lsum[QPW];
+#pragma unroll
+  for (int qb = 0; qb < QPW; ++qb) { m[qb] = NEG_BIG; lsum[qb] = 0.f; }
 
   while (true) {
     __syncthreads();
     const int32_t cnt = gen.fill(desc, (int32_t)threadIdx.x, 64 * F32_WAVES);
     if (cnt == 0) break;
     __syncthreads();
-    for (int32_t t = 2 * wave; t < cnt; t += 2 * F32_WAVES) {
+    for (int32_t t = 2 * kw; t < cnt; t += 2 * KW) {
       const Desc d[2] = {uniform_desc(desc, t, cnt), uniform_desc(desc, t + 1, cnt)};
-      f32x4 st[2][4];
+      f32x4 st[2][QPW];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         int32_t key = desc_key(d[s2], cols, l16, n);
@@ -1098,28 +1111,28 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
           kop[4 * s] = x[0]; kop[4 * s + 1] = x[1]; kop[4 * s + 2] = x[2]; kop[4 * s + 3] = x[3];
         }
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
+        for (int qb = 0; qb < QPW; ++qb) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < DK; ++s) acc = mfma_f32(kop[s], qop[qb][s], acc);
           st[s2][qb] = acc;
         }
       }
-      if ((d[0].b | d[1].b) & F_MASK) mask_tile<4>(st, d, cols, r0, n, lane);
-      float alpha[4];
-      if (update_max<4>(st, m, scale_log2, alpha)) {
+      if ((d[0].b | d[1].b) & F_MASK) mask_tile<QPW>(st, d, cols, q0, n, lane);
+      float alpha[QPW];
+      if (update_max<QPW>(st, m, scale_log2, alpha)) {
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
+        for (int qb = 0; qb < QPW; ++qb) {
           lsum[qb] *= alpha[qb];
 #pragma unroll
           for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha[qb];
         }
       }
-      exp_tile<4>(st, m, scale_log2);
+      exp_tile<QPW>(st, m, scale_log2);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) lsum[qb] += (st[s2][qb][0] + st[s2][qb][1]) + (st[s2][qb][2] + st[s2][qb][3]);
+        for (int qb = 0; qb < QPW; ++qb) lsum[qb] += (st[s2][qb][0] + st[s2][qb][1]) + (st[s2][qb][2] + st[s2][qb][3]);
       // O^T += V^T P^T, one MFMA per (sub-block, i): lane group g carries key
       // slot 4g + i, whose V row the lane reads at dim 16db + l16.
 #pragma unroll
@@ -1134,55 +1147,56 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
           for (int db = 0; db < DB; ++db) {
             float a = valid ? vrow[16 * db] : 0.f;
 #pragma unroll
-            for (int qb = 0; qb < 4; ++qb) oacc[db][qb] = mfma_f32(a, st[s2][qb][i], oacc[db][qb]);
+            for (int qb = 0; qb < QPW; ++qb) oacc[db][qb] = mfma_f32(a, st[s2][qb][i], oacc[db][qb]);
           }
         }
     }
   }
 
-  // Every lane's state covers the same query columns in every wave (the max
-  // is per column, the sums and O per lane), so the merge is lane by lane:
-  // element e of a lane at mbuf[(w - 1) * MW * 64 + e * 64 + lane].
-  if (wave > 0) {
-    float* dst = mbuf + (size_t)(wave - 1) * MW * 64 + lane;
+  // The waves of a query group hold the same query columns lane by lane (the
+  // max is per column, the sums and O per lane), so the merge is lane by lane:
+  // element e of a lane of wave w >= QH at mbuf[(w - QH) * MW * 64 + e * 64 + lane].
+  // Wave qh (kw = 0) merges waves qh + QH, qh + 2 QH, ... in that order.
+  if (kw > 0) {
+    float* dst = mbuf + (size_t)(wave - QH) * MW * 64 + lane;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+    for (int qb = 0; qb < QPW; ++qb) {
       dst[qb * 64] = m[qb];
-      dst[(4 + qb) * 64] = lsum[qb];
+      dst[(QPW + qb) * 64] = lsum[qb];
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
+      for (int qb = 0; qb < QPW; ++qb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(8 + 16 * db + 4 * qb + i) * 64] = oacc[db][qb][i];
+        for (int i = 0; i < 4; ++i) dst[(2 * QPW + 4 * QPW * db + 4 * qb + i) * 64] = oacc[db][qb][i];
   }
   __syncthreads();
-  if (wave > 0) return;
-  for (int32_t w = 1; w < F32_WAVES; ++w) {
-    const float* src = mbuf + (size_t)(w - 1) * MW * 64 + lane;
-    float a0[4], a1[4];
+  if (kw > 0) return;
+  for (int32_t k = 1; k < KW; ++k) {
+    const float* src = mbuf + (size_t)(qh + QH * k - QH) * MW * 64 + lane;
+    float a0[QPW], a1[QPW];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+    for (int qb = 0; qb < QPW; ++qb) {
       const float mw = src[qb * 64], mx = fmaxf(m[qb], mw);
       a0[qb] = fast_exp2(m[qb] - mx);
       a1[qb] = fast_exp2(mw - mx);
       m[qb] = mx;
-      lsum[qb] = lsum[qb] * a0[qb] + src[(4 + qb) * 64] * a1[qb];
+      lsum[qb] = lsum[qb] * a0[qb] + src[(QPW + qb) * 64] * a1[qb];
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
+      for (int qb = 0; qb < QPW; ++qb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          oacc[db][qb][i] = oacc[db][qb][i] * a0[qb] + src[(8 + 16 * db + 4 * qb + i) * 64] * a1[qb];
+          oacc[db][qb][i] = oacc[db][qb][i] * a0[qb] + src[(2 * QPW + 4 * QPW * db + 4 * qb + i) * 64] * a1[qb];
   }
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < QPW; ++qb) {
     float lt = xor_sum(xor_sum(lsum[qb], 16), 32);
     float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    int32_t row = r0 + 16 * qb + l16;
+    int32_t row = q0 + 16 * qb + l16;
     if (row < n) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)

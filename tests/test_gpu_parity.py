@@ -234,7 +234,7 @@ def test_vs_build_index(n, nv, ns, with0):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("n,D,dt,with0", [(1000, 128, "bf16", True), (64 * 5 + 3, 64, "f32", True),
                                           (777, 128, "bf16", False), (300, 64, "bf16", True),
-                                          (64 * 4, 128, "f32", False)])
+                                          (64 * 4, 128, "f32", False), (64 * 5 + 29, 128, "f32", True)])
 def test_attention_vs_given_indices(n, D, dt, with0):
     say(f"attention_vs n={n} D={D} {dt}")
     B, Hq, Hkv = 1, 4, 2
@@ -268,7 +268,7 @@ def test_attention_vs_given_indices(n, D, dt, with0):
     assert float(np.abs(oh[0, 0]).max()) == 0.0
 
 
-@pytest.mark.parametrize("n,D,dt", [(1000, 128, "bf16"), (64 * 6 + 1, 64, "f32")])
+@pytest.mark.parametrize("n,D,dt", [(1000, 128, "bf16"), (64 * 6 + 1, 64, "f32"), (64 * 6 + 40, 128, "f32")])
 def test_attention_blocks_given_indices(n, D, dt):
     say(f"attention_blocks n={n} D={D} {dt}")
     q, k, v = rand_qkv(2, 2, 1, n, D, dt, seed=3 * n)
@@ -296,15 +296,17 @@ def test_attention_blocks_given_indices(n, D, dt):
             check_attention(oh[b, h], O.assemble(ref, n, D), f"b{b} h{h}")
 
 
-def test_attention_blocks_f32_long_rows():
+@pytest.mark.parametrize("D", [64, 128])
+def test_attention_blocks_f32_long_rows(D):
     """fp32 query blocks with more than 1024 key sub-blocks: every key block up
     to the diagonal is listed, so the last query blocks of a 19211-token head
     hold up to 1201 sub-blocks, more than one refill of the descriptor array
-    that the work-group's four waves share and split. Sampled query blocks
-    (both sides of the 1024-sub-block line, the ragged last one) against the
-    oracle; every output row finite."""
-    n, D = 64 * 300 + 11, 64
-    say(f"attention_blocks f32 long rows n={n}")
+    that the work-group's four waves share (at D = 128 two waves per query
+    half split the keys). Sampled query blocks (both sides of the
+    1024-sub-block line, the ragged last one) against the oracle; every output
+    row finite."""
+    n = 64 * 300 + 11
+    say(f"attention_blocks f32 long rows n={n} D={D}")
     q, k, v = rand_qkv(1, 1, 1, n, D, "f32", seed=77)
     nb = O.num_blocks(n)
     sel = np.zeros((1, nb, nb), np.int32)
@@ -326,6 +328,7 @@ def test_attention_blocks_f32_long_rows():
 
 @pytest.mark.parametrize("n,D,dt,init,local", [(1000, 128, "bf16", 1, 2), (1000, 128, "bf16", 0, 1),
                                                (64 * 9 + 5, 64, "f32", 2, 3), (500, 128, "bf16", 3, 64),
+                                               (64 * 8 + 50, 128, "f32", 1, 3),
                                                # bf16 panels at head_dim 64: an even and an odd
                                                # block count, windows crossing panel edges
                                                (1000, 64, "bf16", 1, 3), (64 * 7 + 33, 64, "bf16", 2, 2)])
