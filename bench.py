@@ -14,7 +14,10 @@ stages, then every head's attention in one launch) and reported as
 `one_launch`.
 
 Default workload: the 1M-token Llama-3-8B-shaped mixed layer (the named
-workload that runs every step of the path); the 128K layer is timed beside it.
+workload that runs every step of the path); the other named workloads are
+timed beside it under `secondary`, each over at least 300 ms of steps
+(`timed_steps`), so that a layer of a fraction of a millisecond is not
+timed as host jitter.
 
 Per-stage times (`stages_ms`, and the after-prefill calls) time each call
 alone with HIP events after a 512 MiB write that leaves none of its inputs in
@@ -130,15 +133,21 @@ class ClockSampler:
         m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", out, re.I)
         return float(m.group(1)) if m else None
 
+    def _sample(self):
+        v = self._one()
+        if v is not None:
+            self.samples.append(v)
+
     def _run(self):
-        while not self._stop.is_set():
-            v = self._one()
-            if v is not None:
-                self.samples.append(v)
-            self._stop.wait(self.period)
+        while not self._stop.wait(self.period):
+            self._sample()
 
     def __enter__(self):
+        # The first sample is taken here, before the timed region: starting a
+        # child process from this (large) process can stall its launches for
+        # milliseconds, which a layer of a fraction of a millisecond would show.
         if ClockSampler.enabled:
+            self._sample()
             self._thr = threading.Thread(target=self._run, daemon=True)
             self._thr.start()
         return self
@@ -682,7 +691,11 @@ def committed_traffic(workload):
 
 
 # ----------------------------------------------------------------------------
-def run_layer(w, steps, warmup, with_cpu, cpu_full=False, after_prefill=True, cpu_seconds=(12.0, 5.0, 1.0)):
+def run_layer(w, steps, warmup, with_cpu, cpu_full=False, after_prefill=True, cpu_seconds=(12.0, 5.0, 1.0),
+              min_timed_ms=None):
+    """One workload's record. steps: the timed steps; with min_timed_ms, at
+    least as many as fill that many milliseconds (short layers, whose few
+    steps would otherwise time host jitter)."""
     dev = torch.device("cuda:0")
     log(f"[bench] workload {w.name}: generating inputs on {dev}")
     x = synthetic.make_inputs(w, device=dev)
@@ -698,6 +711,10 @@ def run_layer(w, steps, warmup, with_cpu, cpu_full=False, after_prefill=True, cp
     for _ in range(warmup):
         layer.step()
     torch.cuda.synchronize()
+    if min_timed_ms:
+        est = time_events(layer.step, 3)
+        steps = max(steps, int(math.ceil(min_timed_ms / max(est, 1e-3))))
+        log(f"[bench] {w.name}: {steps} timed steps (about {est:.3f} ms each)")
     s = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     with ClockSampler() as clk:
@@ -712,7 +729,7 @@ def run_layer(w, steps, warmup, with_cpu, cpu_full=False, after_prefill=True, cp
     res = {
         "ms_per_layer": ms, "tflops": f_total / (ms * 1e-3) / 1e12,
         "ms_per_layer_median": per_step[len(per_step) // 2], "ms_per_layer_min": per_step[0],
-        "dtype": w.dtype,
+        "steps": steps, "dtype": w.dtype,
         "clock_during_steps": clk.summary(),
         "flops_computed_blocks": f_total, "flops_per_pattern": flops,
         "flops_dense_causal": dense, "density_vs_dense": f_total / dense,
@@ -754,6 +771,10 @@ def run_layer(w, steps, warmup, with_cpu, cpu_full=False, after_prefill=True, cp
     return res
 
 
+# the secondary workloads are timed over at least this long (their own step
+# count, reported as timed_steps)
+SECONDARY_MIN_MS = 300.0
+
 # layers whose whole-layer oracle finishes in seconds (timed in full)
 FULL_ORACLE = ("vs_head_4k_f32", "bs_mha4_32k_bf16")
 
@@ -773,6 +794,7 @@ def layer_record(r):
         "ms_per_layer": round(r["ms_per_layer"], 4),
         "ms_per_layer_median": round(r["ms_per_layer_median"], 4),
         "ms_per_layer_min": round(r["ms_per_layer_min"], 4),
+        "timed_steps": r["steps"],
         "tflops": round(r["tflops"], 3),
         "pct_peak": round(100 * r["tflops"] / peak, 2),
         "peak_tflops": peak,
@@ -864,7 +886,8 @@ def main():
     for name in names:
         w2 = synthetic.BY_NAME[name]
         sec = run_layer(w2, args.steps, args.warmup, not args.no_cpu_baseline,
-                        cpu_full=w2.name in FULL_ORACLE, after_prefill=False, cpu_seconds=(5.0, 3.0, 1.0))
+                        cpu_full=w2.name in FULL_ORACLE, after_prefill=False, cpu_seconds=(5.0, 3.0, 1.0),
+                        min_timed_ms=SECONDARY_MIN_MS)
         rec = {"workload": w2.name, "config": workload_config(w2), "dtype": w2.dtype}
         rec.update(layer_record(sec))
         if "cpu_baseline" in sec:
