@@ -75,8 +75,8 @@ struct Tile<uint16_t, D> {
 #pragma unroll
     for (int s = 0; s < DS; ++s) k.v[s] = src[s];
   }
-  __device__ void scores_k(const KReg& k, int32_t j0, const Window& w, f32x4 (&out)[4]) const {
-    const int32_t l16 = wave_lane() & 15;
+  // unmasked scores: the MFMAs alone
+  __device__ void scores_raw(const KReg& k, f32x4 (&out)[4]) const {
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -84,7 +84,10 @@ struct Tile<uint16_t, D> {
       for (int s = 0; s < DS; ++s) acc = mfma_bf16(qop[qb][s], k.v[s], acc);
       out[qb] = acc;
     }
-    finish(out, j0, l16, w);
+  }
+  __device__ void scores_k(const KReg& k, int32_t j0, const Window& w, f32x4 (&out)[4]) const {
+    scores_raw(k, out);
+    finish(out, j0, wave_lane() & 15, w);
   }
   // mask only a step that reaches the window's first row (or a window of
   // fewer than 64 rows): earlier keys precede every window row
@@ -283,11 +286,11 @@ __device__ __forceinline__ void est_stats(const EstArgs& a) {
 
   const int32_t j_begin = chunk * C, j_end = min(a.seq_len, j_begin + C);
   const float sc = a.scale_log2;
-  auto step = [&](const f32x4 (&x)[4]) {
-    // running (max, sum) with a deferred max: d = x * scale * log2(e) - m in
-    // one FMA; the reference m is raised only when d exceeds 8 (then d = 0)
-    // one compare per step: the largest d against the margin (a v_max3 tree)
-    f32x4 d[4];
+  // running (max, sum) with a deferred max, one step in two parts. pre:
+  // d = x * scale * log2(e) - m in one FMA, and the reference m raised only
+  // where d exceeds 8 (then d = 0); one compare per step, the largest d
+  // against the margin (a v_max3 tree). post: the sums take 2^d.
+  auto pre = [&](const f32x4 (&x)[4], f32x4 (&d)[4]) {
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
@@ -308,6 +311,8 @@ __device__ __forceinline__ void est_stats(const EstArgs& a) {
             d[qb][i] = 0.f;
           }
     }
+  };
+  auto post = [&](const f32x4 (&d)[4]) {
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
@@ -321,6 +326,15 @@ __device__ __forceinline__ void est_stats(const EstArgs& a) {
     // every step issues its INSTR loads, past the chunk's end too (rows of
     // the next chunk, or zeros past the slab, into stages never read), so
     // that the wait count in ring.read is exact
+    // One step of lag: the sums of step t take their 2^d in the same basic
+    // block as the MFMAs of step t + 1, interleaved with them, so that the
+    // exponentials issue while the matrix core works. The lagged d starts
+    // at -inf, which adds exact zeros; the order of the updates is that of
+    // the steps.
+    f32x4 dp[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) dp[qb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    const int32_t l16 = wave_lane() & 15;
 #pragma unroll
     for (int u = 0; u < KR_STAGES - 1; ++u) ring.issue(j_begin + 16 * u, stage[u]);
     for (int32_t t0 = j_begin; t0 < j_end; t0 += 16 * KR_STAGES) {
@@ -333,18 +347,31 @@ __device__ __forceinline__ void est_stats(const EstArgs& a) {
           typename Tile<T, D>::KReg kc;
           ring.read(stage[u], kc);
           f32x4 x[4];
-          tile.scores_k(kc, j0, w, x);
-          step(x);
+          tile.scores_raw(kc, x);
+          post(dp);
+#pragma unroll
+          for (int r = 0; r < 4 * Tile<T, D>::DS; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+          }
+          // the sums are formed here, in the MFMAs' block (not sunk past the
+          // mask's branch)
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb) asm volatile("" ::"v"(z[qb][0]), "v"(z[qb][1]), "v"(z[qb][2]), "v"(z[qb][3]));
+          Tile<T, D>::finish(x, j0, l16, w);
+          pre(x, dp);
         }
       }
     }
+    post(dp);
     __builtin_amdgcn_s_waitcnt(0);  // no DMA into LDS outlives the loop
   } else {
     KStream<T, D> kst(tile, ks, j_begin, w);
     for (int32_t j0 = j_begin; j0 < j_end; j0 += 16) {
-      f32x4 x[4];
+      f32x4 x[4], d[4];
       kst.scores(tile, ks, j0, w, x);
-      step(x);
+      pre(x, d);
+      post(d);
     }
   }
   // merge the 16 key columns of each row (lanes with equal l >> 4)
