@@ -1038,19 +1038,17 @@ __device__ void attend_single(const uint16_t* __restrict__ qs, const uint16_t* _
 // ---------------------------------------------------------------------------
 // fp32 kernel (MFMA 16x16x4 f32: one k value per lane, so V needs no transpose)
 //
-// F32_WAVES waves share a query block: they fill the descriptor array
-// together (the generator's state is the same in every wave). At D = 64 every
-// wave holds all 64 queries and wave w takes the sub-block pairs w,
-// w + F32_WAVES, ...; at D = 128 (where 64 queries of Q and O would not fit
-// the registers) waves 0 and 2 hold queries 0-31, waves 1 and 3 queries
-// 32-63, and each pair splits the sub-block pairs two ways. At the end the
-// partial (max, sum, O) of the waves of a query group meet in LDS and the
-// group's first wave merges them in wave order. A short sequence has few
-// query blocks, so one wave per block would leave most of the chip idle; more
-// than 256 VGPRs per wave allow one wave per SIMD, so four waves per
-// work-group.
+// f32_waves(D) waves share a query block: they fill the descriptor array
+// together (the generator's state is the same in every wave). Even waves hold
+// queries 0-31, odd waves queries 32-63, and the waves of each half split the
+// sub-block pairs (wave w takes pairs w / 2, w / 2 + waves / 2, ...). At the
+// end the partial (max, sum, O) of the waves of a half meet in LDS and the
+// half's first wave merges them in wave order. A short sequence has few query
+// blocks, so one wave per block would leave most of the chip idle: at D = 64
+// a wave fits 256 VGPRs, and eight waves per work-group run two per SIMD; at
+// D = 128 a wave takes more than 256 VGPRs (one per SIMD), so four.
 // ---------------------------------------------------------------------------
-constexpr int F32_WAVES = 4;
+__host__ __device__ constexpr int f32_waves(int D) { return D >= 128 ? 4 : 8; }
 template <int D, class R>
 __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict__ ks,
                            const float* __restrict__ vs, float* __restrict__ os, int32_t n,
@@ -1058,14 +1056,14 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
   constexpr int DK = D / 4;   // k-steps of Q.K; lane group g holds dims DK*g .. DK*g + DK-1
   constexpr int DB = D / 16;
   // 16-query blocks per wave: a wave's Q and O take 2 * QPW * D / 4 VGPRs per
-  // lane, so at D = 128 the waves split the 64 queries in two halves and the
-  // keys two ways instead of four
-  constexpr int QPW = D >= 128 ? 2 : 4;
+  // lane, so the waves split the 64 queries in two halves
+  constexpr int NW = f32_waves(D);
+  constexpr int QPW = 2;
   constexpr int QH = 4 / QPW;            // query groups of the work-group
-  constexpr int KW = F32_WAVES / QH;     // waves splitting the keys of a group
+  constexpr int KW = NW / QH;            // waves splitting the keys of a group
   constexpr int MW = DB * 4 * QPW + 2 * QPW;  // merged floats per lane: max, sum, O
   __shared__ Desc desc[SB_CAP];
-  __shared__ float mbuf[(F32_WAVES - QH) * MW * 64];
+  __shared__ float mbuf[(NW - QH) * MW * 64];
   const int32_t lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
   const int32_t qh = wave % QH, kw = wave / QH;
@@ -1094,7 +1092,7 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
 
   while (true) {
     __syncthreads();
-    const int32_t cnt = gen.fill(desc, (int32_t)threadIdx.x, 64 * F32_WAVES);
+    const int32_t cnt = gen.fill(desc, (int32_t)threadIdx.x, 64 * NW);
     if (cnt == 0) break;
     __syncthreads();
     for (int32_t t = 2 * kw; t < cnt; t += 2 * KW) {
@@ -1207,7 +1205,7 @@ __device__ void attend_f32(const float* __restrict__ qs, const float* __restrict
 
 // ---------------------------------------------------------------------------
 // kernels per index mode
-// fp32: one work-group (F32_WAVES waves) per (row, query block)
+// fp32: one work-group (f32_waves(D) waves) per (row, query block)
 // bf16: one work-group (four waves) per (row, panel of two query blocks)
 // ---------------------------------------------------------------------------
 template <class R>
@@ -1245,7 +1243,7 @@ __device__ __forceinline__ int32_t num_blocks(int32_t n) { return (n + BLOCK - 1
 __device__ __forceinline__ int32_t num_panels(int32_t n) { return (num_blocks(n) + PANEL - 1) / PANEL; }
 
 template <int D>
-__global__ __launch_bounds__(64 * F32_WAVES) void attn_vs_f32_kernel(AttnArgs a, VsIndex ix) {
+__global__ __launch_bounds__(64 * f32_waves(D)) void attn_vs_f32_kernel(AttnArgs a, VsIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
   work_item(a.hm, a.wo, nb, row, blk);
@@ -1257,7 +1255,7 @@ __global__ __launch_bounds__(64 * F32_WAVES) void attn_vs_f32_kernel(AttnArgs a,
 }
 
 template <int D>
-__global__ __launch_bounds__(64 * F32_WAVES) void attn_blocks_f32_kernel(AttnArgs a, BlockIndex ix) {
+__global__ __launch_bounds__(64 * f32_waves(D)) void attn_blocks_f32_kernel(AttnArgs a, BlockIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
   work_item(a.hm, a.wo, nb, row, blk);
@@ -1267,7 +1265,7 @@ __global__ __launch_bounds__(64 * F32_WAVES) void attn_blocks_f32_kernel(AttnArg
 }
 
 template <int D>
-__global__ __launch_bounds__(64 * F32_WAVES) void attn_stream_f32_kernel(AttnArgs a, StreamIndex ix) {
+__global__ __launch_bounds__(64 * f32_waves(D)) void attn_stream_f32_kernel(AttnArgs a, StreamIndex ix) {
   const int32_t nb = num_blocks(a.seq_len);
   int32_t row, blk;
   work_item(a.hm, a.wo, nb, row, blk);
@@ -1388,7 +1386,7 @@ hipError_t launch_attention_vs(const AttnArgs& a, const VsIndex& ix, hipStream_t
                        dim3(64 * SB_WAVES), 0, s, a, ix);
   else
     hipLaunchKernelGGL(a.head_dim == 64 ? attn_vs_f32_kernel<64> : attn_vs_f32_kernel<128>, grid,
-                       dim3(64 * F32_WAVES), 0, s, a, ix);
+                       dim3(64 * f32_waves(a.head_dim)), 0, s, a, ix);
   return hipGetLastError();
 }
 
@@ -1400,7 +1398,7 @@ hipError_t launch_attention_blocks(const AttnArgs& a, const BlockIndex& ix, hipS
                        dim3(64 * SB_WAVES), 0, s, a, ix);
   else
     hipLaunchKernelGGL(a.head_dim == 64 ? attn_blocks_f32_kernel<64> : attn_blocks_f32_kernel<128>, grid,
-                       dim3(64 * F32_WAVES), 0, s, a, ix);
+                       dim3(64 * f32_waves(a.head_dim)), 0, s, a, ix);
   return hipGetLastError();
 }
 
@@ -1444,7 +1442,7 @@ hipError_t launch_attention_stream(const AttnArgs& a, const StreamIndex& ix, hip
                        dim3(64 * PANEL_WAVES), 0, s, a, ix);
   else
     hipLaunchKernelGGL(a.head_dim == 64 ? attn_stream_f32_kernel<64> : attn_stream_f32_kernel<128>, grid,
-                       dim3(64 * F32_WAVES), 0, s, a, ix);
+                       dim3(64 * f32_waves(a.head_dim)), 0, s, a, ix);
   return hipGetLastError();
 }
 
